@@ -50,7 +50,7 @@ def sdpa_brute(q, k, v, bias=None, mask=None, scale=None, is_causal=False, q_off
 
     kvl = per_b(kv_lengths, Lkv)
     kvl = [min(max(t, 0), Lkv) for t in kvl]
-    ql = per_b(q_lengths, Lq)
+    ql = [min(max(t, 0), Lq) for t in per_b(q_lengths, Lq)]
     head_list = []                       # explicit repetition of every K/V head
     for g in range(Hkv):
         head_list += [g] * (Hq // Hkv)

@@ -106,8 +106,8 @@ def sdpa(q, k, v, bias=None, mask=None, scale=None, is_causal=False, q_offset=0,
     q, k, v: float arrays (bf16 inputs are passed as their exact float values).
     bias: float [Bb][Hb][Lq][Lkv] or None. mask: bool/uint8 of the same kind or None.
     scale: None means 1/sqrt(qk_head_dim). is_causal: False, True or "bottom_right".
-    q_offset: int or [B]. kv_lengths, q_lengths: None, int or [B]; kv_lengths is clamped
-    to [0, Lkv]. ``return_weights`` also returns the weights [B][Hq][n][Lkv] (small shapes).
+    q_offset: int or [B]. kv_lengths, q_lengths: None, int or [B]; they are clamped to
+    [0, Lkv] and [0, Lq] (the pages do not say what lengths beyond the arrays mean). ``return_weights`` also returns the weights [B][Hq][n][Lkv] (small shapes).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -123,7 +123,7 @@ def sdpa(q, k, v, bias=None, mask=None, scale=None, is_causal=False, q_offset=0,
         scale = 1.0 / np.sqrt(D)
     rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
     kvl = None if kv_lengths is None else [min(max(t, 0), Lkv) for t in _per_batch(kv_lengths, B, Lkv)]
-    ql = None if q_lengths is None else _per_batch(q_lengths, B, Lq)
+    ql = None if q_lengths is None else [min(max(t, 0), Lq) for t in _per_batch(q_lengths, B, Lq)]
     offs = causal_offsets(is_causal, q_offset, kvl, ql, B, Lq, Lkv)
     if qk_norm:
         q = rms_rows(q)
