@@ -1,0 +1,198 @@
+/*
+ * sdpa.h -- C ABI of libsdpa_mi355x.so: multi-head scaled dot-product attention on MI355X (gfx950).
+ *
+ * The operation and its arguments follow the page "Neural Network primitives from NNlib.jl"
+ * (Flux documentation), section "Attention" and its "Arguments" list:
+ *
+ *     out = softmax(scale * q^T k + bias, where allowed) * v
+ *
+ * with grouped-query K/V heads, is_causal (true, or bottom-right aligned), q_offset,
+ * kv_lengths, q_lengths, an additive bias and a boolean mask that combine by AND. A query that
+ * may attend no key gets NaN ("Fused implementation" section); a query at or past q_lengths
+ * gets 0 ("Arguments": q_lengths).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are described by sdpa_tensor: dims and strides (in elements) in NNlib order,
+ *   fastest first. q/k/v/out are {head_dim, heads, seq, batch}; bias/mask are
+ *   {kv_len, q_len, heads, batch}, where a dim of size 1 broadcasts ("Arguments": bias, mask).
+ *   This is C-order [batch][seq][heads][head_dim] for contiguous q/k/v/out. Extra NNlib batch
+ *   dims are flattened into dims[3] by the caller; an unbatched array has dims[3] == 1.
+ * - All data pointers are DEVICE pointers unless stated; the caller owns every buffer. The
+ *   library never allocates, frees or retains memory, never synchronizes, and never reads a
+ *   device array on the host (the NNlib page notes, under maxlen, that such a read waits for
+ *   the device). Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is the
+ *   default stream).
+ * - Device-resident integers are not validated: kv_lengths and q_lengths are clamped to
+ *   [0, kv_len] and [0, q_len]; a negative q_offset is legal; cache rows outside the cache are
+ *   not written.
+ * - Every host-detectable error returns a status without touching the GPU; the thread-local
+ *   sdpa_last_error() tells what failed. The library is stateless and thread-safe.
+ */
+#ifndef SDPA_MI355X_H
+#define SDPA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exported entry points keep default visibility; the library builds everything else hidden. */
+#if defined(__GNUC__) || defined(__clang__)
+#define SDPA_API __attribute__((visibility("default")))
+#else
+#define SDPA_API
+#endif
+
+typedef enum {
+  SDPA_OK = 0,
+  SDPA_ERR_NULL = 1,         /* a required pointer is NULL */
+  SDPA_ERR_SHAPE = 2,        /* dims/strides disagree with the operation */
+  SDPA_ERR_DTYPE = 3,        /* a dtype the argument does not accept */
+  SDPA_ERR_UNSUPPORTED = 4,  /* legal request with no kernel (e.g. head_dim > 256) */
+  SDPA_ERR_WORKSPACE = 5,    /* workspace / storage too small */
+  SDPA_ERR_HIP = 6           /* a HIP launch failed */
+} sdpa_status;
+
+typedef enum { SDPA_F32 = 0, SDPA_BF16 = 1, SDPA_U8 = 2 } sdpa_dtype;
+
+/* "Arguments": is_causal. TRUE: query i attends keys j <= q_offset + i. BOTTOM_RIGHT: the
+ * same with q_offset = kv_len_b - q_len_b, each the given length or else the array size. */
+typedef enum { SDPA_CAUSAL_NONE = 0, SDPA_CAUSAL_TRUE = 1, SDPA_CAUSAL_BOTTOM_RIGHT = 2 } sdpa_causal;
+
+typedef struct {
+  void* data;
+  int32_t dtype;        /* sdpa_dtype */
+  int32_t reserved;
+  int64_t dims[4];      /* NNlib order, fastest first */
+  int64_t strides[4];   /* elements; q/k/v/out need strides[0] == 1 */
+} sdpa_tensor;
+
+/* Block information of a runtime boolean mask (pull request "Support dynamic masks in splash
+ * attention #25213": blocks classed empty/partial/full, only non-empty blocks visited, partial
+ * blocks stored). Filled by build_block_mask_info; every pointer points into the caller's
+ * storage. Blocks are ordered by flat index (mask batch, mask head, q-block, kv-block). */
+typedef struct {
+  int32_t mask_batch, mask_heads;   /* 1 (broadcast) or the full size */
+  int32_t q_len, kv_len;            /* mask size the info was built from */
+  int32_t n_qb, n_kb, bq, bkv;      /* block grid and block size */
+  int8_t* block_mask;               /* [mask_batch][mask_heads][n_qb][n_kb]: 0 empty, 1 partial, 2 full */
+  int32_t* mask_next;               /* same shape: partial -> index into partial_bits, else 0 */
+  int32_t* row_ptr;                 /* [mask_batch*mask_heads*n_qb + 1]: CSR row starts */
+  int32_t* data_next;               /* [row_ptr[last]]: kv-block index of each non-empty block, ascending per row */
+  uint32_t* partial_bits;           /* [n_partial][bq][bkv/32]: bit (c%32) of word r*(bkv/32)+c/32 = element (r,c); 1 = attend */
+  int32_t* n_partial;               /* device scalar */
+} sdpa_block_mask_info;
+
+/* ---------------------------------------------------------------------------------------
+ * sdpa_fwd -- attention forward ("Attention", "Arguments", "Fused implementation").
+ *
+ * q    {Dqk, Hq, Lq, B}; k {Dqk, Hkv, Lkv, B}; v {Dv, Hkv, Lkv, B}; Hq % Hkv == 0, and query head h
+ *      reads K/V head h / (Hq/Hkv) ("Attention": grouped-query attention). F32 or BF16, all three
+ *      the same dtype. out {Dv, Hq, Lq, B}, F32 or BF16. Arithmetic is fp32 (bf16 products
+ *      accumulate in fp32).
+ * bias NULL, or F32/BF16 {Lkv|1, Lq|1, Hq|1, B|1}; added to the scaled logits, not scaled.
+ * mask NULL, or U8 {Lkv|1, Lq|1, Hq|1, B|1}; nonzero = may attend.
+ * mask_info  NULL, or block info built from the mask by build_block_mask_info. When given it
+ *      replaces `mask` (which is then not read), lets the kernel skip empty blocks and skip the
+ *      element test on full blocks. Its mask_batch/mask_heads must be 1 or B/Hq and its
+ *      q_len/kv_len must be Lq/Lkv.
+ * scale  multiplier of q.k; NaN selects 1/sqrt(Dqk). 0 and negative values are legal.
+ * is_causal  sdpa_causal. q_offset: device int32 [B], or NULL to use q_offset_all.
+ * kv_lengths device int32 [B], or NULL to use kv_length_all (< 0 means none).
+ * q_lengths  device int32 [B], or NULL to use q_length_all (< 0 means none).
+ * qk_norm  0 off; 1 normalizes every q and k head vector by its RMS with eps 1e-6 before the
+ *      dot product (TensorTonic page "Static Arguments in jit", its normalisation formula).
+ * workspace  device scratch of at least sdpa_fwd_workspace_bytes(); may be NULL when that is 0.
+ * Lq == 0 does nothing. Lkv == 0 gives NaN rows.
+ * ------------------------------------------------------------------------------------- */
+SDPA_API sdpa_status sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
+                     const sdpa_tensor* bias, const sdpa_tensor* mask,
+                     const sdpa_block_mask_info* mask_info,
+                     float scale, int32_t is_causal,
+                     const int32_t* q_offset, int32_t q_offset_all,
+                     const int32_t* kv_lengths, int32_t kv_length_all,
+                     const int32_t* q_lengths, int32_t q_length_all,
+                     int32_t qk_norm,
+                     sdpa_tensor* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace sdpa_fwd needs for these shapes (0 when none). Host only. */
+SDPA_API size_t sdpa_fwd_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
+                                int32_t qk_norm);
+
+/* ---------------------------------------------------------------------------------------
+ * sdpa_decode -- one query position per sequence against a KV cache: the cached attention of
+ * the keras issue on MultiHeadAttention (its list of extensions puts cached attention first)
+ * and the decode loop of the Flax discussion on nnx.MultiHeadAttention with decode=True.
+ * Same result as sdpa_fwd with Lq == 1, is_causal = BOTTOM_RIGHT and these kv_lengths (the
+ * NNlib "Examples" show that equivalence for a cache).
+ *
+ * q {D, Hq, 1, B} BF16 or F32; k_cache, v_cache {D, Hkv, capacity, B}, same dtype;
+ * kv_lengths device int32 [B] (required): keys [0, kv_lengths[b]) are attended;
+ * out {D, Hq, 1, B} F32 or BF16. num_splits: key splits per sequence (0 = library choice);
+ * the partial results are merged by a log-sum-exp pass. workspace: at least
+ * sdpa_decode_workspace_bytes(). kv_lengths[b] == 0 gives a NaN row.
+ * ------------------------------------------------------------------------------------- */
+SDPA_API sdpa_status sdpa_decode(const sdpa_tensor* q, const sdpa_tensor* k_cache, const sdpa_tensor* v_cache,
+                        const int32_t* kv_lengths, float scale, int32_t num_splits,
+                        sdpa_tensor* out, void* workspace, size_t workspace_bytes, void* stream);
+
+SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k_cache, int32_t num_splits);
+
+/* ---------------------------------------------------------------------------------------
+ * kv_cache_update -- writes row t of k_new/v_new of batch b at cache position
+ * write_index[b] + t (keras issue: a cache-update index says where new keys/values go; Flax
+ * discussion: the cache grows one position per decode step). A bit-exact copy. Rows whose
+ * position falls outside [0, capacity) are skipped.
+ * k_cache, v_cache {D, Hkv, capacity, B}, in place; k_new, v_new {D, Hkv, T, B}; all four of one
+ * dtype (F32 or BF16). write_index device int32 [B].
+ * ------------------------------------------------------------------------------------- */
+SDPA_API sdpa_status kv_cache_update(sdpa_tensor* k_cache, sdpa_tensor* v_cache,
+                            const sdpa_tensor* k_new, const sdpa_tensor* v_new,
+                            const int32_t* write_index, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * build_block_mask_info -- block information of a runtime (device) boolean mask (pull request
+ * "Support dynamic masks in splash attention #25213"). mask U8 {Lkv, Lq, Hm|1, Bm|1};
+ * bq >= 1, bkv a multiple of 32. A block is classed by its in-range elements; bits of a ragged
+ * edge block past the mask are 0. storage: device memory of at least
+ * sdpa_block_mask_info_bytes(); info: HOST struct, filled with pointers into storage. The
+ * result is deterministic and bit-exact.
+ * ------------------------------------------------------------------------------------- */
+SDPA_API sdpa_status sdpa_block_mask_info_bytes(const sdpa_tensor* mask, int32_t bq, int32_t bkv, size_t* bytes);
+SDPA_API sdpa_status build_block_mask_info(const sdpa_tensor* mask, int32_t bq, int32_t bkv,
+                                  void* storage, size_t storage_bytes,
+                                  sdpa_block_mask_info* info, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * head_rms_norm -- per-head RMS normalisation (TensorTonic page "Static Arguments in jit"):
+ * every head vector v becomes v / sqrt(mean(v^2) + eps). x, y {Dh, H, T, B}, F32 or BF16 (same
+ * dtype); fp32 arithmetic. y may alias x.
+ * ------------------------------------------------------------------------------------- */
+SDPA_API sdpa_status head_rms_norm(const sdpa_tensor* x, sdpa_tensor* y, float eps, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * sdpa_debug_allowed_mask -- writes allowed[b][h][i][j] (U8 {Lkv, Lq, Hq, B}) as the attention
+ * kernels decide it: mask AND causal rule AND kv_lengths ("Arguments", the AND rule). For
+ * bit-exact tests of the masking logic; arguments as in sdpa_fwd.
+ * ------------------------------------------------------------------------------------- */
+SDPA_API sdpa_status sdpa_debug_allowed_mask(const sdpa_tensor* q, const sdpa_tensor* k,
+                                    const sdpa_tensor* mask, const sdpa_block_mask_info* mask_info,
+                                    int32_t is_causal, const int32_t* q_offset, int32_t q_offset_all,
+                                    const int32_t* kv_lengths, int32_t kv_length_all,
+                                    const int32_t* q_lengths, int32_t q_length_all,
+                                    sdpa_tensor* allowed, void* stream);
+
+/* Status text; detail of the last non-OK status on this thread (empty if none). */
+SDPA_API const char* sdpa_status_string(int32_t status);
+SDPA_API const char* sdpa_last_error(void);
+
+/* Library version string, e.g. "sdpa_mi355x 0.1 gfx950". */
+SDPA_API const char* sdpa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SDPA_MI355X_H */

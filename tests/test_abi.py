@@ -1,0 +1,181 @@
+"""The C ABI on the CPU: the library loads, exports every function include/sdpa.h declares,
+and rejects every host-detectable bad argument with its status before touching the GPU.
+No call here launches a kernel."""
+import ctypes
+import math
+
+import pytest
+
+import transformer_attention_sdpa_amd as sa
+from transformer_attention_sdpa_amd import _native as N
+
+FAKE = 0x1000   # a non-NULL address; validation fails before any pointer is used
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sa.load()
+
+
+def T(dims, dtype=N.SDPA_BF16, strides=None, data=FAKE):
+    """Descriptor with NNlib-order dims (fastest first); contiguous strides by default."""
+    t = N.SdpaTensor()
+    t.data = data
+    t.dtype = dtype
+    st = strides
+    if st is None:
+        st, acc = [], 1
+        for d in dims:
+            st.append(acc)
+            acc *= d
+    for i in range(4):
+        t.dims[i] = dims[i]
+        t.strides[i] = st[i]
+    return t
+
+
+def fwd(lib, q, k, v, out, bias=None, mask=None, info=None, scale=math.nan, causal=0, qk_norm=0,
+        ws=None, ws_bytes=0):
+    r = lib.sdpa_fwd(ctypes.byref(q) if q else None, ctypes.byref(k) if k else None,
+                     ctypes.byref(v) if v else None, ctypes.byref(bias) if bias else None,
+                     ctypes.byref(mask) if mask else None, ctypes.byref(info) if info else None,
+                     scale, causal, None, 0, None, -1, None, -1, qk_norm,
+                     ctypes.byref(out) if out else None, ws, ws_bytes, None)
+    return r, lib.sdpa_last_error().decode()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = sa.header_functions()
+    assert {"sdpa_fwd", "sdpa_decode", "kv_cache_update", "build_block_mask_info"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(N.PROTOTYPES), "binding prototypes and header disagree"
+
+
+def test_status_strings(lib):
+    assert lib.sdpa_status_string(0) == b"ok"
+    assert lib.sdpa_status_string(N.SDPA_ERR_SHAPE) == b"shape mismatch"
+    assert lib.sdpa_status_string(99) == b"unknown status"
+    assert b"gfx950" in lib.sdpa_version()
+
+
+def good(D=64, Hq=8, Hkv=2, Lq=5, Lkv=7, B=3, dt=N.SDPA_BF16):
+    return (T([D, Hq, Lq, B], dt), T([D, Hkv, Lkv, B], dt), T([D, Hkv, Lkv, B], dt), T([D, Hq, Lq, B], dt))
+
+
+CASES = {
+    "gqa_indivisible": (lambda: good(Hq=6, Hkv=4), N.SDPA_ERR_SHAPE, {}),
+    "qk_dim_mismatch": (lambda: (T([64, 8, 5, 3]), T([32, 2, 7, 3]), T([64, 2, 7, 3]), T([64, 8, 5, 3])),
+                        N.SDPA_ERR_SHAPE, {}),
+    "kv_len_mismatch": (lambda: (T([64, 8, 5, 3]), T([64, 2, 7, 3]), T([64, 2, 6, 3]), T([64, 8, 5, 3])),
+                        N.SDPA_ERR_SHAPE, {}),
+    "batch_mismatch": (lambda: (T([64, 8, 5, 3]), T([64, 2, 7, 2]), T([64, 2, 7, 2]), T([64, 8, 5, 3])),
+                       N.SDPA_ERR_SHAPE, {}),
+    "out_shape": (lambda: good()[:3] + (T([64, 8, 6, 3]),), N.SDPA_ERR_SHAPE, {}),
+    "inner_stride": (lambda: (T([64, 8, 5, 3], strides=[2, 128, 1024, 5120]),) + good()[1:], N.SDPA_ERR_SHAPE, {}),
+    "mixed_dtype": (lambda: (T([64, 8, 5, 3], N.SDPA_F32),) + good()[1:], N.SDPA_ERR_DTYPE, {}),
+    "u8_inputs": (lambda: good(dt=N.SDPA_U8), N.SDPA_ERR_DTYPE, {}),
+    "head_dim_too_big": (lambda: good(D=320), N.SDPA_ERR_UNSUPPORTED, {}),
+    "bad_causal": (lambda: good(), N.SDPA_ERR_SHAPE, {"causal": 3}),
+    "bad_qk_norm": (lambda: good(), N.SDPA_ERR_SHAPE, {"qk_norm": 2}),
+    "bias_bad_dim": (lambda: good(), N.SDPA_ERR_SHAPE, {"bias": T([7, 5, 4, 3])}),
+    "bias_u8": (lambda: good(), N.SDPA_ERR_DTYPE, {"bias": T([7, 5, 8, 3], N.SDPA_U8)}),
+    "mask_bf16": (lambda: good(), N.SDPA_ERR_DTYPE, {"mask": T([7, 5, 1, 1], N.SDPA_BF16)}),
+    "mask_bad_dim": (lambda: good(), N.SDPA_ERR_SHAPE, {"mask": T([7, 4, 1, 1], N.SDPA_U8)}),
+    "qk_norm_no_workspace": (lambda: good(), N.SDPA_ERR_WORKSPACE, {"qk_norm": 1}),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_fwd_validation(lib, name):
+    make, status, kw = CASES[name]
+    q, k, v, out = make()
+    r, msg = fwd(lib, q, k, v, out, **kw)
+    assert r == status, (name, r, msg)
+    assert msg, "a failing call must leave a message"
+
+
+def test_fwd_null_descriptors(lib):
+    q, k, v, out = good()
+    assert fwd(lib, None, k, v, out)[0] == N.SDPA_ERR_NULL
+    assert fwd(lib, q, k, v, None)[0] == N.SDPA_ERR_NULL
+    q0 = T([64, 8, 5, 3], data=None)
+    assert fwd(lib, q0, k, v, out)[0] == N.SDPA_ERR_NULL
+
+
+def test_fwd_empty_query_is_a_noop_without_a_gpu(lib):
+    q, k, v, out = good(Lq=0)
+    assert fwd(lib, q, k, v, out)[0] == N.SDPA_OK
+
+
+def test_mask_info_validation(lib):
+    q, k, v, out = good(Lq=300, Lkv=260)
+    info = N.BlockMaskInfoC()
+    info.mask_batch, info.mask_heads, info.q_len, info.kv_len = 1, 1, 300, 260
+    info.bq, info.bkv, info.n_qb, info.n_kb = 128, 128, 3, 3
+    for f in ("block_mask", "mask_next", "row_ptr", "data_next", "partial_bits", "n_partial"):
+        setattr(info, f, FAKE)
+    info.n_kb = 2                                        # wrong grid
+    assert fwd(lib, q, k, v, out, info=info)[0] == N.SDPA_ERR_SHAPE
+    info.n_kb = 3
+    info.kv_len = 259                                    # built for another length
+    assert fwd(lib, q, k, v, out, info=info)[0] == N.SDPA_ERR_SHAPE
+    info.kv_len = 260
+    info.mask_heads = 3                                  # neither 1 nor Hq
+    assert fwd(lib, q, k, v, out, info=info)[0] == N.SDPA_ERR_SHAPE
+
+
+def test_workspace_sizes(lib):
+    q, k, v, _ = good(D=64, Hq=8, Hkv=2, Lq=5, Lkv=7, B=3)
+    assert lib.sdpa_fwd_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0) == 0
+    assert lib.sdpa_fwd_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 1) == 3 * 7 * 2 * 4
+    qd = T([128, 32, 1, 64])
+    kc = T([128, 8, 8192, 64])
+    # 512 keys per split by default -> 16 splits; (D + 2) floats per (b, head, split)
+    assert lib.sdpa_decode_workspace_bytes(ctypes.byref(qd), ctypes.byref(kc), 0) == 64 * 32 * 16 * 130 * 4
+    assert lib.sdpa_decode_workspace_bytes(ctypes.byref(qd), ctypes.byref(kc), 4) == 64 * 32 * 4 * 130 * 4
+
+
+def test_decode_validation(lib):
+    qd, kc, vc, od = T([128, 32, 1, 4]), T([128, 8, 64, 4]), T([128, 8, 64, 4]), T([128, 32, 1, 4])
+    def call(q=qd, k=kc, v=vc, o=od, kvl=FAKE, splits=0, ws=FAKE, wsb=1 << 30):
+        return lib.sdpa_decode(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), kvl, math.nan, splits,
+                               ctypes.byref(o), ws, wsb, None)
+    assert call(kvl=None) == N.SDPA_ERR_NULL
+    assert call(q=T([128, 32, 2, 4]), o=T([128, 32, 2, 4])) == N.SDPA_ERR_SHAPE
+    assert call(splits=-1) == N.SDPA_ERR_SHAPE
+    assert call(wsb=16) == N.SDPA_ERR_WORKSPACE
+    assert call(k=T([64, 8, 64, 4])) == N.SDPA_ERR_SHAPE
+    assert call(q=T([128, 30, 1, 4]), o=T([128, 30, 1, 4])) == N.SDPA_ERR_SHAPE      # 30 % 8
+
+
+def test_kv_cache_update_validation(lib):
+    kc, vc = T([128, 8, 64, 4]), T([128, 8, 64, 4])
+    kn, vn = T([128, 8, 1, 4]), T([128, 8, 1, 4])
+    def call(a=kc, b=vc, c=kn, d=vn, wi=FAKE):
+        return lib.kv_cache_update(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c), ctypes.byref(d), wi, None)
+    assert call(wi=None) == N.SDPA_ERR_NULL
+    assert call(c=T([128, 4, 1, 4]), d=T([128, 4, 1, 4])) == N.SDPA_ERR_SHAPE
+    assert call(b=T([128, 8, 32, 4])) == N.SDPA_ERR_SHAPE
+    assert call(c=T([128, 8, 1, 4], N.SDPA_F32)) == N.SDPA_ERR_DTYPE
+
+
+def test_block_mask_info_bytes(lib):
+    m = T([8192, 8192, 1, 1], N.SDPA_U8)
+    nb = ctypes.c_size_t()
+    assert lib.sdpa_block_mask_info_bytes(ctypes.byref(m), 128, 128, ctypes.byref(nb)) == N.SDPA_OK
+    blocks = 64 * 64
+    assert nb.value >= blocks * (1 + 4 + 4) + 65 * 4 + 4 + blocks * 128 * 4 * 4
+    assert lib.sdpa_block_mask_info_bytes(ctypes.byref(m), 128, 48, ctypes.byref(nb)) == N.SDPA_ERR_SHAPE
+    assert lib.sdpa_block_mask_info_bytes(ctypes.byref(T([64, 64, 1, 1], N.SDPA_BF16)), 32, 32,
+                                          ctypes.byref(nb)) == N.SDPA_ERR_DTYPE
+    info = N.BlockMaskInfoC()
+    assert lib.build_block_mask_info(ctypes.byref(m), 128, 128, FAKE, 16, ctypes.byref(info),
+                                     None) == N.SDPA_ERR_WORKSPACE
+
+
+def test_head_rms_norm_validation(lib):
+    x = T([4, 2, 3, 1], N.SDPA_F32)
+    assert lib.head_rms_norm(ctypes.byref(x), ctypes.byref(T([4, 2, 3, 2], N.SDPA_F32)), 1e-6, None) == N.SDPA_ERR_SHAPE
+    assert lib.head_rms_norm(ctypes.byref(x), ctypes.byref(T([4, 2, 3, 1], N.SDPA_BF16)), 1e-6, None) == N.SDPA_ERR_DTYPE
+    assert lib.head_rms_norm(ctypes.byref(x), ctypes.byref(T([4, 2, 3, 1], N.SDPA_F32)), -1.0, None) == N.SDPA_ERR_SHAPE

@@ -1,0 +1,148 @@
+"""GPU parity of kv_cache_update (bit-exact), sdpa_decode (oracle tolerance) and the
+per-head RMS norm (printed examples) on MI355X."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import say, dev, assert_close
+import transformer_attention_sdpa_amd as sa
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kv_cache_update_bit_exact(lib, dtype):
+    say(f"kv_cache_update {dtype}")
+    rng = np.random.default_rng(3)
+    B, cap, H, D, T = 5, 40, 3, 24, 3
+    mk = (lambda s: workloads.f32_to_bf16(rng.standard_normal(s, dtype=np.float32))) if dtype == "bf16" \
+        else (lambda s: rng.standard_normal(s, dtype=np.float32))
+    kc, vc, kn, vn = mk((B, cap, H, D)), mk((B, cap, H, D)), mk((B, T, H, D)), mk((B, T, H, D))
+    widx = np.array([0, 37, 39, -2, 12], dtype=np.int32)        # tail rows past the cache are skipped
+    ek, ev = oracle.kv_cache_update(kc, vc, kn, vn, widx)
+    tkc, tvc = dev(kc, dtype), dev(vc, dtype)
+    sa.kv_cache_update(tkc, tvc, dev(kn, dtype), dev(vn, dtype), torch.as_tensor(widx, device="cuda"))
+    torch.cuda.synchronize()
+    view = np.uint16 if dtype == "bf16" else np.uint32
+    gk = tkc.cpu().view(torch.int16 if dtype == "bf16" else torch.int32).numpy().view(view)
+    gv = tvc.cpu().view(torch.int16 if dtype == "bf16" else torch.int32).numpy().view(view)
+    np.testing.assert_array_equal(gk, ek.view(view))
+    np.testing.assert_array_equal(gv, ev.view(view))
+
+
+def decode_case(B, Hq, Hkv, D, cap, kv_min, kv_max, base):
+    return workloads.gqa_decode(B=B, Hq=Hq, Hkv=Hkv, D=D, capacity=cap, kv_min=kv_min, kv_max=kv_max, base=base)
+
+
+def run_decode(d: workloads.Decode, num_splits=0, out_dtype=torch.float32):
+    q = dev(d.q, "bf16")
+    kc, vc = dev(d.k_cache, "bf16"), dev(d.v_cache, "bf16")
+    sa.kv_cache_update(kc, vc, dev(d.k_new, "bf16"), dev(d.v_new, "bf16"),
+                       torch.as_tensor(d.write_index, device="cuda"))
+    kvl = torch.as_tensor(d.kv_lengths, device="cuda")
+    out = sa.sdpa_decode(q, kc, vc, kvl, scale=d.scale, num_splits=num_splits, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, kc, vc
+
+
+def oracle_decode(d: workloads.Decode, batches=None):
+    kc, vc = oracle.kv_cache_update(d.k_cache, d.v_cache, d.k_new, d.v_new, d.write_index)
+    bs = range(d.q.shape[0]) if batches is None else batches
+    outs = []
+    for b in bs:
+        n = int(d.kv_lengths[b])
+        f = workloads.bf16_to_f32
+        outs.append(oracle.sdpa(f(d.q[b:b + 1]), f(kc[b:b + 1, :n]), f(vc[b:b + 1, :n]), scale=d.scale,
+                                is_causal="bottom_right")[0])
+    return np.stack(outs)
+
+
+@pytest.mark.parametrize("shape", [(4, 32, 8, 128, 700, 1, 700), (3, 8, 8, 128, 300, 60, 300),
+                                   (2, 16, 2, 128, 1000, 500, 1000), (3, 8, 2, 64, 200, 1, 200),
+                                   (2, 12, 4, 96, 150, 20, 150)])
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_decode_small(lib, shape, num_splits):
+    B, Hq, Hkv, D, cap, lo, hi = shape
+    say(f"decode {shape} splits={num_splits}")
+    d = decode_case(B, Hq, Hkv, D, cap, lo, hi, base=500 + B + Hq)
+    out, _, _ = run_decode(d, num_splits)
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()                                # the NaN-poisoned tail is never read
+    assert_close(got, oracle_decode(d), "bf16", f"decode {shape}")
+
+
+def test_decode_equals_fwd_bottom_right(lib):
+    say("decode vs fwd")
+    d = decode_case(3, 16, 4, 128, 520, 100, 520, base=601)
+    out, kc, vc = run_decode(d)
+    q = dev(d.q, "bf16")
+    kvl = torch.as_tensor(d.kv_lengths, device="cuda")
+    ref = sa.sdpa(q, kc, vc, is_causal="bottom_right", kv_lengths=kvl, scale=d.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(out.cpu().numpy(), ref.cpu().numpy(), rtol=0, atol=2e-5)
+
+
+def test_decode_zero_length_is_nan(lib):
+    say("decode zero length")
+    d = decode_case(2, 8, 2, 128, 128, 1, 128, base=602)
+    q = dev(d.q, "bf16")
+    kc, vc = dev(d.k_cache, "bf16"), dev(d.v_cache, "bf16")
+    kvl = torch.tensor([0, 5], dtype=torch.int32, device="cuda")
+    out = sa.sdpa_decode(q, kc, vc, kvl, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isnan(got[0]).all() and np.isfinite(got[1]).all()
+
+
+def test_incremental_decode_matches_causal_prefill(lib):
+    # Flax discussion: nnx.MultiHeadAttention(8, 512) decodes with a cache of 100 positions
+    # (8 heads x 64 features), the cache growing one position per step.
+    say("incremental decode 8x64, cache 100")
+    B, H, D, cap, steps = 1, 8, 64, 100, 99
+    rng = np.random.default_rng(17)
+    ks = workloads.f32_to_bf16(rng.random((B, steps, H, D), dtype=np.float32))
+    vs = workloads.f32_to_bf16(rng.random((B, steps, H, D), dtype=np.float32))
+    qs = workloads.f32_to_bf16(rng.random((B, steps, H, D), dtype=np.float32))
+    kc = torch.zeros(B, cap, H, D, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kd, vd, qd = dev(ks, "bf16"), dev(vs, "bf16"), dev(qs, "bf16")
+    outs = []
+    for t in range(steps):
+        sa.kv_cache_update(kc, vc, kd[:, t:t + 1], vd[:, t:t + 1], torch.tensor([t], dtype=torch.int32, device="cuda"))
+        outs.append(sa.sdpa_decode(qd[:, t:t + 1], kc, vc, torch.tensor([t + 1], dtype=torch.int32, device="cuda"),
+                                   out_dtype=torch.float32))
+    got = torch.cat(outs, dim=1).cpu().numpy()
+    f = workloads.bf16_to_f32
+    ref = oracle.sdpa(f(qs), f(ks), f(vs), is_causal=True)
+    assert_close(got, ref, "bf16", "incremental decode")
+
+
+def test_head_rms_norm_printed_examples(lib):
+    with open(os.path.join(HERE, "golden", "rms_norm_examples.json")) as fh:
+        g = json.load(fh)
+    for ex in g["examples"]:
+        say(f"rms norm example heads={ex['num_heads']}")
+        x = torch.tensor(ex["x"], dtype=torch.float32, device="cuda")
+        r = sa.per_head_rms_norm(x, ex["num_heads"])
+        torch.cuda.synchronize()
+        tol = g["print_resolution"] * 0.5 + 1e-6      # printed to 6 decimals, fp32 arithmetic
+        np.testing.assert_allclose(r["heads"].cpu().numpy(), np.array(ex["heads"]), rtol=0, atol=tol)
+        np.testing.assert_allclose(r["merged"].cpu().numpy(), np.array(ex["merged"]), rtol=0, atol=tol)
+
+
+def test_head_rms_norm_random_vs_oracle(lib):
+    say("rms norm random")
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((3, 5, 6, 128), dtype=np.float32) * 3
+    x[1, 2, 4] = 0.0
+    y = sa.head_rms_norm(torch.as_tensor(x, device="cuda"))
+    torch.cuda.synchronize()
+    ref = oracle.rms_rows(x)
+    np.testing.assert_allclose(y.cpu().numpy(), ref, rtol=0, atol=2e-6)
+    assert np.all(y.cpu().numpy()[1, 2, 4] == 0.0)

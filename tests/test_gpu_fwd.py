@@ -1,0 +1,205 @@
+"""GPU parity of sdpa_fwd against the fp64 oracle (MI355X only).
+
+Sizes are chosen so the oracle finishes in seconds while the kernels still see several tiles
+and a ragged tail. Every option of the NNlib "Arguments" list that the ABI exposes is covered,
+alone and combined, in fp32 and bf16, with GQA, MQA and plain multi-head layouts.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import say, dev, gpu_inputs, run_gpu, run_oracle, assert_close, per_batch
+import transformer_attention_sdpa_amd as sa
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_f32_workload(lib):
+    w = workloads.tiny_f32()
+    say("tiny_f32 B1 H2 D16 L64")
+    got = run_gpu(w).cpu().numpy()
+    assert_close(got, run_oracle(w), "f32", "tiny_f32")
+
+
+def test_nnlib_examples(lib):
+    # page "Neural Network primitives from NNlib.jl", "Examples": shapes in (head_dim, heads, seq,
+    # batch) order, inputs uniform in [0, 1) as there
+    say("nnlib examples")
+    basic = workloads.random_attention(11, 4, 20, 30, 8, 8, 16, dist="uniform")
+    assert_close(run_gpu(basic).cpu().numpy(), run_oracle(basic), "f32", "basic (16,8,20,4)")
+    gqa = workloads.random_attention(12, 4, 20, 30, 8, 2, 16, dist="uniform")
+    out = run_gpu(gqa)
+    assert tuple(out.shape) == (4, 20, 8, 16)
+    assert_close(out.cpu().numpy(), run_oracle(gqa), "f32", "gqa 8 over 2")
+    gqa.kv_lengths = np.array([12, 30, 30, 30], dtype=np.int32)
+    assert_close(run_gpu(gqa).cpu().numpy(), run_oracle(gqa), "f32", "padded kv_lengths")
+    dec = workloads.random_attention(13, 4, 3, 64, 8, 8, 16, dist="uniform")
+    dec.is_causal, dec.kv_lengths = "bottom_right", np.array([13, 23, 33, 43], dtype=np.int32)
+    a = run_gpu(dec).cpu().numpy()
+    assert_close(a, run_oracle(dec), "f32", "decode bottom_right")
+    dec.is_causal, dec.q_offset = True, np.array([10, 20, 30, 40], dtype=np.int32)
+    b = run_gpu(dec).cpu().numpy()
+    np.testing.assert_array_equal(a, b)          # the two spellings are the same call
+
+
+FEATURES = [
+    dict(),
+    dict(is_causal=True),
+    dict(is_causal=True, q_offset=[37, -5]),
+    dict(is_causal="bottom_right", kv_lengths=[150, 61]),
+    dict(kv_lengths=[129, 3]),
+    dict(bias_shape=(2, 4, 130, 150)),
+    dict(bias_shape=(1, 4, 1, 150), is_causal=True),
+    dict(bias_shape=(2, 1, 130, 1), kv_lengths=[100, 150]),
+    dict(mask_shape=(2, 4, 130, 150)),
+    dict(mask_shape=(1, 1, 130, 150), is_causal="bottom_right"),
+    dict(mask_shape=(2, 1, 130, 150), bias_shape=(1, 4, 130, 150), is_causal=True, q_offset=20,
+         kv_lengths=[140, 90]),
+    dict(qk_norm=True),
+    dict(qk_norm=True, is_causal=True, bias_shape=(2, 4, 130, 150)),
+    dict(scale=0.0),
+    dict(scale=-0.3, is_causal=True),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [16, 64, 128])
+@pytest.mark.parametrize("hkv", [4, 1])
+@pytest.mark.parametrize("case", range(len(FEATURES)))
+def test_features(lib, case, hkv, D, dtype):
+    f = dict(FEATURES[case])
+    kvl = f.pop("kv_lengths", None)
+    qo = f.pop("q_offset", 0)
+    w = workloads.random_attention(1000 + case * 7 + hkv + D, 2, 130, 150, 4, hkv, D, dtype=dtype,
+                                   bias_dtype="bf16" if dtype == "bf16" else "f32",
+                                   q_offset=np.array(qo, dtype=np.int32) if isinstance(qo, list) else qo,
+                                   kv_lengths=None if kvl is None else np.array(kvl, dtype=np.int32), **f)
+    say(f"features case={case} {FEATURES[case]} hkv={hkv} D={D} {dtype}")
+    assert_close(run_gpu(w).cpu().numpy(), run_oracle(w), dtype, f"case {case}")
+    if w.mask is not None and dtype == "bf16":
+        # the block-info path gives the same numbers as the dense mask
+        info = run_gpu(w, use_mask_info=True, bq=64, bkv=64).cpu().numpy()
+        np.testing.assert_array_equal(info, run_gpu(w).cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_value_head_dim_differs(lib, dtype):
+    w = workloads.random_attention(77, 2, 70, 90, 4, 2, 64, Dv=32, dtype=dtype, is_causal=True)
+    say(f"Dv != D {dtype}")
+    assert_close(run_gpu(w).cpu().numpy(), run_oracle(w), dtype, "dv=32")
+
+
+def test_q_lengths_zero_rows(lib):
+    w = workloads.random_attention(78, 2, 50, 60, 2, 2, 64, dtype="bf16", is_causal="bottom_right")
+    ql = np.array([20, 50], dtype=np.int32)
+    say("q_lengths")
+    got = run_gpu(w, q_lengths=ql).cpu().numpy()
+    ref = run_oracle(w, q_lengths=ql)
+    assert np.all(got[0, 20:] == 0.0)
+    assert_close(got, ref, "bf16", "q_lengths")
+
+
+def test_bf16_output(lib):
+    w = workloads.random_attention(79, 2, 200, 200, 4, 2, 128, dtype="bf16", is_causal=True)
+    say("bf16 output")
+    got = run_gpu(w, out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert_close(got, run_oracle(w), "bf16", "bf16 out")
+
+
+def test_fully_masked_rows_are_nan(lib):
+    say("fully masked rows")
+    w = workloads.random_attention(80, 2, 40, 70, 2, 1, 64, dtype="bf16", is_causal=True,
+                                   q_offset=np.array([-3, 0], dtype=np.int32))
+    got = run_gpu(w).cpu().numpy()
+    assert np.isnan(got[0, :3]).all() and np.isfinite(got[0, 3:]).all()
+    assert_close(got, run_oracle(w), "bf16", "negative offset")
+    w.kv_lengths = np.array([0, 70], dtype=np.int32)
+    got = run_gpu(w).cpu().numpy()
+    assert np.isnan(got[0]).all()
+    assert_close(got, run_oracle(w), "bf16", "kv_lengths 0")
+    w2 = workloads.random_attention(81, 1, 40, 70, 2, 2, 64, dtype="bf16", mask_shape=(1, 2, 40, 70))
+    w2.mask[0, 1, 7] = 0
+    got = run_gpu(w2).cpu().numpy()
+    assert np.isnan(got[0, 7, 1]).all()
+    assert_close(got, run_oracle(w2), "bf16", "all-false mask row")
+
+
+def test_empty_keys_and_queries(lib):
+    say("empty")
+    w = workloads.random_attention(82, 2, 5, 0, 2, 2, 64, dtype="bf16")
+    assert np.isnan(run_gpu(w).cpu().numpy()).all()
+    w = workloads.random_attention(83, 2, 0, 9, 2, 2, 64, dtype="bf16")
+    assert run_gpu(w).shape == (2, 0, 2, 64)
+
+
+def test_kv_tail_poison_is_never_read(lib):
+    # keys past kv_lengths hold NaN: the output must not see them (0 * NaN would be NaN)
+    w = workloads.random_attention(84, 2, 100, 200, 4, 2, 128, dtype="bf16", is_causal="bottom_right",
+                                   kv_lengths=np.array([77, 130], dtype=np.int32))
+    for b, n in enumerate(w.kv_lengths):
+        w.k[b, n:] = workloads.BF16_NAN_BITS
+        w.v[b, n:] = workloads.BF16_NAN_BITS
+    say("nan tail")
+    got = run_gpu(w).cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_close(got, run_oracle(w), "bf16", "nan tail")
+
+
+def test_strided_views(lib):
+    # q/k/v as views with padded strides (heads-major storage transposed into [B][L][H][D])
+    say("strided views")
+    g = torch.Generator().manual_seed(5)
+    qb = torch.randn(2, 4, 90, 64 + 8, generator=g)[..., :64]
+    kb = torch.randn(2, 2, 110, 64, generator=g)
+    vb = torch.randn(2, 2, 110, 64, generator=g)
+    q = qb.to(torch.bfloat16).cuda().transpose(1, 2)
+    k = kb.to(torch.bfloat16).cuda().transpose(1, 2)
+    v = vb.to(torch.bfloat16).cuda().transpose(1, 2)
+    out_store = torch.empty(2, 4, 90, 64, dtype=torch.float32, device="cuda")
+    out = out_store.transpose(1, 2)
+    sa.sdpa(q, k, v, is_causal=True, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa(q.float().cpu().numpy(), k.float().cpu().numpy(), v.float().cpu().numpy(), is_causal=True)
+    assert_close(out.cpu().numpy(), ref, "bf16", "strided")
+
+
+def test_bias_minus_inf_acts_as_mask(lib):
+    say("bias -inf")
+    w = workloads.random_attention(85, 1, 64, 96, 2, 2, 64, dtype="f32", bias_shape=(1, 2, 64, 96))
+    w.bias[0, :, :, 50:] = -np.inf
+    got = run_gpu(w).cpu().numpy()
+    m = np.ones((1, 1, 64, 96), dtype=np.uint8)
+    m[..., 50:] = 0
+    w2 = workloads.random_attention(85, 1, 64, 96, 2, 2, 64, dtype="f32", bias_shape=(1, 2, 64, 96))
+    w2.mask = m
+    assert_close(got, run_oracle(w2), "f32", "bias -inf vs mask")
+
+
+@pytest.mark.parametrize("variant", ["dense", "info"])
+def test_debug_allowed_mask_bit_exact(lib, variant):
+    say(f"allowed mask {variant}")
+    B, Lq, Lkv, H = 2, 77, 200, 3
+    rng = np.random.default_rng(9)
+    mask = workloads.block_sparse_mask(Lq, Lkv, 32, k=9, shape_prefix=(2, 1))
+    q = torch.zeros(B, Lq, H, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(B, Lkv, H, 64, dtype=torch.bfloat16, device="cuda")
+    md = dev(mask, "u8")
+    info = sa.build_block_mask_info(md, 32, 64) if variant == "info" else None
+    for causal, qo, kvl, ql in [(False, 0, None, None), (True, [5, -2], [150, 200], None),
+                                ("bottom_right", 0, [180, 64], [77, 50]), (True, 120, None, None)]:
+        got = sa.debug_allowed_mask(q, k, None if info else md, mask_info=info, is_causal=causal,
+                                    q_offset=per_batch(np.array(qo, dtype=np.int32)) if isinstance(qo, list) else qo,
+                                    kv_lengths=per_batch(np.array(kvl, dtype=np.int32)) if kvl else None,
+                                    q_lengths=per_batch(np.array(ql, dtype=np.int32)) if ql else None).cpu().numpy()
+        kvl_c = [min(max(x, 0), Lkv) for x in kvl] if kvl else None
+        ql_c = ql if ql else None
+        offs = oracle.causal_offsets(causal, qo, kvl_c, ql_c, B, Lq, Lkv)
+        for b in range(B):
+            for h in range(H):
+                ref = oracle.allowed_matrix(np.arange(Lq), Lkv, b, h, B, H, mask,
+                                            None if offs is None else offs[b], None if kvl_c is None else kvl_c[b])
+                np.testing.assert_array_equal(got[b, h], ref.astype(np.uint8))

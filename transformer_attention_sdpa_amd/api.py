@@ -1,0 +1,270 @@
+"""Torch-facing binding of libsdpa_mi355x.so: argument marshalling only.
+
+Tensors use the C-order layout [batch][seq][heads][head_dim] for q/k/v/out and the caches,
+and [batch][heads][q_len][kv_len] for bias/mask (size-1 dims broadcast). This is NNlib's
+column-major (head_dim, heads, seq, batch) with the dims reversed, so each descriptor passed
+to the library is the torch shape and strides read backwards. Every computation runs in the
+HIP library on the caller's current stream; nothing here computes on the host or falls back
+to another implementation.
+"""
+import ctypes
+import math
+
+import numpy as np
+import torch
+
+from . import _native as N
+
+_DTYPE = {torch.float32: N.SDPA_F32, torch.bfloat16: N.SDPA_BF16, torch.uint8: N.SDPA_U8,
+          torch.bool: N.SDPA_U8}
+_CAUSAL = {False: N.CAUSAL_NONE, None: N.CAUSAL_NONE, True: N.CAUSAL_TRUE,
+           "bottom_right": N.CAUSAL_BOTTOM_RIGHT}
+
+
+def desc(t: torch.Tensor) -> N.SdpaTensor:
+    """Descriptor of a tensor of up to 4 dims (leading dims are padded with 1)."""
+    if t.dim() > 4:
+        raise ValueError("at most 4 dims")
+    if t.dtype not in _DTYPE:
+        raise TypeError(f"dtype {t.dtype} is not accepted")
+    shape = [1] * (4 - t.dim()) + list(t.shape)
+    stride = [0] * (4 - t.dim()) + list(t.stride())
+    d = N.SdpaTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = _DTYPE[t.dtype]
+    for i in range(4):
+        d.dims[i] = shape[3 - i]
+        d.strides[i] = stride[3 - i]
+    return d
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s, ctypes.c_void_p(s.cuda_stream)
+
+
+def _per_batch_arg(x, B, device, none_value):
+    """int / None / [B] values -> (device int32 pointer or None, scalar, keep-alive tensor)."""
+    if x is None:
+        return None, none_value, None
+    if isinstance(x, (int, np.integer)):
+        return None, int(x), None
+    t = torch.as_tensor(x, dtype=torch.int32, device=device).reshape(-1)
+    if t.numel() == 1:
+        t = t.expand(B)
+    t = t.contiguous()
+    if t.numel() != B:
+        raise ValueError("per-batch argument needs one entry per batch element")
+    return t.data_ptr(), 0, t
+
+
+def _mask_u8(mask):
+    if mask is None:
+        return None
+    if mask.dtype == torch.bool:
+        return mask.view(torch.uint8)
+    if mask.dtype != torch.uint8:
+        raise TypeError("mask must be bool or uint8")
+    return mask
+
+
+class BlockMaskInfo:
+    """Block information of a runtime mask, held in one device buffer (see build_block_mask_info)."""
+
+    def __init__(self, storage: torch.Tensor, c: N.BlockMaskInfoC, mask_shape):
+        self.storage = storage
+        self.c = c
+        self.mask_shape = tuple(mask_shape)
+
+    @property
+    def n_blocks(self):
+        c = self.c
+        return c.mask_batch * c.mask_heads * c.n_qb * c.n_kb
+
+    def _view(self, ptr, count, dtype):
+        base = self.storage.data_ptr()
+        off = ptr - base
+        nbytes = count * torch.empty((), dtype=dtype).element_size()
+        return self.storage[off:off + nbytes].view(dtype)
+
+    def to_numpy(self) -> dict:
+        """Copy the info to the host (synchronizes): the layout of ``oracle.block_mask_info``."""
+        c = self.c
+        shape = (c.mask_batch, c.mask_heads, c.n_qb, c.n_kb)
+        nb = self.n_blocks
+        nrows = c.mask_batch * c.mask_heads * c.n_qb
+        row_ptr = self._view(c.row_ptr, nrows + 1, torch.int32).cpu().numpy()
+        n_partial = int(self._view(c.n_partial, 1, torch.int32).cpu().item())
+        words = c.bkv // 32
+        return {
+            "block_mask": self._view(c.block_mask, nb, torch.int8).cpu().numpy().reshape(shape),
+            "mask_next": self._view(c.mask_next, nb, torch.int32).cpu().numpy().reshape(shape),
+            "row_ptr": row_ptr,
+            "data_next": self._view(c.data_next, int(row_ptr[-1]), torch.int32).cpu().numpy(),
+            "partial_bits": self._view(c.partial_bits, n_partial * c.bq * words, torch.int32)
+                                .cpu().numpy().view(np.uint32).reshape(n_partial, c.bq, words),
+            "n_partial": n_partial, "n_qb": c.n_qb, "n_kb": c.n_kb,
+        }
+
+
+def build_block_mask_info(mask: torch.Tensor, bq: int = 128, bkv: int = 128, stream=None) -> BlockMaskInfo:
+    """Block info of a runtime device mask [Mb][Mh][Lq][Lkv] (bool or uint8)."""
+    lib = N.load()
+    m = _mask_u8(mask)
+    dm = desc(m)
+    nbytes = ctypes.c_size_t()
+    N.check(lib.sdpa_block_mask_info_bytes(ctypes.byref(dm), bq, bkv, ctypes.byref(nbytes)))
+    storage = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=mask.device)
+    info = N.BlockMaskInfoC()
+    s, sp = _stream(stream)
+    N.check(lib.build_block_mask_info(ctypes.byref(dm), bq, bkv, ctypes.c_void_p(storage.data_ptr()),
+                                      storage.numel(), ctypes.byref(info), sp))
+    if stream is not None:
+        storage.record_stream(s)
+    return BlockMaskInfo(storage, info, m.shape)
+
+
+def sdpa(q, k, v, bias=None, mask=None, *, mask_info: BlockMaskInfo = None, scale=None, is_causal=False,
+         q_offset=0, kv_lengths=None, q_lengths=None, qk_norm=False, out=None, out_dtype=None, stream=None):
+    """Scaled dot-product attention. q [B][Lq][Hq][D], k [B][Lkv][Hkv][D], v [B][Lkv][Hkv][Dv].
+
+    is_causal: False, True or "bottom_right". q_offset, kv_lengths, q_lengths: int, None or a
+    [B] int32 tensor on the device. scale: None = 1/sqrt(D). Returns out [B][Lq][Hq][Dv].
+    """
+    lib = N.load()
+    B, Lq, Hq, _ = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, Lq, Hq, Dv), dtype=out_dtype or q.dtype, device=q.device)
+    dq, dk, dv, do = desc(q), desc(k), desc(v), desc(out)
+    db = desc(bias) if bias is not None else None
+    m = _mask_u8(mask) if mask_info is None else None
+    dm = desc(m) if m is not None else None
+    qo_ptr, qo_all, qo_keep = _per_batch_arg(q_offset, B, q.device, 0)
+    kv_ptr, kv_all, kv_keep = _per_batch_arg(kv_lengths, B, q.device, -1)
+    ql_ptr, ql_all, ql_keep = _per_batch_arg(q_lengths, B, q.device, -1)
+    ws_bytes = lib.sdpa_fwd_workspace_bytes(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(bool(qk_norm)))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    s, sp = _stream(stream)
+    st = lib.sdpa_fwd(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                      ctypes.byref(db) if db is not None else None,
+                      ctypes.byref(dm) if dm is not None else None,
+                      ctypes.byref(mask_info.c) if mask_info is not None else None,
+                      float("nan") if scale is None else float(scale), _CAUSAL[is_causal],
+                      qo_ptr, qo_all, kv_ptr, kv_all, ql_ptr, ql_all, int(bool(qk_norm)),
+                      ctypes.byref(do), ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
+                      ws_bytes, sp)
+    N.check(st)
+    if stream is not None:
+        for t in (ws, qo_keep, kv_keep, ql_keep):
+            if t is not None:
+                t.record_stream(s)
+    return out
+
+
+def decode_workspace_bytes(q, k_cache, num_splits=0) -> int:
+    lib = N.load()
+    dq, dk = desc(q), desc(k_cache)
+    return int(lib.sdpa_decode_workspace_bytes(ctypes.byref(dq), ctypes.byref(dk), int(num_splits)))
+
+
+def sdpa_decode(q, k_cache, v_cache, kv_lengths, *, scale=None, num_splits=0, out=None, out_dtype=None,
+                workspace=None, stream=None):
+    """One query per sequence: q [B][1][Hq][D] against caches [B][cap][Hkv][D], keys [0, kv_lengths[b])."""
+    lib = N.load()
+    B, _, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, 1, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    dq, dk, dv, do = desc(q), desc(k_cache), desc(v_cache), desc(out)
+    kv = torch.as_tensor(kv_lengths, dtype=torch.int32, device=q.device).contiguous()
+    need = int(lib.sdpa_decode_workspace_bytes(ctypes.byref(dq), ctypes.byref(dk), int(num_splits)))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    s, sp = _stream(stream)
+    N.check(lib.sdpa_decode(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.c_void_p(kv.data_ptr()),
+                            float("nan") if scale is None else float(scale), int(num_splits), ctypes.byref(do),
+                            ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), sp))
+    if stream is not None:
+        ws.record_stream(s)
+        kv.record_stream(s)
+    return out
+
+
+def kv_cache_update(k_cache, v_cache, k_new, v_new, write_index, stream=None):
+    """In place: cache[b][write_index[b] + t] = new[b][t] for k and v (rows outside the cache skipped)."""
+    lib = N.load()
+    B = k_cache.shape[0]
+    wi = torch.as_tensor(write_index, dtype=torch.int32, device=k_cache.device).contiguous()
+    if wi.numel() != B:
+        raise ValueError("write_index needs one entry per batch element")
+    dkc, dvc, dkn, dvn = desc(k_cache), desc(v_cache), desc(k_new), desc(v_new)
+    s, sp = _stream(stream)
+    N.check(lib.kv_cache_update(ctypes.byref(dkc), ctypes.byref(dvc), ctypes.byref(dkn), ctypes.byref(dvn),
+                                ctypes.c_void_p(wi.data_ptr()), sp))
+    if stream is not None:
+        wi.record_stream(s)
+    return k_cache, v_cache
+
+
+def head_rms_norm(x, eps=1e-6, out=None, stream=None):
+    """x [B][T][H][Dh] -> every head vector divided by sqrt(mean(v^2) + eps)."""
+    lib = N.load()
+    y = torch.empty_like(x) if out is None else out
+    dx, dy = desc(x), desc(y)
+    _, sp = _stream(stream)
+    N.check(lib.head_rms_norm(ctypes.byref(dx), ctypes.byref(dy), float(eps), sp))
+    return y
+
+
+def per_head_rms_norm(x, num_heads: int, eps=1e-6) -> dict:
+    """The per-head RMS norm of the TensorTonic page "Static Arguments in jit": x (B, T, D) ->
+    {"heads": (B, H, T, D/H), "merged": (B, T, D)}. The GPU computes the merged array; "heads" is
+    a view of it with the head and token axes swapped."""
+    B, T, D = x.shape
+    if D % num_heads:
+        raise ValueError("num_heads must divide D")
+    merged = head_rms_norm(x.reshape(B, T, num_heads, D // num_heads), eps).reshape(B, T, D)
+    heads = merged.view(B, T, num_heads, D // num_heads).transpose(1, 2)
+    return {"heads": heads, "merged": merged}
+
+
+def debug_allowed_mask(q, k, mask=None, *, mask_info=None, is_causal=False, q_offset=0, kv_lengths=None,
+                       q_lengths=None, stream=None):
+    """uint8 [B][Hq][Lq][Lkv]: 1 where the kernels let query i attend key j."""
+    lib = N.load()
+    B, Lq, Hq, _ = q.shape
+    Lkv = k.shape[1]
+    allowed = torch.empty((B, Hq, Lq, Lkv), dtype=torch.uint8, device=q.device)
+    dq, dk, da = desc(q), desc(k), desc(allowed)
+    m = _mask_u8(mask) if mask_info is None else None
+    dm = desc(m) if m is not None else None
+    qo_ptr, qo_all, _k1 = _per_batch_arg(q_offset, B, q.device, 0)
+    kv_ptr, kv_all, _k2 = _per_batch_arg(kv_lengths, B, q.device, -1)
+    ql_ptr, ql_all, _k3 = _per_batch_arg(q_lengths, B, q.device, -1)
+    _, sp = _stream(stream)
+    N.check(lib.sdpa_debug_allowed_mask(ctypes.byref(dq), ctypes.byref(dk),
+                                        ctypes.byref(dm) if dm is not None else None,
+                                        ctypes.byref(mask_info.c) if mask_info is not None else None,
+                                        _CAUSAL[is_causal], qo_ptr, qo_all, kv_ptr, kv_all, ql_ptr, ql_all,
+                                        ctypes.byref(da), sp))
+    return allowed
+
+
+def from_numpy(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Host array -> device tensor: ``dtype`` "bf16" takes uint16 bit patterns, "f32" float32,
+    "u8" uint8, "i32" int32 (a bit copy, no arithmetic)."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    elif dtype == "u8":
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8))
+    elif dtype == "i32":
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32))
+    else:
+        raise ValueError(dtype)
+    return t.to(device)
+
+
+def to_numpy_f32(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> float32 numpy (bf16 widened exactly; a copy, no other arithmetic)."""
+    return t.detach().float().cpu().numpy()

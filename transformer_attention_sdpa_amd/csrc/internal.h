@@ -1,0 +1,102 @@
+// internal.h -- argument blocks and launchers shared between the C-ABI layer (api.hip) and the
+// kernel files. Not installed; the public interface is include/sdpa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "sdpa.h"
+
+namespace sdpa {
+
+// Everything an attention kernel reads, resolved on the host from the sdpa_tensor descriptors.
+// Strides are in elements; head_dim has stride 1 for q/k/v/out. Broadcast dims of bias/mask
+// carry stride 0.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int B, Lq, Lkv, Hq, Hkv, D, Dv;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int in_dtype, out_dtype;
+
+  const void* bias;            // nullptr: no bias
+  int bias_dtype;
+  int64_t bias_sb, bias_sh, bias_sq, bias_sk;
+
+  const uint8_t* mask;         // dense mask (nullptr: none, or block info in use)
+  int64_t mask_sb, mask_sh, mask_sq, mask_sk;
+
+  const int8_t* bm_class;      // block mask info (nullptr: none)
+  const int32_t* bm_next;
+  const int32_t* bm_row_ptr;
+  const int32_t* bm_data_next;
+  const uint32_t* bm_bits;
+  int bm_batch, bm_heads, bm_nqb, bm_nkb, bm_bq, bm_bkv;
+
+  float scale;
+  int causal;                  // sdpa_causal
+  const int32_t* q_offset;     int q_offset_all;
+  const int32_t* kv_lengths;   int kv_length_all;   // < 0: none
+  const int32_t* q_lengths;    int q_length_all;    // < 0: none
+  int qk_norm;
+  const float* k_rinv;         // [B][Lkv][Hkv]: 1/rms of each key head vector (qk_norm only)
+};
+
+struct DecodeArgs {
+  const void* q;               // [B][1][Hq][D]
+  const void* k;               // [B][cap][Hkv][D]
+  const void* v;
+  void* out;                   // [B][1][Hq][D]
+  int B, Hq, Hkv, D, cap;
+  int64_t q_sb, q_sh, k_sb, k_ss, k_sh, v_sb, v_ss, v_sh, o_sb, o_sh;
+  int out_dtype;
+  const int32_t* kv_lengths;
+  float scale_log2;            // scale * log2(e)
+  int split_len, max_splits;
+  float* part_o;               // [B][Hq][max_splits][D]
+  float* part_ml;              // [B][Hq][max_splits][2]: running max (log2 units), sum
+};
+
+struct MaskInfoArgs {
+  const uint8_t* mask;
+  int64_t sb, sh, sq, sk;
+  int Mb, Mh, Lq, Lkv, bq, bkv, n_qb, n_kb;
+  int8_t* cls;
+  int32_t* next;
+  int32_t* row_ptr;
+  int32_t* data_next;
+  uint32_t* bits;
+  int32_t* n_partial;
+};
+
+constexpr float kRmsEps = 1e-6f;
+
+// Launchers (each returns hipSuccess or the launch error).
+hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t s);
+bool fwd_mfma_supports(const AttnArgs& a);
+hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t s);
+hipError_t launch_row_rinv(const void* x, int dtype, int64_t sb, int64_t ss, int64_t sh, int B, int L,
+                           int H, int D, float eps, float* rinv, hipStream_t s);
+hipError_t launch_head_rms_norm(const void* x, void* y, int dtype, int64_t xsb, int64_t xss, int64_t xsh,
+                                int64_t ysb, int64_t yss, int64_t ysh, int B, int T, int H, int Dh,
+                                float eps, hipStream_t s);
+bool decode_fast_supports(const DecodeArgs& a, int in_dtype);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_kv_cache_update(void* kc, void* vc, const void* kn, const void* vn, int elem_bytes,
+                                  int B, int T, int H, int D, int cap,
+                                  int64_t kc_sb, int64_t kc_ss, int64_t kc_sh,
+                                  int64_t vc_sb, int64_t vc_ss, int64_t vc_sh,
+                                  int64_t kn_sb, int64_t kn_ss, int64_t kn_sh,
+                                  int64_t vn_sb, int64_t vn_ss, int64_t vn_sh,
+                                  const int32_t* write_index, hipStream_t s);
+hipError_t launch_mask_info(const MaskInfoArgs& m, hipStream_t s);
+hipError_t launch_debug_allowed(const AttnArgs& a, uint8_t* out, int64_t sb, int64_t sh, int64_t sq,
+                                int64_t sk, hipStream_t s);
+
+}  // namespace sdpa
