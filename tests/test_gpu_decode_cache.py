@@ -85,7 +85,10 @@ def test_decode_equals_fwd_bottom_right(lib):
     kvl = torch.as_tensor(d.kv_lengths, device="cuda")
     ref = sa.sdpa(q, kc, vc, is_causal="bottom_right", kv_lengths=kvl, scale=d.scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    np.testing.assert_allclose(out.cpu().numpy(), ref.cpu().numpy(), rtol=0, atol=2e-5)
+    # same operation; the forward kernel rounds P to bf16 for the matrix cores, decode keeps it in
+    # fp32, so the two agree to the bf16 bar rather than bit for bit
+    assert_close(out.cpu().numpy(), ref.cpu().numpy(), "bf16", "decode vs fwd")
+    assert_close(out.cpu().numpy(), oracle_decode(d), "bf16", "decode vs oracle")
 
 
 def test_decode_zero_length_is_nan(lib):

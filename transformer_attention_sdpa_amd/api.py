@@ -28,7 +28,13 @@ def desc(t: torch.Tensor) -> N.SdpaTensor:
     if t.dtype not in _DTYPE:
         raise TypeError(f"dtype {t.dtype} is not accepted")
     shape = [1] * (4 - t.dim()) + list(t.shape)
-    stride = [0] * (4 - t.dim()) + list(t.stride())
+    if t.numel() == 0:                      # no element is addressed: report contiguous strides
+        stride, acc = [0] * 4, 1
+        for i in range(3, -1, -1):
+            stride[i] = acc
+            acc *= max(shape[i], 1)
+    else:
+        stride = [0] * (4 - t.dim()) + list(t.stride())
     d = N.SdpaTensor()
     d.data = t.data_ptr() if t.numel() > 0 else None
     d.dtype = _DTYPE[t.dtype]

@@ -1,17 +1,485 @@
-// fwd_mfma.hip -- bf16 attention forward on the gfx950 matrix cores (in progress).
+// fwd_mfma.hip -- bf16 attention forward on the gfx950 matrix cores (head dims 64 and 128).
+//
+// What it computes is the "Fused implementation" of the page "Neural Network primitives from
+// NNlib.jl": the output is built tile by tile with the softmax taken online over tiles of keys,
+// so the weights are never materialized. Every option of that page's "Arguments" list that the
+// ABI exposes is honoured: GQA, causal (top-left with q_offset, or bottom-right), kv_lengths,
+// q_lengths, an additive bias and a boolean mask (dense, or as block info from
+// build_block_mask_info so that empty blocks are never visited and full blocks skip the element
+// test -- the block-sparse scheme of the splash-attention pull request "Support dynamic masks in
+// splash attention #25213").
+//
+// Mapping onto CDNA4
+// ------------------
+// * One workgroup = 4 waves = a tile of 128 query rows of one (batch, head); each wave owns 32
+//   rows. The workgroup streams tiles of 64 keys of the matching K/V head through LDS, double
+//   buffered: the global loads of tile t+1 are issued before tile t is consumed.
+// * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16
+//   head-dim values from LDS, B = the wave's Q^T kept in registers for the whole loop). K rows are
+//   written to LDS in a permuted order so that the 16 accumulator entries a lane receives are 16
+//   consecutive keys of one query row. That makes every row reduction mostly in-lane (one swap
+//   with lane^32) and lets the probabilities P^T feed the next MFMA directly as its B operand, in
+//   registers, with no LDS round trip.
+// * O^T += V^T P^T with the same instruction; V is transposed into LDS while being staged
+//   (pairs of keys packed into one 32-bit LDS word).
+// * The online softmax runs in the exp2 domain: logits are multiplied by scale*log2(e) (and the
+//   bias by log2(e)), so each probability costs one v_exp_f32. A row that has seen no allowed key
+//   keeps m = -inf and contributes nothing; if it ends with l = 0 it is written as NaN
+//   ("Fused implementation": a query that attends no key).
+// * Element masking (causal, kv_lengths, mask) is applied only on tiles that need it; tiles past
+//   a wave's causal limit are skipped by that wave, tiles past the workgroup's limit are not
+//   loaded. Keys past kv_lengths are loaded as zeros, so a poisoned cache tail never reaches
+//   the arithmetic (0 * NaN would).
+// * Grid: q tiles fastest (heaviest causal tile first), then heads, then batch, remapped so that
+//   the workgroups sharing one K/V head land on the same XCD (the hardware deals consecutive
+//   workgroups round-robin over the 8 XCDs; each XCD has its own L2).
 #include "device_common.h"
 
 namespace sdpa {
 
-bool fwd_mfma_supports(const AttnArgs& a) {
-  (void)a;
-  return false;
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr int BM = 128;            // query rows per workgroup
+constexpr int BN = 64;             // keys per tile
+constexpr int NT = 256;            // threads per workgroup
+constexpr int VP = BN + 8;         // V^T row pitch in LDS (bf16): 144 bytes
+constexpr float LOG2E = 1.4426950408889634f;
+
+enum { BIAS_NONE = 0, BIAS_BF16 = 1, BIAS_F32 = 2 };
+enum { MASK_NONE = 0, MASK_DENSE = 1, MASK_INFO = 2 };
+
+// LDS row holding key k (0..31) of a 32-key block: inverse of the A-row -> key permutation that
+// makes accumulator entry 4*i + j of lane half h hold key 16*h + 4*i + j.
+__device__ __forceinline__ int k_lds_row(int k) { return 8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3); }
+
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+template <int D>
+struct Smem {
+  static constexpr int KP = D + 8;                       // K row pitch (bf16)
+  static constexpr int K_ELEMS = BN * KP;
+  static constexpr int V_ELEMS = D * VP;
+  static constexpr int STAGE = K_ELEMS + V_ELEMS;        // bf16 elements per stage
+  static constexpr int BYTES = 2 * STAGE * 2 + 2 * BN * 4;
+};
+
+template <int D, int BIAS, int MASK>
+__global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, int remap) {
+  using S = Smem<D>;
+  constexpr int KP = S::KP;
+  constexpr int DC = D / 16;         // 16-wide head-dim chunks (MFMA k steps for q.k)
+  constexpr int DB = D / 32;         // 32-row blocks of O^T
+  constexpr int KCH = BN * (D / 8) / NT;   // 16-byte K chunks per thread per tile
+  constexpr int VIT = 32 * (D / 8) / NT;   // (key pair, chunk) V items per thread per tile
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem_raw);
+  float* krv_lds = reinterpret_cast<float*>(smem_raw + 2 * S::STAGE * 2);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ql = lane & 31, hh = lane >> 5;
+
+  int n = blockIdx.x;
+  if (remap) {
+    const int per = gridDim.x >> 3;
+    n = (n & 7) * per + (n >> 3);
+  }
+  const int qt = n_qt - 1 - (n % n_qt);
+  const int h = (n / n_qt) % a.Hq;
+  const int b = n / (n_qt * a.Hq);
+  const int q0 = qt * BM;
+  const int g = h / (a.Hq / a.Hkv);
+  const int nkv = batch_kv_len(a, b);
+  const int nq = batch_q_len(a, b);
+  const int64_t off = batch_causal_offset(a, b);
+  const bool causal = a.causal != SDPA_CAUSAL_NONE;
+
+  const int i_me = q0 + 32 * wave + ql;                  // this lane's query row
+  const int row_end = min(q0 + BM, nq);                  // rows below this produce attention output
+  const int wave_first = q0 + 32 * wave;
+  const int wave_last = min(wave_first + 31, row_end - 1);
+
+  // key limit of the workgroup and of this wave
+  int64_t k_end = nkv;
+  if (causal) { const int64_t lim = off + (int64_t)(row_end - 1) + 1; if (lim < k_end) k_end = lim; }
+  if (row_end <= q0) k_end = 0;
+  if (k_end < 0) k_end = 0;
+  int64_t k_end_w = nkv;
+  if (causal) { const int64_t lim = off + (int64_t)wave_last + 1; if (lim < k_end_w) k_end_w = lim; }
+  if (wave_last < wave_first) k_end_w = 0;
+  if (k_end_w < 0) k_end_w = 0;
+
+  // tiles to visit: all tiles below k_end, or the non-empty blocks of the mask info
+  int n_tiles = 0, csr_begin = 0, sub_per_blk = 1;
+  int64_t info_row = 0;
+  if constexpr (MASK == MASK_INFO) {
+    const int mb = a.bm_batch > 1 ? b : 0, mh = a.bm_heads > 1 ? h : 0;
+    info_row = ((int64_t)mb * a.bm_heads + mh) * a.bm_nqb + qt;
+    csr_begin = a.bm_row_ptr[info_row];
+    const int csr_end = a.bm_row_ptr[info_row + 1];
+    sub_per_blk = a.bm_bkv / BN;
+    int cnt = 0;
+    for (int e = csr_begin; e < csr_end; ++e) {
+      if ((int64_t)a.bm_data_next[e] * a.bm_bkv >= k_end) break;   // ascending: the rest lie past k_end
+      ++cnt;
+    }
+    n_tiles = cnt * sub_per_blk;
+  } else {
+    n_tiles = (int)((k_end + BN - 1) / BN);
+  }
+  auto tile_k0 = [&](int t) -> int {
+    if constexpr (MASK == MASK_INFO) return a.bm_data_next[csr_begin + t / sub_per_blk] * a.bm_bkv + (t % sub_per_blk) * BN;
+    else return t * BN;
+  };
+
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + g * a.k_sh;
+  const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + g * a.v_sh;
+
+  // ---- Q^T operand (stays in registers) -------------------------------------------------
+  bf16x8 qB[DC];
+  float c_lane = a.scale * LOG2E;
+  {
+    const bool ok = i_me < a.Lq;
+    const uint16_t* qrow = qp + b * a.q_sb + (int64_t)(ok ? i_me : 0) * a.q_ss + h * a.q_sh;
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      uint4 x = ok ? *reinterpret_cast<const uint4*>(qrow + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
+      qB[c] = __builtin_bit_cast(bf16x8, x);
+      if (a.qk_norm) {
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float lo = __uint_as_float(w[t] << 16), hi = __uint_as_float(w[t] & 0xffff0000u);
+          ss += lo * lo + hi * hi;
+        }
+      }
+    }
+    if (a.qk_norm) {
+      ss += __shfl_xor(ss, 32, 64);
+      c_lane *= 1.0f / sqrtf(ss / D + kRmsEps);
+    }
+  }
+
+  // ---- staging of one K/V tile: global -> registers -> LDS --------------------------------
+  uint4 kr[KCH], vr0[VIT], vr1[VIT];
+  float krv = 0.f;
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int c = tid + NT * u;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int j = k0 + row;
+      kr[u] = j < nkv ? *reinterpret_cast<const uint4*>(kp + (int64_t)j * a.k_ss + col) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < VIT; ++u) {
+      const int it = tid + NT * u;
+      const int pr = it & 31, col = (it >> 5) * 8;
+      const int j = k0 + 2 * pr;
+      vr0[u] = j < nkv ? *reinterpret_cast<const uint4*>(vp + (int64_t)j * a.v_ss + col) : make_uint4(0, 0, 0, 0);
+      vr1[u] = j + 1 < nkv ? *reinterpret_cast<const uint4*>(vp + (int64_t)(j + 1) * a.v_ss + col)
+                           : make_uint4(0, 0, 0, 0);
+    }
+    if (a.qk_norm && tid < BN) {
+      const int j = k0 + tid;
+      krv = j < nkv ? a.k_rinv[((int64_t)b * a.Lkv + j) * a.Hkv + g] : 0.f;
+    }
+  };
+  auto sstore = [&](int stage) {
+    uint16_t* ks = lds + stage * S::STAGE;
+    uint16_t* vt = ks + S::K_ELEMS;
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int c = tid + NT * u;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int lrow = (row & ~31) + k_lds_row(row & 31);
+      *reinterpret_cast<uint4*>(ks + lrow * KP + col) = kr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VIT; ++u) {
+      const int it = tid + NT * u;
+      const int pr = it & 31, col = (it >> 5) * 8;
+      const uint32_t w0[4] = {vr0[u].x, vr0[u].y, vr0[u].z, vr0[u].w};
+      const uint32_t w1[4] = {vr1[u].x, vr1[u].y, vr1[u].z, vr1[u].w};
+      uint32_t* dst = reinterpret_cast<uint32_t*>(vt + col * VP) + pr;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        dst[(2 * t) * (VP / 2)] = pack_lo(w0[t], w1[t]);
+        dst[(2 * t + 1) * (VP / 2)] = pack_hi(w0[t], w1[t]);
+      }
+    }
+    if (a.qk_norm && tid < BN) krv_lds[stage * BN + tid] = krv;
+  };
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int64_t bias_row = (BIAS != BIAS_NONE && i_me < a.Lq)
+                               ? b * a.bias_sb + h * a.bias_sh + (int64_t)i_me * a.bias_sq : -1;
+  const int64_t mask_row = (MASK == MASK_DENSE && i_me < a.Lq)
+                               ? b * a.mask_sb + h * a.mask_sh + (int64_t)i_me * a.mask_sq : -1;
+
+  if (n_tiles > 0) {
+    gload(tile_k0(0));
+    sstore(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int stage = t & 1;
+    const int k0 = tile_k0(t);
+    if (t + 1 < n_tiles) gload(tile_k0(t + 1));
+
+    if (k0 < k_end_w) {
+      const uint16_t* ks = lds + stage * S::STAGE;
+      const uint16_t* vt = ks + S::K_ELEMS;
+
+      // -- S^T = K Q^T for two 32-key blocks -----------------------------------------------
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (32 * kb + ql) * KP + 16 * c + 8 * hh);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qB[c], s[kb], 0, 0, 0);
+        }
+      }
+
+      // -- logits in the exp2 domain, bias, masking ---------------------------------------
+      // lane (ql, hh) holds, in s[kb][e], the key k0 + 32*kb + 16*hh + e of query i_me
+      bool need_mask = (k0 + BN > nkv) || (causal && (int64_t)k0 + BN - 1 > off + wave_first) ||
+                       (MASK == MASK_DENSE);
+      int blk_cls = 2;
+      int64_t blk_id = 0;
+      if constexpr (MASK == MASK_INFO) {
+        const int kb_blk = a.bm_data_next[csr_begin + t / sub_per_blk];
+        blk_id = info_row * a.bm_nkb + kb_blk;
+        blk_cls = a.bm_class[blk_id];
+        if (blk_cls == 1) need_mask = true;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int jb = k0 + 32 * kb + 16 * hh;          // first key of this lane's 16
+        float x[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = s[kb][e] * c_lane;
+        if (a.qk_norm) {
+          const float4* kq = reinterpret_cast<const float4*>(krv_lds + stage * BN + 32 * kb + 16 * hh);
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const float4 r4 = kq[v4];
+            x[4 * v4 + 0] *= r4.x; x[4 * v4 + 1] *= r4.y; x[4 * v4 + 2] *= r4.z; x[4 * v4 + 3] *= r4.w;
+          }
+        }
+        if constexpr (BIAS != BIAS_NONE) {
+          if (bias_row >= 0) {
+            if (a.bias_vec && jb + 16 <= a.Lkv) {
+              if constexpr (BIAS == BIAS_BF16) {
+                const uint4* bp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.bias) + bias_row + jb);  // sk == 1
+                const uint4 b0 = bp[0], b1 = bp[1];
+                const uint32_t w[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                  x[2 * e] = fmaf(__uint_as_float(w[e] << 16), LOG2E, x[2 * e]);
+                  x[2 * e + 1] = fmaf(__uint_as_float(w[e] & 0xffff0000u), LOG2E, x[2 * e + 1]);
+                }
+              } else {
+                const float4* bp = reinterpret_cast<const float4*>(static_cast<const float*>(a.bias) + bias_row + jb);
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                  const float4 f = bp[v4];
+                  x[4 * v4 + 0] = fmaf(f.x, LOG2E, x[4 * v4 + 0]);
+                  x[4 * v4 + 1] = fmaf(f.y, LOG2E, x[4 * v4 + 1]);
+                  x[4 * v4 + 2] = fmaf(f.z, LOG2E, x[4 * v4 + 2]);
+                  x[4 * v4 + 3] = fmaf(f.w, LOG2E, x[4 * v4 + 3]);
+                }
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 16; ++e)
+                if (jb + e < a.Lkv)
+                  x[e] = fmaf(load_elem(a.bias, bias_row + (int64_t)(jb + e) * a.bias_sk, a.bias_dtype), LOG2E, x[e]);
+            }
+          }
+        }
+        if (need_mask) {
+          uint32_t bits = 0xffffu;
+          if constexpr (MASK == MASK_DENSE) {
+            bits = 0;
+            if (mask_row >= 0) {
+              const uint8_t* mp = a.mask + mask_row + (int64_t)jb * a.mask_sk;
+              if (a.mask_vec && jb + 16 <= a.Lkv) {
+                const uint4 m4 = *reinterpret_cast<const uint4*>(mp);
+                const uint32_t w[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+                for (int e = 0; e < 16; ++e) bits |= (((w[e >> 2] >> (8 * (e & 3))) & 0xffu) != 0) << e;
+              } else {
+                for (int e = 0; e < 16; ++e)
+                  if (jb + e < a.Lkv) bits |= (mp[(int64_t)e * a.mask_sk] != 0) << e;
+              }
+            }
+          } else if constexpr (MASK == MASK_INFO) {
+            if (blk_cls == 1) {
+              bits = 0;
+              const int r_in = i_me - qt * BM;
+              if (r_in < a.bm_bq && i_me < a.Lq) {
+                const int col = jb - (int)(blk_id % a.bm_nkb) * a.bm_bkv;
+                const uint32_t w = a.bm_bits[((int64_t)a.bm_next[blk_id] * a.bm_bq + r_in) * (a.bm_bkv / 32) + (col >> 5)];
+                bits = (w >> (col & 31)) & 0xffffu;
+              }
+            }
+          }
+          const int64_t lim = causal ? off + i_me : (int64_t)INT32_MAX;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int j = jb + e;
+            const bool ok = (j < nkv) && ((int64_t)j <= lim) && ((bits >> e) & 1u);
+            x[e] = ok ? x[e] : -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][e] = x[e];
+      }
+
+      // -- online softmax (row = lane pair l, l^32) ---------------------------------------
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run, mt);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float psum = 0.f;
+      bf16x8 pB[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          bf16x8 pk;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(s[kb][8 * sh + e] - m_use);
+            psum += p;
+            pk[e] = static_cast<__bf16>(p);
+          }
+          pB[kb][sh] = pk;
+        }
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+
+      // -- O^T += V^T P^T ---------------------------------------------------------------
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+          for (int d = 0; d < DB; ++d) {
+            const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + (32 * d + ql) * VP + 32 * kb + 16 * hh + 8 * sh);
+            o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pB[kb][sh], o[d], 0, 0, 0);
+          }
+    }
+
+    if (t + 1 < n_tiles) sstore(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O / l; NaN for rows without keys; 0 past q_lengths -------------------------
+  if (i_me >= a.Lq) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const bool zero_row = i_me >= nq;
+  const float inv = zero_row ? 0.f : (l_tot > 0.f ? 1.0f / l_tot : NAN);
+  const int64_t orow = b * a.o_sb + (int64_t)i_me * a.o_ss + h * a.o_sh;
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int dcol = 32 * d + 8 * i + 4 * hh;
+      float r[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = zero_row ? 0.f : (l_tot > 0.f ? o[d][4 * i + j] * inv : NAN);
+      if (a.out_dtype == SDPA_F32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow + dcol) = make_float4(r[0], r[1], r[2], r[3]);
+      } else {
+        const uint32_t w0 = (uint32_t)float_to_bf16_bits(r[0]) | ((uint32_t)float_to_bf16_bits(r[1]) << 16);
+        const uint32_t w1 = (uint32_t)float_to_bf16_bits(r[2]) | ((uint32_t)float_to_bf16_bits(r[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow + dcol) = make_uint2(w0, w1);
+      }
+    }
 }
 
-hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t s) {
-  (void)a;
-  (void)s;
-  return hipErrorNotSupported;
+template <int D, int BIAS, int MASK>
+hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
+  const int n_qt = (a.Lq + BM - 1) / BM;
+  const int64_t nwg = (int64_t)n_qt * a.Hq * a.B;
+  const int remap = (nwg % 8) == 0 ? 1 : 0;
+  const size_t smem = Smem<D>::BYTES;
+  static bool attr_set = false;                // raising the dynamic LDS limit is idempotent
+  if (!attr_set) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_mfma_kernel<D, BIAS, MASK>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, BIAS, MASK>), dim3((unsigned)nwg), dim3(NT), smem, s, a, n_qt, remap);
+  return hipGetLastError();
+}
+
+template <int D, int BIAS>
+hipError_t launch_mask(const AttnArgs& a, hipStream_t s) {
+  if (a.bm_class) return launch_t<D, BIAS, MASK_INFO>(a, s);
+  if (a.mask) return launch_t<D, BIAS, MASK_DENSE>(a, s);
+  return launch_t<D, BIAS, MASK_NONE>(a, s);
+}
+
+template <int D>
+hipError_t launch_bias(const AttnArgs& a, hipStream_t s) {
+  if (!a.bias) return launch_mask<D, BIAS_NONE>(a, s);
+  if (a.bias_dtype == SDPA_BF16) return launch_mask<D, BIAS_BF16>(a, s);
+  return launch_mask<D, BIAS_F32>(a, s);
+}
+
+bool al(const void* p, int n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+}  // namespace
+
+bool fwd_mfma_supports(const AttnArgs& a) {
+  if (a.in_dtype != SDPA_BF16 || a.D != a.Dv || (a.D != 64 && a.D != 128)) return false;
+  if (!al(a.q, 16) || !al(a.k, 16) || !al(a.v, 16) || !al(a.out, 16)) return false;
+  if ((a.q_sb | a.q_ss | a.q_sh | a.k_sb | a.k_ss | a.k_sh | a.v_sb | a.v_ss | a.v_sh) & 7) return false;
+  if ((a.o_sb | a.o_ss | a.o_sh) & 3) return false;
+  if (a.bm_class && (a.bm_bq != BM || a.bm_bkv % BN)) return false;
+  const int64_t nwg = (int64_t)((a.Lq + BM - 1) / BM) * a.Hq * a.B;
+  return nwg > 0 && nwg < (int64_t)INT32_MAX;
+}
+
+hipError_t launch_fwd_mfma(const AttnArgs& args, hipStream_t s) {
+  AttnArgs a = args;
+  // 16-byte loads of 16 consecutive keys need unit key stride and 16-byte aligned runs
+  const int per16 = a.bias_dtype == SDPA_BF16 ? 8 : 4;
+  a.bias_vec = a.bias && a.bias_sk == 1 && al(a.bias, 16) && (a.bias_sb % per16) == 0 &&
+               (a.bias_sh % per16) == 0 && (a.bias_sq % per16) == 0;
+  a.mask_vec = a.mask && a.mask_sk == 1 && al(a.mask, 16) && (a.mask_sb % 16) == 0 && (a.mask_sh % 16) == 0 &&
+               (a.mask_sq % 16) == 0;
+  if (a.D == 128) return launch_bias<128>(a, s);
+  return launch_bias<64>(a, s);
 }
 
 }  // namespace sdpa

@@ -41,6 +41,7 @@ struct AttnArgs {
 
   float scale;
   int causal;                  // sdpa_causal
+  int bias_vec, mask_vec;      // 1: bias/mask rows allow 16-byte vector loads (set by the MFMA launcher)
   const int32_t* q_offset;     int q_offset_all;
   const int32_t* kv_lengths;   int kv_length_all;   // < 0: none
   const int32_t* q_lengths;    int q_length_all;    // < 0: none
