@@ -1,0 +1,247 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-calibration]
+
+A step is one causal bf16 prefill (batch 4, 16 heads, head dim 128, 4096 queries over 4096
+keys, scale 1/sqrt(128)) through sdpa_fwd: one launch of the MFMA forward kernel. Inputs are
+seeded N(0,1) draws rounded to bf16 (workloads.causal_prefill), resident in HBM before timing.
+W untimed steps, then exactly K timed steps between two device synchronizations. The headline
+``value`` is algorithmic TFLOP/s: 4 * D flops per allowed (query, key) pair, i.e. the exact
+causal count B*H*L*(L+1)/2 pairs (diagonal-tile work is not credited).
+
+The same run times the GQA decode step (batch 64, 32 query heads over 8 K/V heads, head dim
+128, cache capacity 8192, kv_lengths ~ U{1024..8192}): kv_cache_update at kv_len-1, then
+sdpa_decode. Its metric is KV-read GB/s: the algorithmic bytes are the K and V rows of the
+attended keys, sum_b kv_len_b * Hkv * D * 2 bytes * 2, plus q and the output.
+
+Printed: one JSON line (rank 0) with the contract fields, a ``roofline`` object for the
+prefill kernel (achieved = algorithmic flops per launch / average launch time measured with
+HIP events on the launch stream; peak = 2500 TFLOP/s bf16 dense MFMA), a ``decode`` object with
+its own roofline against 8000 GB/s, a sampled parity check of the timed outputs against the
+fp64 oracle, and ``cpu_baseline``: the oracle timed on this host's cores on a bounded sample.
+"""
+import argparse
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fwd_mfma_causal_b4h16d128l4096_counters.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc", "fwd_mfma.hip")
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU budget of the oracle baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a 1 GiB device copy (for scaling HBM byte counters)")
+    p.add_argument("--skip-decode", action="store_true")
+    return p.parse_args()
+
+
+def source_hash(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counters_traffic(flops_per_launch):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken from
+    the current kernel source; else None."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    text = open(PROFILE_COUNTERS).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(KERNEL_SOURCE):
+        return None
+    return float(m_bytes.group(1))
+
+
+def time_steps(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / 1e3, wall
+
+
+def oracle_rows_parity(out, w, rows):
+    import numpy as np
+    import oracle
+    got = out[:, rows].float().cpu().numpy().astype(np.float64)
+    ref = oracle.sdpa(w.values("q"), w.values("k"), w.values("v"), scale=w.scale, is_causal=w.is_causal,
+                      q_offset=w.q_offset, rows=rows)
+    d = got - ref
+    return float(np.max(np.abs(d))), float(np.linalg.norm(d) / np.linalg.norm(ref))
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_prefill(w, budget_s):
+    """The fp64 oracle on whole (batch, head) pairs of the prefill workload until the budget is spent."""
+    import numpy as np
+    import oracle
+    B, Lq, Lkv, Hq, Hkv, D, Dv = w.shape
+    q, k, v = w.values("q"), w.values("k"), w.values("v")
+    done, t_total = 0, 0.0
+    pairs = [(b, h) for b in range(B) for h in range(Hq)]
+    for (b, h) in pairs:
+        t0 = time.perf_counter()
+        oracle.sdpa(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, h:h + 1], v[b:b + 1, :, h:h + 1], scale=w.scale,
+                    is_causal=True)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    flops = 4.0 * D * (Lq * (Lq + 1) / 2) * done
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} of {B * Hq} (batch, head) pairs, all {Lq} query rows each, fp64 numpy",
+            "seconds": round(t_total, 2)}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import workloads
+    import transformer_attention_sdpa_amd as sa
+
+    sa.load()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    # ---- causal prefill -------------------------------------------------------------------
+    w = workloads.causal_prefill()
+    B, Lq, Lkv, Hq, Hkv, D, Dv = w.shape
+    q, k, v = (sa.from_numpy(getattr(w, n), "bf16") for n in ("q", "k", "v"))
+    out = torch.empty((B, Lq, Hq, D), dtype=torch.bfloat16, device="cuda")
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    step = lambda: sa.sdpa(q, k, v, is_causal=True, scale=w.scale, out=out)
+    t_gpu, t_wall = time_steps(step, args.steps, args.warmup, stream)
+    pairs = B * Hq * Lq * (Lq + 1) / 2
+    flops = 4.0 * D * pairs
+    per_launch = t_gpu / args.steps
+    tflops = flops / per_launch / 1e12
+    rows = [0, 1, 127, 128, 1000, 2047, 2048, 3333, 4094, 4095]
+    p_max, p_rel = oracle_rows_parity(out, w, rows)
+    result = {
+        "metric": "attention TFLOP/s (causal bf16 prefill) + decode KV-read GB/s, 1 MI355X",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(per_launch * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) rounded to bf16)",
+        "config": {"workload": "causal_prefill", "batch": B, "heads": Hq, "head_dim": D, "q_len": Lq,
+                   "kv_len": Lkv, "is_causal": True, "scale": w.scale, "out_dtype": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": counters_traffic(flops),
+                     "kernel": "fwd_mfma_kernel<128,0,0>", "flops_per_launch": flops},
+        "parity": {"rows_checked": f"{len(rows)} query rows x {B * Hq} (batch, head)", "max_abs": p_max,
+                   "rel_l2": p_rel, "bar": "max_abs <= 2e-2, rel_l2 <= 5e-3 (bf16 output)"},
+        "wall_s_timed_region": round(t_wall, 4),
+    }
+    del q, k, v, out
+    torch.cuda.empty_cache()
+
+    # ---- GQA decode -----------------------------------------------------------------------
+    if not args.skip_decode:
+        d = workloads.gqa_decode()
+        Bd, _, Hqd, Dd = d.q.shape
+        Hkvd = d.k_cache.shape[2]
+        qd = sa.from_numpy(d.q, "bf16")
+        kc, vc = sa.from_numpy(d.k_cache, "bf16"), sa.from_numpy(d.v_cache, "bf16")
+        kn, vn = sa.from_numpy(d.k_new, "bf16"), sa.from_numpy(d.v_new, "bf16")
+        widx = sa.from_numpy(d.write_index, "i32")
+        kvl = sa.from_numpy(d.kv_lengths, "i32")
+        od = torch.empty((Bd, 1, Hqd, Dd), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(sa.decode_workspace_bytes(qd, kc, 0), dtype=torch.uint8, device="cuda")
+
+        def dstep():
+            sa.kv_cache_update(kc, vc, kn, vn, widx)
+            sa.sdpa_decode(qd, kc, vc, kvl, scale=d.scale, out=od, workspace=ws)
+
+        td, _ = time_steps(dstep, args.steps, args.warmup, stream)
+        tdec, _ = time_steps(lambda: sa.sdpa_decode(qd, kc, vc, kvl, scale=d.scale, out=od, workspace=ws),
+                             args.steps, args.warmup, stream)
+        kv_bytes = float(np.sum(d.kv_lengths.astype(np.int64))) * Hkvd * Dd * 2 * 2
+        io_bytes = float(Bd * Hqd * Dd * 2 * 2)
+        gbs = (kv_bytes + io_bytes) / (tdec / args.steps) / 1e9
+        # parity of the decode output on a few sequences
+        import oracle
+        f = workloads.bf16_to_f32
+        sel = [0, Bd // 2, Bd - 1]
+        ekc, evc = oracle.kv_cache_update(d.k_cache[sel], d.v_cache[sel], d.k_new[sel], d.v_new[sel],
+                                          d.write_index[sel])
+        refs = [oracle.sdpa(f(d.q[b:b + 1]), f(ekc[i:i + 1, :d.kv_lengths[b]]), f(evc[i:i + 1, :d.kv_lengths[b]]),
+                            scale=d.scale, is_causal="bottom_right")[0] for i, b in enumerate(sel)]
+        got = od[sel].float().cpu().numpy()
+        diff = got - np.stack(refs)
+        result["decode"] = {
+            "metric": "decode KV-read GB/s", "value": round(gbs, 1), "unit": "GB/s",
+            "ms_per_step": round(tdec / args.steps * 1e3, 4),
+            "ms_per_step_with_cache_update": round(td / args.steps * 1e3, 4),
+            "config": {"workload": "gqa_decode", "batch": Bd, "q_heads": Hqd, "kv_heads": Hkvd, "head_dim": Dd,
+                       "capacity": d.k_cache.shape[1], "kv_lengths": "U{1024..8192} (seeded)",
+                       "sum_kv_lengths": int(np.sum(d.kv_lengths))},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "bytes_per_step": kv_bytes + io_bytes,
+                         "note": "split + combine kernels together (one sdpa_decode call)"},
+            "parity": {"sequences_checked": sel, "max_abs": float(np.max(np.abs(diff))),
+                       "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(np.stack(refs)))},
+        }
+        del qd, kc, vc, od, ws
+        torch.cuda.empty_cache()
+
+    # ---- CPU baseline (rank 0, N = 1 only) ------------------------------------------------
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
