@@ -41,6 +41,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128;            // query rows per workgroup
 constexpr int BN = 64;             // keys per tile
@@ -67,7 +68,19 @@ struct Smem {
   static constexpr int BYTES = 2 * STAGE * 2 + 2 * BN * 4;
 };
 
-template <int D, int BIAS, int MASK>
+// Buffer resource over `bytes` bytes from `base`: loads past the end return 0 (the hardware's
+// range check), which zero-fills ragged tails without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+constexpr float RESCALE_SLACK = 8.0f;   // log2 units: the running max moves only when a row's max grows by more
+
+template <int D, int BIAS, int MASK, bool NORM>
 __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, int remap) {
   using S = Smem<D>;
   constexpr int KP = S::KP;
@@ -75,6 +88,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
   constexpr int DB = D / 32;         // 32-row blocks of O^T
   constexpr int KCH = BN * (D / 8) / NT;   // 16-byte K chunks per thread per tile
   constexpr int VIT = 32 * (D / 8) / NT;   // (key pair, chunk) V items per thread per tile
+  constexpr bool FUSED = (BIAS == BIAS_NONE) && !NORM;   // logits = scale*log2e * q.k only
   extern __shared__ __align__(16) unsigned char smem_raw[];
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem_raw);
   float* krv_lds = reinterpret_cast<float*>(smem_raw + 2 * S::STAGE * 2);
@@ -106,12 +120,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
   // key limit of the workgroup and of this wave
   int64_t k_end = nkv;
   if (causal) { const int64_t lim = off + (int64_t)(row_end - 1) + 1; if (lim < k_end) k_end = lim; }
-  if (row_end <= q0) k_end = 0;
-  if (k_end < 0) k_end = 0;
+  if (row_end <= q0 || k_end < 0) k_end = 0;
   int64_t k_end_w = nkv;
   if (causal) { const int64_t lim = off + (int64_t)wave_last + 1; if (lim < k_end_w) k_end_w = lim; }
-  if (wave_last < wave_first) k_end_w = 0;
-  if (k_end_w < 0) k_end_w = 0;
+  if (wave_last < wave_first || k_end_w < 0) k_end_w = 0;
 
   // tiles to visit: all tiles below k_end, or the non-empty blocks of the mask info
   int n_tiles = 0, csr_begin = 0, sub_per_blk = 1;
@@ -136,22 +148,23 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
     else return t * BN;
   };
 
-  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + g * a.k_sh;
   const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + g * a.v_sh;
+  const int k_row_bytes = (int)(a.k_ss * 2), v_row_bytes = (int)(a.v_ss * 2);
 
-  // ---- Q^T operand (stays in registers) -------------------------------------------------
+  // ---- Q^T operand (stays in registers); rows past Lq load as zeros ------------------------
   bf16x8 qB[DC];
   float c_lane = a.scale * LOG2E;
   {
-    const bool ok = i_me < a.Lq;
-    const uint16_t* qrow = qp + b * a.q_sb + (int64_t)(ok ? i_me : 0) * a.q_ss + h * a.q_sh;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(a.q) + b * a.q_sb + h * a.q_sh,
+                                                (int64_t)a.Lq * a.q_ss * 2);
+    const int qoff = i_me * (int)(a.q_ss * 2) + 16 * hh;
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-      uint4 x = ok ? *reinterpret_cast<const uint4*>(qrow + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
+      const uint4 x = buf_load16(rq, qoff + 32 * c);
       qB[c] = __builtin_bit_cast(bf16x8, x);
-      if (a.qk_norm) {
+      if constexpr (NORM) {
         const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -160,35 +173,49 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
         }
       }
     }
-    if (a.qk_norm) {
+    if constexpr (NORM) {
       ss += __shfl_xor(ss, 32, 64);
       c_lane *= 1.0f / sqrtf(ss / D + kRmsEps);
     }
+    // Q must have landed before the loop: otherwise the wait-count analysis, which cannot tell
+    // the loop-invariant Q loads from the per-tile K/V loads, makes every q.k MFMA wait for the
+    // next tile's loads and the prefetch stops overlapping the compute.
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- staging of one K/V tile: global -> registers -> LDS --------------------------------
+  // Per-thread byte offsets inside a tile are fixed; each tile gets fresh buffer resources whose
+  // range ends at kv_len, so keys past kv_lengths arrive as zeros (never a poisoned tail).
+  int koff[KCH], voff0[VIT];
+#pragma unroll
+  for (int u = 0; u < KCH; ++u) {
+    const int c = tid + NT * u;
+    koff[u] = (c / (D / 8)) * k_row_bytes + (c % (D / 8)) * 16;
+  }
+#pragma unroll
+  for (int u = 0; u < VIT; ++u) {
+    const int it = tid + NT * u;
+    voff0[u] = (2 * (it & 31)) * v_row_bytes + (it >> 5) * 16;
+  }
   uint4 kr[KCH], vr0[VIT], vr1[VIT];
   float krv = 0.f;
   auto gload = [&](int k0) {
+    const int rows = nkv - k0;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (int64_t)k0 * a.k_ss, (int64_t)rows * k_row_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (int64_t)k0 * a.v_ss, (int64_t)rows * v_row_bytes);
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int c = tid + NT * u;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int j = k0 + row;
-      kr[u] = j < nkv ? *reinterpret_cast<const uint4*>(kp + (int64_t)j * a.k_ss + col) : make_uint4(0, 0, 0, 0);
-    }
+    for (int u = 0; u < KCH; ++u) kr[u] = buf_load16(rk, koff[u]);
 #pragma unroll
     for (int u = 0; u < VIT; ++u) {
-      const int it = tid + NT * u;
-      const int pr = it & 31, col = (it >> 5) * 8;
-      const int j = k0 + 2 * pr;
-      vr0[u] = j < nkv ? *reinterpret_cast<const uint4*>(vp + (int64_t)j * a.v_ss + col) : make_uint4(0, 0, 0, 0);
-      vr1[u] = j + 1 < nkv ? *reinterpret_cast<const uint4*>(vp + (int64_t)(j + 1) * a.v_ss + col)
-                           : make_uint4(0, 0, 0, 0);
+      vr0[u] = buf_load16(rv, voff0[u]);
+      vr1[u] = buf_load16(rv, voff0[u] + v_row_bytes);
     }
-    if (a.qk_norm && tid < BN) {
-      const int j = k0 + tid;
-      krv = j < nkv ? a.k_rinv[((int64_t)b * a.Lkv + j) * a.Hkv + g] : 0.f;
+    if constexpr (NORM) {
+      if (tid < BN) {
+        const int j = k0 + tid;
+        krv = j < nkv ? a.k_rinv[((int64_t)b * a.Lkv + j) * a.Hkv + g] : 0.f;
+      }
     }
   };
   auto sstore = [&](int stage) {
@@ -214,7 +241,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
         dst[(2 * t + 1) * (VP / 2)] = pack_hi(w0[t], w1[t]);
       }
     }
-    if (a.qk_norm && tid < BN) krv_lds[stage * BN + tid] = krv;
+    if constexpr (NORM) {
+      if (tid < BN) krv_lds[stage * BN + tid] = krv;
+    }
   };
 
   f32x16 o[DB];
@@ -244,20 +273,22 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
       const uint16_t* ks = lds + stage * S::STAGE;
       const uint16_t* vt = ks + S::K_ELEMS;
 
-      // -- S^T = K Q^T for two 32-key blocks -----------------------------------------------
+      // -- S^T = K Q^T for two 32-key blocks (two independent MFMA chains, interleaved) -----
       f32x16 s[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
 #pragma unroll
-        for (int c = 0; c < DC; ++c) {
+      for (int c = 0; c < DC; ++c) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
           const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (32 * kb + ql) * KP + 16 * c + 8 * hh);
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qB[c], s[kb], 0, 0, 0);
         }
       }
 
-      // -- logits in the exp2 domain, bias, masking ---------------------------------------
+      // -- element masking, only on tiles that need it --------------------------------------
       // lane (ql, hh) holds, in s[kb][e], the key k0 + 32*kb + 16*hh + e of query i_me
       bool need_mask = (k0 + BN > nkv) || (causal && (int64_t)k0 + BN - 1 > off + wave_first) ||
                        (MASK == MASK_DENSE);
@@ -269,52 +300,62 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
         blk_cls = a.bm_class[blk_id];
         if (blk_cls == 1) need_mask = true;
       }
+
+      // logits in the exp2 domain. FUSED: s stays raw (the max is taken on raw scores, scaled
+      // once per row); else s becomes scale*log2e*r_q*r_k*s + log2e*bias.
+      if constexpr (!FUSED) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int jb = k0 + 32 * kb + 16 * hh;          // first key of this lane's 16
-        float x[16];
+        for (int kb = 0; kb < 2; ++kb) {
+          const int jb = k0 + 32 * kb + 16 * hh;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = s[kb][e] * c_lane;
-        if (a.qk_norm) {
-          const float4* kq = reinterpret_cast<const float4*>(krv_lds + stage * BN + 32 * kb + 16 * hh);
+          for (int e = 0; e < 16; ++e) s[kb][e] *= c_lane;
+          if constexpr (NORM) {
+            const float4* kq = reinterpret_cast<const float4*>(krv_lds + stage * BN + 32 * kb + 16 * hh);
 #pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            const float4 r4 = kq[v4];
-            x[4 * v4 + 0] *= r4.x; x[4 * v4 + 1] *= r4.y; x[4 * v4 + 2] *= r4.z; x[4 * v4 + 3] *= r4.w;
+            for (int v4 = 0; v4 < 4; ++v4) {
+              const float4 r4 = kq[v4];
+              s[kb][4 * v4 + 0] *= r4.x; s[kb][4 * v4 + 1] *= r4.y;
+              s[kb][4 * v4 + 2] *= r4.z; s[kb][4 * v4 + 3] *= r4.w;
+            }
           }
-        }
-        if constexpr (BIAS != BIAS_NONE) {
-          if (bias_row >= 0) {
-            if (a.bias_vec && jb + 16 <= a.Lkv) {
-              if constexpr (BIAS == BIAS_BF16) {
-                const uint4* bp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.bias) + bias_row + jb);  // sk == 1
-                const uint4 b0 = bp[0], b1 = bp[1];
-                const uint32_t w[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+          if constexpr (BIAS != BIAS_NONE) {
+            if (bias_row >= 0) {
+              if (a.bias_vec && jb + 16 <= a.Lkv) {
+                if constexpr (BIAS == BIAS_BF16) {
+                  const uint4* bp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.bias) + bias_row + jb);
+                  const uint4 b0 = bp[0], b1 = bp[1];
+                  const uint32_t w[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                  x[2 * e] = fmaf(__uint_as_float(w[e] << 16), LOG2E, x[2 * e]);
-                  x[2 * e + 1] = fmaf(__uint_as_float(w[e] & 0xffff0000u), LOG2E, x[2 * e + 1]);
+                  for (int e = 0; e < 8; ++e) {
+                    s[kb][2 * e] = fmaf(__uint_as_float(w[e] << 16), LOG2E, s[kb][2 * e]);
+                    s[kb][2 * e + 1] = fmaf(__uint_as_float(w[e] & 0xffff0000u), LOG2E, s[kb][2 * e + 1]);
+                  }
+                } else {
+                  const float4* bp = reinterpret_cast<const float4*>(static_cast<const float*>(a.bias) + bias_row + jb);
+#pragma unroll
+                  for (int v4 = 0; v4 < 4; ++v4) {
+                    const float4 f = bp[v4];
+                    s[kb][4 * v4 + 0] = fmaf(f.x, LOG2E, s[kb][4 * v4 + 0]);
+                    s[kb][4 * v4 + 1] = fmaf(f.y, LOG2E, s[kb][4 * v4 + 1]);
+                    s[kb][4 * v4 + 2] = fmaf(f.z, LOG2E, s[kb][4 * v4 + 2]);
+                    s[kb][4 * v4 + 3] = fmaf(f.w, LOG2E, s[kb][4 * v4 + 3]);
+                  }
                 }
               } else {
-                const float4* bp = reinterpret_cast<const float4*>(static_cast<const float*>(a.bias) + bias_row + jb);
 #pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4) {
-                  const float4 f = bp[v4];
-                  x[4 * v4 + 0] = fmaf(f.x, LOG2E, x[4 * v4 + 0]);
-                  x[4 * v4 + 1] = fmaf(f.y, LOG2E, x[4 * v4 + 1]);
-                  x[4 * v4 + 2] = fmaf(f.z, LOG2E, x[4 * v4 + 2]);
-                  x[4 * v4 + 3] = fmaf(f.w, LOG2E, x[4 * v4 + 3]);
-                }
+                for (int e = 0; e < 16; ++e)
+                  if (jb + e < a.Lkv)
+                    s[kb][e] = fmaf(load_elem(a.bias, bias_row + (int64_t)(jb + e) * a.bias_sk, a.bias_dtype), LOG2E,
+                                    s[kb][e]);
               }
-            } else {
-#pragma unroll
-              for (int e = 0; e < 16; ++e)
-                if (jb + e < a.Lkv)
-                  x[e] = fmaf(load_elem(a.bias, bias_row + (int64_t)(jb + e) * a.bias_sk, a.bias_dtype), LOG2E, x[e]);
             }
           }
         }
-        if (need_mask) {
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int jb = k0 + 32 * kb + 16 * hh;
           uint32_t bits = 0xffffu;
           if constexpr (MASK == MASK_DENSE) {
             bits = 0;
@@ -336,7 +377,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
               const int r_in = i_me - qt * BM;
               if (r_in < a.bm_bq && i_me < a.Lq) {
                 const int col = jb - (int)(blk_id % a.bm_nkb) * a.bm_bkv;
-                const uint32_t w = a.bm_bits[((int64_t)a.bm_next[blk_id] * a.bm_bq + r_in) * (a.bm_bkv / 32) + (col >> 5)];
+                const uint32_t w =
+                    a.bm_bits[((int64_t)a.bm_next[blk_id] * a.bm_bq + r_in) * (a.bm_bkv / 32) + (col >> 5)];
                 bits = (w >> (col & 31)) & 0xffffu;
               }
             }
@@ -346,24 +388,33 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
           for (int e = 0; e < 16; ++e) {
             const int j = jb + e;
             const bool ok = (j < nkv) && ((int64_t)j <= lim) && ((bits >> e) & 1u);
-            x[e] = ok ? x[e] : -INFINITY;
+            s[kb][e] = ok ? s[kb][e] : -INFINITY;
           }
         }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[kb][e] = x[e];
       }
 
-      // -- online softmax (row = lane pair l, l^32) ---------------------------------------
+      // -- online softmax (a row is the lane pair l, l^32) ---------------------------------
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float psum = 0.f;
+      if constexpr (FUSED) mt *= c_lane;                 // c_lane > 0 (the launcher requires it)
+      // the running max only moves when some row's max grew by more than RESCALE_SLACK; in
+      // between, probabilities may reach 2^RESCALE_SLACK, which fp32 and bf16 hold exactly enough
+      const bool grow = mt > m_run + RESCALE_SLACK;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mt : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on a row's first keys
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       bf16x8 pB[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -372,19 +423,21 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
           bf16x8 pk;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(s[kb][8 * sh + e] - m_use);
-            psum += p;
+            const float xe = s[kb][8 * sh + e];
+            const float p = FUSED ? __builtin_amdgcn_exp2f(fmaf(xe, c_lane, -m_use))
+                                  : __builtin_amdgcn_exp2f(xe - m_use);
             pk[e] = static_cast<__bf16>(p);
           }
           pB[kb][sh] = pk;
+          // row sum of the same bf16 probabilities the MFMA consumes
+          const uint4 pw = __builtin_bit_cast(uint4, pk);
+          const uint32_t pws[4] = {pw.x, pw.y, pw.z, pw.w};
+#pragma unroll
+          for (int t2 = 0; t2 < 4; ++t2)
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pws[t2]),
+                                                    __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l_run, false);
         }
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
 
       // -- O^T += V^T P^T ---------------------------------------------------------------
 #pragma unroll
@@ -426,7 +479,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
     }
 }
 
-template <int D, int BIAS, int MASK>
+template <int D, int BIAS, int MASK, bool NORM>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   const int n_qt = (a.Lq + BM - 1) / BM;
   const int64_t nwg = (int64_t)n_qt * a.Hq * a.B;
@@ -434,19 +487,26 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   const size_t smem = Smem<D>::BYTES;
   static bool attr_set = false;                // raising the dynamic LDS limit is idempotent
   if (!attr_set) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_mfma_kernel<D, BIAS, MASK>),
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_mfma_kernel<D, BIAS, MASK, NORM>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     attr_set = true;
   }
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, BIAS, MASK>), dim3((unsigned)nwg), dim3(NT), smem, s, a, n_qt, remap);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, BIAS, MASK, NORM>), dim3((unsigned)nwg), dim3(NT), smem, s, a, n_qt,
+                     remap);
   return hipGetLastError();
+}
+
+template <int D, int BIAS, int MASK>
+hipError_t launch_norm(const AttnArgs& a, hipStream_t s) {
+  if (a.qk_norm) return launch_t<D, BIAS, MASK, true>(a, s);
+  return launch_t<D, BIAS, MASK, false>(a, s);
 }
 
 template <int D, int BIAS>
 hipError_t launch_mask(const AttnArgs& a, hipStream_t s) {
-  if (a.bm_class) return launch_t<D, BIAS, MASK_INFO>(a, s);
-  if (a.mask) return launch_t<D, BIAS, MASK_DENSE>(a, s);
-  return launch_t<D, BIAS, MASK_NONE>(a, s);
+  if (a.bm_class) return launch_norm<D, BIAS, MASK_INFO>(a, s);
+  if (a.mask) return launch_norm<D, BIAS, MASK_DENSE>(a, s);
+  return launch_norm<D, BIAS, MASK_NONE>(a, s);
 }
 
 template <int D>
@@ -466,6 +526,13 @@ bool fwd_mfma_supports(const AttnArgs& a) {
   if ((a.q_sb | a.q_ss | a.q_sh | a.k_sb | a.k_ss | a.k_sh | a.v_sb | a.v_ss | a.v_sh) & 7) return false;
   if ((a.o_sb | a.o_ss | a.o_sh) & 3) return false;
   if (a.bm_class && (a.bm_bq != BM || a.bm_bkv % BN)) return false;
+  // the softmax takes the row max on raw scores scaled once: the scale must be positive
+  if (!(a.scale > 0.f)) return false;
+  // buffer loads: rows at least head_dim long, 32-bit byte ranges per (batch, head) slice
+  if (a.q_ss < a.D || a.k_ss < a.D || a.v_ss < a.D) return false;
+  if ((int64_t)a.Lq * a.q_ss * 2 > INT32_MAX || (int64_t)a.Lkv * a.k_ss * 2 > INT32_MAX ||
+      (int64_t)a.Lkv * a.v_ss * 2 > INT32_MAX)
+    return false;
   const int64_t nwg = (int64_t)((a.Lq + BM - 1) / BM) * a.Hq * a.B;
   return nwg > 0 && nwg < (int64_t)INT32_MAX;
 }
