@@ -60,12 +60,11 @@ __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __b
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
 template <int D>
-struct Smem {
+struct Smem {                                            // two K buffers, two V^T buffers, key factors
   static constexpr int KP = D + 8;                       // K row pitch (bf16)
   static constexpr int K_ELEMS = BN * KP;
   static constexpr int V_ELEMS = D * VP;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;        // bf16 elements per stage
-  static constexpr int BYTES = 2 * STAGE * 2 + 2 * BN * 4;
+  static constexpr int BYTES = 2 * (K_ELEMS + V_ELEMS) * 2 + 2 * BN * 4;
 };
 
 // Buffer resource over `bytes` bytes from `base`: loads past the end return 0 (the hardware's
@@ -90,8 +89,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
   constexpr int VIT = 32 * (D / 8) / NT;   // (key pair, chunk) V items per thread per tile
   constexpr bool FUSED = (BIAS == BIAS_NONE) && !NORM;   // logits = scale*log2e * q.k only
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  uint16_t* lds = reinterpret_cast<uint16_t*>(smem_raw);
-  float* krv_lds = reinterpret_cast<float*>(smem_raw + 2 * S::STAGE * 2);
+  uint16_t* const kbuf0 = reinterpret_cast<uint16_t*>(smem_raw);
+  uint16_t* const vbuf0 = kbuf0 + 2 * S::K_ELEMS;
+  float* const krv0 = reinterpret_cast<float*>(vbuf0 + 2 * S::V_ELEMS);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -147,6 +147,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
     if constexpr (MASK == MASK_INFO) return a.bm_data_next[csr_begin + t / sub_per_blk] * a.bm_bkv + (t % sub_per_blk) * BN;
     else return t * BN;
   };
+  // staging runs ahead of the last tile without branches: past the end it reloads the last tile
+  auto tile_k0c = [&](int t) -> int { return tile_k0(t < n_tiles ? t : (n_tiles > 0 ? n_tiles - 1 : 0)); };
 
   const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + g * a.k_sh;
   const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + g * a.v_sh;
@@ -184,9 +186,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- staging of one K/V tile: global -> registers -> LDS --------------------------------
+  // ---- staging of K/V tiles: global -> registers -> LDS ----------------------------------
   // Per-thread byte offsets inside a tile are fixed; each tile gets fresh buffer resources whose
   // range ends at kv_len, so keys past kv_lengths arrive as zeros (never a poisoned tail).
+  // K runs two tiles ahead of the compute (its scores are formed one iteration early), V one.
   int koff[KCH], voff0[VIT];
 #pragma unroll
   for (int u = 0; u < KCH; ++u) {
@@ -200,12 +203,13 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
   }
   uint4 kr[KCH], vr0[VIT], vr1[VIT];
   float krv = 0.f;
-  auto gload = [&](int k0) {
-    const int rows = nkv - k0;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (int64_t)k0 * a.k_ss, (int64_t)rows * k_row_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (int64_t)k0 * a.v_ss, (int64_t)rows * v_row_bytes);
+  auto gload_k = [&](int k0) {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (int64_t)k0 * a.k_ss, (int64_t)(nkv - k0) * k_row_bytes);
 #pragma unroll
     for (int u = 0; u < KCH; ++u) kr[u] = buf_load16(rk, koff[u]);
+  };
+  auto gload_v = [&](int k0) {
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (int64_t)k0 * a.v_ss, (int64_t)(nkv - k0) * v_row_bytes);
 #pragma unroll
     for (int u = 0; u < VIT; ++u) {
       vr0[u] = buf_load16(rv, voff0[u]);
@@ -218,9 +222,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
       }
     }
   };
-  auto sstore = [&](int stage) {
-    uint16_t* ks = lds + stage * S::STAGE;
-    uint16_t* vt = ks + S::K_ELEMS;
+  auto sstore_k = [&](int stage) {
+    uint16_t* ks = kbuf0 + stage * S::K_ELEMS;
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
       const int c = tid + NT * u;
@@ -228,6 +231,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
       const int lrow = (row & ~31) + k_lds_row(row & 31);
       *reinterpret_cast<uint4*>(ks + lrow * KP + col) = kr[u];
     }
+  };
+  auto sstore_v = [&](int stage) {
+    uint16_t* vt = vbuf0 + stage * S::V_ELEMS;
 #pragma unroll
     for (int u = 0; u < VIT; ++u) {
       const int it = tid + NT * u;
@@ -242,7 +248,30 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
       }
     }
     if constexpr (NORM) {
-      if (tid < BN) krv_lds[stage * BN + tid] = krv;
+      if (tid < BN) krv0[stage * BN + tid] = krv;
+    }
+  };
+  // K(t+2) into the K buffer freed by K(t), V(t+1) into the one freed by V(t-1); then the
+  // loads of K(t+3) and V(t+2). Past the last tile this stages copies nobody reads.
+  auto staging = [&](int t) {
+    sstore_k(t & 1);
+    sstore_v((t + 1) & 1);
+    gload_k(tile_k0c(t + 3));
+    gload_v(tile_k0c(t + 2));
+  };
+  // S^T = K Q^T for two 32-key blocks (two independent MFMA chains, interleaved)
+  auto compute_s = [&](const uint16_t* ks, f32x16 (&sacc)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (32 * kb + ql) * KP + 16 * c + 8 * hh);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qB[c], sacc[kb], 0, 0, 0);
+      }
     }
   };
 
@@ -251,45 +280,30 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
   for (int d = 0; d < DB; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  // finite start: exp2 of (masked -inf) - m_run is 0, and any finite score grows it at once
+  float m_run = -1.0e30f, l_run = 0.f;
 
   const int64_t bias_row = (BIAS != BIAS_NONE && i_me < a.Lq)
                                ? b * a.bias_sb + h * a.bias_sh + (int64_t)i_me * a.bias_sq : -1;
   const int64_t mask_row = (MASK == MASK_DENSE && i_me < a.Lq)
                                ? b * a.mask_sb + h * a.mask_sh + (int64_t)i_me * a.mask_sq : -1;
 
+  // ---- pipeline prologue: K0, V0, K1 in LDS; K2 and V1 in flight; S(0) formed -------------
+  f32x16 s_cur[2];
   if (n_tiles > 0) {
-    gload(tile_k0(0));
-    sstore(0);
+    gload_k(tile_k0(0)); gload_v(tile_k0(0)); sstore_k(0); sstore_v(0);
+    gload_k(tile_k0c(1)); sstore_k(1);
+    gload_k(tile_k0c(2)); gload_v(tile_k0c(1));
   }
   __syncthreads();
+  if (n_tiles > 0 && tile_k0(0) < k_end_w) compute_s(kbuf0, s_cur);
+  __syncthreads();                                       // K buffer 0 is rewritten in iteration 0
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int stage = t & 1;
     const int k0 = tile_k0(t);
-    if (t + 1 < n_tiles) gload(tile_k0(t + 1));
-
     if (k0 < k_end_w) {
-      const uint16_t* ks = lds + stage * S::STAGE;
-      const uint16_t* vt = ks + S::K_ELEMS;
-
-      // -- S^T = K Q^T for two 32-key blocks (two independent MFMA chains, interleaved) -----
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (32 * kb + ql) * KP + 16 * c + 8 * hh);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qB[c], s[kb], 0, 0, 0);
-        }
-      }
-
       // -- element masking, only on tiles that need it --------------------------------------
-      // lane (ql, hh) holds, in s[kb][e], the key k0 + 32*kb + 16*hh + e of query i_me
+      // lane (ql, hh) holds, in s_cur[kb][e], the key k0 + 32*kb + 16*hh + e of query i_me
       bool need_mask = (k0 + BN > nkv) || (causal && (int64_t)k0 + BN - 1 > off + wave_first) ||
                        (MASK == MASK_DENSE);
       int blk_cls = 2;
@@ -300,7 +314,6 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
         blk_cls = a.bm_class[blk_id];
         if (blk_cls == 1) need_mask = true;
       }
-
       // logits in the exp2 domain. FUSED: s stays raw (the max is taken on raw scores, scaled
       // once per row); else s becomes scale*log2e*r_q*r_k*s + log2e*bias.
       if constexpr (!FUSED) {
@@ -308,14 +321,14 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
         for (int kb = 0; kb < 2; ++kb) {
           const int jb = k0 + 32 * kb + 16 * hh;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) s[kb][e] *= c_lane;
+          for (int e = 0; e < 16; ++e) s_cur[kb][e] *= c_lane;
           if constexpr (NORM) {
-            const float4* kq = reinterpret_cast<const float4*>(krv_lds + stage * BN + 32 * kb + 16 * hh);
+            const float4* kq = reinterpret_cast<const float4*>(krv0 + (t & 1) * BN + 32 * kb + 16 * hh);
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
               const float4 r4 = kq[v4];
-              s[kb][4 * v4 + 0] *= r4.x; s[kb][4 * v4 + 1] *= r4.y;
-              s[kb][4 * v4 + 2] *= r4.z; s[kb][4 * v4 + 3] *= r4.w;
+              s_cur[kb][4 * v4 + 0] *= r4.x; s_cur[kb][4 * v4 + 1] *= r4.y;
+              s_cur[kb][4 * v4 + 2] *= r4.z; s_cur[kb][4 * v4 + 3] *= r4.w;
             }
           }
           if constexpr (BIAS != BIAS_NONE) {
@@ -327,26 +340,26 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
                   const uint32_t w[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
                   for (int e = 0; e < 8; ++e) {
-                    s[kb][2 * e] = fmaf(__uint_as_float(w[e] << 16), LOG2E, s[kb][2 * e]);
-                    s[kb][2 * e + 1] = fmaf(__uint_as_float(w[e] & 0xffff0000u), LOG2E, s[kb][2 * e + 1]);
+                    s_cur[kb][2 * e] = fmaf(__uint_as_float(w[e] << 16), LOG2E, s_cur[kb][2 * e]);
+                    s_cur[kb][2 * e + 1] = fmaf(__uint_as_float(w[e] & 0xffff0000u), LOG2E, s_cur[kb][2 * e + 1]);
                   }
                 } else {
                   const float4* bp = reinterpret_cast<const float4*>(static_cast<const float*>(a.bias) + bias_row + jb);
 #pragma unroll
                   for (int v4 = 0; v4 < 4; ++v4) {
                     const float4 f = bp[v4];
-                    s[kb][4 * v4 + 0] = fmaf(f.x, LOG2E, s[kb][4 * v4 + 0]);
-                    s[kb][4 * v4 + 1] = fmaf(f.y, LOG2E, s[kb][4 * v4 + 1]);
-                    s[kb][4 * v4 + 2] = fmaf(f.z, LOG2E, s[kb][4 * v4 + 2]);
-                    s[kb][4 * v4 + 3] = fmaf(f.w, LOG2E, s[kb][4 * v4 + 3]);
+                    s_cur[kb][4 * v4 + 0] = fmaf(f.x, LOG2E, s_cur[kb][4 * v4 + 0]);
+                    s_cur[kb][4 * v4 + 1] = fmaf(f.y, LOG2E, s_cur[kb][4 * v4 + 1]);
+                    s_cur[kb][4 * v4 + 2] = fmaf(f.z, LOG2E, s_cur[kb][4 * v4 + 2]);
+                    s_cur[kb][4 * v4 + 3] = fmaf(f.w, LOG2E, s_cur[kb][4 * v4 + 3]);
                   }
                 }
               } else {
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
                   if (jb + e < a.Lkv)
-                    s[kb][e] = fmaf(load_elem(a.bias, bias_row + (int64_t)(jb + e) * a.bias_sk, a.bias_dtype), LOG2E,
-                                    s[kb][e]);
+                    s_cur[kb][e] = fmaf(load_elem(a.bias, bias_row + (int64_t)(jb + e) * a.bias_sk, a.bias_dtype),
+                                        LOG2E, s_cur[kb][e]);
               }
             }
           }
@@ -388,23 +401,26 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
           for (int e = 0; e < 16; ++e) {
             const int j = jb + e;
             const bool ok = (j < nkv) && ((int64_t)j <= lim) && ((bits >> e) & 1u);
-            s[kb][e] = ok ? s[kb][e] : -INFINITY;
+            s_cur[kb][e] = ok ? s_cur[kb][e] : -INFINITY;
           }
         }
       }
 
-      // -- online softmax (a row is the lane pair l, l^32) ---------------------------------
+      // -- online softmax statistics (a row is the lane pair l, l^32) ------------------------
+      // The running max m_run (shared by both halves of a row) only moves when a row's max grew
+      // by more than RESCALE_SLACK; in between, probabilities may reach 2^RESCALE_SLACK, which
+      // fp32 sums and bf16 probabilities hold without loss. Each lane first tests its own 32
+      // scores; only when some lane exceeds the slack do the halves exchange maxima (a
+      // cross-lane exchange goes through the LDS queue and would drain it every tile).
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s_cur[kb][e]);
       if constexpr (FUSED) mt *= c_lane;                 // c_lane > 0 (the launcher requires it)
-      // the running max only moves when some row's max grew by more than RESCALE_SLACK; in
-      // between, probabilities may reach 2^RESCALE_SLACK, which fp32 and bf16 hold exactly enough
-      const bool grow = mt > m_run + RESCALE_SLACK;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + RESCALE_SLACK)) {
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));          // row max over both halves
+        const bool grow = mt > m_run + RESCALE_SLACK;
         const float m_new = grow ? mt : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on a row's first keys
         l_run *= alpha;
@@ -414,44 +430,140 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
           for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
         m_run = m_new;
       }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      bf16x8 pB[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          bf16x8 pk;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float xe = s[kb][8 * sh + e];
-            const float p = FUSED ? __builtin_amdgcn_exp2f(fmaf(xe, c_lane, -m_use))
-                                  : __builtin_amdgcn_exp2f(xe - m_use);
-            pk[e] = static_cast<__bf16>(p);
-          }
-          pB[kb][sh] = pk;
+      const float m_use = m_run;
+
+      // -- the tile body, in chunks the compiler may not reorder across ---------------------
+      // The matrix cores and the VALU only run side by side when their instructions alternate
+      // in program order, so the body is cut into chunks fenced by sched_barrier(0):
+      //   A  (DC chunks): 2 MFMAs of S(t+1) = K(t+1) Q^T, and 24 of the 32 probabilities of S(t)
+      //   B1 (2*DB chunks): 1 MFMA of O += V P for keys 0..31 of the tile, and the last 8
+      //      probabilities (keys 32..63, needed only by B2)
+      //   B2 (2*DB chunks): 1 MFMA of O += V P for keys 32..63, and the staging of K(t+2),
+      //      V(t+1) into LDS and the loads of K(t+3), V(t+2)
+      // Each chunk also issues the LDS fragment read of the next chunk.
+      constexpr int NA = DC, NB = 2 * DB;
+      constexpr int EL_A = 24, EL_B = 32 - EL_A;
+      float pf[32];                                      // probabilities of this lane's 32 keys
+      uint32_t pw[16];                                   // the same, packed as bf16 pairs
+      auto prob = [&](int f) {                           // element f = 16*kb + 8*sh + e
+        const float xe = s_cur[f >> 4][f & 15];
+        pf[f] = FUSED ? __builtin_amdgcn_exp2f(fmaf(xe, c_lane, -m_use)) : __builtin_amdgcn_exp2f(xe - m_use);
+        if (f & 1) {
+          typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+          const bf16x2v pr = {static_cast<__bf16>(pf[f - 1]), static_cast<__bf16>(pf[f])};
+          pw[f >> 1] = __builtin_bit_cast(uint32_t, pr);
           // row sum of the same bf16 probabilities the MFMA consumes
-          const uint4 pw = __builtin_bit_cast(uint4, pk);
-          const uint32_t pws[4] = {pw.x, pw.y, pw.z, pw.w};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l_run, false);
+        }
+      };
+      auto pb = [&](int kb, int sh) -> bf16x8 {
+        const uint4 w = make_uint4(pw[8 * kb + 4 * sh + 0], pw[8 * kb + 4 * sh + 1], pw[8 * kb + 4 * sh + 2],
+                                   pw[8 * kb + 4 * sh + 3]);
+        return __builtin_bit_cast(bf16x8, w);
+      };
+      const uint16_t* ksn = kbuf0 + ((t + 1) & 1) * S::K_ELEMS;
+      const uint16_t* vt = vbuf0 + (t & 1) * S::V_ELEMS;
+      auto kfrag = [&](int c, int kb) {
+        return *reinterpret_cast<const bf16x8*>(ksn + (32 * kb + ql) * KP + 16 * c + 8 * hh);
+      };
+      auto vfrag = [&](int i) {                          // i = (kb*2 + sh)*DB + d
+        const int d = i % DB, sh = (i / DB) & 1, kb = i / (2 * DB);
+        return *reinterpret_cast<const bf16x8*>(vt + (32 * d + ql) * VP + 32 * kb + 16 * hh + 8 * sh);
+      };
+
+      // LDS fragments are read PF chunks ahead of the MFMA that consumes them
+      constexpr int PF = 2;
+      f32x16 s_next[2];
+      bf16x8 kf[PF + 1][2];
 #pragma unroll
-          for (int t2 = 0; t2 < 4; ++t2)
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pws[t2]),
-                                                    __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l_run, false);
+      for (int c = 0; c < PF; ++c) {
+        kf[c][0] = kfrag(c, 0);
+        kf[c][1] = kfrag(c, 1);
+      }
+      bf16x8 vf[PF + 1];
+#pragma unroll
+      for (int c = 0; c < NA; ++c) {                     // ---- block A
+        if (c + PF < NA) {
+          kf[(c + PF) % (PF + 1)][0] = kfrag(c + PF, 0);
+          kf[(c + PF) % (PF + 1)][1] = kfrag(c + PF, 1);
+        } else {
+          vf[(c + PF - NA) % (PF + 1)] = vfrag(c + PF - NA);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (c == 0) {
+            f32x16 z;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) z[e] = 0.f;
+            s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][kb], qB[0], z, 0, 0, 0);
+          } else {
+            s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c % (PF + 1)][kb], qB[c], s_next[kb], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int f = c * EL_A / NA; f < (c + 1) * EL_A / NA; ++f) prob(f);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {                     // ---- block B1: keys 0..31
+        vf[(i + PF) % (PF + 1)] = vfrag(i + PF);
+        o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % (PF + 1)], pb(0, i / DB), o[i % DB], 0, 0, 0);
+#pragma unroll
+        for (int f = EL_A + i * EL_B / NB; f < EL_A + (i + 1) * EL_B / NB; ++f) prob(f);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // staging ops: K writes, V writes (4 row pairs per item), then the loads that refill the
+      // staging registers
+      constexpr int OPS = KCH + 4 * VIT + KCH + VIT;
+      const int kn = tile_k0c(t + 3), vn = tile_k0c(t + 2);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (int64_t)kn * a.k_ss, (int64_t)(nkv - kn) * k_row_bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (int64_t)vn * a.v_ss, (int64_t)(nkv - vn) * v_row_bytes);
+      uint16_t* ks_w = kbuf0 + (t & 1) * S::K_ELEMS;
+      uint16_t* vt_w = vbuf0 + ((t + 1) & 1) * S::V_ELEMS;
+      auto stage_op = [&](int j) {
+        if (j < KCH) {
+          const int c = tid + NT * j;
+          const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+          const int lrow = (row & ~31) + k_lds_row(row & 31);
+          *reinterpret_cast<uint4*>(ks_w + lrow * KP + col) = kr[j];
+        } else if (j < KCH + 4 * VIT) {
+          const int u = (j - KCH) >> 2, q4 = (j - KCH) & 3;
+          const int it = tid + NT * u;
+          const int pr = it & 31, col = (it >> 5) * 8;
+          const uint32_t w0 = q4 == 0 ? vr0[u].x : q4 == 1 ? vr0[u].y : q4 == 2 ? vr0[u].z : vr0[u].w;
+          const uint32_t w1 = q4 == 0 ? vr1[u].x : q4 == 1 ? vr1[u].y : q4 == 2 ? vr1[u].z : vr1[u].w;
+          uint32_t* dst = reinterpret_cast<uint32_t*>(vt_w + col * VP) + pr;
+          dst[(2 * q4) * (VP / 2)] = pack_lo(w0, w1);
+          dst[(2 * q4 + 1) * (VP / 2)] = pack_hi(w0, w1);
+        } else if (j < 2 * KCH + 4 * VIT) {
+          const int u = j - KCH - 4 * VIT;
+          kr[u] = buf_load16(rk, koff[u]);
+        } else {
+          const int u = j - 2 * KCH - 4 * VIT;
+          vr0[u] = buf_load16(rv, voff0[u]);
+          vr1[u] = buf_load16(rv, voff0[u] + v_row_bytes);
+        }
+      };
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {                     // ---- block B2: keys 32..63 + staging
+        if (i + PF < NB) vf[(NB + i + PF) % (PF + 1)] = vfrag(NB + i + PF);
+        o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(NB + i) % (PF + 1)], pb(1, i / DB), o[i % DB], 0, 0, 0);
+#pragma unroll
+        for (int j = i * OPS / NB; j < (i + 1) * OPS / NB; ++j) stage_op(j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (NORM) {
+        if (tid < BN) krv0[((t + 1) & 1) * BN + tid] = krv;
+        if (tid < BN) {
+          const int j = vn + tid;
+          krv = j < nkv ? a.k_rinv[((int64_t)b * a.Lkv + j) * a.Hkv + g] : 0.f;
         }
       }
-
-      // -- O^T += V^T P^T ---------------------------------------------------------------
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-          for (int d = 0; d < DB; ++d) {
-            const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + (32 * d + ql) * VP + 32 * kb + 16 * hh + 8 * sh);
-            o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pB[kb][sh], o[d], 0, 0, 0);
-          }
+      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_next[kb];
+    } else {
+      staging(t);
     }
-
-    if (t + 1 < n_tiles) sstore(stage ^ 1);
     __syncthreads();
   }
 
