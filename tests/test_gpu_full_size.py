@@ -1,0 +1,108 @@
+"""GPU parity at the five workloads' full sizes, in the launch configurations the benchmark
+times, checked on sampled outputs the oracle computes row by row and on properties that hold
+at any size.
+
+Sampled query rows sit on the kernels' tile edges (128-row query tiles, 64-key K/V tiles), at
+the first and last rows and in between. The oracle sees exactly the values the GPU sees.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import say, dev, gpu_inputs, assert_close
+import transformer_attention_sdpa_amd as sa
+
+pytestmark = pytest.mark.gpu
+f32 = workloads.bf16_to_f32
+
+
+def _rows_oracle(w, rows):
+    """Oracle output for query rows `rows` of every (batch, head) of workload w."""
+    return oracle.sdpa(w.values("q"), w.values("k"), w.values("v"), bias=w.values("bias"), mask=w.mask,
+                       scale=w.scale, is_causal=w.is_causal, q_offset=w.q_offset, kv_lengths=w.kv_lengths,
+                       rows=rows)
+
+
+def test_causal_prefill_b4_h16_d128_l4096(lib):
+    say("full size: causal prefill B4 H16 D128 L4096")
+    w = workloads.causal_prefill()
+    t = gpu_inputs(w)
+    rows = [0, 1, 63, 64, 127, 128, 129, 1000, 2047, 2048, 3333, 4094, 4095]
+    ref = _rows_oracle(w, rows)
+    for out_dtype in (torch.bfloat16, torch.float32):      # bf16 is what the benchmark times
+        out = sa.sdpa(t["q"], t["k"], t["v"], is_causal=True, scale=w.scale, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        got = out[:, rows].float().cpu().numpy()
+        assert_close(got, ref, "bf16", f"causal prefill rows, out {out_dtype}")
+        assert torch.isfinite(out).all().item()
+        if out_dtype == torch.float32:
+            # causal row 0 sees one key: p = 1, so the output is V's row 0 exactly
+            v0 = t["v"][:, 0].float()
+            assert torch.equal(out[:, 0], v0)
+
+
+def test_gqa_decode_b64_hq32_hkv8_cap8192(lib):
+    say("full size: GQA decode B64 Hq32 Hkv8 D128 cap 8192")
+    d = workloads.gqa_decode()
+    B, _, Hq, D = d.q.shape
+    q = dev(d.q, "bf16")
+    kc, vc = dev(d.k_cache, "bf16"), dev(d.v_cache, "bf16")
+    kn, vn = dev(d.k_new, "bf16"), dev(d.v_new, "bf16")
+    widx = dev(d.write_index, "i32")
+    kvl = dev(d.kv_lengths, "i32")
+    sa.kv_cache_update(kc, vc, kn, vn, widx)
+    outs = {dt: sa.sdpa_decode(q, kc, vc, kvl, scale=d.scale, out_dtype=dt) for dt in (torch.bfloat16, torch.float32)}
+    torch.cuda.synchronize()
+    # the written rows are the new rows, bit for bit
+    bidx = torch.arange(B, device="cuda")
+    wi = widx.long()
+    assert torch.equal(kc[bidx, wi].view(torch.int16), kn[:, 0].view(torch.int16))
+    assert torch.equal(vc[bidx, wi].view(torch.int16), vn[:, 0].view(torch.int16))
+    # every output is finite: no slot past kv_lengths (NaN-filled) was read
+    for o in outs.values():
+        assert torch.isfinite(o).all().item()
+    lens = d.kv_lengths
+    sel = sorted({0, B // 2, B - 1, int(np.argmin(lens)), int(np.argmax(lens))})
+    ekc, evc = oracle.kv_cache_update(d.k_cache[sel], d.v_cache[sel], d.k_new[sel], d.v_new[sel], d.write_index[sel])
+    ref = np.stack([oracle.sdpa(f32(d.q[b:b + 1]), f32(ekc[i:i + 1, :lens[b]]), f32(evc[i:i + 1, :lens[b]]),
+                                scale=d.scale, is_causal="bottom_right")[0] for i, b in enumerate(sel)])
+    for dt, o in outs.items():
+        assert_close(o[sel].float().cpu().numpy(), ref, "bf16", f"decode batches {sel}, out {dt}")
+
+
+def test_bias_block_mask_b2_h16_d64_l8192(lib):
+    say("full size: ALiBi bias + block-sparse mask B2 H16 D64 L8192")
+    w = workloads.bias_block_mask()
+    t = gpu_inputs(w)
+    info = sa.build_block_mask_info(t["mask"], 128, 128)
+    out_info = sa.sdpa(t["q"], t["k"], t["v"], t["bias"], None, mask_info=info, scale=w.scale,
+                       out_dtype=torch.float32)
+    out_dense = sa.sdpa(t["q"], t["k"], t["v"], t["bias"], t["mask"], scale=w.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    # skipping empty blocks and dropping the per-element test on full blocks changes nothing
+    assert torch.equal(torch.nan_to_num(out_info, nan=7.0), torch.nan_to_num(out_dense, nan=7.0))
+    assert torch.equal(torch.isnan(out_info), torch.isnan(out_dense))
+    rows = [0, 1, 127, 128, 4095, 4096, 8190, 8191]
+    # not causal: the sampled rows form a problem of their own (bias and mask rows sliced alike)
+    ref = oracle.sdpa(f32(w.q[:, rows]), w.values("k"), w.values("v"), bias=f32(w.bias[:, :, rows]),
+                      mask=w.mask[..., rows, :], scale=w.scale)
+    assert_close(out_info[:, rows].cpu().numpy(), ref, "bf16", "bias + block mask rows")
+    # rows whose mask row is all false are NaN, the rest finite
+    empty_rows = ~w.mask[0, 0].any(axis=1)
+    got_nan = torch.isnan(out_info[0, :, 0, 0]).cpu().numpy()
+    np.testing.assert_array_equal(got_nan, empty_rows)
+
+
+def test_chunked_prefill_b1_hq32_hkv8_kv131072(lib):
+    say("full size: chunked prefill B1 Hq32 Hkv8 D128 kv 131072 q 2048 at offset 129024")
+    w = workloads.chunked_prefill()
+    t = gpu_inputs(w)
+    out = sa.sdpa(t["q"], t["k"], t["v"], is_causal=True, q_offset=w.q_offset, scale=w.scale,
+                  out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    rows = [0, 1, 127, 128, 1024, 2046, 2047]
+    ref = _rows_oracle(w, rows)
+    assert_close(out[:, rows].cpu().numpy(), ref, "bf16", "chunked prefill rows")
