@@ -19,6 +19,8 @@
 //     M = max m_s, out = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s. This merge is exact because
 //     the online softmax is associative (NNlib "Fused implementation": softmax taken online
 //     over tiles of keys). No key at all gives NaN ("Fused implementation").
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace sdpa {
@@ -172,13 +174,32 @@ __global__ __launch_bounds__(kDecD) void decode_combine_kernel(DecodeArgs a) {
   const int nkv = clampi(a.kv_lengths[b], 0, a.cap);
   const int nsp = (nkv + a.split_len - 1) / a.split_len;
   const int64_t slot0 = ((int64_t)b * a.Hq + hq) * a.max_splits;
+  const float* ml = a.part_ml + 2 * slot0;
+  const float* po = a.part_o + slot0 * kDecD + d;
+  // four splits per round, so that the loads of a round are in flight together
   float M = -INFINITY;
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, a.part_ml[2 * (slot0 + s)]);
+  for (int s = 0; s < nsp; s += 4) {
+    float t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t[u] = s + u < nsp ? ml[2 * (s + u)] : -INFINITY;
+    M = fmaxf(M, fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])));
+  }
   float L = 0.f, O = 0.f;
-  for (int s = 0; s < nsp; ++s) {
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[2 * (slot0 + s)] - M);
-    L = fmaf(w, a.part_ml[2 * (slot0 + s) + 1], L);
-    O = fmaf(w, a.part_o[(slot0 + s) * kDecD + d], O);
+  for (int s = 0; s < nsp; s += 4) {
+    float mm[4], ll[4], oo[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = s + u < nsp;
+      mm[u] = ok ? ml[2 * (s + u)] : -INFINITY;
+      ll[u] = ok ? ml[2 * (s + u) + 1] : 0.f;
+      oo[u] = ok ? po[(int64_t)(s + u) * kDecD] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = (s + u < nsp) ? __builtin_amdgcn_exp2f(mm[u] - M) : 0.f;
+      L = fmaf(w, ll[u], L);
+      O = fmaf(w, oo[u], O);
+    }
   }
   const float res = (nsp > 0 && L > 0.f) ? O / L : NAN;
   store_elem(a.out, b * a.o_sb + hq * a.o_sh + d, a.out_dtype, res);

@@ -30,9 +30,9 @@
 //   a wave's causal limit are skipped by that wave, tiles past the workgroup's limit are not
 //   loaded. Keys past kv_lengths are loaded as zeros, so a poisoned cache tail never reaches
 //   the arithmetic (0 * NaN would).
-// * Grid: q tiles fastest (heaviest causal tile first), then heads, then batch, remapped so that
-//   the workgroups sharing one K/V head land on the same XCD (the hardware deals consecutive
-//   workgroups round-robin over the 8 XCDs; each XCD has its own L2).
+// * Grid: every XCD (the hardware deals consecutive workgroups round-robin over the 8 XCDs; each
+//   has its own L2) gets a contiguous set of heads. Non-causal launches run one head's tiles
+//   back to back (K/V reuse in L2); causal launches run longest tile first across all heads.
 #include "device_common.h"
 
 namespace sdpa {
@@ -80,7 +80,7 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) 
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units: the running max moves only when a row's max grows by more
 
 template <int D, int BIAS, int MASK, bool NORM>
-__global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, int remap) {
+__global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, int remap, int order) {
   using S = Smem<D>;
   constexpr int KP = S::KP;
   constexpr int DC = D / 16;         // 16-wide head-dim chunks (MFMA k steps for q.k)
@@ -97,14 +97,34 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, hh = lane >> 5;
 
-  int n = blockIdx.x;
-  if (remap) {
-    const int per = gridDim.x >> 3;
-    n = (n & 7) * per + (n >> 3);
+  // Workgroup -> (query tile, batch*head). The hardware deals workgroups round-robin over the
+  // 8 XCDs (each with its own L2), so with remap every XCD gets a contiguous set of heads.
+  // order 0 (head-major): one head's tiles back to back, heaviest causal tile first, so the
+  // concurrently running workgroups of an XCD share few K/V heads. order 1 (rank-major, for
+  // causal launches): all heads' heaviest tiles first, then the next rank -- longest work first
+  // across the whole launch, so no heavy tile starts at the end and leaves the chip idle.
+  const int HB = a.Hq * a.B;
+  int qt, bh;
+  if (order == 1) {
+    if (remap) {                                  // HB % 8 == 0
+      const int per_x = HB >> 3, k = blockIdx.x >> 3;
+      qt = n_qt - 1 - k / per_x;
+      bh = (blockIdx.x & 7) * per_x + k % per_x;
+    } else {
+      qt = n_qt - 1 - (int)(blockIdx.x / HB);
+      bh = blockIdx.x % HB;
+    }
+  } else {
+    int n = blockIdx.x;
+    if (remap) {                                  // gridDim % 8 == 0
+      const int per = gridDim.x >> 3;
+      n = (n & 7) * per + (n >> 3);
+    }
+    qt = n_qt - 1 - (n % n_qt);
+    bh = n / n_qt;
   }
-  const int qt = n_qt - 1 - (n % n_qt);
-  const int h = (n / n_qt) % a.Hq;
-  const int b = n / (n_qt * a.Hq);
+  const int h = bh % a.Hq;
+  const int b = bh / a.Hq;
   const int q0 = qt * BM;
   const int g = h / (a.Hq / a.Hkv);
   const int nkv = batch_kv_len(a, b);
@@ -595,7 +615,8 @@ template <int D, int BIAS, int MASK, bool NORM>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   const int n_qt = (a.Lq + BM - 1) / BM;
   const int64_t nwg = (int64_t)n_qt * a.Hq * a.B;
-  const int remap = (nwg % 8) == 0 ? 1 : 0;
+  const int order = a.causal != SDPA_CAUSAL_NONE ? 1 : 0;
+  const int remap = order == 1 ? ((a.Hq * a.B) % 8 == 0 ? 1 : 0) : (nwg % 8) == 0 ? 1 : 0;
   const size_t smem = Smem<D>::BYTES;
   static bool attr_set = false;                // raising the dynamic LDS limit is idempotent
   if (!attr_set) {
@@ -604,7 +625,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     attr_set = true;
   }
   hipLaunchKernelGGL((fwd_mfma_kernel<D, BIAS, MASK, NORM>), dim3((unsigned)nwg), dim3(NT), smem, s, a, n_qt,
-                     remap);
+                     remap, order);
   return hipGetLastError();
 }
 
