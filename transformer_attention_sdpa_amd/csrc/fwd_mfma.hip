@@ -33,6 +33,8 @@
 // * Grid: every XCD (the hardware deals consecutive workgroups round-robin over the 8 XCDs; each
 //   has its own L2) gets a contiguous set of heads. Non-causal launches run one head's tiles
 //   back to back (K/V reuse in L2); causal launches run longest tile first across all heads.
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace sdpa {
@@ -46,26 +48,34 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr int BM = 128;            // query rows per workgroup
 constexpr int BN = 64;             // keys per tile
 constexpr int NT = 256;            // threads per workgroup
-constexpr int VP = BN + 8;         // V^T row pitch in LDS (bf16): 144 bytes
 constexpr float LOG2E = 1.4426950408889634f;
 
 enum { BIAS_NONE = 0, BIAS_BF16 = 1, BIAS_F32 = 2 };
 enum { MASK_NONE = 0, MASK_DENSE = 1, MASK_INFO = 2 };
 
-// LDS row holding key k (0..31) of a 32-key block: inverse of the A-row -> key permutation that
-// makes accumulator entry 4*i + j of lane half h hold key 16*h + 4*i + j.
-__device__ __forceinline__ int k_lds_row(int k) { return 8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+// Key held by LDS row r (0..31) of a 32-key block of K: the A operand of S^T = K Q^T takes row
+// r, and this order makes accumulator entry 4*i + j of lane half h hold key 16*h + 4*i + j.
+__device__ __forceinline__ int k_row_key(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
 
+// LDS tiles hold whole 16-byte chunks (8 bf16) of D-element rows with no padding; the chunk
+// positions within a row are XOR-swizzled so that the reads below hit distinct banks:
+//   K: the 16 lanes of a half-wave read one chunk of 16 consecutive rows (b128 reads);
+//   V: a transposed read covers 4 consecutive rows x 4 chunks per 32 lanes.
 template <int D>
-struct Smem {                                            // two K buffers, two V^T buffers, key factors
-  static constexpr int KP = D + 8;                       // K row pitch (bf16)
-  static constexpr int K_ELEMS = BN * KP;
-  static constexpr int V_ELEMS = D * VP;
-  static constexpr int BYTES = 2 * (K_ELEMS + V_ELEMS) * 2 + 2 * BN * 4;
-};
+__device__ __forceinline__ int k_swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int v_swz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
+// One wave instruction of a direct global -> LDS load: lane l copies 16 bytes from byte offset
+// voff of r into lds + 16*l (M0 holds lds). (Kept out of the kernel body: used there
+// directly, the host pass drops the kernel's stub.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
 
 // Buffer resource over `bytes` bytes from `base`: loads past the end return 0 (the hardware's
 // range check), which zero-fills ragged tails without branches.
@@ -81,17 +91,16 @@ constexpr float RESCALE_SLACK = 8.0f;   // log2 units: the running max moves onl
 
 template <int D, int BIAS, int MASK, bool NORM>
 __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, int remap, int order) {
-  using S = Smem<D>;
-  constexpr int KP = S::KP;
   constexpr int DC = D / 16;         // 16-wide head-dim chunks (MFMA k steps for q.k)
   constexpr int DB = D / 32;         // 32-row blocks of O^T
-  constexpr int KCH = BN * (D / 8) / NT;   // 16-byte K chunks per thread per tile
-  constexpr int VIT = 32 * (D / 8) / NT;   // (key pair, chunk) V items per thread per tile
+  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int SPT = BN * CPR / NT; // direct-load instructions per thread per tile (K or V)
+  constexpr int TILE = BN * D;       // elements of one K or V tile in LDS
   constexpr bool FUSED = (BIAS == BIAS_NONE) && !NORM;   // logits = scale*log2e * q.k only
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  uint16_t* const kbuf0 = reinterpret_cast<uint16_t*>(smem_raw);
-  uint16_t* const vbuf0 = kbuf0 + 2 * S::K_ELEMS;
-  float* const krv0 = reinterpret_cast<float*>(vbuf0 + 2 * S::V_ELEMS);
+  // Four statically distinct tile buffers, so that the compiler's wait-count tracking can tell a
+  // read of one from a direct load in flight into another.
+  __shared__ __align__(16) uint16_t kbuf0[TILE], kbuf1[TILE], vbuf0[TILE], vbuf1[TILE];
+  __shared__ __align__(16) float krv_s[NORM ? 2 * BN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -206,35 +215,31 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- staging of K/V tiles: global -> registers -> LDS ----------------------------------
-  // Per-thread byte offsets inside a tile are fixed; each tile gets fresh buffer resources whose
-  // range ends at kv_len, so keys past kv_lengths arrive as zeros (never a poisoned tail).
-  // K runs two tiles ahead of the compute (its scores are formed one iteration early), V one.
-  int koff[KCH], voff0[VIT];
+  // ---- K/V tiles: direct global -> LDS loads --------------------------------------------
+  // Instruction u of wave w fills slots 256*u + 64*w + lane of a tile (slot = 16 bytes). K slot
+  // (row R, position p) holds chunk p ^ k_swz(R) of key 32*(R/32) + k_row_key(R%32); V slot
+  // (row r, position p) holds chunk p ^ v_swz(r) of key r. Each tile gets fresh buffer resources
+  // whose range ends at kv_len, so keys past kv_lengths arrive as zeros (never a poisoned tail).
+  int kdoff[SPT], vdoff[SPT];
 #pragma unroll
-  for (int u = 0; u < KCH; ++u) {
-    const int c = tid + NT * u;
-    koff[u] = (c / (D / 8)) * k_row_bytes + (c % (D / 8)) * 16;
+  for (int u = 0; u < SPT; ++u) {
+    const int sl = NT * u + tid, row = sl / CPR, pos = sl % CPR;
+    kdoff[u] = ((row & ~31) + k_row_key(row & 31)) * k_row_bytes + (pos ^ k_swz<D>(row)) * 16;
+    vdoff[u] = row * v_row_bytes + (pos ^ v_swz<D>(row)) * 16;
   }
-#pragma unroll
-  for (int u = 0; u < VIT; ++u) {
-    const int it = tid + NT * u;
-    voff0[u] = (2 * (it & 31)) * v_row_bytes + (it >> 5) * 16;
-  }
-  uint4 kr[KCH], vr0[VIT], vr1[VIT];
-  float krv = 0.f;
-  auto gload_k = [&](int k0) {
+  auto dma_k = [&](int k0, uint16_t* dst) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (int64_t)k0 * a.k_ss, (int64_t)(nkv - k0) * k_row_bytes);
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) kr[u] = buf_load16(rk, koff[u]);
+    for (int u = 0; u < SPT; ++u) dma16(rk, dst + 8 * (NT * u + 64 * wave), kdoff[u]);
   };
-  auto gload_v = [&](int k0) {
+  auto dma_v = [&](int k0, uint16_t* dst) {
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (int64_t)k0 * a.v_ss, (int64_t)(nkv - k0) * v_row_bytes);
 #pragma unroll
-    for (int u = 0; u < VIT; ++u) {
-      vr0[u] = buf_load16(rv, voff0[u]);
-      vr1[u] = buf_load16(rv, voff0[u] + v_row_bytes);
-    }
+    for (int u = 0; u < SPT; ++u) dma16(rv, dst + 8 * (NT * u + 64 * wave), vdoff[u]);
+  };
+  // key factors 1/rms of the keys of a tile (QK-norm only): one per thread below BN
+  float krv = 0.f;
+  auto load_krv = [&](int k0) {
     if constexpr (NORM) {
       if (tid < BN) {
         const int j = k0 + tid;
@@ -242,42 +247,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
       }
     }
   };
-  auto sstore_k = [&](int stage) {
-    uint16_t* ks = kbuf0 + stage * S::K_ELEMS;
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int c = tid + NT * u;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int lrow = (row & ~31) + k_lds_row(row & 31);
-      *reinterpret_cast<uint4*>(ks + lrow * KP + col) = kr[u];
-    }
-  };
-  auto sstore_v = [&](int stage) {
-    uint16_t* vt = vbuf0 + stage * S::V_ELEMS;
-#pragma unroll
-    for (int u = 0; u < VIT; ++u) {
-      const int it = tid + NT * u;
-      const int pr = it & 31, col = (it >> 5) * 8;
-      const uint32_t w0[4] = {vr0[u].x, vr0[u].y, vr0[u].z, vr0[u].w};
-      const uint32_t w1[4] = {vr1[u].x, vr1[u].y, vr1[u].z, vr1[u].w};
-      uint32_t* dst = reinterpret_cast<uint32_t*>(vt + col * VP) + pr;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        dst[(2 * t) * (VP / 2)] = pack_lo(w0[t], w1[t]);
-        dst[(2 * t + 1) * (VP / 2)] = pack_hi(w0[t], w1[t]);
-      }
-    }
-    if constexpr (NORM) {
-      if (tid < BN) krv0[stage * BN + tid] = krv;
-    }
-  };
-  // K(t+2) into the K buffer freed by K(t), V(t+1) into the one freed by V(t-1); then the
-  // loads of K(t+3) and V(t+2). Past the last tile this stages copies nobody reads.
-  auto staging = [&](int t) {
-    sstore_k(t & 1);
-    sstore_v((t + 1) & 1);
-    gload_k(tile_k0c(t + 3));
-    gload_v(tile_k0c(t + 2));
+  // K fragment (A operand of S^T = K Q^T): LDS row R = 32*kb + ql, head-dim elements 16*c + 8*hh
+  auto kfrag_at = [&](const uint16_t* ks, int c, int kb) -> bf16x8 {
+    const int row = 32 * kb + ql;
+    return *reinterpret_cast<const bf16x8*>(ks + row * D + (((2 * c + hh) ^ k_swz<D>(row)) << 3));
   };
   // S^T = K Q^T for two 32-key blocks (two independent MFMA chains, interleaved)
   auto compute_s = [&](const uint16_t* ks, f32x16 (&sacc)[2]) {
@@ -288,11 +261,23 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (32 * kb + ql) * KP + 16 * c + 8 * hh);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qB[c], sacc[kb], 0, 0, 0);
-      }
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag_at(ks, c, kb), qB[c], sacc[kb], 0, 0, 0);
     }
+  };
+  // V^T fragment (A operand of O^T += V^T P^T) by two transposed reads: within each 16-lane
+  // group the read hands lane i the values of 4 rows at the column lane i addresses, so lane L
+  // receives V[32*kb + 16*(L/32) + 8*sh + t][32*d + L%32], t = 0..7 -- the keys whose
+  // probabilities lane L holds as the B operand.
+  const int vr_l = 16 * (lane >> 5) + ((lane & 15) >> 2);          // row within the 8-row step
+  const int vc_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);        // column within 32 (elements)
+  const int vsw = v_swz<D>(vr_l);                                    // same for rows vr_l + 4, + 8k
+  auto vfrag_at = [&](const uint16_t* vt, int kb, int sh, int d) -> bf16x8 {
+    const int col = 32 * d + vc_l;
+    const uint16_t* p0 = vt + (32 * kb + 8 * sh + vr_l) * D + ((((col >> 3) ^ vsw) << 3) | (col & 7));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 4 * D));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
   };
 
   f32x16 o[DB];
@@ -308,18 +293,38 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
   const int64_t mask_row = (MASK == MASK_DENSE && i_me < a.Lq)
                                ? b * a.mask_sb + h * a.mask_sh + (int64_t)i_me * a.mask_sq : -1;
 
-  // ---- pipeline prologue: K0, V0, K1 in LDS; K2 and V1 in flight; S(0) formed -------------
+  // ---- pipeline prologue: K0, V0, K1 in LDS; S(0) formed ----------------------------------
+  // K(t) lives in buffer t & 1, V(t) in buffer t & 1.
   f32x16 s_cur[2];
   if (n_tiles > 0) {
-    gload_k(tile_k0(0)); gload_v(tile_k0(0)); sstore_k(0); sstore_v(0);
-    gload_k(tile_k0c(1)); sstore_k(1);
-    gload_k(tile_k0c(2)); gload_v(tile_k0c(1));
+    dma_k(tile_k0(0), kbuf0);
+    dma_v(tile_k0(0), vbuf0);
+    dma_k(tile_k0c(1), kbuf1);
+    load_krv(tile_k0(0));
+    __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (NORM) {
+      if (tid < BN) krv_s[tid] = krv;
+    }
   }
   __syncthreads();
   if (n_tiles > 0 && tile_k0(0) < k_end_w) compute_s(kbuf0, s_cur);
-  __syncthreads();                                       // K buffer 0 is rewritten in iteration 0
+  __syncthreads();                                       // K buffer 0 is refilled in iteration 0
 
-  for (int t = 0; t < n_tiles; ++t) {
+  // ---- one tile; P = t & 1 fixes every buffer's role at compile time -----------------------
+  // At the start the direct loads of K(t+2) (into the K buffer freed by K(t), whose scores were
+  // formed in the previous iteration) and V(t+1) (into the V buffer freed by V(t-1)) are
+  // issued; they land while this tile is computed. The iteration ends with every load of this
+  // wave complete and a barrier, so no load is pending across the loop header (the compiler's
+  // wait-count tracking is conservative where the header merges its incoming states).
+  auto iter = [&](auto PAR_, int t) {
+    constexpr int P = decltype(PAR_)::value;
+    uint16_t* const kfree = P ? kbuf1 : kbuf0;
+    const uint16_t* const knext = P ? kbuf0 : kbuf1;
+    uint16_t* const vfree = P ? vbuf0 : vbuf1;
+    const uint16_t* const vcur = P ? vbuf1 : vbuf0;
+    dma_k(tile_k0c(t + 2), kfree);
+    dma_v(tile_k0c(t + 1), vfree);
+    load_krv(tile_k0c(t + 1));
     const int k0 = tile_k0(t);
     if (k0 < k_end_w) {
       // -- element masking, only on tiles that need it --------------------------------------
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
 #pragma unroll
           for (int e = 0; e < 16; ++e) s_cur[kb][e] *= c_lane;
           if constexpr (NORM) {
-            const float4* kq = reinterpret_cast<const float4*>(krv0 + (t & 1) * BN + 32 * kb + 16 * hh);
+            const float4* kq = reinterpret_cast<const float4*>(krv_s + P * BN + 32 * kb + 16 * hh);
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
               const float4 r4 = kq[v4];
@@ -481,14 +486,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
                                    pw[8 * kb + 4 * sh + 3]);
         return __builtin_bit_cast(bf16x8, w);
       };
-      const uint16_t* ksn = kbuf0 + ((t + 1) & 1) * S::K_ELEMS;
-      const uint16_t* vt = vbuf0 + (t & 1) * S::V_ELEMS;
-      auto kfrag = [&](int c, int kb) {
-        return *reinterpret_cast<const bf16x8*>(ksn + (32 * kb + ql) * KP + 16 * c + 8 * hh);
-      };
+      auto kfrag = [&](int c, int kb) { return kfrag_at(knext, c, kb); };
       auto vfrag = [&](int i) {                          // i = (kb*2 + sh)*DB + d
-        const int d = i % DB, sh = (i / DB) & 1, kb = i / (2 * DB);
-        return *reinterpret_cast<const bf16x8*>(vt + (32 * d + ql) * VP + 32 * kb + 16 * hh + 8 * sh);
+        return vfrag_at(vcur, i / (2 * DB), (i / DB) & 1, i % DB);
       };
 
       // LDS fragments are read PF chunks ahead of the MFMA that consumes them
@@ -532,59 +532,27 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
         for (int f = EL_A + i * EL_B / NB; f < EL_A + (i + 1) * EL_B / NB; ++f) prob(f);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // staging ops: K writes, V writes (4 row pairs per item), then the loads that refill the
-      // staging registers
-      constexpr int OPS = KCH + 4 * VIT + KCH + VIT;
-      const int kn = tile_k0c(t + 3), vn = tile_k0c(t + 2);
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (int64_t)kn * a.k_ss, (int64_t)(nkv - kn) * k_row_bytes);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (int64_t)vn * a.v_ss, (int64_t)(nkv - vn) * v_row_bytes);
-      uint16_t* ks_w = kbuf0 + (t & 1) * S::K_ELEMS;
-      uint16_t* vt_w = vbuf0 + ((t + 1) & 1) * S::V_ELEMS;
-      auto stage_op = [&](int j) {
-        if (j < KCH) {
-          const int c = tid + NT * j;
-          const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-          const int lrow = (row & ~31) + k_lds_row(row & 31);
-          *reinterpret_cast<uint4*>(ks_w + lrow * KP + col) = kr[j];
-        } else if (j < KCH + 4 * VIT) {
-          const int u = (j - KCH) >> 2, q4 = (j - KCH) & 3;
-          const int it = tid + NT * u;
-          const int pr = it & 31, col = (it >> 5) * 8;
-          const uint32_t w0 = q4 == 0 ? vr0[u].x : q4 == 1 ? vr0[u].y : q4 == 2 ? vr0[u].z : vr0[u].w;
-          const uint32_t w1 = q4 == 0 ? vr1[u].x : q4 == 1 ? vr1[u].y : q4 == 2 ? vr1[u].z : vr1[u].w;
-          uint32_t* dst = reinterpret_cast<uint32_t*>(vt_w + col * VP) + pr;
-          dst[(2 * q4) * (VP / 2)] = pack_lo(w0, w1);
-          dst[(2 * q4 + 1) * (VP / 2)] = pack_hi(w0, w1);
-        } else if (j < 2 * KCH + 4 * VIT) {
-          const int u = j - KCH - 4 * VIT;
-          kr[u] = buf_load16(rk, koff[u]);
-        } else {
-          const int u = j - 2 * KCH - 4 * VIT;
-          vr0[u] = buf_load16(rv, voff0[u]);
-          vr1[u] = buf_load16(rv, voff0[u] + v_row_bytes);
-        }
-      };
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {                     // ---- block B2: keys 32..63 + staging
+      for (int i = 0; i < NB; ++i) {                     // ---- block B2: keys 32..63
         if (i + PF < NB) vf[(NB + i + PF) % (PF + 1)] = vfrag(NB + i + PF);
         o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(NB + i) % (PF + 1)], pb(1, i / DB), o[i % DB], 0, 0, 0);
-#pragma unroll
-        for (int j = i * OPS / NB; j < (i + 1) * OPS / NB; ++j) stage_op(j);
         __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (NORM) {
-        if (tid < BN) krv0[((t + 1) & 1) * BN + tid] = krv;
-        if (tid < BN) {
-          const int j = vn + tid;
-          krv = j < nkv ? a.k_rinv[((int64_t)b * a.Lkv + j) * a.Hkv + g] : 0.f;
-        }
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_next[kb];
-    } else {
-      staging(t);
+    }
+    __builtin_amdgcn_s_waitcnt(0);                       // this wave's loads have landed
+    if constexpr (NORM) {
+      if (tid < BN) krv_s[(1 - P) * BN + tid] = krv;
     }
     __syncthreads();
+  };
+  std::integral_constant<int, 0> I0;
+  std::integral_constant<int, 1> I1;
+  for (int t = 0; t < n_tiles; t += 2) {
+    iter(I0, t);
+    if (t + 1 >= n_tiles) break;
+    iter(I1, t + 1);
   }
 
   // ---- epilogue: O / l; NaN for rows without keys; 0 past q_lengths -------------------------
@@ -617,14 +585,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   const int64_t nwg = (int64_t)n_qt * a.Hq * a.B;
   const int order = a.causal != SDPA_CAUSAL_NONE ? 1 : 0;
   const int remap = order == 1 ? ((a.Hq * a.B) % 8 == 0 ? 1 : 0) : (nwg % 8) == 0 ? 1 : 0;
-  const size_t smem = Smem<D>::BYTES;
-  static bool attr_set = false;                // raising the dynamic LDS limit is idempotent
-  if (!attr_set) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_mfma_kernel<D, BIAS, MASK, NORM>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, BIAS, MASK, NORM>), dim3((unsigned)nwg), dim3(NT), smem, s, a, n_qt,
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, BIAS, MASK, NORM>), dim3((unsigned)nwg), dim3(NT), 0, s, a, n_qt,
                      remap, order);
   return hipGetLastError();
 }
