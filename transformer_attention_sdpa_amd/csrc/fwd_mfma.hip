@@ -271,11 +271,22 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
   const int vr_l = 16 * (lane >> 5) + ((lane & 15) >> 2);          // row within the 8-row step
   const int vc_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);        // column within 32 (elements)
   const int vsw = v_swz<D>(vr_l);                                    // same for rows vr_l + 4, + 8k
-  auto vfrag_at = [&](const uint16_t* vt, int kb, int sh, int d) -> bf16x8 {
+  // per-lane offsets of the two reads of a fragment, for each 32-column block d. The upper one
+  // is hidden from the optimizer: folded back into "lower + 4 rows", its pointer chain grows
+  // past what the compiler tracks to keep the buffer's alias information, and every such read
+  // would then wait for all direct loads in flight.
+  int voff_lo[DB], voff_hi[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) {
     const int col = 32 * d + vc_l;
-    const uint16_t* p0 = vt + (32 * kb + 8 * sh + vr_l) * D + ((((col >> 3) ^ vsw) << 3) | (col & 7));
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 4 * D));
+    voff_lo[d] = vr_l * D + ((((col >> 3) ^ vsw) << 3) | (col & 7));
+    voff_hi[d] = voff_lo[d] + 4 * D;
+    asm volatile("" : "+v"(voff_hi[d]));
+  }
+  auto vfrag_at = [&](const uint16_t* vt, int kb, int sh, int d) -> bf16x8 {
+    const int rows = (32 * kb + 8 * sh) * D;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vt + (rows + voff_lo[d])));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vt + (rows + voff_hi[d])));
     const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
   };
