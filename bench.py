@@ -40,8 +40,10 @@ KERNEL_SOURCE = os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc", "fw
 def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    # the GPU's clocks take some 10-20 ms of sustained work to ramp up after the idle seconds of
+    # input generation: 100 untimed launches (about 30 ms of prefill) reach the steady state
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU budget of the oracle baseline")
     p.add_argument("--copy-calibration", action="store_true",
