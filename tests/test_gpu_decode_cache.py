@@ -149,3 +149,27 @@ def test_head_rms_norm_random_vs_oracle(lib):
     ref = oracle.rms_rows(x)
     np.testing.assert_allclose(y.cpu().numpy(), ref, rtol=0, atol=2e-6)
     assert np.all(y.cpu().numpy()[1, 2, 4] == 0.0)
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 16), (16, 8), (32, 8), (32, 4), (32, 2), (16, 1)])
+def test_decode_tile_and_split_edges(lib, hq, hkv):
+    # the matrix-core decode works in 32-key tiles and 512-key splits: lengths on and around
+    # both edges, every query-heads-per-K/V-head ratio it takes (1..16), default splits
+    lens = np.array([1, 2, 31, 32, 33, 63, 511, 512, 513, 1024, 1025, 1040], dtype=np.int32)
+    say(f"decode edges hq={hq} hkv={hkv}")
+    d = decode_case(len(lens), hq, hkv, 128, 1040, 1040, 1040, base=700 + hq + hkv)
+    d.kv_lengths = lens                                   # rows past each length are never read
+    out, _, _ = run_decode(d)
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_close(got, oracle_decode(d), "bf16", f"decode edges {hq}/{hkv}")
+
+
+def test_decode_batch_above_64(lib):
+    # more sequences than one wave's lanes: the one-workgroup-per-split form
+    say("decode batch 70")
+    d = decode_case(70, 8, 2, 128, 600, 1, 600, base=720)
+    out, _, _ = run_decode(d)
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_close(got, oracle_decode(d), "bf16", "decode batch 70")

@@ -8,19 +8,19 @@
 //
 // The work is bound by streaming the cache from HBM (about 4 flops per byte), so the design
 // is about bytes in flight and coalescing, not about matrix units:
-//   pass 1 (decode_split): one workgroup per (K/V head g, key split s, sequence b). It streams
-//     its split in tiles of 64 keys: 16-byte loads of whole K and V rows into LDS, the loads of
-//     the next tile issued before the current one is consumed. Every query head that shares g
-//     (grouped-query attention) is scored from the same tile: lane = key for q.k (bf16 dot2
-//     with fp32 accumulate), lane = pair of head-dim elements for p*V. The online softmax is
-//     kept in the exp2 domain (logits pre-multiplied by scale*log2 e). The split writes its
-//     running max m, sum l and unnormalised output o in fp32.
+//   pass 1: one workgroup per (K/V head g, key split s, sequence b) scores every query head
+//     that shares g (grouped-query attention) from the same K/V tiles and writes the split's
+//     running max m, sum l and unnormalised output o in fp32. The online softmax is kept in
+//     the exp2 domain (logits pre-multiplied by scale*log2 e).
+//     - decode_split_mfma (head dim 128, 512-key splits, up to 16 query heads per K/V head):
+//       one wave streams 32-key tiles through a three-stage LDS ring filled by direct global ->
+//       LDS loads and does q.k and p.V on the matrix cores (see that kernel).
+//     - decode_split (the other bf16 shapes): 256 threads stream 64-key tiles through LDS with
+//       16-byte loads, lane = key for q.k (bf16 dot2), lane = pair of head-dim elements for p.V.
 //   pass 2 (decode_combine): per (query head, sequence), the splits merge by log-sum-exp:
 //     M = max m_s, out = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s. This merge is exact because
 //     the online softmax is associative (NNlib "Fused implementation": softmax taken online
 //     over tiles of keys). No key at all gives NaN ("Fused implementation").
-#include <algorithm>
-
 #include "device_common.h"
 
 namespace sdpa {
@@ -169,6 +169,216 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
   }
 }
 
+// ---- matrix-core variant of pass 1 --------------------------------------------------------
+// One wave per (K/V head g, 512-key split, sequence b). The split streams through LDS in
+// 32-key tiles, filled by direct global -> LDS loads into a ring of three stages, so that two
+// tiles are in flight while one is computed; there are no staging registers and no LDS stores.
+// The 16 tiles of a split are unrolled into straight-line code: every stage is a distinct LDS
+// array, which lets the compiler's wait-count tracking tell a read of one stage from a load in
+// flight into another.
+//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 head-dim values of K, B = Q^T with
+//     the group's r query heads as columns (padded to 16 with zeros).
+//   The 16x16 accumulator gives lane l the scores of keys 4*(l/16) + i (i = 0..3) of a 16-key
+//     block for head l%16. For a 32-key chunk the lane's 8 probabilities, taken as the MFMA k
+//     index 8*(l/16) + s (s < 4: block 0, s >= 4: block 1), are directly the B operand of
+//     O^T += V^T P^T; the A operand V^T is read with ds_read_b64_tr_b16 for the same key order.
+//   Softmax in the exp2 domain as in pass 1 above; row sums of the bf16 probabilities the
+//     MFMA consumes.
+constexpr int kMfTile = 32;                    // keys per tile
+constexpr int kMfSplit = 512;                  // keys per split (16 tiles)
+constexpr int kMfTileElems = kMfTile * kDecD;  // 4096 bf16 = 8 KB
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void dec_lds_void;
+
+// One wave instruction of a direct load: lane l copies 16 bytes from byte offset voff of r into
+// lds + 16*l. (Kept out of the kernel body: used there directly, the host pass drops the stub.)
+__device__ __forceinline__ void dec_dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (dec_lds_void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dec_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+// 16-byte chunk positions of a 256-byte LDS row are XOR-swizzled: K fragment reads (16 rows,
+// one chunk) and transposed V reads (8 rows, two chunks per 32 lanes) then hit distinct banks.
+__device__ __forceinline__ int dec_kswz(int row) { return row & 15; }
+__device__ __forceinline__ int dec_vswz(int row) { return 2 * (row & 7); }
+
+// Per-lane state of one wave of the matrix-core pass 1. The loop-invariant offsets are set once;
+// the softmax state and the output accumulators belong to the chunk being processed.
+struct MfWave {
+  int lane, col, grp;
+  int kdo[8], vdo[8];          // direct-load byte offsets (K, V) of the lane's 8 slots per tile
+  int vo_lo[8], vo_hi[8];      // element offsets of the two transposed V reads per 16-row block
+  bf16x8_t qf[4];              // Q^T operand of the current (sequence, K/V head)
+  f32x4_t o[8];                // O^T accumulators, 16 head-dim rows each
+  float m, lp0, lp1;           // running max (log2 units), two partial row sums
+};
+
+__device__ __forceinline__ void mf_init(MfWave& w, const DecodeArgs& a) {
+  w.lane = threadIdx.x & 63;
+  w.col = w.lane & 15;
+  w.grp = w.lane >> 4;
+  const int k_row_bytes = (int)(a.k_ss * 2), v_row_bytes = (int)(a.v_ss * 2);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int sl = 64 * u + w.lane, row = sl >> 4, pos = sl & 15;
+    w.kdo[u] = row * k_row_bytes + ((pos ^ dec_kswz(row)) << 4);
+    w.vdo[u] = row * v_row_bytes + ((pos ^ dec_vswz(row)) << 4);
+  }
+  const int vrow = 4 * w.grp + ((w.lane & 15) >> 2);
+  const int vsw = dec_vswz(vrow);                   // rows vrow + 16 share it
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const int c = 16 * db + 4 * (w.lane & 3);
+    w.vo_lo[db] = vrow * kDecD + ((((c >> 3) ^ vsw) << 3) | (c & 7));
+    w.vo_hi[db] = w.vo_lo[db] + 16 * kDecD;
+    asm volatile("" : "+v"(w.vo_hi[db]));           // keeps each address one step from its buffer
+  }
+}
+
+// Q^T (B operand) of sequence b, K/V head g: lane holds query head g*r + col, head-dim
+// 32*c + 8*grp + 0..7; padded columns (col >= r) are zero. Resets the chunk state.
+__device__ __forceinline__ void mf_begin(MfWave& w, const DecodeArgs& a, int b, int g, int r) {
+  const bool head_ok = w.col < r;
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + (int64_t)(g * r + (head_ok ? w.col : 0)) * a.q_sh;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint4 x = head_ok ? *reinterpret_cast<const uint4*>(qp + 32 * c + 8 * w.grp) : make_uint4(0, 0, 0, 0);
+    w.qf[c] = __builtin_bit_cast(bf16x8_t, x);
+  }
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w.o[db][e] = 0.f;
+  w.m = -INFINITY;
+  w.lp0 = 0.f;
+  w.lp1 = 0.f;
+}
+
+// Direct loads of keys [j0, j0 + 32) of (b, g) into one ring stage; rows at or past j_end read 0.
+__device__ __forceinline__ void mf_load(const MfWave& w, const DecodeArgs& a, int b, int g, int j0, int j_end,
+                                        uint16_t* kd, uint16_t* vd) {
+  const int64_t rows = (int64_t)j_end - j0;
+  const uint16_t* kb = static_cast<const uint16_t*>(a.k) + b * a.k_sb + g * a.k_sh + (int64_t)j0 * a.k_ss;
+  const uint16_t* vb = static_cast<const uint16_t*>(a.v) + b * a.v_sb + g * a.v_sh + (int64_t)j0 * a.v_ss;
+  const __amdgpu_buffer_rsrc_t rk = dec_rsrc(kb, rows * a.k_ss * 2);
+  const __amdgpu_buffer_rsrc_t rv = dec_rsrc(vb, rows * a.v_ss * 2);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) dec_dma16(rk, kd + 512 * u, w.kdo[u]);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) dec_dma16(rv, vd + 512 * u, w.vdo[u]);
+}
+
+// One 32-key tile (keys j0.. of which those below j_end count) from a ring stage.
+__device__ __forceinline__ void mf_tile(MfWave& w, const DecodeArgs& a, int j0, int j_end, const uint16_t* ks,
+                                        const uint16_t* vs) {
+  f32x4_t sc[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sc[kb][e] = 0.f;
+    const int row = 16 * kb + w.col;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(ks + row * kDecD + (((4 * c + w.grp) ^ dec_kswz(row)) << 3));
+      sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, w.qf[c], sc[kb], 0, 0, 0);
+    }
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + 16 * kb + 4 * w.grp + i;
+      const float x = j < j_end ? sc[kb][i] * a.scale_log2 : -INFINITY;
+      sc[kb][i] = x;
+      tmax = fmaxf(tmax, x);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  const float m_new = fmaxf(w.m, tmax);             // finite: the tile holds a key of the chunk
+  const float alpha = __builtin_amdgcn_exp2f(w.m - m_new);
+  w.m = m_new;
+  w.lp0 *= alpha;
+  w.lp1 *= alpha;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w.o[db][e] *= alpha;
+  uint32_t pw[4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const bf16x2_t p01 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][0] - m_new)),
+                          static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][1] - m_new))};
+    const bf16x2_t p23 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][2] - m_new)),
+                          static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][3] - m_new))};
+    pw[2 * kb] = __builtin_bit_cast(uint32_t, p01);
+    pw[2 * kb + 1] = __builtin_bit_cast(uint32_t, p23);
+    w.lp0 = __builtin_amdgcn_fdot2_f32_bf16(p01, __builtin_bit_cast(bf16x2_t, 0x3f803f80u), w.lp0, false);
+    w.lp1 = __builtin_amdgcn_fdot2_f32_bf16(p23, __builtin_bit_cast(bf16x2_t, 0x3f803f80u), w.lp1, false);
+  }
+  const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(vs + w.vo_lo[db]));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(vs + w.vo_hi[db]));
+    const s16x8_t vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    w.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv), pb, w.o[db], 0, 0, 0);
+  }
+}
+
+// Partials of one chunk: running max (log2 units), row sum, unnormalised output.
+__device__ __forceinline__ void mf_store(const MfWave& w, const DecodeArgs& a, int b, int g, int r, int split) {
+  float lsum = w.lp0 + w.lp1;
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (w.col >= r) return;
+  const int64_t slot = ((int64_t)b * a.Hq + g * r + w.col) * a.max_splits + split;
+  if (w.grp == 0) {
+    a.part_ml[2 * slot] = w.m;
+    a.part_ml[2 * slot + 1] = lsum;
+  }
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    *reinterpret_cast<float4*>(a.part_o + slot * kDecD + 16 * db + 4 * w.grp) =
+        make_float4(w.o[db][0], w.o[db][1], w.o[db][2], w.o[db][3]);
+}
+
+constexpr int kMfTiles = kMfSplit / kMfTile;     // 16 tiles per chunk
+
+// One workgroup (one wave) per (K/V head, split, sequence).
+__global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
+  __shared__ __align__(16) uint16_t k0s[kMfTileElems], k1s[kMfTileElems], k2s[kMfTileElems];
+  __shared__ __align__(16) uint16_t v0s[kMfTileElems], v1s[kMfTileElems], v2s[kMfTileElems];
+  const int r = a.Hq / a.Hkv;
+  const int g = blockIdx.x % a.Hkv;
+  const int split = blockIdx.x / a.Hkv;
+  const int b = blockIdx.y;
+  const int nkv = clampi(a.kv_lengths[b], 0, a.cap);
+  const int j_begin = split * kMfSplit;
+  if (j_begin >= nkv) return;                       // wave-uniform
+  const int j_end = min(j_begin + kMfSplit, nkv);
+  MfWave w;
+  mf_init(w, a);
+  mf_begin(w, a, b, g, r);
+  uint16_t* const kst[3] = {k0s, k1s, k2s};
+  uint16_t* const vst[3] = {v0s, v1s, v2s};
+  mf_load(w, a, b, g, j_begin, j_end, kst[0], vst[0]);
+  mf_load(w, a, b, g, j_begin + kMfTile, j_end, kst[1], vst[1]);
+#pragma unroll
+  for (int t = 0; t < kMfTiles; ++t) {              // three stages: two tiles in flight
+    if (t + 2 < kMfTiles) mf_load(w, a, b, g, j_begin + kMfTile * (t + 2), j_end, kst[(t + 2) % 3], vst[(t + 2) % 3]);
+    if (j_begin + kMfTile * t < j_end) mf_tile(w, a, j_begin + kMfTile * t, j_end, kst[t % 3], vst[t % 3]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);                    // no direct load may land after the wave ends
+  mf_store(w, a, b, g, r, split);
+}
+
 __global__ __launch_bounds__(kDecD) void decode_combine_kernel(DecodeArgs a) {
   const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int nkv = clampi(a.kv_lengths[b], 0, a.cap);
@@ -219,10 +429,22 @@ bool decode_fast_supports(const DecodeArgs& a, int in_dtype) {
   return true;
 }
 
+// The matrix-core pass 1 takes 512-key splits, up to 16 query heads per K/V head and 16-byte
+// aligned query rows (the rest of decode_fast_supports holds as well).
+static bool decode_mfma_supports(const DecodeArgs& a) {
+  const int r = a.Hq / a.Hkv;
+  if (a.split_len != kMfSplit || r > 16) return false;
+  if ((reinterpret_cast<uintptr_t>(a.q) & 15) || ((a.q_sb | a.q_sh) & 7)) return false;
+  // byte offsets of 32 rows and the 32-bit buffer ranges
+  if ((int64_t)kMfTile * a.k_ss * 2 > INT32_MAX || (int64_t)kMfTile * a.v_ss * 2 > INT32_MAX) return false;
+  return true;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int r = a.Hq / a.Hkv;
   dim3 grid(a.Hkv * a.max_splits, a.B);
-  if (r <= 4) hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kDecThreads), 0, s, a);
+  if (decode_mfma_supports(a)) hipLaunchKernelGGL(decode_split_mfma_kernel, grid, dim3(64), 0, s, a);
+  else if (r <= 4) hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kDecThreads), 0, s, a);
   else hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kDecThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
