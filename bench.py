@@ -33,8 +33,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fwd_mfma_causal_b4h16d128l4096_counters.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc", "fwd_mfma.hip")
+PREFILL_COUNTERS = (os.path.join(ROOT, "profiles", "fwd_mfma_causal_b4h16d128l4096_counters.txt"),
+                    os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc", "fwd_mfma.hip"))
+DECODE_COUNTERS = (os.path.join(ROOT, "profiles", "decode_gqa_b64h32kv8d128_counters.txt"),
+                   os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc", "decode.hip"))
 
 
 def parse_args():
@@ -58,15 +60,16 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def counters_traffic(flops_per_launch):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken from
-    the current kernel source; else None."""
-    if not os.path.exists(PROFILE_COUNTERS):
+def counters_traffic(counters):
+    """HBM bytes per launch from a committed rocprofv3 counter summary (path, kernel source), if
+    it was taken from the current kernel source; else None."""
+    summary, source = counters
+    if not os.path.exists(summary):
         return None
-    text = open(PROFILE_COUNTERS).read()
+    text = open(summary).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(KERNEL_SOURCE):
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(source):
         return None
     return float(m_bytes.group(1))
 
@@ -178,7 +181,7 @@ def main():
         "config": {"workload": "causal_prefill", "batch": B, "heads": Hq, "head_dim": D, "q_len": Lq,
                    "kv_len": Lkv, "is_causal": True, "scale": w.scale, "out_dtype": "bf16"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": counters_traffic(flops),
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": counters_traffic(PREFILL_COUNTERS),
                      "kernel": "fwd_mfma_kernel<128,0,0>", "flops_per_launch": flops},
         "parity": {"rows_checked": f"{len(rows)} query rows x {B * Hq} (batch, head)", "max_abs": p_max,
                    "rel_l2": p_rel, "bar": "max_abs <= 2e-2, rel_l2 <= 5e-3 (bf16 output)"},
@@ -228,7 +231,7 @@ def main():
                        "capacity": d.k_cache.shape[1], "kv_lengths": "U{1024..8192} (seeded)",
                        "sum_kv_lengths": int(np.sum(d.kv_lengths))},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counters_traffic(DECODE_COUNTERS),
                          "bytes_per_step": kv_bytes + io_bytes,
                          "note": "split + combine kernels together (one sdpa_decode call)"},
             "parity": {"sequences_checked": sel, "max_abs": float(np.max(np.abs(diff))),
