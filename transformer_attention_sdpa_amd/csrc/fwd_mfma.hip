@@ -12,20 +12,25 @@
 // Mapping onto CDNA4
 // ------------------
 // * One workgroup = 4 waves = a tile of 128 query rows of one (batch, head); each wave owns 32
-//   rows. The workgroup streams tiles of 64 keys of the matching K/V head through LDS, double
-//   buffered: the global loads of tile t+1 are issued before tile t is consumed.
+//   rows; two workgroups share a CU (two waves per SIMD). The workgroup streams tiles of 64 keys
+//   of the matching K/V head through LDS. Direct global -> LDS loads (no staging registers) of
+//   K(t+2) and V(t+1) are issued as tile t starts and have landed by its end.
 // * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16
 //   head-dim values from LDS, B = the wave's Q^T kept in registers for the whole loop). K rows are
 //   written to LDS in a permuted order so that the 16 accumulator entries a lane receives are 16
 //   consecutive keys of one query row. That makes every row reduction mostly in-lane (one swap
 //   with lane^32) and lets the probabilities P^T feed the next MFMA directly as its B operand, in
 //   registers, with no LDS round trip.
-// * O^T += V^T P^T with the same instruction; V is transposed into LDS while being staged
-//   (pairs of keys packed into one 32-bit LDS word).
-// * The online softmax runs in the exp2 domain: logits are multiplied by scale*log2(e) (and the
-//   bias by log2(e)), so each probability costs one v_exp_f32. A row that has seen no allowed key
-//   keeps m = -inf and contributes nothing; if it ends with l = 0 it is written as NaN
-//   ("Fused implementation": a query that attends no key).
+// * O^T += V^T P^T with the same instruction; V stays row-major in LDS and its A operand is read
+//   with ds_read_b64_tr_b16, which transposes 16-bit elements on the way out of LDS.
+// * S(t+1) is formed while the probabilities of S(t) are taken, so that the matrix cores and the
+//   VALU work on independent instructions.
+// * The online softmax runs in the exp2 domain. Without bias and QK-norm, scale*log2(e) is
+//   folded into Q once and the q.k MFMAs start from -m (the running max) instead of zero, so a
+//   probability is a single v_exp_f32 of the accumulator; otherwise the logits are multiplied by
+//   scale*log2(e) (and the bias by log2(e)) first. A row that has seen no allowed key
+//   contributes nothing; if it ends with l = 0 it is written as NaN ("Fused implementation": a
+//   query that attends no key).
 // * Element masking (causal, kv_lengths, mask) is applied only on tiles that need it; tiles past
 //   a wave's causal limit are skipped by that wave, tiles past the workgroup's limit are not
 //   loaded. Keys past kv_lengths are loaded as zeros, so a poisoned cache tail never reaches
@@ -193,7 +198,18 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-      const uint4 x = buf_load16(rq, qoff + 32 * c);
+      uint4 x = buf_load16(rq, qoff + 32 * c);
+      if constexpr (FUSED) {
+        // scale*log2e folded into Q (rounded to bf16 once): the q.k MFMAs then emit logits in
+        // the exp2 domain, and the softmax needs no multiply per score
+        uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float lo = __uint_as_float(w[t] << 16) * c_lane, hi = __uint_as_float(w[t] & 0xffff0000u) * c_lane;
+          w[t] = (uint32_t)float_to_bf16_bits(lo) | ((uint32_t)float_to_bf16_bits(hi) << 16);
+        }
+        x = make_uint4(w[0], w[1], w[2], w[3]);
+      }
       qB[c] = __builtin_bit_cast(bf16x8, x);
       if constexpr (NORM) {
         const uint32_t w[4] = {x.x, x.y, x.z, x.w};
@@ -296,8 +312,16 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
   for (int d = 0; d < DB; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
-  // finite start: exp2 of (masked -inf) - m_run is 0, and any finite score grows it at once
-  float m_run = -1.0e30f, l_run = 0.f;
+  // Running max m_run (log2 units) and row sum l_run.
+  //  * FUSED: the scores are kept relative to the running max -- the q.k MFMAs start from
+  //    -m_run instead of zero, so they emit scale*log2e*q.k - m_run and a
+  //    probability is one exp2. m_run starts at 0 with threshold thr = -inf: the first tile
+  //    holding an allowed key of a row sets the row's max outright; after that the max moves
+  //    only when it grows by more than RESCALE_SLACK.
+  //  * otherwise: finite start, so exp2 of (masked -inf) - m_run is 0, and any finite score
+  //    grows it at once.
+  float m_run = FUSED ? 0.f : -1.0e30f, l_run = 0.f;
+  float thr = -INFINITY;
 
   const int64_t bias_row = (BIAS != BIAS_NONE && i_me < a.Lq)
                                ? b * a.bias_sb + h * a.bias_sh + (int64_t)i_me * a.bias_sq : -1;
@@ -305,8 +329,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
                                ? b * a.mask_sb + h * a.mask_sh + (int64_t)i_me * a.mask_sq : -1;
 
   // ---- pipeline prologue: K0, V0, K1 in LDS; S(0) formed ----------------------------------
-  // K(t) lives in buffer t & 1, V(t) in buffer t & 1.
-  f32x16 s_cur[2];
+  // K(t) lives in buffer t & 1, V(t) in buffer t & 1; S(t) in s_even (FUSED: s_odd for odd t).
+  f32x16 s_even[2], s_odd[2];
   if (n_tiles > 0) {
     dma_k(tile_k0(0), kbuf0);
     dma_v(tile_k0(0), vbuf0);
@@ -318,7 +342,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
     }
   }
   __syncthreads();
-  if (n_tiles > 0 && tile_k0(0) < k_end_w) compute_s(kbuf0, s_cur);
+  if (n_tiles > 0 && tile_k0(0) < k_end_w) compute_s(kbuf0, s_even);   // m_run = 0: from zero
   __syncthreads();                                       // K buffer 0 is refilled in iteration 0
 
   // ---- one tile; P = t & 1 fixes every buffer's role at compile time -----------------------
@@ -329,6 +353,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
   // wait-count tracking is conservative where the header merges its incoming states).
   auto iter = [&](auto PAR_, int t) {
     constexpr int P = decltype(PAR_)::value;
+    // FUSED: the two score tiles swap roles every tile; otherwise (more live registers in the
+    // bias and norm variants) S(t+1) is copied over S(t) at the end of the tile
+    constexpr bool SWAP = FUSED && P;
+    f32x16(&s_cur)[2] = SWAP ? s_odd : s_even;          // S(t)
+    f32x16(&s_next)[2] = SWAP ? s_even : s_odd;         // S(t+1), formed in block A
     uint16_t* const kfree = P ? kbuf1 : kbuf0;
     const uint16_t* const knext = P ? kbuf0 : kbuf1;
     uint16_t* const vfree = P ? vbuf0 : vbuf1;
@@ -453,8 +482,27 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s_cur[kb][e]);
-      if constexpr (FUSED) mt *= c_lane;                 // c_lane > 0 (the launcher requires it)
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + RESCALE_SLACK)) {
+      if constexpr (FUSED) {
+        // s_cur holds scores minus m_run: mt is the growth of the row max (thr: see above)
+        if (__builtin_amdgcn_ballot_w64(mt > thr)) {
+          mt = fmaxf(mt, __shfl_xor(mt, 32, 64));        // row max over both halves
+          const bool grow = mt > thr;                    // thr is the same for both halves
+          const float dlt = grow ? mt : 0.f;
+          // a row's first keys: nothing accumulated yet (and exp2(-dlt) may overflow)
+          const float alpha = thr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(-dlt);
+          l_run *= alpha;
+#pragma unroll
+          for (int d = 0; d < DB; ++d)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s_cur[kb][e] -= dlt;
+          m_run += dlt;
+          if (grow) thr = RESCALE_SLACK;
+        }
+      } else if (__builtin_amdgcn_ballot_w64(mt > m_run + RESCALE_SLACK)) {
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));          // row max over both halves
         const bool grow = mt > m_run + RESCALE_SLACK;
         const float m_new = grow ? mt : m_run;
@@ -483,7 +531,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
       uint32_t pw[16];                                   // the same, packed as bf16 pairs
       auto prob = [&](int f) {                           // element f = 16*kb + 8*sh + e
         const float xe = s_cur[f >> 4][f & 15];
-        pf[f] = FUSED ? __builtin_amdgcn_exp2f(fmaf(xe, c_lane, -m_use)) : __builtin_amdgcn_exp2f(xe - m_use);
+        pf[f] = FUSED ? __builtin_amdgcn_exp2f(xe) : __builtin_amdgcn_exp2f(xe - m_use);
         if (f & 1) {
           typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
           const bf16x2v pr = {static_cast<__bf16>(pf[f - 1]), static_cast<__bf16>(pf[f])};
@@ -504,8 +552,16 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
 
       // LDS fragments are read PF chunks ahead of the MFMA that consumes them
       constexpr int PF = 2;
-      f32x16 s_next[2];
       bf16x8 kf[PF + 1][2];
+      // the C operand that starts S(t+1): zero, or -m_run broadcast (FUSED). Built here from an
+      // opaque copy of m_run, so that its 16 registers live only until the first two MFMAs.
+      f32x16 c0;
+      {
+        float m0 = FUSED ? -m_run : 0.f;
+        if constexpr (FUSED) asm volatile("" : "+v"(m0));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) c0[e] = m0;
+      }
 #pragma unroll
       for (int c = 0; c < PF; ++c) {
         kf[c][0] = kfrag(c, 0);
@@ -523,10 +579,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (c == 0) {
-            f32x16 z;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) z[e] = 0.f;
-            s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][kb], qB[0], z, 0, 0, 0);
+            s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][kb], qB[0], c0, 0, 0, 0);
           } else {
             s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c % (PF + 1)][kb], qB[c], s_next[kb], 0, 0, 0);
           }
@@ -549,8 +602,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
         o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(NB + i) % (PF + 1)], pb(1, i / DB), o[i % DB], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (!FUSED) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_next[kb];
+        for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_next[kb];
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);                       // this wave's loads have landed
     if constexpr (NORM) {
