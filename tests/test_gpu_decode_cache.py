@@ -85,8 +85,9 @@ def test_decode_equals_fwd_bottom_right(lib):
     kvl = torch.as_tensor(d.kv_lengths, device="cuda")
     ref = sa.sdpa(q, kc, vc, is_causal="bottom_right", kv_lengths=kvl, scale=d.scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    # same operation; the forward kernel rounds P to bf16 for the matrix cores, decode keeps it in
-    # fp32, so the two agree to the bf16 bar rather than bit for bit
+    # same operation, but the two kernels round differently (the forward kernel folds the scale
+    # into bf16 Q and sums over 64-key tiles, decode sums bf16 P over 512-key splits and merges
+    # them), so they agree to the bf16 bar rather than bit for bit
     assert_close(out.cpu().numpy(), ref.cpu().numpy(), "bf16", "decode vs fwd")
     assert_close(out.cpu().numpy(), oracle_decode(d), "bf16", "decode vs oracle")
 
@@ -163,6 +164,18 @@ def test_decode_tile_and_split_edges(lib, hq, hkv):
     got = out.cpu().numpy()
     assert np.isfinite(got).all()
     assert_close(got, oracle_decode(d), "bf16", f"decode edges {hq}/{hkv}")
+
+
+@pytest.mark.parametrize("B", [130, 260])
+def test_decode_large_batches(lib, B):
+    # 130 sequences: the linear work order locates items across three 64-sequence chunks;
+    # 260: more sequences than that order takes, so the (split, sequence) grid
+    say(f"decode batch {B}")
+    d = decode_case(B, 8, 2, 128, 1100, 1, 1100, base=730 + B)
+    out, _, _ = run_decode(d)
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_close(got, oracle_decode(d), "bf16", f"decode batch {B}")
 
 
 def test_decode_batch_above_64(lib):

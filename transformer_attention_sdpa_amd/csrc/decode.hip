@@ -14,7 +14,8 @@
 //     the exp2 domain (logits pre-multiplied by scale*log2 e).
 //     - decode_split_mfma (head dim 128, 512-key splits, up to 16 query heads per K/V head):
 //       one wave streams 32-key tiles through a three-stage LDS ring filled by direct global ->
-//       LDS loads and does q.k and p.V on the matrix cores (see that kernel).
+//       LDS loads and does q.k and p.V on the matrix cores (see that kernel). Its grid is
+//       linear: all full splits first, then the partial ones, then idle workgroups (mf_locate).
 //     - decode_split (the other bf16 shapes): 256 threads stream 64-key tiles through LDS with
 //       16-byte loads, lane = key for q.k (bf16 dot2), lane = pair of head-dim elements for p.V.
 //   pass 2 (decode_combine): per (query head, sequence), the splits merge by log-sum-exp:
@@ -351,15 +352,67 @@ __device__ __forceinline__ void mf_store(const MfWave& w, const DecodeArgs& a, i
 
 constexpr int kMfTiles = kMfSplit / kMfTile;     // 16 tiles per chunk
 
-// One workgroup (one wave) per (K/V head, split, sequence).
+// Work order of the linear grid (batches up to kLinMaxB sequences): item i of K/V head g is
+// workgroup Hkv*i + g; the items are the full splits of all sequences, sequence by sequence,
+// then the partial last splits; workgroups past the last item exit at once. Compared with a
+// (split, sequence) grid, the workgroups with nothing to do no longer hold slots in between the
+// real ones (each keeps its LDS until it has read kv_lengths and left), and the shorter partial
+// splits run last. Every lane reads the lengths of sequences lane, lane + 64, ... (all loads in
+// flight together); a wave prefix sum of the split counts then locates the item.
+constexpr int kLinMaxB = 256;
+
+__device__ __forceinline__ bool mf_locate(const DecodeArgs& a, int item, int& b, int& split, int& nkv) {
+  const int lane = threadIdx.x & 63;
+  int len[kLinMaxB / 64];
+#pragma unroll
+  for (int c = 0; c < kLinMaxB / 64; ++c) {
+    const int bb = 64 * c + lane;
+    len[c] = bb < a.B ? clampi(a.kv_lengths[bb], 0, a.cap) : 0;
+  }
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {            // 0: full splits, 1: partial last splits
+#pragma unroll
+    for (int c = 0; c < kLinMaxB / 64; ++c) {
+      const int cnt = pass == 0 ? len[c] / kMfSplit : (len[c] % kMfSplit != 0 ? 1 : 0);
+      int incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      const int tot = __shfl(incl, 63, 64);
+      if (item < tot) {                             // wave-uniform
+        const int l = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl > item));
+        b = 64 * c + l;
+        nkv = __shfl(len[c], l, 64);
+        split = pass == 0 ? item - __shfl(incl - cnt, l, 64) : nkv / kMfSplit;
+        return true;
+      }
+      item -= tot;
+    }
+  }
+  return false;
+}
+
+// One workgroup (one wave) per (K/V head, split, sequence); LINEAR: see mf_locate, else the grid
+// is (Hkv * max_splits, B) and splits past a sequence's length exit at once.
+template <bool LINEAR>
 __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   __shared__ __align__(16) uint16_t k0s[kMfTileElems], k1s[kMfTileElems], k2s[kMfTileElems];
   __shared__ __align__(16) uint16_t v0s[kMfTileElems], v1s[kMfTileElems], v2s[kMfTileElems];
   const int r = a.Hq / a.Hkv;
   const int g = blockIdx.x % a.Hkv;
-  const int split = blockIdx.x / a.Hkv;
-  const int b = blockIdx.y;
-  const int nkv = clampi(a.kv_lengths[b], 0, a.cap);
+  int b, split, nkv;
+  if constexpr (LINEAR) {
+    if (!mf_locate(a, (int)(blockIdx.x / a.Hkv), b, split, nkv)) return;
+    b = __builtin_amdgcn_readfirstlane(b);
+    split = __builtin_amdgcn_readfirstlane(split);
+    nkv = __builtin_amdgcn_readfirstlane(nkv);
+  } else {
+    split = blockIdx.x / a.Hkv;
+    b = blockIdx.y;
+    nkv = clampi(a.kv_lengths[b], 0, a.cap);
+  }
   const int j_begin = split * kMfSplit;
   if (j_begin >= nkv) return;                       // wave-uniform
   const int j_end = min(j_begin + kMfSplit, nkv);
@@ -443,7 +496,12 @@ static bool decode_mfma_supports(const DecodeArgs& a) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int r = a.Hq / a.Hkv;
   dim3 grid(a.Hkv * a.max_splits, a.B);
-  if (decode_mfma_supports(a)) hipLaunchKernelGGL(decode_split_mfma_kernel, grid, dim3(64), 0, s, a);
+  if (decode_mfma_supports(a)) {
+    if (a.B <= kLinMaxB && (int64_t)a.Hkv * a.max_splits * a.B <= INT32_MAX)
+      hipLaunchKernelGGL(decode_split_mfma_kernel<true>, dim3(a.Hkv * a.max_splits * a.B), dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL(decode_split_mfma_kernel<false>, grid, dim3(64), 0, s, a);
+  }
   else if (r <= 4) hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kDecThreads), 0, s, a);
   else hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kDecThreads), 0, s, a);
   hipError_t e = hipGetLastError();
