@@ -123,17 +123,20 @@ SDPA_API size_t sdpa_fwd_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor
                                 int32_t qk_norm);
 
 /* ---------------------------------------------------------------------------------------
- * sdpa_decode -- one query position per sequence against a KV cache: the cached attention of
- * the keras issue on MultiHeadAttention (its list of extensions puts cached attention first)
- * and the decode loop of the Flax discussion on nnx.MultiHeadAttention with decode=True.
- * Same result as sdpa_fwd with Lq == 1, is_causal = BOTTOM_RIGHT and these kv_lengths (the
- * NNlib "Examples" show that equivalence for a cache).
+ * sdpa_decode -- the newest T query positions of each sequence against a KV cache: the cached
+ * attention of the keras issue on MultiHeadAttention (its list of extensions puts cached
+ * attention first) and the decode loop of the Flax discussion on nnx.MultiHeadAttention with
+ * decode=True (T = 1); T > 1 is the NNlib "Examples" cache case with several new queries.
+ * Same result as sdpa_fwd with Lq == T, is_causal = BOTTOM_RIGHT and these kv_lengths (page
+ * "Neural Network primitives from NNlib.jl", "Arguments": is_causal and kv_lengths): query t
+ * (0-based) of sequence b attends keys [0, kv_lengths[b] - T + t].
  *
- * q {D, Hq, 1, B} BF16 or F32; k_cache, v_cache {D, Hkv, capacity, B}, same dtype;
- * kv_lengths device int32 [B] (required): keys [0, kv_lengths[b]) are attended;
- * out {D, Hq, 1, B} F32 or BF16. num_splits: key splits per sequence (0 = library choice);
+ * q {D, Hq, T, B} BF16 or F32, 0 <= T <= capacity; k_cache, v_cache {D, Hkv, capacity, B}, same
+ * dtype; kv_lengths device int32 [B] (required), clamped to [0, capacity];
+ * out {D, Hq, T, B} F32 or BF16. num_splits: key splits per sequence (0 = library choice);
  * the partial results are merged by a log-sum-exp pass. workspace: at least
- * sdpa_decode_workspace_bytes(). kv_lengths[b] == 0 gives a NaN row.
+ * sdpa_decode_workspace_bytes(), which grows with T. A query with no key to attend
+ * (kv_lengths[b] - T + t < 0) gives a NaN row.
  * ------------------------------------------------------------------------------------- */
 SDPA_API sdpa_status sdpa_decode(const sdpa_tensor* q, const sdpa_tensor* k_cache, const sdpa_tensor* v_cache,
                         const int32_t* kv_lengths, float scale, int32_t num_splits,

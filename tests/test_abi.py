@@ -134,6 +134,9 @@ def test_workspace_sizes(lib):
     # 512 keys per split by default -> 16 splits; (D + 2) floats per (b, head, split)
     assert lib.sdpa_decode_workspace_bytes(ctypes.byref(qd), ctypes.byref(kc), 0) == 64 * 32 * 16 * 130 * 4
     assert lib.sdpa_decode_workspace_bytes(ctypes.byref(qd), ctypes.byref(kc), 4) == 64 * 32 * 4 * 130 * 4
+    # T query tokens: one partial per (b, token, head, split)
+    q3 = T([128, 32, 3, 64])
+    assert lib.sdpa_decode_workspace_bytes(ctypes.byref(q3), ctypes.byref(kc), 0) == 64 * 3 * 32 * 16 * 130 * 4
 
 
 def test_decode_validation(lib):
@@ -142,7 +145,9 @@ def test_decode_validation(lib):
         return lib.sdpa_decode(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), kvl, math.nan, splits,
                                ctypes.byref(o), ws, wsb, None)
     assert call(kvl=None) == N.SDPA_ERR_NULL
-    assert call(q=T([128, 32, 2, 4]), o=T([128, 32, 2, 4])) == N.SDPA_ERR_SHAPE
+    assert call(q=T([128, 32, 65, 4]), o=T([128, 32, 65, 4])) == N.SDPA_ERR_SHAPE   # more tokens than capacity
+    assert call(q=T([128, 32, 3, 4]), o=T([128, 32, 2, 4])) == N.SDPA_ERR_SHAPE    # out tokens != q tokens
+    assert call(q=T([128, 32, 3, 4]), o=T([128, 32, 3, 4]), wsb=4 * 3 * 32 * 130 * 4 - 1) == N.SDPA_ERR_WORKSPACE
     assert call(splits=-1) == N.SDPA_ERR_SHAPE
     assert call(wsb=16) == N.SDPA_ERR_WORKSPACE
     assert call(k=T([64, 8, 64, 4])) == N.SDPA_ERR_SHAPE

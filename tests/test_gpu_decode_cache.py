@@ -186,3 +186,48 @@ def test_decode_batch_above_64(lib):
     got = out.cpu().numpy()
     assert np.isfinite(got).all()
     assert_close(got, oracle_decode(d), "bf16", "decode batch 70")
+
+
+def decode_case_t(B, Hq, Hkv, D, T, cap, kv_min, kv_max, base):
+    return workloads.gqa_decode(B=B, Hq=Hq, Hkv=Hkv, D=D, capacity=cap, kv_min=kv_min, kv_max=kv_max, base=base,
+                                q_len=T)
+
+
+@pytest.mark.parametrize("shape,num_splits", [
+    ((3, 32, 8, 128, 3, 700, 1, 700), 0),      # 4 heads x 3 tokens in one column group
+    ((2, 16, 2, 128, 4, 1100, 2, 1100), 0),    # 8 x 4: two column groups
+    ((2, 8, 8, 128, 16, 600, 20, 600), 0),     # 1 x 16 tokens
+    ((2, 32, 2, 128, 2, 1040, 1000, 1040), 0),  # 16 x 2: two groups, lengths around the split edges
+    ((70, 8, 2, 128, 3, 600, 1, 600), 0),      # more sequences than one wave's lanes
+    ((3, 32, 8, 128, 3, 700, 1, 700), 3),      # explicit splits: the general kernel
+    ((3, 8, 2, 64, 3, 300, 1, 300), 0),        # head dim 64: the general kernel
+    ((2, 8, 8, 128, 20, 300, 30, 300), 0),     # 20 tokens: the general kernel
+])
+def test_decode_multi_token(lib, shape, num_splits):
+    # query t of sequence b attends keys [0, kv_lengths[b] - T + t]; a sequence shorter than T
+    # leaves its first queries with no key at all (NaN rows, in the same places as the oracle)
+    B, Hq, Hkv, D, T, cap, lo, hi = shape
+    say(f"decode T={T} {shape} splits={num_splits}")
+    d = decode_case_t(B, Hq, Hkv, D, T, cap, lo, hi, base=740 + B + Hq + T)
+    out, _, _ = run_decode(d, num_splits)
+    assert out.shape == (B, T, Hq, D)
+    assert_close(out.cpu().numpy(), oracle_decode(d), "bf16", f"decode T={T} {shape}")
+
+
+def test_decode_three_queries_nnlib_cache_example(lib):
+    # NNlib "Examples": three new queries against caches of kv_lengths [13, 23, 33, 43] behave
+    # as q_offset [10, 20, 30, 40]; the same lengths here, 8 heads of 128
+    say("decode T=3 at kv_lengths 13, 23, 33, 43")
+    d = decode_case_t(4, 8, 8, 128, 3, 48, 48, 48, base=760)
+    d.kv_lengths = np.array([13, 23, 33, 43], dtype=np.int32)
+    out, kc, vc = run_decode(d)
+    assert np.isfinite(out.cpu().numpy()).all()
+    assert_close(out.cpu().numpy(), oracle_decode(d), "bf16", "decode T=3 vs oracle")
+    # the cache slots past kv_lengths hold NaN sentinels: sdpa_fwd is told the lengths too, as
+    # decode is (a causally masked NaN value row would still poison the product, 0 * NaN)
+    q = dev(d.q, "bf16")
+    kvl = torch.as_tensor(d.kv_lengths, device="cuda")
+    ref = sa.sdpa(q, kc, vc, is_causal=True, q_offset=torch.tensor([10, 20, 30, 40], dtype=torch.int32, device="cuda"),
+                  kv_lengths=kvl, scale=d.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref.cpu().numpy(), "bf16", "decode T=3 vs fwd with q_offset")

@@ -176,11 +176,12 @@ def decode_workspace_bytes(q, k_cache, num_splits=0) -> int:
 
 def sdpa_decode(q, k_cache, v_cache, kv_lengths, *, scale=None, num_splits=0, out=None, out_dtype=None,
                 workspace=None, stream=None):
-    """One query per sequence: q [B][1][Hq][D] against caches [B][cap][Hkv][D], keys [0, kv_lengths[b])."""
+    """The newest T queries of each sequence, q [B][T][Hq][D], against caches [B][cap][Hkv][D]:
+    query t attends keys [0, kv_lengths[b] - T + t] (bottom-right causal)."""
     lib = N.load()
-    B, _, Hq, D = q.shape
+    B, T, Hq, D = q.shape
     if out is None:
-        out = torch.empty((B, 1, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+        out = torch.empty((B, T, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
     dq, dk, dv, do = desc(q), desc(k_cache), desc(v_cache), desc(out)
     kv = torch.as_tensor(kv_lengths, dtype=torch.int32, device=q.device).contiguous()
     need = int(lib.sdpa_decode_workspace_bytes(ctypes.byref(dq), ctypes.byref(dk), int(num_splits)))

@@ -253,7 +253,8 @@ size_t sdpa_decode_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k_ca
   const int64_t cap = k_cache->dims[2];
   const int64_t len = decode_split_len(cap, num_splits);
   const int64_t max_splits = (cap + len - 1) / len;
-  return (size_t)(q->dims[3] * q->dims[1] * max_splits * (q->dims[0] + 2)) * sizeof(float);
+  const int64_t T = q->dims[2] > 0 ? q->dims[2] : 0;
+  return (size_t)(q->dims[3] * T * q->dims[1] * max_splits * (q->dims[0] + 2)) * sizeof(float);
 }
 
 sdpa_status sdpa_decode(const sdpa_tensor* q, const sdpa_tensor* kc, const sdpa_tensor* vc, const int32_t* kv_lengths,
@@ -262,7 +263,8 @@ sdpa_status sdpa_decode(const sdpa_tensor* q, const sdpa_tensor* kc, const sdpa_
   g_err.clear();
   if (!q || !kc || !vc || !out) return fail(SDPA_ERR_NULL, "q, k_cache, v_cache and out are required");
   if (!kv_lengths) return fail(SDPA_ERR_NULL, "kv_lengths is required for decode");
-  if (q->dims[2] != 1) return fail(SDPA_ERR_SHAPE, "decode takes one query position (q dims[2] == 1)");
+  if (q->dims[2] < 0 || q->dims[2] > kc->dims[2])
+    return fail(SDPA_ERR_SHAPE, "decode takes 0 to capacity query positions (q dims[2])");
   if (num_splits < 0) return fail(SDPA_ERR_SHAPE, "num_splits must be >= 0");
   if (kc->dims[0] != vc->dims[0] || q->dims[0] != vc->dims[0])
     return fail(SDPA_ERR_SHAPE, "decode needs equal q, k and v head dims");
@@ -273,16 +275,16 @@ sdpa_status sdpa_decode(const sdpa_tensor* q, const sdpa_tensor* kc, const sdpa_
   const size_t need = sdpa_decode_workspace_bytes(q, kc, num_splits);
   if (workspace_bytes < need || (need && !workspace))
     return fail(SDPA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
-  if (a.B == 0) return SDPA_OK;
+  if (a.B == 0 || a.Lq == 0) return SDPA_OK;
   if (!a.q || !a.out || (a.Lkv > 0 && (!a.k || !a.v))) return fail(SDPA_ERR_NULL, "a tensor's data is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   DecodeArgs d;
   std::memset(&d, 0, sizeof d);
   d.q = a.q; d.k = a.k; d.v = a.v; d.out = a.out;
-  d.B = a.B; d.Hq = a.Hq; d.Hkv = a.Hkv; d.D = a.D; d.cap = a.Lkv;
-  d.q_sb = a.q_sb; d.q_sh = a.q_sh; d.k_sb = a.k_sb; d.k_ss = a.k_ss; d.k_sh = a.k_sh;
-  d.v_sb = a.v_sb; d.v_ss = a.v_ss; d.v_sh = a.v_sh; d.o_sb = a.o_sb; d.o_sh = a.o_sh;
+  d.B = a.B; d.T = a.Lq; d.Hq = a.Hq; d.Hkv = a.Hkv; d.D = a.D; d.cap = a.Lkv;
+  d.q_sb = a.q_sb; d.q_ss = a.q_ss; d.q_sh = a.q_sh; d.k_sb = a.k_sb; d.k_ss = a.k_ss; d.k_sh = a.k_sh;
+  d.v_sb = a.v_sb; d.v_ss = a.v_ss; d.v_sh = a.v_sh; d.o_sb = a.o_sb; d.o_ss = a.o_ss; d.o_sh = a.o_sh;
   d.out_dtype = a.out_dtype;
   d.kv_lengths = kv_lengths;
   d.scale_log2 = a.scale * 1.4426950408889634f;
@@ -290,10 +292,10 @@ sdpa_status sdpa_decode(const sdpa_tensor* q, const sdpa_tensor* kc, const sdpa_
   d.max_splits = (int)((a.Lkv + d.split_len - 1) / d.split_len);
   if (d.max_splits > 0 && decode_fast_supports(d, a.in_dtype)) {
     d.part_o = static_cast<float*>(workspace);
-    d.part_ml = d.part_o + (size_t)a.B * a.Hq * d.max_splits * a.D;
+    d.part_ml = d.part_o + (size_t)a.B * a.Lq * a.Hq * d.max_splits * a.D;
     return hip_status(launch_decode(d, s), "sdpa_decode");
   }
-  // any other shape: the general kernel at one query, bottom-right causal, these kv_lengths
+  // any other shape: the general kernel at these T queries, bottom-right causal, these kv_lengths
   return hip_status(launch_fwd_generic(a, s), "sdpa_decode (generic)");
 }
 

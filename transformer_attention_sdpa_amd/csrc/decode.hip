@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
     const float lsum = wave_sum(l[u]);
     if (!active[u]) continue;
     const int hq = g * r + wave + 4 * u;
-    const int64_t slot = ((int64_t)b * a.Hq + hq) * a.max_splits + split;
+    const int64_t slot = ((int64_t)b * a.Hq + hq) * a.max_splits + split;   // one query token (T == 1)
     if (lane == 0) {
       a.part_ml[2 * slot] = m[u];
       a.part_ml[2 * slot + 1] = lsum;
@@ -218,6 +218,9 @@ struct MfWave {
   bf16x8_t qf[4];              // Q^T operand of the current (sequence, K/V head)
   f32x4_t o[8];                // O^T accumulators, 16 head-dim rows each
   float m, lp0, lp1;           // running max (log2 units), two partial row sums
+  bool cvalid;                 // this lane's column is a (query head, token) of the group
+  int hq, tok;                 // its query head and token
+  int jlim;                    // its keys end here (bottom-right causal), within the split
 };
 
 __device__ __forceinline__ void mf_init(MfWave& w, const DecodeArgs& a) {
@@ -242,14 +245,24 @@ __device__ __forceinline__ void mf_init(MfWave& w, const DecodeArgs& a) {
   }
 }
 
-// Q^T (B operand) of sequence b, K/V head g: lane holds query head g*r + col, head-dim
-// 32*c + 8*grp + 0..7; padded columns (col >= r) are zero. Resets the chunk state.
-__device__ __forceinline__ void mf_begin(MfWave& w, const DecodeArgs& a, int b, int g, int r) {
-  const bool head_ok = w.col < r;
-  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + (int64_t)(g * r + (head_ok ? w.col : 0)) * a.q_sh;
+// Q^T (B operand) of sequence b, K/V head g, column group cg: the group's r*T (query head,
+// token) pairs, token-minor, fill the 16 columns of each group; lane holds column col, head-dim
+// 32*c + 8*grp + 0..7; columns past the pairs are zero. Query token t of a sequence with nkv
+// keys attends keys below nkv - T + 1 + t (bottom-right causal); jlim is that limit cut to the
+// split [.., j_end). Resets the chunk state.
+__device__ __forceinline__ void mf_begin(MfWave& w, const DecodeArgs& a, int b, int g, int r, int cg, int nkv,
+                                         int j_end) {
+  const int pc = 16 * cg + w.col;
+  w.cvalid = pc < r * a.T;
+  const int hl = w.cvalid ? pc / a.T : 0;
+  w.tok = w.cvalid ? pc - hl * a.T : 0;
+  w.hq = g * r + hl;
+  w.jlim = min(j_end, nkv - a.T + 1 + w.tok);
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + (int64_t)w.tok * a.q_ss +
+                       (int64_t)w.hq * a.q_sh;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const uint4 x = head_ok ? *reinterpret_cast<const uint4*>(qp + 32 * c + 8 * w.grp) : make_uint4(0, 0, 0, 0);
+    const uint4 x = w.cvalid ? *reinterpret_cast<const uint4*>(qp + 32 * c + 8 * w.grp) : make_uint4(0, 0, 0, 0);
     w.qf[c] = __builtin_bit_cast(bf16x8_t, x);
   }
 #pragma unroll
@@ -296,14 +309,17 @@ __device__ __forceinline__ void mf_tile(MfWave& w, const DecodeArgs& a, int j0, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = j0 + 16 * kb + 4 * w.grp + i;
-      const float x = j < j_end ? sc[kb][i] * a.scale_log2 : -INFINITY;
+      const float x = j < w.jlim ? sc[kb][i] * a.scale_log2 : -INFINITY;
       sc[kb][i] = x;
       tmax = fmaxf(tmax, x);
     }
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-  const float m_new = fmaxf(w.m, tmax);             // finite: the tile holds a key of the chunk
-  const float alpha = __builtin_amdgcn_exp2f(w.m - m_new);
+  // a column may have no key in this tile yet (several tokens): its max stays -inf, and
+  // m_use = 0 keeps alpha and the probabilities at 0 instead of NaN
+  const float m_new = fmaxf(w.m, tmax);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(w.m - m_use);
   w.m = m_new;
   w.lp0 *= alpha;
   w.lp1 *= alpha;
@@ -314,10 +330,10 @@ __device__ __forceinline__ void mf_tile(MfWave& w, const DecodeArgs& a, int j0, 
   uint32_t pw[4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const bf16x2_t p01 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][0] - m_new)),
-                          static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][1] - m_new))};
-    const bf16x2_t p23 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][2] - m_new)),
-                          static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][3] - m_new))};
+    const bf16x2_t p01 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][0] - m_use)),
+                          static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][1] - m_use))};
+    const bf16x2_t p23 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][2] - m_use)),
+                          static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][3] - m_use))};
     pw[2 * kb] = __builtin_bit_cast(uint32_t, p01);
     pw[2 * kb + 1] = __builtin_bit_cast(uint32_t, p23);
     w.lp0 = __builtin_amdgcn_fdot2_f32_bf16(p01, __builtin_bit_cast(bf16x2_t, 0x3f803f80u), w.lp0, false);
@@ -338,8 +354,8 @@ __device__ __forceinline__ void mf_store(const MfWave& w, const DecodeArgs& a, i
   float lsum = w.lp0 + w.lp1;
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
-  if (w.col >= r) return;
-  const int64_t slot = ((int64_t)b * a.Hq + g * r + w.col) * a.max_splits + split;
+  if (!w.cvalid) return;
+  const int64_t slot = (((int64_t)b * a.T + w.tok) * a.Hq + w.hq) * a.max_splits + split;
   if (w.grp == 0) {
     a.part_ml[2 * slot] = w.m;
     a.part_ml[2 * slot + 1] = lsum;
@@ -394,22 +410,29 @@ __device__ __forceinline__ bool mf_locate(const DecodeArgs& a, int item, int& b,
   return false;
 }
 
-// One workgroup (one wave) per (K/V head, split, sequence); LINEAR: see mf_locate, else the grid
-// is (Hkv * max_splits, B) and splits past a sequence's length exit at once.
+// (query head, token) column groups of 16 per K/V head
+__host__ __device__ __forceinline__ int mf_groups(const DecodeArgs& a) { return ((a.Hq / a.Hkv) * a.T + 15) / 16; }
+
+// One workgroup (one wave) per (K/V head, column group, split, sequence): blockIdx.x = Hkv *
+// (groups * i + cg) + g. LINEAR: i is an item of mf_locate; else i is the split and the
+// sequence is blockIdx.y, and splits past a sequence's length exit at once.
 template <bool LINEAR>
 __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   __shared__ __align__(16) uint16_t k0s[kMfTileElems], k1s[kMfTileElems], k2s[kMfTileElems];
   __shared__ __align__(16) uint16_t v0s[kMfTileElems], v1s[kMfTileElems], v2s[kMfTileElems];
   const int r = a.Hq / a.Hkv;
+  const int ng = mf_groups(a);
   const int g = blockIdx.x % a.Hkv;
+  const int rest = blockIdx.x / a.Hkv;
+  const int cg = rest % ng;
   int b, split, nkv;
   if constexpr (LINEAR) {
-    if (!mf_locate(a, (int)(blockIdx.x / a.Hkv), b, split, nkv)) return;
+    if (!mf_locate(a, rest / ng, b, split, nkv)) return;
     b = __builtin_amdgcn_readfirstlane(b);
     split = __builtin_amdgcn_readfirstlane(split);
     nkv = __builtin_amdgcn_readfirstlane(nkv);
   } else {
-    split = blockIdx.x / a.Hkv;
+    split = rest / ng;
     b = blockIdx.y;
     nkv = clampi(a.kv_lengths[b], 0, a.cap);
   }
@@ -418,7 +441,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   const int j_end = min(j_begin + kMfSplit, nkv);
   MfWave w;
   mf_init(w, a);
-  mf_begin(w, a, b, g, r);
+  mf_begin(w, a, b, g, r, cg, nkv, j_end);
   uint16_t* const kst[3] = {k0s, k1s, k2s};
   uint16_t* const vst[3] = {v0s, v1s, v2s};
   mf_load(w, a, b, g, j_begin, j_end, kst[0], vst[0]);
@@ -433,10 +456,11 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
 }
 
 __global__ __launch_bounds__(kDecD) void decode_combine_kernel(DecodeArgs a) {
-  const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int hq = blockIdx.x % a.Hq, bt = blockIdx.x / a.Hq, d = threadIdx.x;   // bt = b * T + token
+  const int b = bt / a.T, t = bt - b * a.T;
   const int nkv = clampi(a.kv_lengths[b], 0, a.cap);
   const int nsp = (nkv + a.split_len - 1) / a.split_len;
-  const int64_t slot0 = ((int64_t)b * a.Hq + hq) * a.max_splits;
+  const int64_t slot0 = ((int64_t)bt * a.Hq + hq) * a.max_splits;
   const float* ml = a.part_ml + 2 * slot0;
   const float* po = a.part_o + slot0 * kDecD + d;
   // four splits per round, so that the loads of a round are in flight together
@@ -465,31 +489,35 @@ __global__ __launch_bounds__(kDecD) void decode_combine_kernel(DecodeArgs a) {
     }
   }
   const float res = (nsp > 0 && L > 0.f) ? O / L : NAN;
-  store_elem(a.out, b * a.o_sb + hq * a.o_sh + d, a.out_dtype, res);
+  store_elem(a.out, b * a.o_sb + t * a.o_ss + hq * a.o_sh + d, a.out_dtype, res);
 }
 
 }  // namespace
 
-bool decode_fast_supports(const DecodeArgs& a, int in_dtype) {
-  if (in_dtype != SDPA_BF16 || a.D != kDecD) return false;
-  const int r = a.Hq / a.Hkv;
-  if (r > 8) return false;
-  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-  // 16-byte row loads: rows aligned, strides multiples of 8 elements; q rows 4-byte aligned
-  if (!al16(a.k) || !al16(a.v)) return false;
-  if ((a.k_sb | a.k_ss | a.k_sh | a.v_sb | a.v_ss | a.v_sh) & 7) return false;
-  if ((reinterpret_cast<uintptr_t>(a.q) & 3) || ((a.q_sb | a.q_sh) & 1)) return false;
+// The matrix-core pass 1: 512-key splits, up to 16 query tokens and 8 column groups, 16-byte
+// aligned query rows (the K/V conditions of decode_fast_supports hold as well).
+constexpr int kMfMaxT = 16, kMfMaxGroups = 8;
+static bool decode_mfma_supports(const DecodeArgs& a) {
+  if (a.split_len != kMfSplit || a.T < 1 || a.T > kMfMaxT || mf_groups(a) > kMfMaxGroups) return false;
+  if ((reinterpret_cast<uintptr_t>(a.q) & 15) || ((a.q_sb | a.q_ss | a.q_sh) & 7)) return false;
+  // byte offsets of 32 rows and the 32-bit buffer ranges
+  if ((int64_t)kMfTile * a.k_ss * 2 > INT32_MAX || (int64_t)kMfTile * a.v_ss * 2 > INT32_MAX) return false;
   return true;
 }
 
-// The matrix-core pass 1 takes 512-key splits, up to 16 query heads per K/V head and 16-byte
-// aligned query rows (the rest of decode_fast_supports holds as well).
-static bool decode_mfma_supports(const DecodeArgs& a) {
-  const int r = a.Hq / a.Hkv;
-  if (a.split_len != kMfSplit || r > 16) return false;
-  if ((reinterpret_cast<uintptr_t>(a.q) & 15) || ((a.q_sb | a.q_sh) & 7)) return false;
-  // byte offsets of 32 rows and the 32-bit buffer ranges
-  if ((int64_t)kMfTile * a.k_ss * 2 > INT32_MAX || (int64_t)kMfTile * a.v_ss * 2 > INT32_MAX) return false;
+bool decode_fast_supports(const DecodeArgs& a, int in_dtype) {
+  if (in_dtype != SDPA_BF16 || a.D != kDecD) return false;
+  // grid limits: sequences in grid.y of the (split, sequence) grids, one combine workgroup per
+  // (query head, sequence, token)
+  if (a.B > 65535 || (int64_t)a.Hq * a.B * a.T > INT32_MAX) return false;
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  // 16-byte row loads: rows aligned, strides multiples of 8 elements
+  if (!al16(a.k) || !al16(a.v)) return false;
+  if ((a.k_sb | a.k_ss | a.k_sh | a.v_sb | a.v_ss | a.v_sh) & 7) return false;
+  if (decode_mfma_supports(a)) return true;
+  // the vector pass 1: one query token, up to 8 query heads per K/V head, 4-byte aligned q rows
+  if (a.T != 1 || a.Hq / a.Hkv > 8) return false;
+  if ((reinterpret_cast<uintptr_t>(a.q) & 3) || ((a.q_sb | a.q_sh) & 1)) return false;
   return true;
 }
 
@@ -497,16 +525,17 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int r = a.Hq / a.Hkv;
   dim3 grid(a.Hkv * a.max_splits, a.B);
   if (decode_mfma_supports(a)) {
-    if (a.B <= kLinMaxB && (int64_t)a.Hkv * a.max_splits * a.B <= INT32_MAX)
-      hipLaunchKernelGGL(decode_split_mfma_kernel<true>, dim3(a.Hkv * a.max_splits * a.B), dim3(64), 0, s, a);
+    const int64_t per_seq = (int64_t)a.Hkv * mf_groups(a) * a.max_splits;
+    if (a.B <= kLinMaxB && per_seq * a.B <= INT32_MAX)
+      hipLaunchKernelGGL(decode_split_mfma_kernel<true>, dim3((unsigned)(per_seq * a.B)), dim3(64), 0, s, a);
     else
-      hipLaunchKernelGGL(decode_split_mfma_kernel<false>, grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL(decode_split_mfma_kernel<false>, dim3((unsigned)per_seq, a.B), dim3(64), 0, s, a);
   }
   else if (r <= 4) hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kDecThreads), 0, s, a);
   else hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kDecThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.Hq, a.B), dim3(kDecD), 0, s, a);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((int64_t)a.Hq * a.B * a.T)), dim3(kDecD), 0, s, a);
   return hipGetLastError();
 }
 

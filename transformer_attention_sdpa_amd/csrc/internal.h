@@ -50,18 +50,18 @@ struct AttnArgs {
 };
 
 struct DecodeArgs {
-  const void* q;               // [B][1][Hq][D]
+  const void* q;               // [B][T][Hq][D]
   const void* k;               // [B][cap][Hkv][D]
   const void* v;
-  void* out;                   // [B][1][Hq][D]
-  int B, Hq, Hkv, D, cap;
-  int64_t q_sb, q_sh, k_sb, k_ss, k_sh, v_sb, v_ss, v_sh, o_sb, o_sh;
+  void* out;                   // [B][T][Hq][D]
+  int B, T, Hq, Hkv, D, cap;   // T: query tokens per sequence (the last T of its kv_lengths[b] keys)
+  int64_t q_sb, q_ss, q_sh, k_sb, k_ss, k_sh, v_sb, v_ss, v_sh, o_sb, o_ss, o_sh;
   int out_dtype;
   const int32_t* kv_lengths;
   float scale_log2;            // scale * log2(e)
   int split_len, max_splits;
-  float* part_o;               // [B][Hq][max_splits][D]
-  float* part_ml;              // [B][Hq][max_splits][2]: running max (log2 units), sum
+  float* part_o;               // [B][T][Hq][max_splits][D]
+  float* part_ml;              // [B][T][Hq][max_splits][2]: running max (log2 units), sum
 };
 
 struct MaskInfoArgs {

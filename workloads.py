@@ -179,12 +179,12 @@ def causal_prefill(B=4, H=16, D=128, L=4096, base=SEED_BASE) -> Attention:
 
 @dataclass
 class Decode:
-    """One decode step: KV caches, the new K/V rows, the write index and the query."""
+    """One decode step: KV caches, the T new K/V rows, the write index and the T queries."""
     name: str
-    q: np.ndarray            # bf16 bits [B][1][Hq][D]
+    q: np.ndarray            # bf16 bits [B][T][Hq][D]
     k_cache: np.ndarray      # bf16 bits [B][capacity][Hkv][D]
     v_cache: np.ndarray
-    k_new: np.ndarray        # bf16 bits [B][1][Hkv][D]
+    k_new: np.ndarray        # bf16 bits [B][T][Hkv][D]
     v_new: np.ndarray
     kv_lengths: np.ndarray   # int32 [B], lengths after the update
     scale: float
@@ -192,27 +192,29 @@ class Decode:
 
     @property
     def write_index(self) -> np.ndarray:
-        return (self.kv_lengths - 1).astype(np.int32)
+        """The T new rows go to slots kv_lengths[b] - T .. kv_lengths[b] - 1."""
+        return (self.kv_lengths - self.q.shape[1]).astype(np.int32)
 
 
 def gqa_decode(B=64, Hq=32, Hkv=8, D=128, capacity=8192, kv_min=1024, kv_max=8192,
-               base=SEED_BASE) -> Decode:
-    """GQA decode with a KV cache.
+               base=SEED_BASE, q_len=1) -> Decode:
+    """GQA decode with a KV cache; q_len new tokens per sequence (1: one decode step).
 
-    kv_lengths[b] ~ U{kv_min..kv_max}. Cache slots [0, kv_lengths[b]-1) hold N(0,1) past rows
-    (per-batch sub-streams, so one batch element can be regenerated alone); slots from
-    kv_lengths[b]-1 on hold a bf16 NaN, so a read of an unwritten slot shows in the output.
-    The new row goes to slot kv_lengths[b]-1.
+    kv_lengths[b] ~ U{kv_min..kv_max}. Cache slots [0, kv_lengths[b]-q_len) hold N(0,1) past
+    rows (per-batch sub-streams, so one batch element can be regenerated alone); slots from
+    kv_lengths[b]-q_len on hold a bf16 NaN, so a read of an unwritten slot shows in the output.
+    The new rows go to slots kv_lengths[b]-q_len .. kv_lengths[b]-1 (those below 0 are dropped
+    by the cache update).
     """
     k = 2
     kvlen = rng_for(k, TAG_KVLEN, base=base).integers(kv_min, kv_max + 1, size=B).astype(np.int32)
-    q = normal_tensor(rng_for(k, TAG_Q, base=base), (B, 1, Hq, D), "bf16")
-    k_new = normal_tensor(rng_for(k, TAG_KNEW, base=base), (B, 1, Hkv, D), "bf16")
-    v_new = normal_tensor(rng_for(k, TAG_VNEW, base=base), (B, 1, Hkv, D), "bf16")
+    q = normal_tensor(rng_for(k, TAG_Q, base=base), (B, q_len, Hq, D), "bf16")
+    k_new = normal_tensor(rng_for(k, TAG_KNEW, base=base), (B, q_len, Hkv, D), "bf16")
+    v_new = normal_tensor(rng_for(k, TAG_VNEW, base=base), (B, q_len, Hkv, D), "bf16")
     k_cache = np.full((B, capacity, Hkv, D), BF16_NAN_BITS, dtype=np.uint16)
     v_cache = np.full((B, capacity, Hkv, D), BF16_NAN_BITS, dtype=np.uint16)
     for b in range(B):
-        n = int(kvlen[b]) - 1
+        n = max(int(kvlen[b]) - q_len, 0)
         k_cache[b, :n] = decode_cache_rows(k, TAG_K, b, n, Hkv, D, base)
         v_cache[b, :n] = decode_cache_rows(k, TAG_V, b, n, Hkv, D, base)
     return Decode("gqa_decode", q, k_cache, v_cache, k_new, v_new, kvlen, 1.0 / math.sqrt(D))
