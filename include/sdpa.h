@@ -56,7 +56,9 @@ typedef enum {
   SDPA_ERR_HIP = 6           /* a HIP launch failed */
 } sdpa_status;
 
-typedef enum { SDPA_F32 = 0, SDPA_BF16 = 1, SDPA_U8 = 2 } sdpa_dtype;
+/* F16 is IEEE binary16, the other 16-bit input NNlib's fused implementation takes ("Fused
+ * implementation": bf16/f16 GPU arrays). */
+typedef enum { SDPA_F32 = 0, SDPA_BF16 = 1, SDPA_U8 = 2, SDPA_F16 = 3 } sdpa_dtype;
 
 /* "Arguments": is_causal. TRUE: query i attends keys j <= q_offset + i. BOTTOM_RIGHT: the
  * same with q_offset = kv_len_b - q_len_b, each the given length or else the array size. */
@@ -90,10 +92,10 @@ typedef struct {
  * sdpa_fwd -- attention forward ("Attention", "Arguments", "Fused implementation").
  *
  * q    {Dqk, Hq, Lq, B}; k {Dqk, Hkv, Lkv, B}; v {Dv, Hkv, Lkv, B}; Hq % Hkv == 0, and query head h
- *      reads K/V head h / (Hq/Hkv) ("Attention": grouped-query attention). F32 or BF16, all three
- *      the same dtype. out {Dv, Hq, Lq, B}, F32 or BF16. Arithmetic is fp32 (bf16 products
- *      accumulate in fp32).
- * bias NULL, or F32/BF16 {Lkv|1, Lq|1, Hq|1, B|1}; added to the scaled logits, not scaled.
+ *      reads K/V head h / (Hq/Hkv) ("Attention": grouped-query attention). F32, BF16 or F16, all
+ *      three the same dtype. out {Dv, Hq, Lq, B}, F32, BF16 or F16. Arithmetic is fp32 (16-bit
+ *      products accumulate in fp32).
+ * bias NULL, or F32/BF16/F16 {Lkv|1, Lq|1, Hq|1, B|1}; added to the scaled logits, not scaled.
  * mask NULL, or U8 {Lkv|1, Lq|1, Hq|1, B|1}; nonzero = may attend.
  * mask_info  NULL, or block info built from the mask by build_block_mask_info. When given it
  *      replaces `mask` (which is then not read), lets the kernel skip empty blocks and skip the
@@ -131,9 +133,9 @@ SDPA_API size_t sdpa_fwd_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor
  * "Neural Network primitives from NNlib.jl", "Arguments": is_causal and kv_lengths): query t
  * (0-based) of sequence b attends keys [0, kv_lengths[b] - T + t].
  *
- * q {D, Hq, T, B} BF16 or F32, 0 <= T <= capacity; k_cache, v_cache {D, Hkv, capacity, B}, same
+ * q {D, Hq, T, B} F32, BF16 or F16, 0 <= T <= capacity; k_cache, v_cache {D, Hkv, capacity, B}, same
  * dtype; kv_lengths device int32 [B] (required), clamped to [0, capacity];
- * out {D, Hq, T, B} F32 or BF16. num_splits: key splits per sequence (0 = library choice);
+ * out {D, Hq, T, B} F32, BF16 or F16. num_splits: key splits per sequence (0 = library choice);
  * the partial results are merged by a log-sum-exp pass. workspace: at least
  * sdpa_decode_workspace_bytes(), which grows with T. A query with no key to attend
  * (kv_lengths[b] - T + t < 0) gives a NaN row.
@@ -150,7 +152,7 @@ SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_tensor* q, const sdpa_ten
  * discussion: the cache grows one position per decode step). A bit-exact copy. Rows whose
  * position falls outside [0, capacity) are skipped.
  * k_cache, v_cache {D, Hkv, capacity, B}, in place; k_new, v_new {D, Hkv, T, B}; all four of one
- * dtype (F32 or BF16). write_index device int32 [B].
+ * dtype (F32, BF16 or F16). write_index device int32 [B].
  * ------------------------------------------------------------------------------------- */
 SDPA_API sdpa_status kv_cache_update(sdpa_tensor* k_cache, sdpa_tensor* v_cache,
                             const sdpa_tensor* k_new, const sdpa_tensor* v_new,
@@ -171,7 +173,7 @@ SDPA_API sdpa_status build_block_mask_info(const sdpa_tensor* mask, int32_t bq, 
 
 /* ---------------------------------------------------------------------------------------
  * head_rms_norm -- per-head RMS normalisation (TensorTonic page "Static Arguments in jit"):
- * every head vector v becomes v / sqrt(mean(v^2) + eps). x, y {Dh, H, T, B}, F32 or BF16 (same
+ * every head vector v becomes v / sqrt(mean(v^2) + eps). x, y {Dh, H, T, B}, F32, BF16 or F16 (same
  * dtype); fp32 arithmetic. y may alias x.
  * ------------------------------------------------------------------------------------- */
 SDPA_API sdpa_status head_rms_norm(const sdpa_tensor* x, sdpa_tensor* y, float eps, void* stream);

@@ -16,22 +16,21 @@ pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_kv_cache_update_bit_exact(lib, dtype):
     say(f"kv_cache_update {dtype}")
     rng = np.random.default_rng(3)
     B, cap, H, D, T = 5, 40, 3, 24, 3
-    mk = (lambda s: workloads.f32_to_bf16(rng.standard_normal(s, dtype=np.float32))) if dtype == "bf16" \
-        else (lambda s: rng.standard_normal(s, dtype=np.float32))
+    mk = lambda s: workloads.to_storage(rng.standard_normal(s, dtype=np.float32), dtype)
     kc, vc, kn, vn = mk((B, cap, H, D)), mk((B, cap, H, D)), mk((B, T, H, D)), mk((B, T, H, D))
     widx = np.array([0, 37, 39, -2, 12], dtype=np.int32)        # tail rows past the cache are skipped
     ek, ev = oracle.kv_cache_update(kc, vc, kn, vn, widx)
     tkc, tvc = dev(kc, dtype), dev(vc, dtype)
     sa.kv_cache_update(tkc, tvc, dev(kn, dtype), dev(vn, dtype), torch.as_tensor(widx, device="cuda"))
     torch.cuda.synchronize()
-    view = np.uint16 if dtype == "bf16" else np.uint32
-    gk = tkc.cpu().view(torch.int16 if dtype == "bf16" else torch.int32).numpy().view(view)
-    gv = tvc.cpu().view(torch.int16 if dtype == "bf16" else torch.int32).numpy().view(view)
+    view = np.uint32 if dtype == "f32" else np.uint16
+    gk = tkc.cpu().view(torch.int32 if dtype == "f32" else torch.int16).numpy().view(view)
+    gv = tvc.cpu().view(torch.int32 if dtype == "f32" else torch.int16).numpy().view(view)
     np.testing.assert_array_equal(gk, ek.view(view))
     np.testing.assert_array_equal(gv, ev.view(view))
 
@@ -41,9 +40,9 @@ def decode_case(B, Hq, Hkv, D, cap, kv_min, kv_max, base):
 
 
 def run_decode(d: workloads.Decode, num_splits=0, out_dtype=torch.float32):
-    q = dev(d.q, "bf16")
-    kc, vc = dev(d.k_cache, "bf16"), dev(d.v_cache, "bf16")
-    sa.kv_cache_update(kc, vc, dev(d.k_new, "bf16"), dev(d.v_new, "bf16"),
+    q = dev(d.q, d.dtype)
+    kc, vc = dev(d.k_cache, d.dtype), dev(d.v_cache, d.dtype)
+    sa.kv_cache_update(kc, vc, dev(d.k_new, d.dtype), dev(d.v_new, d.dtype),
                        torch.as_tensor(d.write_index, device="cuda"))
     kvl = torch.as_tensor(d.kv_lengths, device="cuda")
     out = sa.sdpa_decode(q, kc, vc, kvl, scale=d.scale, num_splits=num_splits, out_dtype=out_dtype)
@@ -57,7 +56,7 @@ def oracle_decode(d: workloads.Decode, batches=None):
     outs = []
     for b in bs:
         n = int(d.kv_lengths[b])
-        f = workloads.bf16_to_f32
+        f = lambda a: workloads.widen(a, d.dtype)
         outs.append(oracle.sdpa(f(d.q[b:b + 1]), f(kc[b:b + 1, :n]), f(vc[b:b + 1, :n]), scale=d.scale,
                                 is_causal="bottom_right")[0])
     return np.stack(outs)
@@ -231,3 +230,27 @@ def test_decode_three_queries_nnlib_cache_example(lib):
                   kv_lengths=kvl, scale=d.scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy(), ref.cpu().numpy(), "bf16", "decode T=3 vs fwd with q_offset")
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_decode_f16(lib, T):
+    # f16 caches: the matrix-core pass on its f16 MFMA, one and several query tokens
+    say(f"decode f16 T={T}")
+    d = workloads.gqa_decode(B=3, Hq=32, Hkv=8, D=128, capacity=1100, kv_min=1, kv_max=1100, base=780 + T,
+                             q_len=T, dtype="f16")
+    for od in (torch.float32, torch.float16):
+        out, _, _ = run_decode(d, out_dtype=od)
+        assert out.dtype == od
+        assert_close(out.float().cpu().numpy(), oracle_decode(d), "f16", f"decode f16 T={T} out {od}")
+
+
+def test_head_rms_norm_f16(lib):
+    say("rms norm f16")
+    rng = np.random.default_rng(9)
+    x = workloads.to_storage(rng.standard_normal((2, 5, 6, 64), dtype=np.float32) * 3, "f16")
+    y = sa.head_rms_norm(torch.as_tensor(x, device="cuda"))
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float16
+    ref = oracle.rms_rows(x.astype(np.float32))
+    # one f16 rounding of results below ~4: half an ulp is at most 2^-9
+    np.testing.assert_allclose(y.float().cpu().numpy(), ref, rtol=2 ** -10, atol=2 ** -12)

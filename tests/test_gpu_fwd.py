@@ -66,7 +66,7 @@ FEATURES = [
 ]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("D", [16, 64, 128])
 @pytest.mark.parametrize("hkv", [4, 1])
 @pytest.mark.parametrize("case", range(len(FEATURES)))
@@ -75,18 +75,18 @@ def test_features(lib, case, hkv, D, dtype):
     kvl = f.pop("kv_lengths", None)
     qo = f.pop("q_offset", 0)
     w = workloads.random_attention(1000 + case * 7 + hkv + D, 2, 130, 150, 4, hkv, D, dtype=dtype,
-                                   bias_dtype="bf16" if dtype == "bf16" else "f32",
+                                   bias_dtype="bf16" if dtype == "bf16" else "f32",   # f16: fp32 bias
                                    q_offset=np.array(qo, dtype=np.int32) if isinstance(qo, list) else qo,
                                    kv_lengths=None if kvl is None else np.array(kvl, dtype=np.int32), **f)
     say(f"features case={case} {FEATURES[case]} hkv={hkv} D={D} {dtype}")
     assert_close(run_gpu(w).cpu().numpy(), run_oracle(w), dtype, f"case {case}")
-    if w.mask is not None and dtype == "bf16":
+    if w.mask is not None and dtype != "f32":
         # the block-info path gives the same numbers as the dense mask
         info = run_gpu(w, use_mask_info=True, bq=128, bkv=64).cpu().numpy()
         np.testing.assert_array_equal(info, run_gpu(w).cpu().numpy())
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_value_head_dim_differs(lib, dtype):
     w = workloads.random_attention(77, 2, 70, 90, 4, 2, 64, Dv=32, dtype=dtype, is_causal=True)
     say(f"Dv != D {dtype}")
@@ -208,3 +208,16 @@ def test_debug_allowed_mask_bit_exact(lib, variant):
                 ref = oracle.allowed_matrix(np.arange(Lq), Lkv, b, h, B, H, mask,
                                             None if offs is None else offs[b], None if kvl_c is None else kvl_c[b])
                 np.testing.assert_array_equal(got[b, h], ref.astype(np.uint8))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_f16_bias_and_f16_output(lib, D):
+    # an f16 bias (the general kernel) and f16 outputs (both kernels) against the oracle
+    say(f"f16 bias, f16 out, D={D}")
+    w = workloads.random_attention(91 + D, 2, 130, 150, 4, 2, D, dtype="f16", bias_shape=(2, 4, 130, 150),
+                                   bias_dtype="f16", is_causal=True)
+    assert_close(run_gpu(w).cpu().numpy(), run_oracle(w), "f16", "f16 bias")
+    w2 = workloads.random_attention(95 + D, 2, 130, 150, 4, 2, D, dtype="f16", is_causal=True)
+    out = run_gpu(w2, out_dtype=torch.float16)
+    assert out.dtype == torch.float16
+    assert_close(out.float().cpu().numpy(), run_oracle(w2), "f16", "f16 out")

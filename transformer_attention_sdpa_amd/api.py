@@ -15,8 +15,8 @@ import torch
 
 from . import _native as N
 
-_DTYPE = {torch.float32: N.SDPA_F32, torch.bfloat16: N.SDPA_BF16, torch.uint8: N.SDPA_U8,
-          torch.bool: N.SDPA_U8}
+_DTYPE = {torch.float32: N.SDPA_F32, torch.bfloat16: N.SDPA_BF16, torch.float16: N.SDPA_F16,
+          torch.uint8: N.SDPA_U8, torch.bool: N.SDPA_U8}
 _CAUSAL = {False: N.CAUSAL_NONE, None: N.CAUSAL_NONE, True: N.CAUSAL_TRUE,
            "bottom_right": N.CAUSAL_BOTTOM_RIGHT}
 
@@ -257,10 +257,13 @@ def debug_allowed_mask(q, k, mask=None, *, mask_info=None, is_causal=False, q_of
 
 
 def from_numpy(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
-    """Host array -> device tensor: ``dtype`` "bf16" takes uint16 bit patterns, "f32" float32,
+    """Host array -> device tensor: ``dtype`` "bf16" takes uint16 bit patterns, "f16" float16,
+    "f32" float32,
     "u8" uint8, "i32" int32 (a bit copy, no arithmetic)."""
     if dtype == "bf16":
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f16":
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16))
     elif dtype == "f32":
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
     elif dtype == "u8":

@@ -32,7 +32,7 @@ sdpa_status hip_status(hipError_t e, const char* what) {
   return fail(SDPA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool is_float(int dt) { return dt == SDPA_F32 || dt == SDPA_BF16; }
+bool is_float(int dt) { return dt == SDPA_F32 || dt == SDPA_BF16 || dt == SDPA_F16; }
 
 bool dims_ok(const sdpa_tensor* t) {
   for (int i = 0; i < 4; ++i)
@@ -72,8 +72,8 @@ sdpa_status resolve_attention(const sdpa_tensor* q, const sdpa_tensor* k, const 
   if (!dims_ok(q) || !dims_ok(k) || (v && !dims_ok(v)) || (out && !dims_ok(out)))
     return fail(SDPA_ERR_SHAPE, "a dim is negative or exceeds int32");
   if (!is_float(q->dtype) || k->dtype != q->dtype || (v && v->dtype != q->dtype))
-    return fail(SDPA_ERR_DTYPE, "q, k and v must all be F32 or all BF16");
-  if (out && !is_float(out->dtype)) return fail(SDPA_ERR_DTYPE, "out must be F32 or BF16");
+    return fail(SDPA_ERR_DTYPE, "q, k and v must share one dtype: F32, BF16 or F16");
+  if (out && !is_float(out->dtype)) return fail(SDPA_ERR_DTYPE, "out must be F32, BF16 or F16");
   const int64_t D = q->dims[0], Hq = q->dims[1], Lq = q->dims[2], B = q->dims[3];
   const int64_t Hkv = k->dims[1], Lkv = k->dims[2];
   if (D < 1) return fail(SDPA_ERR_SHAPE, "head_dim must be at least 1");
@@ -111,7 +111,7 @@ sdpa_status resolve_attention(const sdpa_tensor* q, const sdpa_tensor* k, const 
   a.in_dtype = q->dtype;
 
   if (bias) {
-    if (!is_float(bias->dtype)) return fail(SDPA_ERR_DTYPE, "bias must be F32 or BF16");
+    if (!is_float(bias->dtype)) return fail(SDPA_ERR_DTYPE, "bias must be F32, BF16 or F16");
     if (!dims_ok(bias)) return fail(SDPA_ERR_SHAPE, "bias dims out of range");
     int64_t st[4];
     sdpa_status s = bcast_strides(bias, "bias", Lkv, Lq, Hq, B, st);
@@ -285,6 +285,7 @@ sdpa_status sdpa_decode(const sdpa_tensor* q, const sdpa_tensor* kc, const sdpa_
   d.B = a.B; d.T = a.Lq; d.Hq = a.Hq; d.Hkv = a.Hkv; d.D = a.D; d.cap = a.Lkv;
   d.q_sb = a.q_sb; d.q_ss = a.q_ss; d.q_sh = a.q_sh; d.k_sb = a.k_sb; d.k_ss = a.k_ss; d.k_sh = a.k_sh;
   d.v_sb = a.v_sb; d.v_ss = a.v_ss; d.v_sh = a.v_sh; d.o_sb = a.o_sb; d.o_ss = a.o_ss; d.o_sh = a.o_sh;
+  d.in_dtype = a.in_dtype;
   d.out_dtype = a.out_dtype;
   d.kv_lengths = kv_lengths;
   d.scale_log2 = a.scale * 1.4426950408889634f;
@@ -306,7 +307,7 @@ sdpa_status kv_cache_update(sdpa_tensor* kc, sdpa_tensor* vc, const sdpa_tensor*
   if (!write_index) return fail(SDPA_ERR_NULL, "write_index is required");
   if (!dims_ok(kc) || !dims_ok(vc) || !dims_ok(kn) || !dims_ok(vn)) return fail(SDPA_ERR_SHAPE, "dims out of range");
   if (!is_float(kc->dtype) || vc->dtype != kc->dtype || kn->dtype != kc->dtype || vn->dtype != kc->dtype)
-    return fail(SDPA_ERR_DTYPE, "caches and new rows must share one dtype, F32 or BF16");
+    return fail(SDPA_ERR_DTYPE, "caches and new rows must share one dtype, F32, BF16 or F16");
   for (int i = 0; i < 4; ++i)
     if (vc->dims[i] != kc->dims[i] || vn->dims[i] != kn->dims[i])
       return fail(SDPA_ERR_SHAPE, "k and v caches (and new rows) must have equal dims");
@@ -318,7 +319,7 @@ sdpa_status kv_cache_update(sdpa_tensor* kc, sdpa_tensor* vc, const sdpa_tensor*
   const int T = (int)kn->dims[2];
   if ((int64_t)B * T * H * D == 0) return SDPA_OK;
   if (!kc->data || !vc->data || !kn->data || !vn->data) return fail(SDPA_ERR_NULL, "a tensor's data is NULL");
-  const int eb = kc->dtype == SDPA_BF16 ? 2 : 4;
+  const int eb = kc->dtype == SDPA_F32 ? 4 : 2;
   return hip_status(launch_kv_cache_update(kc->data, vc->data, kn->data, vn->data, eb, B, T, H, D, cap,
                                            kc->strides[3], kc->strides[2], kc->strides[1],
                                            vc->strides[3], vc->strides[2], vc->strides[1],
@@ -380,7 +381,7 @@ sdpa_status head_rms_norm(const sdpa_tensor* x, sdpa_tensor* y, float eps, void*
   g_err.clear();
   if (!x || !y) return fail(SDPA_ERR_NULL, "x and y descriptors are required");
   if (!dims_ok(x) || !dims_ok(y)) return fail(SDPA_ERR_SHAPE, "dims out of range");
-  if (!is_float(x->dtype) || y->dtype != x->dtype) return fail(SDPA_ERR_DTYPE, "x and y must share F32 or BF16");
+  if (!is_float(x->dtype) || y->dtype != x->dtype) return fail(SDPA_ERR_DTYPE, "x and y must share F32, BF16 or F16");
   for (int i = 0; i < 4; ++i)
     if (x->dims[i] != y->dims[i]) return fail(SDPA_ERR_SHAPE, "x and y dims differ");
   if (x->strides[0] != 1 || y->strides[0] != 1) return fail(SDPA_ERR_SHAPE, "head_dim stride must be 1");

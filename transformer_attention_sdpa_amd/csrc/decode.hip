@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
 // The 16 tiles of a split are unrolled into straight-line code: every stage is a distinct LDS
 // array, which lets the compiler's wait-count tracking tell a read of one stage from a load in
 // flight into another.
-//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 head-dim values of K, B = Q^T with
+//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (or _f16): A = 16 keys x 32 head-dim values of K, B = Q^T with
 //     the group's r query heads as columns (padded to 16 with zeros).
 //   The 16x16 accumulator gives lane l the scores of keys 4*(l/16) + i (i = 0..3) of a 16-key
 //     block for head l%16. For a 32-key chunk the lane's 8 probabilities, taken as the MFMA k
@@ -194,6 +194,33 @@ typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void dec_lds_void;
+
+// The 16-bit input type of the matrix-core pass 1: bf16 or IEEE f16 (MFMA and conversions).
+template <bool F16> struct DecIn;
+template <> struct DecIn<false> {
+  typedef __bf16 x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+  typedef __bf16 x2 __attribute__((ext_vector_type(2)));
+  __device__ static f32x4_t mfma(x8 a, x8 b, f32x4_t c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+  __device__ static uint32_t pack(float a, float b) {
+    const x2 p = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, p);
+  }
+  __device__ static float sum2(uint32_t p, float acc) {   // acc + both packed values
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(x2, p), __builtin_bit_cast(x2, 0x3f803f80u), acc, false);
+  }
+};
+template <> struct DecIn<true> {
+  typedef _Float16 x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+  typedef _Float16 x2 __attribute__((ext_vector_type(2)));
+  __device__ static f32x4_t mfma(x8 a, x8 b, f32x4_t c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+  __device__ static uint32_t pack(float a, float b) {
+    const x2 p = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, p);
+  }
+  __device__ static float sum2(uint32_t p, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(x2, p), __builtin_bit_cast(x2, 0x3c003c00u), acc, false);
+  }
+};
 
 // One wave instruction of a direct load: lane l copies 16 bytes from byte offset voff of r into
 // lds + 16*l. (Kept out of the kernel body: used there directly, the host pass drops the stub.)
@@ -215,7 +242,7 @@ struct MfWave {
   int lane, col, grp;
   int kdo[8], vdo[8];          // direct-load byte offsets (K, V) of the lane's 8 slots per tile
   int vo_lo[8], vo_hi[8];      // element offsets of the two transposed V reads per 16-row block
-  bf16x8_t qf[4];              // Q^T operand of the current (sequence, K/V head)
+  uint4 qf[4];                 // Q^T operand of the current (sequence, K/V head), 8 16-bit values each
   f32x4_t o[8];                // O^T accumulators, 16 head-dim rows each
   float m, lp0, lp1;           // running max (log2 units), two partial row sums
   bool cvalid;                 // this lane's column is a (query head, token) of the group
@@ -263,7 +290,7 @@ __device__ __forceinline__ void mf_begin(MfWave& w, const DecodeArgs& a, int b, 
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const uint4 x = w.cvalid ? *reinterpret_cast<const uint4*>(qp + 32 * c + 8 * w.grp) : make_uint4(0, 0, 0, 0);
-    w.qf[c] = __builtin_bit_cast(bf16x8_t, x);
+    w.qf[c] = x;
   }
 #pragma unroll
   for (int db = 0; db < 8; ++db)
@@ -289,6 +316,7 @@ __device__ __forceinline__ void mf_load(const MfWave& w, const DecodeArgs& a, in
 }
 
 // One 32-key tile (keys j0.. of which those below j_end count) from a ring stage.
+template <bool F16>
 __device__ __forceinline__ void mf_tile(MfWave& w, const DecodeArgs& a, int j0, int j_end, const uint16_t* ks,
                                         const uint16_t* vs) {
   f32x4_t sc[2];
@@ -299,8 +327,9 @@ __device__ __forceinline__ void mf_tile(MfWave& w, const DecodeArgs& a, int j0, 
     const int row = 16 * kb + w.col;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(ks + row * kDecD + (((4 * c + w.grp) ^ dec_kswz(row)) << 3));
-      sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, w.qf[c], sc[kb], 0, 0, 0);
+      using x8 = typename DecIn<F16>::x8;
+      const x8 ka = *reinterpret_cast<const x8*>(ks + row * kDecD + (((4 * c + w.grp) ^ dec_kswz(row)) << 3));
+      sc[kb] = DecIn<F16>::mfma(ka, __builtin_bit_cast(x8, w.qf[c]), sc[kb]);
     }
   }
   float tmax = -INFINITY;
@@ -330,22 +359,19 @@ __device__ __forceinline__ void mf_tile(MfWave& w, const DecodeArgs& a, int j0, 
   uint32_t pw[4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const bf16x2_t p01 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][0] - m_use)),
-                          static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][1] - m_use))};
-    const bf16x2_t p23 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][2] - m_use)),
-                          static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kb][3] - m_use))};
-    pw[2 * kb] = __builtin_bit_cast(uint32_t, p01);
-    pw[2 * kb + 1] = __builtin_bit_cast(uint32_t, p23);
-    w.lp0 = __builtin_amdgcn_fdot2_f32_bf16(p01, __builtin_bit_cast(bf16x2_t, 0x3f803f80u), w.lp0, false);
-    w.lp1 = __builtin_amdgcn_fdot2_f32_bf16(p23, __builtin_bit_cast(bf16x2_t, 0x3f803f80u), w.lp1, false);
+    pw[2 * kb] = DecIn<F16>::pack(__builtin_amdgcn_exp2f(sc[kb][0] - m_use), __builtin_amdgcn_exp2f(sc[kb][1] - m_use));
+    pw[2 * kb + 1] = DecIn<F16>::pack(__builtin_amdgcn_exp2f(sc[kb][2] - m_use), __builtin_amdgcn_exp2f(sc[kb][3] - m_use));
+    w.lp0 = DecIn<F16>::sum2(pw[2 * kb], w.lp0);
+    w.lp1 = DecIn<F16>::sum2(pw[2 * kb + 1], w.lp1);
   }
-  const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+  using x8 = typename DecIn<F16>::x8;
+  const x8 pb = __builtin_bit_cast(x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
     const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(vs + w.vo_lo[db]));
     const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(vs + w.vo_hi[db]));
     const s16x8_t vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    w.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv), pb, w.o[db], 0, 0, 0);
+    w.o[db] = DecIn<F16>::mfma(__builtin_bit_cast(x8, vv), pb, w.o[db]);
   }
 }
 
@@ -416,7 +442,7 @@ __host__ __device__ __forceinline__ int mf_groups(const DecodeArgs& a) { return 
 // One workgroup (one wave) per (K/V head, column group, split, sequence): blockIdx.x = Hkv *
 // (groups * i + cg) + g. LINEAR: i is an item of mf_locate; else i is the split and the
 // sequence is blockIdx.y, and splits past a sequence's length exit at once.
-template <bool LINEAR>
+template <bool LINEAR, bool F16>
 __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   __shared__ __align__(16) uint16_t k0s[kMfTileElems], k1s[kMfTileElems], k2s[kMfTileElems];
   __shared__ __align__(16) uint16_t v0s[kMfTileElems], v1s[kMfTileElems], v2s[kMfTileElems];
@@ -449,7 +475,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int t = 0; t < kMfTiles; ++t) {              // three stages: two tiles in flight
     if (t + 2 < kMfTiles) mf_load(w, a, b, g, j_begin + kMfTile * (t + 2), j_end, kst[(t + 2) % 3], vst[(t + 2) % 3]);
-    if (j_begin + kMfTile * t < j_end) mf_tile(w, a, j_begin + kMfTile * t, j_end, kst[t % 3], vst[t % 3]);
+    if (j_begin + kMfTile * t < j_end) mf_tile<F16>(w, a, j_begin + kMfTile * t, j_end, kst[t % 3], vst[t % 3]);
   }
   __builtin_amdgcn_s_waitcnt(0);                    // no direct load may land after the wave ends
   mf_store(w, a, b, g, r, split);
@@ -506,7 +532,7 @@ static bool decode_mfma_supports(const DecodeArgs& a) {
 }
 
 bool decode_fast_supports(const DecodeArgs& a, int in_dtype) {
-  if (in_dtype != SDPA_BF16 || a.D != kDecD) return false;
+  if ((in_dtype != SDPA_BF16 && in_dtype != SDPA_F16) || a.D != kDecD || a.in_dtype != in_dtype) return false;
   // grid limits: sequences in grid.y of the (split, sequence) grids, one combine workgroup per
   // (query head, sequence, token)
   if (a.B > 65535 || (int64_t)a.Hq * a.B * a.T > INT32_MAX) return false;
@@ -515,8 +541,8 @@ bool decode_fast_supports(const DecodeArgs& a, int in_dtype) {
   if (!al16(a.k) || !al16(a.v)) return false;
   if ((a.k_sb | a.k_ss | a.k_sh | a.v_sb | a.v_ss | a.v_sh) & 7) return false;
   if (decode_mfma_supports(a)) return true;
-  // the vector pass 1: one query token, up to 8 query heads per K/V head, 4-byte aligned q rows
-  if (a.T != 1 || a.Hq / a.Hkv > 8) return false;
+  // the vector pass 1: bf16, one query token, up to 8 query heads per K/V head, 4-byte aligned q rows
+  if (in_dtype != SDPA_BF16 || a.T != 1 || a.Hq / a.Hkv > 8) return false;
   if ((reinterpret_cast<uintptr_t>(a.q) & 3) || ((a.q_sb | a.q_sh) & 1)) return false;
   return true;
 }
@@ -526,10 +552,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.Hkv * a.max_splits, a.B);
   if (decode_mfma_supports(a)) {
     const int64_t per_seq = (int64_t)a.Hkv * mf_groups(a) * a.max_splits;
-    if (a.B <= kLinMaxB && per_seq * a.B <= INT32_MAX)
-      hipLaunchKernelGGL(decode_split_mfma_kernel<true>, dim3((unsigned)(per_seq * a.B)), dim3(64), 0, s, a);
-    else
-      hipLaunchKernelGGL(decode_split_mfma_kernel<false>, dim3((unsigned)per_seq, a.B), dim3(64), 0, s, a);
+    const bool lin = a.B <= kLinMaxB && per_seq * a.B <= INT32_MAX;
+    const dim3 g1((unsigned)(per_seq * a.B)), g2((unsigned)per_seq, a.B);
+    if (a.in_dtype == SDPA_F16) {
+      if (lin) hipLaunchKernelGGL((decode_split_mfma_kernel<true, true>), g1, dim3(64), 0, s, a);
+      else hipLaunchKernelGGL((decode_split_mfma_kernel<false, true>), g2, dim3(64), 0, s, a);
+    } else {
+      if (lin) hipLaunchKernelGGL((decode_split_mfma_kernel<true, false>), g1, dim3(64), 0, s, a);
+      else hipLaunchKernelGGL((decode_split_mfma_kernel<false, false>), g2, dim3(64), 0, s, a);
+    }
   }
   else if (r <= 4) hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kDecThreads), 0, s, a);
   else hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kDecThreads), 0, s, a);

@@ -23,13 +23,24 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+__device__ __forceinline__ float f16_bits_to_float(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// fp32 -> IEEE binary16, round to nearest even (overflow to +-inf, NaN stays NaN).
+__device__ __forceinline__ uint16_t float_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
 __device__ __forceinline__ float load_elem(const void* base, int64_t idx, int dtype) {
   if (dtype == SDPA_BF16) return bf16_bits_to_float(static_cast<const uint16_t*>(base)[idx]);
+  if (dtype == SDPA_F16) return f16_bits_to_float(static_cast<const uint16_t*>(base)[idx]);
   return static_cast<const float*>(base)[idx];
 }
 
 __device__ __forceinline__ void store_elem(void* base, int64_t idx, int dtype, float x) {
   if (dtype == SDPA_BF16) static_cast<uint16_t*>(base)[idx] = float_to_bf16_bits(x);
+  else if (dtype == SDPA_F16) static_cast<uint16_t*>(base)[idx] = float_to_f16_bits(x);
   else static_cast<float*>(base)[idx] = x;
 }
 

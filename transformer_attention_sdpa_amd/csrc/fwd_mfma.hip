@@ -50,6 +50,41 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// The 16-bit input type: bf16 or IEEE f16. What differs is the MFMA, the operand vectors and
+// the conversions; everything else (loads, LDS layout, transposed reads) moves 16-bit words.
+template <bool F16> struct In;
+template <> struct In<false> {
+  typedef __bf16 x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+  typedef __bf16 x2 __attribute__((ext_vector_type(2)));
+  __device__ static f32x16 mfma(x8 a, x8 b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
+  __device__ static float lo(uint32_t w) { return __uint_as_float(w << 16); }          // element 0 of a pair
+  __device__ static float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }  // element 1
+  __device__ static uint16_t bits(float f) { return float_to_bf16_bits(f); }
+  __device__ static uint32_t pack(float a, float b) {
+    const x2 p = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, p);
+  }
+  // acc + the two packed values (a dot product with 1, 1)
+  __device__ static float sum2(uint32_t p, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(x2, p), __builtin_bit_cast(x2, 0x3f803f80u), acc, false);
+  }
+};
+template <> struct In<true> {
+  typedef _Float16 x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+  typedef _Float16 x2 __attribute__((ext_vector_type(2)));
+  __device__ static f32x16 mfma(x8 a, x8 b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+  __device__ static float lo(uint32_t w) { return f16_bits_to_float(static_cast<uint16_t>(w)); }
+  __device__ static float hi(uint32_t w) { return f16_bits_to_float(static_cast<uint16_t>(w >> 16)); }
+  __device__ static uint16_t bits(float f) { return float_to_f16_bits(f); }
+  __device__ static uint32_t pack(float a, float b) {
+    const x2 p = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, p);
+  }
+  __device__ static float sum2(uint32_t p, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(x2, p), __builtin_bit_cast(x2, 0x3c003c00u), acc, false);
+  }
+};
+
 constexpr int BM = 128;            // query rows per workgroup
 constexpr int BN = 64;             // keys per tile
 constexpr int NT = 256;            // threads per workgroup
@@ -94,8 +129,10 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) 
 
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units: the running max moves only when a row's max grows by more
 
-template <int D, int BIAS, int MASK, bool NORM>
+template <int D, int BIAS, int MASK, bool NORM, bool F16>
 __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, int remap, int order) {
+  using E = In<F16>;
+  using bf16x8 = typename E::x8;     // the 16-bit operand vector (bf16 or f16)
   constexpr int DC = D / 16;         // 16-wide head-dim chunks (MFMA k steps for q.k)
   constexpr int DB = D / 32;         // 32-row blocks of O^T
   constexpr int CPR = D / 8;         // 16-byte chunks per row
@@ -205,8 +242,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
         uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float lo = __uint_as_float(w[t] << 16) * c_lane, hi = __uint_as_float(w[t] & 0xffff0000u) * c_lane;
-          w[t] = (uint32_t)float_to_bf16_bits(lo) | ((uint32_t)float_to_bf16_bits(hi) << 16);
+          const float lo = E::lo(w[t]) * c_lane, hi = E::hi(w[t]) * c_lane;
+          w[t] = (uint32_t)E::bits(lo) | ((uint32_t)E::bits(hi) << 16);
         }
         x = make_uint4(w[0], w[1], w[2], w[3]);
       }
@@ -215,7 +252,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
         const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float lo = __uint_as_float(w[t] << 16), hi = __uint_as_float(w[t] & 0xffff0000u);
+          const float lo = E::lo(w[t]), hi = E::hi(w[t]);
           ss += lo * lo + hi * hi;
         }
       }
@@ -277,7 +314,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag_at(ks, c, kb), qB[c], sacc[kb], 0, 0, 0);
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] = E::mfma(kfrag_at(ks, c, kb), qB[c], sacc[kb]);
     }
   };
   // V^T fragment (A operand of O^T += V^T P^T) by two transposed reads: within each 16-lane
@@ -533,11 +570,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
         const float xe = s_cur[f >> 4][f & 15];
         pf[f] = FUSED ? __builtin_amdgcn_exp2f(xe) : __builtin_amdgcn_exp2f(xe - m_use);
         if (f & 1) {
-          typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-          const bf16x2v pr = {static_cast<__bf16>(pf[f - 1]), static_cast<__bf16>(pf[f])};
-          pw[f >> 1] = __builtin_bit_cast(uint32_t, pr);
-          // row sum of the same bf16 probabilities the MFMA consumes
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l_run, false);
+          pw[f >> 1] = E::pack(pf[f - 1], pf[f]);
+          // row sum of the same 16-bit probabilities the MFMA consumes
+          l_run = E::sum2(pw[f >> 1], l_run);
         }
       };
       auto pb = [&](int kb, int sh) -> bf16x8 {
@@ -579,9 +614,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (c == 0) {
-            s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][kb], qB[0], c0, 0, 0, 0);
+            s_next[kb] = E::mfma(kf[0][kb], qB[0], c0);
           } else {
-            s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c % (PF + 1)][kb], qB[c], s_next[kb], 0, 0, 0);
+            s_next[kb] = E::mfma(kf[c % (PF + 1)][kb], qB[c], s_next[kb]);
           }
         }
 #pragma unroll
@@ -591,7 +626,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
 #pragma unroll
       for (int i = 0; i < NB; ++i) {                     // ---- block B1: keys 0..31
         vf[(i + PF) % (PF + 1)] = vfrag(i + PF);
-        o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % (PF + 1)], pb(0, i / DB), o[i % DB], 0, 0, 0);
+        o[i % DB] = E::mfma(vf[i % (PF + 1)], pb(0, i / DB), o[i % DB]);
 #pragma unroll
         for (int f = EL_A + i * EL_B / NB; f < EL_A + (i + 1) * EL_B / NB; ++f) prob(f);
         __builtin_amdgcn_sched_barrier(0);
@@ -599,7 +634,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
 #pragma unroll
       for (int i = 0; i < NB; ++i) {                     // ---- block B2: keys 32..63
         if (i + PF < NB) vf[(NB + i + PF) % (PF + 1)] = vfrag(NB + i + PF);
-        o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(NB + i) % (PF + 1)], pb(1, i / DB), o[i % DB], 0, 0, 0);
+        o[i % DB] = E::mfma(vf[(NB + i) % (PF + 1)], pb(1, i / DB), o[i % DB]);
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (!FUSED) {
@@ -637,6 +672,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
       for (int j = 0; j < 4; ++j) r[j] = zero_row ? 0.f : (l_tot > 0.f ? o[d][4 * i + j] * inv : NAN);
       if (a.out_dtype == SDPA_F32) {
         *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow + dcol) = make_float4(r[0], r[1], r[2], r[3]);
+      } else if (a.out_dtype == SDPA_F16) {
+        const uint32_t w0 = (uint32_t)float_to_f16_bits(r[0]) | ((uint32_t)float_to_f16_bits(r[1]) << 16);
+        const uint32_t w1 = (uint32_t)float_to_f16_bits(r[2]) | ((uint32_t)float_to_f16_bits(r[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow + dcol) = make_uint2(w0, w1);
       } else {
         const uint32_t w0 = (uint32_t)float_to_bf16_bits(r[0]) | ((uint32_t)float_to_bf16_bits(r[1]) << 16);
         const uint32_t w1 = (uint32_t)float_to_bf16_bits(r[2]) | ((uint32_t)float_to_bf16_bits(r[3]) << 16);
@@ -645,21 +684,27 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
     }
 }
 
-template <int D, int BIAS, int MASK, bool NORM>
+template <int D, int BIAS, int MASK, bool NORM, bool F16>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   const int n_qt = (a.Lq + BM - 1) / BM;
   const int64_t nwg = (int64_t)n_qt * a.Hq * a.B;
   const int order = a.causal != SDPA_CAUSAL_NONE ? 1 : 0;
   const int remap = order == 1 ? ((a.Hq * a.B) % 8 == 0 ? 1 : 0) : (nwg % 8) == 0 ? 1 : 0;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, BIAS, MASK, NORM>), dim3((unsigned)nwg), dim3(NT), 0, s, a, n_qt,
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, BIAS, MASK, NORM, F16>), dim3((unsigned)nwg), dim3(NT), 0, s, a, n_qt,
                      remap, order);
   return hipGetLastError();
 }
 
+template <int D, int BIAS, int MASK, bool NORM>
+hipError_t launch_in(const AttnArgs& a, hipStream_t s) {
+  if (a.in_dtype == SDPA_F16) return launch_t<D, BIAS, MASK, NORM, true>(a, s);
+  return launch_t<D, BIAS, MASK, NORM, false>(a, s);
+}
+
 template <int D, int BIAS, int MASK>
 hipError_t launch_norm(const AttnArgs& a, hipStream_t s) {
-  if (a.qk_norm) return launch_t<D, BIAS, MASK, true>(a, s);
-  return launch_t<D, BIAS, MASK, false>(a, s);
+  if (a.qk_norm) return launch_in<D, BIAS, MASK, true>(a, s);
+  return launch_in<D, BIAS, MASK, false>(a, s);
 }
 
 template <int D, int BIAS>
@@ -681,7 +726,8 @@ bool al(const void* p, int n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0
 }  // namespace
 
 bool fwd_mfma_supports(const AttnArgs& a) {
-  if (a.in_dtype != SDPA_BF16 || a.D != a.Dv || (a.D != 64 && a.D != 128)) return false;
+  if ((a.in_dtype != SDPA_BF16 && a.in_dtype != SDPA_F16) || a.D != a.Dv || (a.D != 64 && a.D != 128)) return false;
+  if (a.bias && a.bias_dtype == SDPA_F16) return false;     // f16 bias: the general kernel
   if (!al(a.q, 16) || !al(a.k, 16) || !al(a.v, 16) || !al(a.out, 16)) return false;
   if ((a.q_sb | a.q_ss | a.q_sh | a.k_sb | a.k_ss | a.k_sh | a.v_sb | a.v_ss | a.v_sh) & 7) return false;
   if ((a.o_sb | a.o_ss | a.o_sh) & 3) return false;

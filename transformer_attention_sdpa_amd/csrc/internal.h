@@ -56,7 +56,7 @@ struct DecodeArgs {
   void* out;                   // [B][T][Hq][D]
   int B, T, Hq, Hkv, D, cap;   // T: query tokens per sequence (the last T of its kv_lengths[b] keys)
   int64_t q_sb, q_ss, q_sh, k_sb, k_ss, k_sh, v_sb, v_ss, v_sh, o_sb, o_ss, o_sh;
-  int out_dtype;
+  int in_dtype, out_dtype;
   const int32_t* kv_lengths;
   float scale_log2;            // scale * log2(e)
   int split_len, max_splits;

@@ -74,10 +74,29 @@ def rng_for(k: int, tag: int, *sub: int, base: int = SEED_BASE) -> np.random.Gen
     return np.random.default_rng([base + k, tag, *sub])
 
 
+def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values in the stored form of ``dtype``: "bf16" uint16 bits (RNE), "f16" numpy
+    float16 (RNE), "f32" unchanged."""
+    if dtype == "bf16":
+        return f32_to_bf16(x)
+    if dtype == "f16":
+        return np.asarray(x, dtype=np.float32).astype(np.float16)
+    return x
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values of ``dtype`` as float32 (exact for all three)."""
+    if dtype == "bf16":
+        return bf16_to_f32(a)
+    if dtype == "f16":
+        return np.asarray(a, dtype=np.float16).astype(np.float32)
+    return a
+
+
 def normal_tensor(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
-    """N(0,1) draws as float32, or as bfloat16 bits when ``dtype == 'bf16'``."""
+    """N(0,1) draws as float32, in the stored form of ``dtype`` (see to_storage)."""
     x = rng.standard_normal(size=shape, dtype=np.float32)
-    return f32_to_bf16(x) if dtype == "bf16" else x
+    return to_storage(x, dtype)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -86,7 +105,7 @@ def normal_tensor(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
 @dataclass
 class Attention:
     name: str
-    dtype: str                       # "f32" or "bf16": storage of q, k, v (bf16 as uint16 bits)
+    dtype: str                       # "f32", "bf16" or "f16": storage of q, k, v (bf16 as uint16 bits)
     q: np.ndarray                    # [B][Lq][Hq][D]
     k: np.ndarray                    # [B][Lkv][Hkv][D]
     v: np.ndarray                    # [B][Lkv][Hkv][Dv]
@@ -107,12 +126,11 @@ class Attention:
         return B, Lq, Lkv, Hq, Hkv, D, Dv
 
     def values(self, name: str) -> np.ndarray:
-        """Float32 values of a stored tensor (bf16 bits widened exactly)."""
+        """Float32 values of a stored tensor (16-bit storage widened exactly)."""
         a = getattr(self, name)
         if a is None:
             return None
-        is_bf16 = (self.bias_dtype if name == "bias" else self.dtype) == "bf16"
-        return bf16_to_f32(a) if is_bf16 else a
+        return widen(a, self.bias_dtype if name == "bias" else self.dtype)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -134,7 +152,7 @@ def random_attention(seed: int, B, Lq, Lkv, Hq, Hkv, D, Dv=None, dtype="f32", *,
             x = rng.random(size=shape, dtype=np.float32)
         else:
             x = rng.standard_normal(size=shape, dtype=np.float32)
-        return f32_to_bf16(x) if dtype == "bf16" else x
+        return to_storage(x, dtype)
     q = draw(TAG_Q, (B, Lq, Hq, D))
     k = draw(TAG_K, (B, Lkv, Hkv, D))
     v = draw(TAG_V, (B, Lkv, Hkv, Dv))
@@ -142,7 +160,7 @@ def random_attention(seed: int, B, Lq, Lkv, Hq, Hkv, D, Dv=None, dtype="f32", *,
     if bias_shape is not None:
         rng = np.random.default_rng([seed, TAG_BIAS])
         b = rng.standard_normal(size=bias_shape, dtype=np.float32)
-        bias = f32_to_bf16(b) if bias_dtype == "bf16" else b
+        bias = to_storage(b, bias_dtype)
     mask = None
     if mask_shape is not None:
         rng = np.random.default_rng([seed, TAG_MBITS])
@@ -197,32 +215,36 @@ class Decode:
 
 
 def gqa_decode(B=64, Hq=32, Hkv=8, D=128, capacity=8192, kv_min=1024, kv_max=8192,
-               base=SEED_BASE, q_len=1) -> Decode:
+               base=SEED_BASE, q_len=1, dtype="bf16") -> Decode:
     """GQA decode with a KV cache; q_len new tokens per sequence (1: one decode step).
 
     kv_lengths[b] ~ U{kv_min..kv_max}. Cache slots [0, kv_lengths[b]-q_len) hold N(0,1) past
     rows (per-batch sub-streams, so one batch element can be regenerated alone); slots from
-    kv_lengths[b]-q_len on hold a bf16 NaN, so a read of an unwritten slot shows in the output.
+    kv_lengths[b]-q_len on hold a NaN, so a read of an unwritten slot shows in the output.
+    ``dtype`` "bf16" (uint16 bits) or "f16" (numpy float16) storage.
     The new rows go to slots kv_lengths[b]-q_len .. kv_lengths[b]-1 (those below 0 are dropped
     by the cache update).
     """
     k = 2
     kvlen = rng_for(k, TAG_KVLEN, base=base).integers(kv_min, kv_max + 1, size=B).astype(np.int32)
-    q = normal_tensor(rng_for(k, TAG_Q, base=base), (B, q_len, Hq, D), "bf16")
-    k_new = normal_tensor(rng_for(k, TAG_KNEW, base=base), (B, q_len, Hkv, D), "bf16")
-    v_new = normal_tensor(rng_for(k, TAG_VNEW, base=base), (B, q_len, Hkv, D), "bf16")
-    k_cache = np.full((B, capacity, Hkv, D), BF16_NAN_BITS, dtype=np.uint16)
-    v_cache = np.full((B, capacity, Hkv, D), BF16_NAN_BITS, dtype=np.uint16)
+    q = normal_tensor(rng_for(k, TAG_Q, base=base), (B, q_len, Hq, D), dtype)
+    k_new = normal_tensor(rng_for(k, TAG_KNEW, base=base), (B, q_len, Hkv, D), dtype)
+    v_new = normal_tensor(rng_for(k, TAG_VNEW, base=base), (B, q_len, Hkv, D), dtype)
+    if dtype == "bf16":
+        k_cache = np.full((B, capacity, Hkv, D), BF16_NAN_BITS, dtype=np.uint16)
+    else:
+        k_cache = np.full((B, capacity, Hkv, D), np.nan, dtype=np.float16)
+    v_cache = k_cache.copy()
     for b in range(B):
         n = max(int(kvlen[b]) - q_len, 0)
-        k_cache[b, :n] = decode_cache_rows(k, TAG_K, b, n, Hkv, D, base)
-        v_cache[b, :n] = decode_cache_rows(k, TAG_V, b, n, Hkv, D, base)
-    return Decode("gqa_decode", q, k_cache, v_cache, k_new, v_new, kvlen, 1.0 / math.sqrt(D))
+        k_cache[b, :n] = decode_cache_rows(k, TAG_K, b, n, Hkv, D, base, dtype)
+        v_cache[b, :n] = decode_cache_rows(k, TAG_V, b, n, Hkv, D, base, dtype)
+    return Decode("gqa_decode", q, k_cache, v_cache, k_new, v_new, kvlen, 1.0 / math.sqrt(D), dtype)
 
 
-def decode_cache_rows(k, tag, b, n, Hkv, D, base=SEED_BASE) -> np.ndarray:
-    """The n past rows of batch element b's cache (bf16 bits [n][Hkv][D])."""
-    return normal_tensor(rng_for(k, tag, b, base=base), (n, Hkv, D), "bf16")
+def decode_cache_rows(k, tag, b, n, Hkv, D, base=SEED_BASE, dtype="bf16") -> np.ndarray:
+    """The n past rows of batch element b's cache ([n][Hkv][D] in the stored form of dtype)."""
+    return normal_tensor(rng_for(k, tag, b, base=base), (n, Hkv, D), dtype)
 
 
 def alibi_slopes(H: int) -> np.ndarray:
