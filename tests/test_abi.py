@@ -75,6 +75,8 @@ CASES = {
     "inner_stride": (lambda: (T([64, 8, 5, 3], strides=[2, 128, 1024, 5120]),) + good()[1:], N.SDPA_ERR_SHAPE, {}),
     "mixed_dtype": (lambda: (T([64, 8, 5, 3], N.SDPA_F32),) + good()[1:], N.SDPA_ERR_DTYPE, {}),
     "u8_inputs": (lambda: good(dt=N.SDPA_U8), N.SDPA_ERR_DTYPE, {}),
+    "f16_q_bf16_kv": (lambda: (T([64, 8, 5, 3], N.SDPA_F16),) + good()[1:], N.SDPA_ERR_DTYPE, {}),
+    "unknown_dtype": (lambda: good(dt=7), N.SDPA_ERR_DTYPE, {}),
     "head_dim_too_big": (lambda: good(D=320), N.SDPA_ERR_UNSUPPORTED, {}),
     "bad_causal": (lambda: good(), N.SDPA_ERR_SHAPE, {"causal": 3}),
     "bad_qk_norm": (lambda: good(), N.SDPA_ERR_SHAPE, {"qk_norm": 2}),
@@ -163,6 +165,7 @@ def test_kv_cache_update_validation(lib):
     assert call(c=T([128, 4, 1, 4]), d=T([128, 4, 1, 4])) == N.SDPA_ERR_SHAPE
     assert call(b=T([128, 8, 32, 4])) == N.SDPA_ERR_SHAPE
     assert call(c=T([128, 8, 1, 4], N.SDPA_F32)) == N.SDPA_ERR_DTYPE
+    assert call(d=T([128, 8, 1, 4], N.SDPA_F16)) == N.SDPA_ERR_DTYPE     # f16 rows into bf16 caches
 
 
 def test_block_mask_info_bytes(lib):
