@@ -393,6 +393,8 @@ __device__ __forceinline__ void mf_store(const MfWave& w, const DecodeArgs& a, i
 }
 
 constexpr int kMfTiles = kMfSplit / kMfTile;     // 16 tiles per chunk
+// s_waitcnt immediate: lgkmcnt(0), vmcnt and expcnt not waited on
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
 
 // Work order of the linear grid (batches up to kLinMaxB sequences): item i of K/V head g is
 // workgroup Hkv*i + g; the items are the full splits of all sequences, sequence by sequence,
@@ -422,8 +424,8 @@ __device__ __forceinline__ bool mf_locate(const DecodeArgs& a, int item, int& b,
         const int v = __shfl_up(incl, o, 64);
         if (lane >= o) incl += v;
       }
-      const int tot = __shfl(incl, 63, 64);
-      if (item < tot) {                             // wave-uniform
+      const int tot = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+      if (item < tot) {                             // scalar: a uniform branch
         const int l = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl > item));
         b = 64 * c + l;
         nkv = __shfl(len[c], l, 64);
@@ -474,7 +476,14 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   mf_load(w, a, b, g, j_begin + kMfTile, j_end, kst[1], vst[1]);
 #pragma unroll
   for (int t = 0; t < kMfTiles; ++t) {              // three stages: two tiles in flight
-    if (t + 2 < kMfTiles) mf_load(w, a, b, g, j_begin + kMfTile * (t + 2), j_end, kst[(t + 2) % 3], vst[(t + 2) % 3]);
+    if (t + 2 < kMfTiles) {
+      // the stage refilled here was read for tile t-1: those LDS reads must be complete before
+      // the direct loads that overwrite it are issued (the compiler orders a direct load only
+      // before later reads of its data, not after earlier reads of what it replaces)
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_sched_barrier(0);
+      mf_load(w, a, b, g, j_begin + kMfTile * (t + 2), j_end, kst[(t + 2) % 3], vst[(t + 2) % 3]);
+    }
     if (j_begin + kMfTile * t < j_end) mf_tile<F16>(w, a, j_begin + kMfTile * t, j_end, kst[t % 3], vst[t % 3]);
   }
   __builtin_amdgcn_s_waitcnt(0);                    // no direct load may land after the wave ends
