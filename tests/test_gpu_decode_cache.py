@@ -254,3 +254,15 @@ def test_head_rms_norm_f16(lib):
     ref = oracle.rms_rows(x.astype(np.float32))
     # one f16 rounding of results below ~4: half an ulp is at most 2^-9
     np.testing.assert_allclose(y.float().cpu().numpy(), ref, rtol=2 ** -10, atol=2 ** -12)
+
+
+@pytest.mark.parametrize("B", [64, 260])
+def test_decode_repeatable(lib, B):
+    # the direct loads that refill a stage of the LDS ring wait for the reads of what they
+    # replace: repeated calls give the same bits (a refill overtaking those reads once made one
+    # workgroup in a thousand read the next tile)
+    say(f"decode repeatable B={B}")
+    d = decode_case(B, 8, 2, 128, 1100, 1, 1100, base=730 + B)
+    outs = [run_decode(d)[0].cpu().numpy() for _ in range(8)]
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
