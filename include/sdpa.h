@@ -120,6 +120,34 @@ SDPA_API sdpa_status sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const 
                      int32_t qk_norm,
                      sdpa_tensor* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * sdpa_fwd_packed -- attention over packed sequences (page "Neural Network primitives from
+ * NNlib.jl", section "Packed sequences"; "Arguments": q_segments, kv_segments, maxlen). The
+ * inputs hold n_segments sequences one after the other with no batch dimension: q
+ * {Dqk, Hq, Lq_total, 1}, k {Dqk, Hkv, Lkv_total, 1}, v {Dv, Hkv, Lkv_total, 1}, out
+ * {Dv, Hq, Lq_total, 1}; dtypes as for sdpa_fwd. Segment s of the queries attends segment s
+ * of the keys and values only, as batch element s of a padded batch would.
+ *
+ * q_segments  device int32 [n_segments]: segment lengths along q.
+ * kv_segments device int32 [n_segments] along k/v, or NULL: the same as q_segments.
+ * maxlen      -1, or a bound on every segment length (no segment may exceed it). The lengths
+ *             are never read on the host; maxlen only narrows the launch.
+ * is_causal, q_offset, kv_lengths, q_lengths, qk_norm, scale: as for sdpa_fwd, applied within
+ *             each segment; the per-batch arrays take one entry per segment.
+ * The lengths have to add up to Lq_total and Lkv_total; the kernels cut any segment at the end
+ * of the arrays, and rows of q outside every segment are not written. No bias or mask (the
+ * page allows none with segments). workspace: sdpa_fwd_workspace_bytes() of the same tensors.
+ * ------------------------------------------------------------------------------------- */
+SDPA_API sdpa_status sdpa_fwd_packed(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
+                                     const int32_t* q_segments, const int32_t* kv_segments,
+                                     int32_t n_segments, int32_t maxlen,
+                                     float scale, int32_t is_causal,
+                                     const int32_t* q_offset, int32_t q_offset_all,
+                                     const int32_t* kv_lengths, int32_t kv_length_all,
+                                     const int32_t* q_lengths, int32_t q_length_all,
+                                     int32_t qk_norm,
+                                     sdpa_tensor* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace sdpa_fwd needs for these shapes (0 when none). Host only. */
 SDPA_API size_t sdpa_fwd_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
                                 int32_t qk_norm);

@@ -187,3 +187,18 @@ def test_head_rms_norm_validation(lib):
     assert lib.head_rms_norm(ctypes.byref(x), ctypes.byref(T([4, 2, 3, 2], N.SDPA_F32)), 1e-6, None) == N.SDPA_ERR_SHAPE
     assert lib.head_rms_norm(ctypes.byref(x), ctypes.byref(T([4, 2, 3, 1], N.SDPA_BF16)), 1e-6, None) == N.SDPA_ERR_DTYPE
     assert lib.head_rms_norm(ctypes.byref(x), ctypes.byref(T([4, 2, 3, 1], N.SDPA_F32)), -1.0, None) == N.SDPA_ERR_SHAPE
+
+
+def test_packed_validation(lib):
+    q, k, v, o = T([64, 8, 30, 1]), T([64, 2, 40, 1]), T([64, 2, 40, 1]), T([64, 8, 30, 1])
+    def call(q=q, k=k, v=v, o=o, qs=FAKE, ks=None, n=3, maxlen=-1, norm=0, wsb=1 << 30, ws=FAKE):
+        return lib.sdpa_fwd_packed(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), qs, ks, n, maxlen,
+                                   math.nan, 0, None, 0, None, -1, None, -1, norm, ctypes.byref(o), ws, wsb, None)
+    assert call(n=-1) == N.SDPA_ERR_SHAPE
+    assert call(qs=None) == N.SDPA_ERR_NULL
+    assert call(maxlen=-2) == N.SDPA_ERR_SHAPE
+    assert call(q=T([64, 8, 15, 2]), o=T([64, 8, 15, 2])) == N.SDPA_ERR_SHAPE      # a batch dimension
+    assert call(k=T([64, 2, 40, 2]), v=T([64, 2, 40, 2])) == N.SDPA_ERR_SHAPE
+    assert call(norm=1, wsb=16) == N.SDPA_ERR_WORKSPACE
+    assert call(q=T([64, 8, 30, 1], N.SDPA_F16)) == N.SDPA_ERR_DTYPE
+    assert call(n=0) == N.SDPA_OK                                                    # nothing to do

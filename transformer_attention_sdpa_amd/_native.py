@@ -54,6 +54,8 @@ SZ = ctypes.c_size_t
 PROTOTYPES = {
     "sdpa_fwd": (I32, [T, T, T, T, T, ctypes.POINTER(BlockMaskInfoC), ctypes.c_float, I32,
                        I32P, I32, I32P, I32, I32P, I32, I32, T, VP, SZ, VP]),
+    "sdpa_fwd_packed": (I32, [T, T, T, I32P, I32P, I32, I32, ctypes.c_float, I32,
+                              I32P, I32, I32P, I32, I32P, I32, I32, T, VP, SZ, VP]),
     "sdpa_fwd_workspace_bytes": (SZ, [T, T, T, I32]),
     "sdpa_decode": (I32, [T, T, T, I32P, ctypes.c_float, I32, T, VP, SZ, VP]),
     "sdpa_decode_workspace_bytes": (SZ, [T, T, I32]),

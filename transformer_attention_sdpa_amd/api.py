@@ -168,6 +168,48 @@ def sdpa(q, k, v, bias=None, mask=None, *, mask_info: BlockMaskInfo = None, scal
     return out
 
 
+def sdpa_packed(q, k, v, q_segments, kv_segments=None, *, maxlen=None, scale=None, is_causal=False, q_offset=0,
+                kv_lengths=None, q_lengths=None, qk_norm=False, out=None, out_dtype=None, stream=None):
+    """Attention over packed sequences. q [Lq_total][Hq][D], k [Lkv_total][Hkv][D], v [Lkv_total][Hkv][Dv]
+    hold the segments one after the other; q_segments / kv_segments (device int32 tensors, kv =
+    q when None) give their lengths. Segment s of q attends segment s of k/v only; is_causal,
+    q_offset, kv_lengths and q_lengths apply per segment (an int, or one entry per segment).
+    maxlen: None or a bound on every segment. Returns out [Lq_total][Hq][Dv].
+    """
+    lib = N.load()
+    Lq, Hq, _ = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((Lq, Hq, Dv), dtype=out_dtype or q.dtype, device=q.device)
+    qs = torch.as_tensor(q_segments, dtype=torch.int32, device=q.device).reshape(-1).contiguous()
+    ks = None if kv_segments is None else torch.as_tensor(kv_segments, dtype=torch.int32,
+                                                          device=q.device).reshape(-1).contiguous()
+    S = qs.numel()
+    if ks is not None and ks.numel() != S:
+        raise ValueError("q_segments and kv_segments differ in count")
+    dq, dk, dv, do = desc(q.unsqueeze(0)), desc(k.unsqueeze(0)), desc(v.unsqueeze(0)), desc(out.unsqueeze(0))
+    qo_ptr, qo_all, qo_keep = _per_batch_arg(q_offset, S, q.device, 0)
+    kv_ptr, kv_all, kv_keep = _per_batch_arg(kv_lengths, S, q.device, -1)
+    ql_ptr, ql_all, ql_keep = _per_batch_arg(q_lengths, S, q.device, -1)
+    ws_bytes = lib.sdpa_fwd_workspace_bytes(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(bool(qk_norm)))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    s, sp = _stream(stream)
+    st = lib.sdpa_fwd_packed(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                             ctypes.c_void_p(qs.data_ptr()) if S else None,
+                             ctypes.c_void_p(ks.data_ptr()) if ks is not None and S else None, S,
+                             -1 if maxlen is None else int(maxlen),
+                             float("nan") if scale is None else float(scale), _CAUSAL[is_causal],
+                             qo_ptr, qo_all, kv_ptr, kv_all, ql_ptr, ql_all, int(bool(qk_norm)),
+                             ctypes.byref(do), ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
+                             ws_bytes, sp)
+    N.check(st)
+    if stream is not None:
+        for t in (ws, qs, ks, qo_keep, kv_keep, ql_keep):
+            if t is not None:
+                t.record_stream(s)
+    return out
+
+
 def decode_workspace_bytes(q, k_cache, num_splits=0) -> int:
     lib = N.load()
     dq, dk = desc(q), desc(k_cache)

@@ -214,6 +214,44 @@ const char* sdpa_last_error(void) { return g_err.c_str(); }
 
 const char* sdpa_version(void) { return "sdpa_mi355x 0.1 gfx950"; }
 
+sdpa_status sdpa_fwd_packed(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
+                            const int32_t* q_segments, const int32_t* kv_segments, int32_t n_segments, int32_t maxlen,
+                            float scale, int32_t is_causal, const int32_t* q_offset, int32_t q_offset_all,
+                            const int32_t* kv_lengths, int32_t kv_length_all, const int32_t* q_lengths,
+                            int32_t q_length_all, int32_t qk_norm, sdpa_tensor* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!v || !out) return fail(SDPA_ERR_NULL, "v and out descriptors are required");
+  if (n_segments < 0) return fail(SDPA_ERR_SHAPE, "n_segments must be >= 0");
+  if (n_segments > 0 && !q_segments) return fail(SDPA_ERR_NULL, "q_segments is required");
+  if (maxlen < -1) return fail(SDPA_ERR_SHAPE, "maxlen must be -1 (none) or a length");
+  if (!q || !k || q->dims[3] != 1 || k->dims[3] != 1 || out->dims[3] != 1)
+    return fail(SDPA_ERR_SHAPE, "packed sequences have no batch dimension (dims[3] == 1)");
+  AttnArgs a;
+  sdpa_status st = resolve_attention(q, k, v, nullptr, nullptr, nullptr, scale, is_causal, q_offset, q_offset_all,
+                                     kv_lengths, kv_length_all, q_lengths, q_length_all, qk_norm, out, a);
+  if (st != SDPA_OK) return st;
+  const size_t need = sdpa_fwd_workspace_bytes(q, k, v, qk_norm);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(SDPA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (a.Lq == 0 || n_segments == 0) return SDPA_OK;
+  if (!a.q || !a.out || (a.Lkv > 0 && (!a.k || !a.v))) return fail(SDPA_ERR_NULL, "a tensor's data is NULL");
+  a.q_seg = q_segments;
+  a.kv_seg = kv_segments;
+  a.n_seg = n_segments;
+  a.seg_maxlen = maxlen;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (qk_norm && a.Lkv > 0) {
+    a.k_rinv = static_cast<const float*>(workspace);
+    sdpa_status hs = hip_status(launch_row_rinv(a.k, a.in_dtype, a.k_sb, a.k_ss, a.k_sh, 1, a.Lkv, a.Hkv, a.D,
+                                                kRmsEps, static_cast<float*>(workspace), s),
+                                "key RMS factors");
+    if (hs != SDPA_OK) return hs;
+  }
+  if (fwd_mfma_supports(a)) return hip_status(launch_fwd_mfma(a, s), "sdpa_fwd_packed (mfma)");
+  return hip_status(launch_fwd_generic(a, s), "sdpa_fwd_packed (generic)");
+}
+
 size_t sdpa_fwd_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v, int32_t qk_norm) {
   (void)q; (void)v;
   if (!qk_norm || !k) return 0;

@@ -46,6 +46,86 @@ __device__ __forceinline__ void store_elem(void* base, int64_t idx, int dtype, f
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// ---- packed sequences (page "Neural Network primitives from NNlib.jl", "Packed sequences") --
+// A workgroup of a packed launch handles one tile of `tile` query rows of one segment. The
+// tiles are numbered segment by segment; a wave finds the segment of tile `item` by prefix sums
+// of the segment lengths (64 segments per step, every lane one segment). Starts and lengths
+// are cut to the arrays, so lengths that do not add up cannot reach past them.
+struct SegView {
+  int s;                       // segment
+  int tile;                    // tile within the segment
+  int64_t q_start, kv_start;   // first row of the segment in q and in k/v
+  int q_len, kv_len;
+};
+
+__device__ __forceinline__ int64_t wave_incl_scan64(int64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int64_t readfirstlane64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The chunk totals, the running bases and so the loop exit are made scalar: a loop whose exit
+// the compiler must take as divergent would make every value leaving it divergent, and the
+// buffer resources built from them would need waterfall loops.
+__device__ __forceinline__ bool seg_locate(const AttnArgs& a, int item, int tile, SegView& sv) {
+  const int lane = threadIdx.x & 63;
+  const int32_t* kvs = a.kv_seg ? a.kv_seg : a.q_seg;
+  int64_t qbase = 0, kbase = 0, tbase = 0;
+  for (int c0 = 0; c0 < a.n_seg; c0 += 64) {
+    const int s = c0 + lane;
+    const int64_t ql = s < a.n_seg ? max(a.q_seg[s], 0) : 0;
+    const int64_t kl = s < a.n_seg ? max(kvs[s], 0) : 0;
+    const int64_t qi = wave_incl_scan64(ql), ki = wave_incl_scan64(kl);
+    const int64_t q0 = min(qbase + qi - ql, (int64_t)a.Lq), k0 = min(kbase + ki - kl, (int64_t)a.Lkv);
+    const int qn = (int)min(ql, (int64_t)a.Lq - q0), kn = (int)min(kl, (int64_t)a.Lkv - k0);
+    const int64_t nt = (qn + tile - 1) / tile;
+    const int64_t ti = wave_incl_scan64(nt);
+    const int64_t tot = readfirstlane64(__shfl(ti, 63, 64));
+    if (item < tbase + tot) {
+      const int l = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__builtin_amdgcn_ballot_w64(tbase + ti > item)));
+      sv.s = c0 + l;
+      sv.tile = __builtin_amdgcn_readfirstlane((int)(item - tbase - __shfl(ti - nt, l, 64)));
+      sv.q_start = readfirstlane64(__shfl(q0, l, 64));
+      sv.kv_start = readfirstlane64(__shfl(k0, l, 64));
+      sv.q_len = __builtin_amdgcn_readfirstlane(__shfl(qn, l, 64));
+      sv.kv_len = __builtin_amdgcn_readfirstlane(__shfl(kn, l, 64));
+      return true;
+    }
+    tbase += tot;
+    qbase += readfirstlane64(__shfl(qi, 63, 64));
+    kbase += readfirstlane64(__shfl(ki, 63, 64));
+  }
+  return false;
+}
+
+// The arguments of segment sv as a batch of one: pointers moved to the segment's first rows,
+// the segment's lengths as the array lengths, per-segment arrays moved to entry sv.s.
+__device__ __forceinline__ AttnArgs seg_args(const AttnArgs& a, const SegView& sv) {
+  AttnArgs r = a;
+  const int ie = a.in_dtype == SDPA_F32 ? 4 : 2, oe = a.out_dtype == SDPA_F32 ? 4 : 2;
+  r.q = static_cast<const char*>(a.q) + sv.q_start * a.q_ss * ie;
+  r.k = static_cast<const char*>(a.k) + sv.kv_start * a.k_ss * ie;
+  r.v = static_cast<const char*>(a.v) + sv.kv_start * a.v_ss * ie;
+  r.out = static_cast<char*>(a.out) + sv.q_start * a.o_ss * oe;
+  r.Lq = sv.q_len;
+  r.Lkv = sv.kv_len;
+  if (a.q_offset) r.q_offset = a.q_offset + sv.s;
+  if (a.kv_lengths) r.kv_lengths = a.kv_lengths + sv.s;
+  if (a.q_lengths) r.q_lengths = a.q_lengths + sv.s;
+  if (a.k_rinv) r.k_rinv = a.k_rinv + sv.kv_start * a.Hkv;
+  return r;
+}
+
 // Valid keys of batch element b: kv_lengths clamped to [0, Lkv], or Lkv when none is given.
 __device__ __forceinline__ int batch_kv_len(const AttnArgs& a, int b) {
   int n = a.kv_lengths ? a.kv_lengths[b] : (a.kv_length_all >= 0 ? a.kv_length_all : a.Lkv);

@@ -1,5 +1,6 @@
 // fwd_generic.hip -- attention forward for any shape the ABI accepts (head dims up to 256,
-// fp32 or bf16 inputs, every masking option), with fp32 arithmetic and an accurate expf.
+// fp32, bf16 or f16 inputs, every masking option, packed sequences), with fp32 arithmetic and
+// an accurate expf.
 //
 // The softmax is taken online over tiles of 64 keys, so the weights are never materialized
 // (page "Neural Network primitives from NNlib.jl", section "Fused implementation"): one wave
@@ -18,11 +19,24 @@ constexpr int kGenThreads = 256;                 // 4 waves = 4 query rows per w
 constexpr int kGenRows = kGenThreads / 64;
 constexpr int kGenMaxD = 256;                    // largest head dim accepted
 
-__global__ __launch_bounds__(kGenThreads) void fwd_generic_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kGenThreads) void fwd_generic_kernel(AttnArgs args) {
   __shared__ float q_lds[kGenRows][kGenMaxD];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int i = blockIdx.x * kGenRows + wave;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.y;
+  // packed sequences: workgroup x takes tile x (kGenRows rows) of the segments (seg_locate),
+  // and the segment is then a batch of one
+  AttnArgs a = args;
+  int i, b;
+  if (args.q_seg) {
+    SegView sv;
+    if (!seg_locate(args, blockIdx.x, kGenRows, sv)) return;
+    a = seg_args(args, sv);
+    i = sv.tile * kGenRows + wave;
+    b = 0;
+  } else {
+    i = blockIdx.x * kGenRows + wave;
+    b = blockIdx.z;
+  }
   if (i >= a.Lq) return;                         // whole wave leaves together; no block barriers below
 
   const int g = h / (a.Hq / a.Hkv);
@@ -116,6 +130,12 @@ __global__ void debug_allowed_kernel(AttnArgs a, uint8_t* out, int64_t sb, int64
 }  // namespace
 
 hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t s) {
+  if (a.q_seg) {
+    const int64_t n = packed_tiles_bound(a, kGenRows);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fwd_generic_kernel, dim3((unsigned)n, a.Hq, 1), dim3(kGenThreads), 0, s, a);
+    return hipGetLastError();
+  }
   dim3 grid((a.Lq + kGenRows - 1) / kGenRows, a.Hq, a.B);
   hipLaunchKernelGGL(fwd_generic_kernel, grid, dim3(kGenThreads), 0, s, a);
   return hipGetLastError();

@@ -129,8 +129,8 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) 
 
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units: the running max moves only when a row's max grows by more
 
-template <int D, int BIAS, int MASK, bool NORM, bool F16>
-__global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, int remap, int order) {
+template <int D, int BIAS, int MASK, bool NORM, bool F16, bool PACKED>
+__global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt, int remap, int order) {
   using E = In<F16>;
   using bf16x8 = typename E::x8;     // the 16-bit operand vector (bf16 or f16)
   constexpr int DC = D / 16;         // 16-wide head-dim chunks (MFMA k steps for q.k)
@@ -154,9 +154,18 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
   // concurrently running workgroups of an XCD share few K/V heads. order 1 (rank-major, for
   // causal launches): all heads' heaviest tiles first, then the next rank -- longest work first
   // across the whole launch, so no heavy tile starts at the end and leaves the chip idle.
+  // PACKED: workgroup Hq * i + h takes query tile i of the segments (seg_locate) for head h,
+  // and the segment is then a batch of one.
+  AttnArgs a = args;
   const int HB = a.Hq * a.B;
   int qt, bh;
-  if (order == 1) {
+  if constexpr (PACKED) {
+    SegView sv;
+    if (!seg_locate(args, (int)(blockIdx.x / args.Hq), BM, sv)) return;     // workgroup-uniform
+    a = seg_args(args, sv);
+    qt = sv.tile;
+    bh = blockIdx.x % args.Hq;
+  } else if (order == 1) {
     if (remap) {                                  // HB % 8 == 0
       const int per_x = HB >> 3, k = blockIdx.x >> 3;
       qt = n_qt - 1 - k / per_x;
@@ -686,11 +695,20 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs a, int n_qt, i
 
 template <int D, int BIAS, int MASK, bool NORM, bool F16>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
+  if constexpr (BIAS == BIAS_NONE && MASK == MASK_NONE) {
+    if (a.q_seg) {
+      const int64_t nwg = packed_tiles_bound(a, BM) * a.Hq;
+      if (nwg <= 0) return hipSuccess;
+      hipLaunchKernelGGL((fwd_mfma_kernel<D, BIAS, MASK, NORM, F16, true>), dim3((unsigned)nwg), dim3(NT), 0, s,
+                         a, 0, 0, 0);
+      return hipGetLastError();
+    }
+  }
   const int n_qt = (a.Lq + BM - 1) / BM;
   const int64_t nwg = (int64_t)n_qt * a.Hq * a.B;
   const int order = a.causal != SDPA_CAUSAL_NONE ? 1 : 0;
   const int remap = order == 1 ? ((a.Hq * a.B) % 8 == 0 ? 1 : 0) : (nwg % 8) == 0 ? 1 : 0;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, BIAS, MASK, NORM, F16>), dim3((unsigned)nwg), dim3(NT), 0, s, a, n_qt,
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, BIAS, MASK, NORM, F16, false>), dim3((unsigned)nwg), dim3(NT), 0, s, a, n_qt,
                      remap, order);
   return hipGetLastError();
 }
@@ -739,7 +757,8 @@ bool fwd_mfma_supports(const AttnArgs& a) {
   if ((int64_t)a.Lq * a.q_ss * 2 > INT32_MAX || (int64_t)a.Lkv * a.k_ss * 2 > INT32_MAX ||
       (int64_t)a.Lkv * a.v_ss * 2 > INT32_MAX)
     return false;
-  const int64_t nwg = (int64_t)((a.Lq + BM - 1) / BM) * a.Hq * a.B;
+  if (a.q_seg && (a.bias || a.mask || a.bm_class)) return false;
+  const int64_t nwg = (a.q_seg ? packed_tiles_bound(a, BM) : (int64_t)((a.Lq + BM - 1) / BM) * a.B) * a.Hq;
   return nwg > 0 && nwg < (int64_t)INT32_MAX;
 }
 

@@ -47,6 +47,13 @@ struct AttnArgs {
   const int32_t* q_lengths;    int q_length_all;    // < 0: none
   int qk_norm;
   const float* k_rinv;         // [B][Lkv][Hkv]: 1/rms of each key head vector (qk_norm only)
+
+  // packed sequences (B == 1): segment s of the queries attends segment s of the keys/values;
+  // q_offset, q_lengths and kv_lengths then hold one entry per segment. nullptr: batched.
+  const int32_t* q_seg;        // [n_seg] lengths along q
+  const int32_t* kv_seg;       // [n_seg] lengths along k/v
+  int n_seg;
+  int seg_maxlen;              // bound on the segment lengths from the caller, or -1 (host use)
 };
 
 struct DecodeArgs {
@@ -77,6 +84,17 @@ struct MaskInfoArgs {
 };
 
 constexpr float kRmsEps = 1e-6f;
+
+// Query tiles of `tile` rows over all segments of a packed launch, at most: every segment adds
+// at most one partial tile, and none has more than the caller's maxlen rows. Host only.
+inline int64_t packed_tiles_bound(const AttnArgs& a, int tile) {
+  int64_t n = ((int64_t)a.Lq + tile - 1) / tile + a.n_seg;
+  if (a.seg_maxlen >= 0) {
+    const int64_t m = (int64_t)a.n_seg * ((a.seg_maxlen + tile - 1) / tile);
+    if (m < n) n = m;
+  }
+  return n;
+}
 
 // Launchers (each returns hipSuccess or the launch error).
 hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t s);
