@@ -51,6 +51,7 @@ def parse_args():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (for scaling HBM byte counters)")
     p.add_argument("--skip-decode", action="store_true")
+    p.add_argument("--skip-mask-info", action="store_true")
     return p.parse_args()
 
 
@@ -238,6 +239,28 @@ def main():
                        "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(np.stack(refs)))},
         }
         del qd, kc, vc, od, ws
+        torch.cuda.empty_cache()
+
+    # ---- block info of a runtime mask: bytes (U8) and packed bits (U1) --------------------
+    # the 8192 x 8192 mask of the bias + block-sparse workload, 128 x 128 blocks; the bound is
+    # reading the mask (64 MiB as bytes, 8 MiB as bits) plus writing the partial blocks' bits
+    if not args.skip_mask_info:
+        mask = workloads.block_sparse_mask(8192, 8192, 128, k=3)
+        mu8 = sa.from_numpy(mask, "u8")
+        mu1 = sa.PackedMask(sa.from_numpy(workloads.pack_mask_bits(mask, 1), "i32"), mask.shape[-1])
+        mi = {}
+        infos = {}
+        for name, m in (("u8", mu8), ("u1", mu1)):
+            t_mi, _ = time_steps(lambda m=m: sa.build_block_mask_info(m, 128, 128), args.steps, args.warmup, stream)
+            infos[name] = sa.build_block_mask_info(m, 128, 128).to_numpy()
+            mask_bytes = mask.size if name == "u8" else mask.size / 8
+            mi[name] = {"ms": round(t_mi / args.steps * 1e3, 4),
+                        "mask_GB_per_s": round(mask_bytes / (t_mi / args.steps) / 1e9, 1)}
+        same = all(np.array_equal(infos["u8"][k], infos["u1"][k])
+                   for k in ("block_mask", "mask_next", "row_ptr", "data_next", "partial_bits"))
+        result["mask_info"] = {"workload": "bias_block_mask mask, 1 x 1 x 8192 x 8192, 128 x 128 blocks",
+                               "n_partial": int(infos["u8"]["n_partial"]), "u1_equals_u8": bool(same), **mi}
+        del mu8, mu1
         torch.cuda.empty_cache()
 
     # ---- CPU baseline (rank 0, N = 1 only) ------------------------------------------------

@@ -58,7 +58,12 @@ typedef enum {
 
 /* F16 is IEEE binary16, the other 16-bit input NNlib's fused implementation takes ("Fused
  * implementation": bf16/f16 GPU arrays). */
-typedef enum { SDPA_F32 = 0, SDPA_BF16 = 1, SDPA_U8 = 2, SDPA_F16 = 3 } sdpa_dtype;
+typedef enum { SDPA_F32 = 0, SDPA_BF16 = 1, SDPA_U8 = 2, SDPA_F16 = 3, SDPA_U1 = 4 } sdpa_dtype;
+/* SDPA_U1: a boolean mask packed 32 elements per 32-bit word, 8x smaller than U8 (the
+ * splash-attention pull request's review asks for packed booleans where a 100k+ context makes a
+ * byte mask too large). Element c of a row is bit (c mod 32) of word c/32 of that row; dims[0]
+ * counts elements with strides[0] == 1 (or dims[0] == 1 to broadcast); strides[1..3] count
+ * 32-bit words, each row starting on a word. Bits past dims[0] in a row's last word are ignored. */
 
 /* "Arguments": is_causal. TRUE: query i attends keys j <= q_offset + i. BOTTOM_RIGHT: the
  * same with q_offset = kv_len_b - q_len_b, each the given length or else the array size. */
@@ -96,7 +101,7 @@ typedef struct {
  *      three the same dtype. out {Dv, Hq, Lq, B}, F32, BF16 or F16. Arithmetic is fp32 (16-bit
  *      products accumulate in fp32).
  * bias NULL, or F32/BF16/F16 {Lkv|1, Lq|1, Hq|1, B|1}; added to the scaled logits, not scaled.
- * mask NULL, or U8 {Lkv|1, Lq|1, Hq|1, B|1}; nonzero = may attend.
+ * mask NULL, or U8 {Lkv|1, Lq|1, Hq|1, B|1}, nonzero = may attend; or the same as U1 bits.
  * mask_info  NULL, or block info built from the mask by build_block_mask_info. When given it
  *      replaces `mask` (which is then not read), lets the kernel skip empty blocks and skip the
  *      element test on full blocks. Its mask_batch/mask_heads must be 1 or B/Hq and its
@@ -188,7 +193,7 @@ SDPA_API sdpa_status kv_cache_update(sdpa_tensor* k_cache, sdpa_tensor* v_cache,
 
 /* ---------------------------------------------------------------------------------------
  * build_block_mask_info -- block information of a runtime (device) boolean mask (pull request
- * "Support dynamic masks in splash attention #25213"). mask U8 {Lkv, Lq, Hm|1, Bm|1};
+ * "Support dynamic masks in splash attention #25213"). mask U8 or U1 {Lkv, Lq, Hm|1, Bm|1};
  * bq >= 1, bkv a multiple of 32. A block is classed by its in-range elements; bits of a ragged
  * edge block past the mask are 0. storage: device memory of at least
  * sdpa_block_mask_info_bytes(); info: HOST struct, filled with pointers into storage. The

@@ -83,6 +83,8 @@ CASES = {
     "bias_bad_dim": (lambda: good(), N.SDPA_ERR_SHAPE, {"bias": T([7, 5, 4, 3])}),
     "bias_u8": (lambda: good(), N.SDPA_ERR_DTYPE, {"bias": T([7, 5, 8, 3], N.SDPA_U8)}),
     "mask_bf16": (lambda: good(), N.SDPA_ERR_DTYPE, {"mask": T([7, 5, 1, 1], N.SDPA_BF16)}),
+    "mask_u1_strided": (lambda: good(), N.SDPA_ERR_SHAPE, {"mask": T([7, 5, 1, 1], N.SDPA_U1, strides=[2, 1, 1, 1])}),
+    "u1_inputs": (lambda: good(dt=N.SDPA_U1), N.SDPA_ERR_DTYPE, {}),
     "mask_bad_dim": (lambda: good(), N.SDPA_ERR_SHAPE, {"mask": T([7, 4, 1, 1], N.SDPA_U8)}),
     "qk_norm_no_workspace": (lambda: good(), N.SDPA_ERR_WORKSPACE, {"qk_norm": 1}),
 }

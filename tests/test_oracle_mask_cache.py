@@ -101,3 +101,15 @@ def test_kv_cache_update_skips_out_of_range_rows():
     k2, _ = kv_cache_update(kc, vc, kn, vn, np.array([2, -2]))
     np.testing.assert_array_equal(k2[0, :, 0, 0], [0, 0, 1, 1])      # rows 2, 3 written; 4 skipped
     np.testing.assert_array_equal(k2[1, :, 0, 0], [1, 0, 0, 0])      # -2, -1 skipped; 0 written
+
+
+def test_pack_mask_bits_layout():
+    # the U1 layout: element c of a row is bit c % 32 of word c // 32; padding bits as asked
+    rng = np.random.default_rng(5)
+    m = (rng.random((2, 3, 70)) < 0.5).astype(np.uint8)
+    w = workloads.pack_mask_bits(m, pad_bit=1).view(np.uint32)
+    assert w.shape == (2, 3, 3)
+    for idx in np.ndindex(2, 3):
+        for c in range(96):
+            bit = (int(w[idx][c // 32]) >> (c % 32)) & 1
+            assert bit == (m[idx][c] if c < 70 else 1)

@@ -6,7 +6,7 @@ Entry points (same names as the C ABI): ``sdpa`` (sdpa_fwd), ``sdpa_decode``,
 ``debug_allowed_mask``. ``load()`` loads the shared library and raises when it is not built.
 """
 from ._native import load, SdpaError, header_functions, LIB_PATH
-from .api import (sdpa, sdpa_packed, sdpa_decode, kv_cache_update, build_block_mask_info, BlockMaskInfo,
+from .api import (sdpa, sdpa_packed, sdpa_decode, kv_cache_update, build_block_mask_info, BlockMaskInfo, PackedMask,
                   head_rms_norm, per_head_rms_norm, debug_allowed_mask, decode_workspace_bytes,
                   desc, from_numpy, to_numpy_f32)
 
@@ -15,6 +15,6 @@ sdpa_fwd_packed = sdpa_packed
 
 __all__ = ["load", "SdpaError", "header_functions", "LIB_PATH", "sdpa", "sdpa_fwd", "sdpa_packed",
            "sdpa_fwd_packed", "sdpa_decode",
-           "kv_cache_update", "build_block_mask_info", "BlockMaskInfo", "head_rms_norm",
+           "kv_cache_update", "build_block_mask_info", "BlockMaskInfo", "PackedMask", "head_rms_norm",
            "per_head_rms_norm", "debug_allowed_mask", "decode_workspace_bytes", "desc",
            "from_numpy", "to_numpy_f32"]

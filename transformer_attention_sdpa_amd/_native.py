@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(PKG, "libsdpa_mi355x.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "sdpa.h")
 
 SDPA_OK, SDPA_ERR_NULL, SDPA_ERR_SHAPE, SDPA_ERR_DTYPE, SDPA_ERR_UNSUPPORTED, SDPA_ERR_WORKSPACE, SDPA_ERR_HIP = range(7)
-SDPA_F32, SDPA_BF16, SDPA_U8, SDPA_F16 = 0, 1, 2, 3
+SDPA_F32, SDPA_BF16, SDPA_U8, SDPA_F16, SDPA_U1 = 0, 1, 2, 3, 4
 CAUSAL_NONE, CAUSAL_TRUE, CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 
 

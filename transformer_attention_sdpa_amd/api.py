@@ -64,9 +64,39 @@ def _per_batch_arg(x, B, device, none_value):
     return t.data_ptr(), 0, t
 
 
+class PackedMask:
+    """A boolean mask packed 32 elements per 32-bit word along the keys (the U1 layout of
+    include/sdpa.h): element c of a row is bit c % 32 of word c // 32. ``words`` is an int32
+    device tensor [Mb][Mh][Lq][ceil(kv_len / 32)] (leading dims may be 1 to broadcast);
+    ``kv_len`` is the number of keys. The caller packs the bits."""
+
+    def __init__(self, words: torch.Tensor, kv_len: int):
+        if words.dtype != torch.int32:
+            raise TypeError("packed mask words must be int32")
+        if words.shape[-1] != (kv_len + 31) // 32:
+            raise ValueError("packed mask rows need ceil(kv_len / 32) words")
+        if words.stride(-1) != 1:
+            raise ValueError("packed mask words must be contiguous along a row")
+        self.words, self.kv_len = words, int(kv_len)
+        self.device = words.device
+        self.shape = tuple(words.shape[:-1]) + (self.kv_len,)
+
+    def desc(self) -> N.SdpaTensor:
+        d = desc(self.words.view(torch.float32))     # same 32-bit words; dims and strides in words
+        d.data = self.words.data_ptr() if self.words.numel() > 0 else None
+        d.dtype = N.SDPA_U1
+        d.dims[0] = self.kv_len
+        d.strides[0] = 1
+        return d
+
+
+def _mask_desc(m):
+    return m.desc() if isinstance(m, PackedMask) else desc(m)
+
+
 def _mask_u8(mask):
-    if mask is None:
-        return None
+    if mask is None or isinstance(mask, PackedMask):
+        return mask
     if mask.dtype == torch.bool:
         return mask.view(torch.uint8)
     if mask.dtype != torch.uint8:
@@ -114,10 +144,10 @@ class BlockMaskInfo:
 
 
 def build_block_mask_info(mask: torch.Tensor, bq: int = 128, bkv: int = 128, stream=None) -> BlockMaskInfo:
-    """Block info of a runtime device mask [Mb][Mh][Lq][Lkv] (bool or uint8)."""
+    """Block info of a runtime device mask [Mb][Mh][Lq][Lkv] (bool or uint8, or a PackedMask)."""
     lib = N.load()
     m = _mask_u8(mask)
-    dm = desc(m)
+    dm = _mask_desc(m)
     nbytes = ctypes.c_size_t()
     N.check(lib.sdpa_block_mask_info_bytes(ctypes.byref(dm), bq, bkv, ctypes.byref(nbytes)))
     storage = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=mask.device)
@@ -145,7 +175,7 @@ def sdpa(q, k, v, bias=None, mask=None, *, mask_info: BlockMaskInfo = None, scal
     dq, dk, dv, do = desc(q), desc(k), desc(v), desc(out)
     db = desc(bias) if bias is not None else None
     m = _mask_u8(mask) if mask_info is None else None
-    dm = desc(m) if m is not None else None
+    dm = _mask_desc(m) if m is not None else None
     qo_ptr, qo_all, qo_keep = _per_batch_arg(q_offset, B, q.device, 0)
     kv_ptr, kv_all, kv_keep = _per_batch_arg(kv_lengths, B, q.device, -1)
     ql_ptr, ql_all, ql_keep = _per_batch_arg(q_lengths, B, q.device, -1)
@@ -285,7 +315,7 @@ def debug_allowed_mask(q, k, mask=None, *, mask_info=None, is_causal=False, q_of
     allowed = torch.empty((B, Hq, Lq, Lkv), dtype=torch.uint8, device=q.device)
     dq, dk, da = desc(q), desc(k), desc(allowed)
     m = _mask_u8(mask) if mask_info is None else None
-    dm = desc(m) if m is not None else None
+    dm = _mask_desc(m) if m is not None else None
     qo_ptr, qo_all, _k1 = _per_batch_arg(q_offset, B, q.device, 0)
     kv_ptr, kv_all, _k2 = _per_batch_arg(kv_lengths, B, q.device, -1)
     ql_ptr, ql_all, _k3 = _per_batch_arg(q_lengths, B, q.device, -1)

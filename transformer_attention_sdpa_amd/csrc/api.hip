@@ -134,12 +134,15 @@ sdpa_status resolve_attention(const sdpa_tensor* q, const sdpa_tensor* k, const 
     a.bm_batch = mi->mask_batch; a.bm_heads = mi->mask_heads; a.bm_nqb = mi->n_qb; a.bm_nkb = mi->n_kb;
     a.bm_bq = mi->bq; a.bm_bkv = mi->bkv;
   } else if (mask) {
-    if (mask->dtype != SDPA_U8) return fail(SDPA_ERR_DTYPE, "mask must be U8");
+    if (mask->dtype != SDPA_U8 && mask->dtype != SDPA_U1) return fail(SDPA_ERR_DTYPE, "mask must be U8 or U1");
     if (!dims_ok(mask)) return fail(SDPA_ERR_SHAPE, "mask dims out of range");
+    if (mask->dtype == SDPA_U1 && mask->dims[0] != 1 && mask->strides[0] != 1)
+      return fail(SDPA_ERR_SHAPE, "a U1 mask needs its elements contiguous (strides[0] == 1)");
     int64_t st[4];
     sdpa_status s = bcast_strides(mask, "mask", Lkv, Lq, Hq, B, st);
     if (s != SDPA_OK) return s;
     a.mask = static_cast<const uint8_t*>(mask->data);
+    a.mask_u1 = mask->dtype == SDPA_U1;
     a.mask_sb = st[0]; a.mask_sh = st[1]; a.mask_sq = st[2]; a.mask_sk = st[3];
     if (!a.mask && numel(mask) > 0) return fail(SDPA_ERR_NULL, "mask data is NULL");
   }
@@ -172,8 +175,10 @@ struct MaskLayout {
 
 sdpa_status mask_layout(const sdpa_tensor* mask, int32_t bq, int32_t bkv, MaskLayout& L) {
   if (!mask) return fail(SDPA_ERR_NULL, "mask descriptor is required");
-  if (mask->dtype != SDPA_U8) return fail(SDPA_ERR_DTYPE, "mask must be U8");
+  if (mask->dtype != SDPA_U8 && mask->dtype != SDPA_U1) return fail(SDPA_ERR_DTYPE, "mask must be U8 or U1");
   if (!dims_ok(mask)) return fail(SDPA_ERR_SHAPE, "mask dims out of range");
+  if (mask->dtype == SDPA_U1 && mask->dims[0] != 1 && mask->strides[0] != 1)
+    return fail(SDPA_ERR_SHAPE, "a U1 mask needs its elements contiguous (strides[0] == 1)");
   if (bq < 1 || bkv < 32 || bkv % 32) return fail(SDPA_ERR_SHAPE, "bq >= 1 and bkv a positive multiple of 32");
   const int64_t Lkv = mask->dims[0], Lq = mask->dims[1], Mh = mask->dims[2], Mb = mask->dims[3];
   const int64_t n_qb = (Lq + bq - 1) / bq, n_kb = (Lkv + bkv - 1) / bkv;
@@ -407,7 +412,8 @@ sdpa_status build_block_mask_info(const sdpa_tensor* mask, int32_t bq, int32_t b
   MaskInfoArgs m;
   std::memset(&m, 0, sizeof m);
   m.mask = static_cast<const uint8_t*>(mask->data);
-  m.sb = mask->strides[3]; m.sh = mask->strides[2]; m.sq = mask->strides[1]; m.sk = mask->strides[0];
+  m.u1 = mask->dtype == SDPA_U1;
+  m.sb = mask->strides[3]; m.sh = mask->strides[2]; m.sq = mask->strides[1]; m.sk = mask->dims[0] == 1 ? 0 : mask->strides[0];
   m.Mb = info->mask_batch; m.Mh = info->mask_heads; m.Lq = info->q_len; m.Lkv = info->kv_len;
   m.bq = bq; m.bkv = bkv; m.n_qb = info->n_qb; m.n_kb = info->n_kb;
   m.cls = info->block_mask; m.next = info->mask_next; m.row_ptr = info->row_ptr; m.data_next = info->data_next;

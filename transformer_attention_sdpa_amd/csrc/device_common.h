@@ -145,6 +145,13 @@ __device__ __forceinline__ int64_t batch_causal_offset(const AttnArgs& a, int b)
   return 0;
 }
 
+// Element of a dense mask: row at `row` (bytes for U8, 32-bit words for U1), element `col`
+// within the row (already multiplied by the element stride).
+__device__ __forceinline__ bool mask_bit(const uint8_t* mask, int u1, int64_t row, int64_t col) {
+  if (u1) return (reinterpret_cast<const uint32_t*>(mask)[row + (col >> 5)] >> (col & 31)) & 1u;
+  return mask[row + col] != 0;
+}
+
 // Mask element (b, h, i, j): dense array or block info; true when no mask is given.
 __device__ __forceinline__ bool mask_allows(const AttnArgs& a, int b, int h, int i, int j) {
   if (a.bm_class) {
@@ -159,7 +166,7 @@ __device__ __forceinline__ bool mask_allows(const AttnArgs& a, int b, int h, int
     return (w >> (col & 31)) & 1u;
   }
   if (a.mask) {
-    return a.mask[b * a.mask_sb + h * a.mask_sh + (int64_t)i * a.mask_sq + (int64_t)j * a.mask_sk] != 0;
+    return mask_bit(a.mask, a.mask_u1, b * a.mask_sb + h * a.mask_sh + (int64_t)i * a.mask_sq, (int64_t)j * a.mask_sk);
   }
   return true;
 }

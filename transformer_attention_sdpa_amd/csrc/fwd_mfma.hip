@@ -483,7 +483,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
           uint32_t bits = 0xffffu;
           if constexpr (MASK == MASK_DENSE) {
             bits = 0;
-            if (mask_row >= 0) {
+            if (mask_row >= 0 && a.mask_u1) {
+              // U1: the 16 keys from jb (a multiple of 16) are 16 bits of one word of the row
+              const uint32_t* mw = reinterpret_cast<const uint32_t*>(a.mask) + mask_row;
+              if (a.mask_sk == 0) bits = (mw[0] & 1u) ? 0xffffu : 0u;
+              else if (jb < a.Lkv) bits = (mw[jb >> 5] >> (jb & 31)) & 0xffffu;
+            } else if (mask_row >= 0) {
               const uint8_t* mp = a.mask + mask_row + (int64_t)jb * a.mask_sk;
               if (a.mask_vec && jb + 16 <= a.Lkv) {
                 const uint4 m4 = *reinterpret_cast<const uint4*>(mp);
@@ -768,8 +773,8 @@ hipError_t launch_fwd_mfma(const AttnArgs& args, hipStream_t s) {
   const int per16 = a.bias_dtype == SDPA_BF16 ? 8 : 4;
   a.bias_vec = a.bias && a.bias_sk == 1 && al(a.bias, 16) && (a.bias_sb % per16) == 0 &&
                (a.bias_sh % per16) == 0 && (a.bias_sq % per16) == 0;
-  a.mask_vec = a.mask && a.mask_sk == 1 && al(a.mask, 16) && (a.mask_sb % 16) == 0 && (a.mask_sh % 16) == 0 &&
-               (a.mask_sq % 16) == 0;
+  a.mask_vec = a.mask && !a.mask_u1 && a.mask_sk == 1 && al(a.mask, 16) && (a.mask_sb % 16) == 0 &&
+               (a.mask_sh % 16) == 0 && (a.mask_sq % 16) == 0;
   if (a.D == 128) return launch_bias<128>(a, s);
   return launch_bias<64>(a, s);
 }

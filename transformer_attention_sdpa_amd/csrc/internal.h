@@ -30,7 +30,8 @@ struct AttnArgs {
   int64_t bias_sb, bias_sh, bias_sq, bias_sk;
 
   const uint8_t* mask;         // dense mask (nullptr: none, or block info in use)
-  int64_t mask_sb, mask_sh, mask_sq, mask_sk;
+  int64_t mask_sb, mask_sh, mask_sq, mask_sk;   // U1: sb/sh/sq in 32-bit words, sk 0 or 1 (bits)
+  int mask_u1;                 // 1: the mask is U1 bits (see include/sdpa.h), 0: U8 bytes
 
   const int8_t* bm_class;      // block mask info (nullptr: none)
   const int32_t* bm_next;
@@ -73,7 +74,8 @@ struct DecodeArgs {
 
 struct MaskInfoArgs {
   const uint8_t* mask;
-  int64_t sb, sh, sq, sk;
+  int64_t sb, sh, sq, sk;      // U1: sb/sh/sq in 32-bit words, sk 0 or 1 (bits)
+  int u1;                      // 1: U1 bits, 0: U8 bytes
   int Mb, Mh, Lq, Lkv, bq, bkv, n_qb, n_kb;
   int8_t* cls;
   int32_t* next;

@@ -37,12 +37,24 @@ __global__ __launch_bounds__(256) void mask_classify_kernel(MaskInfoArgs m) {
   block_coords(m, blk, bb, hh, qb, kb);
   const int r0 = qb * m.bq, c0 = kb * m.bkv;
   const int nr = min(m.bq, m.Lq - r0), nc = min(m.bkv, m.Lkv - c0);
-  const uint8_t* base = m.mask + bb * m.sb + hh * m.sh + (int64_t)r0 * m.sq + (int64_t)c0 * m.sk;
   int count = 0;
   const int n = nr * nc;
-  for (int e = threadIdx.x; e < n; e += blockDim.x) {
-    const int r = e / nc, c = e - r * nc;
-    count += base[(int64_t)r * m.sq + (int64_t)c * m.sk] != 0;
+  const int64_t row0 = bb * m.sb + hh * m.sh + (int64_t)r0 * m.sq;    // bytes (U8) or words (U1)
+  if (m.u1 && m.sk == 1) {
+    // whole words: the block's columns start on a word (bkv is a multiple of 32)
+    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(m.mask) + row0 + (c0 >> 5);
+    const int nw = (nc + 31) >> 5, tail = nc & 31;
+    for (int e = threadIdx.x; e < nr * nw; e += blockDim.x) {
+      const int r = e / nw, w = e - r * nw;
+      uint32_t bits = w0[(int64_t)r * m.sq + w];
+      if (tail && w == nw - 1) bits &= (1u << tail) - 1u;
+      count += __builtin_popcount(bits);
+    }
+  } else {
+    for (int e = threadIdx.x; e < n; e += blockDim.x) {
+      const int r = e / nc, c = e - r * nc;
+      count += mask_bit(m.mask, m.u1, row0 + (int64_t)r * m.sq, (int64_t)(c0 + c) * m.sk);
+    }
   }
   // workgroup sum
 #pragma unroll
@@ -115,12 +127,25 @@ __global__ __launch_bounds__(256) void mask_pack_kernel(MaskInfoArgs m) {
   const int nr = min(m.bq, m.Lq - r0), nc = min(m.bkv, m.Lkv - c0);
   const int words = m.bkv / 32;
   uint32_t* dst = m.bits + (int64_t)m.next[blk] * m.bq * words;
-  const uint8_t* base = m.mask + bb * m.sb + hh * m.sh + (int64_t)r0 * m.sq + (int64_t)c0 * m.sk;
+  const int64_t row0 = bb * m.sb + hh * m.sh + (int64_t)r0 * m.sq;    // bytes (U8) or words (U1)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (m.u1 && m.sk == 1) {
+    // the block's words as they are, bits past the mask cleared; one word per lane
+    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(m.mask) + row0 + (c0 >> 5);
+    const int nw = (nc + 31) >> 5, tail = nc & 31;
+    for (int r = wave; r < m.bq; r += blockDim.x >> 6) {
+      for (int w = lane; w < words; w += 64) {
+        uint32_t bits = (r < nr && w < nw) ? w0[(int64_t)r * m.sq + w] : 0u;
+        if (tail && w == nw - 1) bits &= (1u << tail) - 1u;
+        dst[(int64_t)r * words + w] = bits;
+      }
+    }
+    return;
+  }
   for (int r = wave; r < m.bq; r += blockDim.x >> 6) {
     for (int c = 0; c < m.bkv; c += 64) {
       const int col = c + lane;
-      const bool bit = r < nr && col < nc && base[(int64_t)r * m.sq + (int64_t)col * m.sk] != 0;
+      const bool bit = r < nr && col < nc && mask_bit(m.mask, m.u1, row0 + (int64_t)r * m.sq, (int64_t)(c0 + col) * m.sk);
       const uint64_t bal = __ballot(bit);
       if (lane == 0) dst[(int64_t)r * words + c / 32] = (uint32_t)bal;
       if (lane == 1 && c / 32 + 1 < words) dst[(int64_t)r * words + c / 32 + 1] = (uint32_t)(bal >> 32);

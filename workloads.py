@@ -311,3 +311,17 @@ def chunked_prefill(B=1, Hq=32, Hkv=8, D=128, Lkv=131072, Lq=2048, q_offset=1290
         normal_tensor(rng_for(k, TAG_K, base=base), (B, Lkv, Hkv, D), "bf16"),
         normal_tensor(rng_for(k, TAG_V, base=base), (B, Lkv, Hkv, D), "bf16"),
         scale=1.0 / math.sqrt(D), is_causal=True, q_offset=q_offset)
+
+
+def pack_mask_bits(mask: np.ndarray, pad_bit: int = 0) -> np.ndarray:
+    """A boolean/uint8 mask [..., Lkv] as the 32-per-word U1 layout: int32 words [..., ceil(Lkv/32)],
+    element c of a row in bit c % 32 of word c // 32. ``pad_bit`` fills the bits past Lkv in each
+    row's last word (they must not matter).
+    """
+    m = np.asarray(mask) != 0
+    Lkv = m.shape[-1]
+    W = (Lkv + 31) // 32
+    full = np.full(m.shape[:-1] + (W * 32,), bool(pad_bit))
+    full[..., :Lkv] = m
+    by = np.packbits(full, axis=-1, bitorder="little")            # 4 bytes per word, little-endian
+    return np.ascontiguousarray(by).view("<u4").astype(np.uint32).view(np.int32)
