@@ -126,6 +126,59 @@ SDPA_API sdpa_status sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const 
                      sdpa_tensor* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * sdpa_fwd_lse -- sdpa_fwd that also writes the log-sum-exp of every query row, which the
+ * gradient (sdpa_bwd) starts from (page "Neural Network primitives from NNlib.jl", section
+ * "Fused implementation": the fused gradient forms the weights again, as exp(s_ij - lse_i)).
+ *
+ * lse  device fp32 [B][Hq][Lq] (contiguous, row i of head h of batch b at (b*Hq + h)*Lq + i),
+ *      or NULL (then this is sdpa_fwd): the natural log of the sum of exp over the row's
+ *      allowed logits (scale and bias included). -inf for a row with no allowed key and for
+ *      the rows at or past q_lengths. Every other argument as for sdpa_fwd.
+ * ------------------------------------------------------------------------------------- */
+SDPA_API sdpa_status sdpa_fwd_lse(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
+                                  const sdpa_tensor* bias, const sdpa_tensor* mask,
+                                  const sdpa_block_mask_info* mask_info,
+                                  float scale, int32_t is_causal,
+                                  const int32_t* q_offset, int32_t q_offset_all,
+                                  const int32_t* kv_lengths, int32_t kv_length_all,
+                                  const int32_t* q_lengths, int32_t q_length_all,
+                                  int32_t qk_norm,
+                                  sdpa_tensor* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * sdpa_bwd -- the gradient of sdpa_fwd with respect to query, key, value and scale (page
+ * "Neural Network primitives from NNlib.jl", section "Fused implementation"). The weights are
+ * formed again from q, k and lse, never stored. A query with no allowed key (NaN output) and
+ * the queries at or past q_lengths (zero output) take no part: their dq rows are 0 and they
+ * add nothing to dk, dv or dscale. Under grouped-query attention dk and dv of a K/V head sum
+ * over the query heads that read it.
+ *
+ * q, k, v, mask, mask_info, scale, is_causal, q_offset, kv_lengths, q_lengths: those of the
+ *      forward call (no bias and no qk_norm: the page sends a call with a bias to the
+ *      materialized path, whose gradient is not this one).
+ * out  the forward output {Dv, Hq, Lq, B}; dout its cotangent, same dims; each F32, BF16 or F16.
+ * lse  device fp32 [B][Hq][Lq] as written by sdpa_fwd_lse for this call.
+ * dq {D, Hq, Lq, B}, dk {D, Hkv, Lkv, B}, dv {Dv, Hkv, Lkv, B}: outputs, each F32, BF16 or F16,
+ *      head_dim stride 1; every element is written (0 for keys that no query attends).
+ * dscale  device fp32 scalar, or NULL: sum over all pairs of dS_ij * <q_i, k_j>.
+ * workspace  device scratch of at least sdpa_bwd_workspace_bytes(); results are deterministic
+ *      (no atomics, fixed reduction order).
+ * ------------------------------------------------------------------------------------- */
+SDPA_API sdpa_status sdpa_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
+                              const sdpa_tensor* out, const sdpa_tensor* dout, const float* lse,
+                              const sdpa_tensor* mask, const sdpa_block_mask_info* mask_info,
+                              float scale, int32_t is_causal,
+                              const int32_t* q_offset, int32_t q_offset_all,
+                              const int32_t* kv_lengths, int32_t kv_length_all,
+                              const int32_t* q_lengths, int32_t q_length_all,
+                              sdpa_tensor* dq, sdpa_tensor* dk, sdpa_tensor* dv, float* dscale,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace sdpa_bwd needs for these shapes. Host only. */
+SDPA_API size_t sdpa_bwd_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v);
+
+/* ---------------------------------------------------------------------------------------
  * sdpa_fwd_packed -- attention over packed sequences (page "Neural Network primitives from
  * NNlib.jl", section "Packed sequences"; "Arguments": q_segments, kv_segments, maxlen). The
  * inputs hold n_segments sequences one after the other with no batch dimension: q

@@ -89,6 +89,8 @@ def sdpa_grad(q, k, v, dout, bias=None, mask=None, scale=None, is_causal=False, 
 
     dout [B][Lq][Hq][Dv]. Returns a dict with dq [B][Lq][Hq][D], dk [B][Lkv][Hkv][D],
     dv [B][Lkv][Hkv][Dv], dscale (float) and, with a bias, dbias of the bias's own shape.
+    dscale_abs is the sum of the magnitudes of dscale's terms: the terms of each row cancel (its
+    dS sums to zero), so a rounding error in dscale is measured against this sum.
     """
     q, k, v, scale, kvl, ql, offs = _prepare(q, k, v, scale, is_causal, q_offset, kv_lengths, q_lengths)
     dout = np.asarray(dout, dtype=np.float64)
@@ -98,7 +100,7 @@ def sdpa_grad(q, k, v, dout, bias=None, mask=None, scale=None, is_causal=False, 
     bias = None if bias is None else np.asarray(bias, dtype=np.float64)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     dbias = None if bias is None else np.zeros_like(bias)
-    dscale = 0.0
+    dscale = dscale_abs = 0.0
     for b in range(B):
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
@@ -118,12 +120,14 @@ def sdpa_grad(q, k, v, dout, bias=None, mask=None, scale=None, is_causal=False, 
             dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
             dq[b, :, h, :] = scale * (dS @ K)
             dk[b, :, g, :] += scale * (dS.T @ Q)
-            dscale += float(np.sum(np.where(allowed, dS * (Q @ K.T), 0.0)))
+            terms = np.where(allowed, dS * (Q @ K.T), 0.0)
+            dscale += float(np.sum(terms))
+            dscale_abs += float(np.sum(np.abs(terms)))
             if dbias is not None:
                 d = dS.sum(axis=0, keepdims=True) if bias.shape[2] == 1 else dS
                 d = d.sum(axis=1, keepdims=True) if bias.shape[3] == 1 else d
                 dbias[b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0] += d
-    out = {"dq": dq, "dk": dk, "dv": dv, "dscale": dscale}
+    out = {"dq": dq, "dk": dk, "dv": dv, "dscale": dscale, "dscale_abs": dscale_abs}
     if dbias is not None:
         out["dbias"] = dbias
     return out

@@ -85,3 +85,22 @@ def assert_close(got, ref, dtype, label=""):
     if tol["rel_l2"] is not None:
         assert rel <= tol["rel_l2"], f"{label}: rel-L2 {rel:.3e} > {tol['rel_l2']}"
     return max_abs, rel
+
+
+def assert_grad_close(got, ref, dtype, label=""):
+    """The bar above, for a gradient: max-abs taken relative to max(1, max |oracle|), since a
+    gradient sums over many pairs and has no fixed magnitude; rel-L2 as for the output."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{label}: non-finite gradient entries"
+    mag = max(1.0, float(np.max(np.abs(ref)))) if ref.size else 1.0
+    d = got - ref
+    max_abs = float(np.max(np.abs(d))) / mag if ref.size else 0.0
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(d) / nref) if nref > 0 else float(np.linalg.norm(d))
+    tol = TOL[dtype]
+    say(f"  {label}: max_abs/mag={max_abs:.3e} (mag {mag:.2f}) rel_l2={rel:.3e}")
+    assert max_abs <= tol["max_abs"], f"{label}: max-abs/mag {max_abs:.3e} > {tol['max_abs']}"
+    if tol["rel_l2"] is not None:
+        assert rel <= tol["rel_l2"], f"{label}: rel-L2 {rel:.3e} > {tol['rel_l2']}"

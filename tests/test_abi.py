@@ -204,3 +204,43 @@ def test_packed_validation(lib):
     assert call(norm=1, wsb=16) == N.SDPA_ERR_WORKSPACE
     assert call(q=T([64, 8, 30, 1], N.SDPA_F16)) == N.SDPA_ERR_DTYPE
     assert call(n=0) == N.SDPA_OK                                                    # nothing to do
+
+
+def bwd(lib, ts, lse=FAKE, mask=None, scale=math.nan, causal=0, ws=FAKE, ws_bytes=1 << 20, dscale=None):
+    q, k, v, out, dout, dq, dk, dv = ts
+    ref = lambda t: ctypes.byref(t) if t else None
+    r = lib.sdpa_bwd(ref(q), ref(k), ref(v), ref(out), ref(dout), lse, ref(mask), None, scale, causal,
+                     None, 0, None, -1, None, -1, ref(dq), ref(dk), ref(dv), dscale, ws, ws_bytes, None)
+    return r, lib.sdpa_last_error().decode()
+
+
+def good_bwd(D=64, Hq=8, Hkv=2, Lq=5, Lkv=7, B=3, dt=N.SDPA_BF16):
+    q, k, v, out = good(D, Hq, Hkv, Lq, Lkv, B, dt)
+    return [q, k, v, out, T([D, Hq, Lq, B], dt), T([D, Hq, Lq, B], dt), T([D, Hkv, Lkv, B], dt),
+            T([D, Hkv, Lkv, B], N.SDPA_F32)]
+
+
+def test_bwd_validation(lib):
+    def with_(i, t):
+        ts = good_bwd()
+        ts[i] = t
+        return ts
+    assert bwd(lib, with_(4, None))[0] == N.SDPA_ERR_NULL                           # no dout
+    assert bwd(lib, with_(5, None))[0] == N.SDPA_ERR_NULL                           # no dq
+    assert bwd(lib, with_(4, T([64, 8, 6, 3])))[0] == N.SDPA_ERR_SHAPE              # dout dims
+    assert bwd(lib, with_(6, T([64, 2, 6, 3])))[0] == N.SDPA_ERR_SHAPE              # dk dims
+    assert bwd(lib, with_(7, T([32, 2, 7, 3])))[0] == N.SDPA_ERR_SHAPE              # dv dims
+    assert bwd(lib, with_(5, T([64, 8, 5, 3], N.SDPA_U8)))[0] == N.SDPA_ERR_DTYPE   # dq dtype
+    assert bwd(lib, with_(4, T([64, 8, 5, 3], strides=[2, 128, 1024, 5120])))[0] == N.SDPA_ERR_SHAPE
+    assert bwd(lib, good_bwd(), lse=None)[0] == N.SDPA_ERR_NULL
+    r, msg = bwd(lib, good_bwd(), ws_bytes=16)
+    assert r == N.SDPA_ERR_WORKSPACE and "workspace" in msg
+    assert bwd(lib, good_bwd(), causal=3)[0] == N.SDPA_ERR_SHAPE
+    assert bwd(lib, good_bwd(dt=N.SDPA_U8))[0] == N.SDPA_ERR_DTYPE
+
+
+def test_bwd_workspace_bytes(lib):
+    q, k, v = good_bwd()[:3]
+    n = lib.sdpa_bwd_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v))
+    rows = 3 * 8 * 5
+    assert n == 3 * ((rows * 4 + 255) // 256 * 256)

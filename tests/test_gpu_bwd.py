@@ -1,0 +1,150 @@
+"""The gradient (sdpa_fwd_lse + sdpa_bwd) against the fp64 oracle gradient, on the GPU.
+
+Page "Neural Network primitives from NNlib.jl", section "Fused implementation": the gradient
+with respect to query, key, value and scale; rows with no allowed key take no part. The GPU
+forward writes the log-sum-exp, the GPU backward starts from it; the oracle computes both from
+the inputs alone. Bar: as for the output, with max-abs relative to the gradient's magnitude
+(gpu_util.assert_grad_close).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import transformer_attention_sdpa_amd as sa
+from gpu_util import say, dev, per_batch, gpu_inputs, assert_close, assert_grad_close
+
+pytestmark = pytest.mark.gpu
+
+
+def run_bwd(w, dout, q_lengths=None, grad_dtype=torch.float32, use_mask_info=False, bq=128, bkv=128,
+            out_dtype=torch.float32):
+    t = gpu_inputs(w)
+    info = sa.build_block_mask_info(t["mask"], bq, bkv) if use_mask_info and t["mask"] is not None else None
+    kw = dict(scale=w.scale, is_causal=w.is_causal, q_offset=per_batch(w.q_offset),
+              kv_lengths=per_batch(w.kv_lengths), q_lengths=per_batch(q_lengths))
+    out, lse = sa.sdpa(t["q"], t["k"], t["v"], None, None if info else t["mask"], mask_info=info,
+                       return_lse=True, out_dtype=out_dtype, **kw)
+    dq, dk, dv, dsc = sa.sdpa_bwd(t["q"], t["k"], t["v"], out, dev(dout, w.dtype), lse,
+                                  None if info else t["mask"], mask_info=info, grad_dtype=grad_dtype, **kw)
+    torch.cuda.synchronize()
+    f = lambda x: x.float().cpu().numpy()
+    return dict(dq=f(dq), dk=f(dk), dv=f(dv), dscale=float(dsc.item()), lse=lse.cpu().numpy())
+
+
+def run_ref(w, dout, q_lengths=None):
+    kw = dict(mask=w.mask, scale=w.scale, is_causal=w.is_causal, q_offset=w.q_offset,
+              kv_lengths=w.kv_lengths, q_lengths=q_lengths)
+    g = oracle.sdpa_grad(w.values("q"), w.values("k"), w.values("v"), workloads.widen(dout, w.dtype), **kw)
+    g["lse"] = oracle.sdpa_lse(w.values("q"), w.values("k"), w.values("v"), **kw)
+    return g
+
+
+def check(got, ref, dtype, label):
+    for n in ("dq", "dk", "dv"):
+        assert_grad_close(got[n], ref[n], dtype, f"{label} {n}")
+    # dscale: the terms of a row cancel, so its error is bounded against the sum of their
+    # magnitudes, at the max-abs bar (f32) or the rel-L2 bar (16-bit inputs)
+    mag = max(1.0, ref["dscale_abs"])
+    tol = 1e-5 if dtype == "f32" else 5e-3
+    say(f"  {label} dscale gpu={got['dscale']:.6g} oracle={ref['dscale']:.6g} (terms {ref['dscale_abs']:.4g})")
+    assert abs(got["dscale"] - ref["dscale"]) <= tol * mag
+    fin = np.isfinite(ref["lse"])
+    np.testing.assert_array_equal(np.isfinite(got["lse"]), fin)
+    assert np.all(got["lse"][~fin] == -np.inf)
+    assert_close(got["lse"][fin], ref["lse"][fin], dtype, f"{label} lse")
+
+
+FEATURES = [
+    dict(),
+    dict(is_causal=True),
+    dict(is_causal=True, q_offset=[37, -5]),
+    dict(is_causal="bottom_right", kv_lengths=[150, 61]),
+    dict(kv_lengths=[129, 3]),
+    dict(mask_shape=(2, 4, 130, 150)),
+    dict(mask_shape=(1, 1, 130, 150), is_causal="bottom_right"),
+    dict(scale=-0.3, is_causal=True),
+    dict(scale=0.0),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("D", [16, 64, 128])
+@pytest.mark.parametrize("hkv", [4, 1])
+@pytest.mark.parametrize("case", range(len(FEATURES)))
+def test_grad_features(lib, case, hkv, D, dtype):
+    f = dict(FEATURES[case])
+    kvl = f.pop("kv_lengths", None)
+    qo = f.pop("q_offset", 0)
+    w = workloads.random_attention(2000 + case * 7 + hkv + D, 2, 130, 150, 4, hkv, D, dtype=dtype,
+                                   q_offset=np.array(qo, dtype=np.int32) if isinstance(qo, list) else qo,
+                                   kv_lengths=None if kvl is None else np.array(kvl, dtype=np.int32), **f)
+    dout = workloads.output_cotangent(w, 3000 + case)
+    say(f"grad case={case} {FEATURES[case]} hkv={hkv} D={D} {dtype}")
+    check(run_bwd(w, dout), run_ref(w, dout), dtype, f"case {case}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grad_q_lengths_and_empty_rows(lib, dtype):
+    # rows past q_lengths and rows that attend nothing take no part, whatever dout holds there
+    w = workloads.random_attention(2100, 2, 70, 90, 4, 2, 64, dtype=dtype, mask_shape=(2, 4, 70, 90))
+    w.mask[0, 1, 5, :] = 0
+    w.mask[1, :, 9, :] = 0
+    ql = np.array([60, 33], dtype=np.int32)
+    dout = workloads.output_cotangent(w, 3100)
+    say(f"grad q_lengths + empty rows {dtype}")
+    got, ref = run_bwd(w, dout, q_lengths=ql), run_ref(w, dout, q_lengths=ql)
+    assert np.all(got["dq"][0, 5, 1] == 0) and np.all(got["dq"][1, 9] == 0) and np.all(got["dq"][1, 33:] == 0)
+    check(got, ref, dtype, "q_lengths")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grad_value_head_dim_differs(lib, dtype):
+    w = workloads.random_attention(2200, 2, 70, 90, 4, 2, 64, Dv=32, dtype=dtype, is_causal=True)
+    dout = workloads.output_cotangent(w, 3200)
+    say(f"grad Dv != D {dtype}")
+    check(run_bwd(w, dout), run_ref(w, dout), dtype, "dv=32")
+
+
+def test_grad_mask_info_and_bits_equal_dense(lib):
+    w = workloads.random_attention(2300, 2, 200, 260, 4, 2, 128, dtype="bf16", mask_shape=(1, 4, 200, 260),
+                                   is_causal="bottom_right")
+    dout = workloads.output_cotangent(w, 3300)
+    say("grad with block info")
+    dense = run_bwd(w, dout)
+    info = run_bwd(w, dout, use_mask_info=True, bq=128, bkv=64)
+    for n in ("dq", "dk", "dv"):
+        np.testing.assert_array_equal(info[n], dense[n])
+    check(dense, run_ref(w, dout), "bf16", "dense mask")
+
+
+@pytest.mark.parametrize("gdt", [torch.bfloat16, torch.float16])
+def test_grad_16bit_outputs(lib, gdt):
+    # 16-bit gradients from a 16-bit saved output (the forward's own dtype)
+    w = workloads.random_attention(2400, 2, 130, 150, 4, 2, 128, dtype="bf16", is_causal=True)
+    dout = workloads.output_cotangent(w, 3400)
+    say(f"grad outputs {gdt}")
+    check(run_bwd(w, dout, grad_dtype=gdt, out_dtype=None), run_ref(w, dout), "bf16", f"{gdt}")
+
+
+def test_grad_is_deterministic(lib):
+    w = workloads.random_attention(2500, 2, 300, 300, 8, 2, 128, dtype="bf16", is_causal=True)
+    dout = workloads.output_cotangent(w, 3500)
+    say("grad repeatable")
+    a, b = run_bwd(w, dout), run_bwd(w, dout)
+    for n in ("dq", "dk", "dv", "lse"):
+        np.testing.assert_array_equal(a[n], b[n])
+    assert a["dscale"] == b["dscale"]
+
+
+@pytest.mark.parametrize("Lq,Lkv", [(0, 40), (40, 0), (1, 1)])
+def test_grad_degenerate_lengths(lib, Lq, Lkv):
+    w = workloads.random_attention(2600, 2, Lq, Lkv, 2, 1, 64, dtype="bf16")
+    dout = workloads.output_cotangent(w, 3600)
+    say(f"grad Lq={Lq} Lkv={Lkv}")
+    got = run_bwd(w, dout)
+    ref = run_ref(w, dout)
+    for n in ("dq", "dk", "dv"):
+        np.testing.assert_allclose(got[n], ref[n], atol=2e-2, rtol=0)
+    assert abs(got["dscale"] - ref["dscale"]) <= 2e-2

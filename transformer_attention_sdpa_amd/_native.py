@@ -54,6 +54,11 @@ SZ = ctypes.c_size_t
 PROTOTYPES = {
     "sdpa_fwd": (I32, [T, T, T, T, T, ctypes.POINTER(BlockMaskInfoC), ctypes.c_float, I32,
                        I32P, I32, I32P, I32, I32P, I32, I32, T, VP, SZ, VP]),
+    "sdpa_fwd_lse": (I32, [T, T, T, T, T, ctypes.POINTER(BlockMaskInfoC), ctypes.c_float, I32,
+                           I32P, I32, I32P, I32, I32P, I32, I32, T, VP, VP, SZ, VP]),
+    "sdpa_bwd": (I32, [T, T, T, T, T, VP, T, ctypes.POINTER(BlockMaskInfoC), ctypes.c_float, I32,
+                       I32P, I32, I32P, I32, I32P, I32, T, T, T, VP, VP, SZ, VP]),
+    "sdpa_bwd_workspace_bytes": (SZ, [T, T, T]),
     "sdpa_fwd_packed": (I32, [T, T, T, I32P, I32P, I32, I32, ctypes.c_float, I32,
                               I32P, I32, I32P, I32, I32P, I32, I32, T, VP, SZ, VP]),
     "sdpa_fwd_workspace_bytes": (SZ, [T, T, T, I32]),

@@ -161,11 +161,13 @@ def build_block_mask_info(mask: torch.Tensor, bq: int = 128, bkv: int = 128, str
 
 
 def sdpa(q, k, v, bias=None, mask=None, *, mask_info: BlockMaskInfo = None, scale=None, is_causal=False,
-         q_offset=0, kv_lengths=None, q_lengths=None, qk_norm=False, out=None, out_dtype=None, stream=None):
+         q_offset=0, kv_lengths=None, q_lengths=None, qk_norm=False, out=None, out_dtype=None, stream=None,
+         return_lse=False):
     """Scaled dot-product attention. q [B][Lq][Hq][D], k [B][Lkv][Hkv][D], v [B][Lkv][Hkv][Dv].
 
     is_causal: False, True or "bottom_right". q_offset, kv_lengths, q_lengths: int, None or a
-    [B] int32 tensor on the device. scale: None = 1/sqrt(D). Returns out [B][Lq][Hq][Dv].
+    [B] int32 tensor on the device. scale: None = 1/sqrt(D). Returns out [B][Lq][Hq][Dv], or
+    (out, lse) with return_lse (sdpa_fwd_lse): lse fp32 [B][Hq][Lq].
     """
     lib = N.load()
     B, Lq, Hq, _ = q.shape
@@ -182,20 +184,63 @@ def sdpa(q, k, v, bias=None, mask=None, *, mask_info: BlockMaskInfo = None, scal
     ws_bytes = lib.sdpa_fwd_workspace_bytes(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(bool(qk_norm)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     s, sp = _stream(stream)
-    st = lib.sdpa_fwd(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
-                      ctypes.byref(db) if db is not None else None,
-                      ctypes.byref(dm) if dm is not None else None,
-                      ctypes.byref(mask_info.c) if mask_info is not None else None,
-                      float("nan") if scale is None else float(scale), _CAUSAL[is_causal],
-                      qo_ptr, qo_all, kv_ptr, kv_all, ql_ptr, ql_all, int(bool(qk_norm)),
-                      ctypes.byref(do), ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
-                      ws_bytes, sp)
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib.sdpa_fwd_lse(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                          ctypes.byref(db) if db is not None else None,
+                          ctypes.byref(dm) if dm is not None else None,
+                          ctypes.byref(mask_info.c) if mask_info is not None else None,
+                          float("nan") if scale is None else float(scale), _CAUSAL[is_causal],
+                          qo_ptr, qo_all, kv_ptr, kv_all, ql_ptr, ql_all, int(bool(qk_norm)),
+                          ctypes.byref(do), ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
+                          ctypes.c_void_p(ws.data_ptr()) if ws is not None else None, ws_bytes, sp)
     N.check(st)
     if stream is not None:
         for t in (ws, qo_keep, kv_keep, ql_keep):
             if t is not None:
                 t.record_stream(s)
-    return out
+    return (out, lse) if return_lse else out
+
+
+def sdpa_bwd(q, k, v, out, dout, lse, mask=None, *, mask_info: BlockMaskInfo = None, scale=None,
+             is_causal=False, q_offset=0, kv_lengths=None, q_lengths=None, grad_dtype=None, stream=None):
+    """Gradient of ``sdpa`` with respect to q, k, v and scale (sdpa_bwd).
+
+    out and lse come from ``sdpa(..., return_lse=True)`` of the same call; dout is the cotangent
+    of out. Returns (dq, dk, dv, dscale): dq/dk/dv of q/k/v's shapes in grad_dtype (default
+    q.dtype), dscale a one-element fp32 tensor.
+    """
+    lib = N.load()
+    B, Lq, Hq, _ = q.shape
+    gd = grad_dtype or q.dtype
+    dq_t = torch.empty(q.shape, dtype=gd, device=q.device)
+    dk_t = torch.empty(k.shape, dtype=gd, device=q.device)
+    dv_t = torch.empty(v.shape, dtype=gd, device=q.device)
+    dscale = torch.empty(1, dtype=torch.float32, device=q.device)
+    tq, tk, tv, to, tdo = desc(q), desc(k), desc(v), desc(out), desc(dout)
+    gq, gk, gv = desc(dq_t), desc(dk_t), desc(dv_t)
+    m = _mask_u8(mask) if mask_info is None else None
+    dm = _mask_desc(m) if m is not None else None
+    qo_ptr, qo_all, qo_keep = _per_batch_arg(q_offset, B, q.device, 0)
+    kv_ptr, kv_all, kv_keep = _per_batch_arg(kv_lengths, B, q.device, -1)
+    ql_ptr, ql_all, ql_keep = _per_batch_arg(q_lengths, B, q.device, -1)
+    ws_bytes = lib.sdpa_bwd_workspace_bytes(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Lq):
+        raise ValueError("lse must be a contiguous fp32 [B][Hq][Lq] tensor")
+    s, sp = _stream(stream)
+    st = lib.sdpa_bwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(to), ctypes.byref(tdo),
+                      ctypes.c_void_p(lse.data_ptr()), ctypes.byref(dm) if dm is not None else None,
+                      ctypes.byref(mask_info.c) if mask_info is not None else None,
+                      float("nan") if scale is None else float(scale), _CAUSAL[is_causal],
+                      qo_ptr, qo_all, kv_ptr, kv_all, ql_ptr, ql_all,
+                      ctypes.byref(gq), ctypes.byref(gk), ctypes.byref(gv), ctypes.c_void_p(dscale.data_ptr()),
+                      ctypes.c_void_p(ws.data_ptr()), ws_bytes, sp)
+    N.check(st)
+    if stream is not None:
+        for t in (ws, qo_keep, kv_keep, ql_keep):
+            if t is not None:
+                t.record_stream(s)
+    return dq_t, dk_t, dv_t, dscale
 
 
 def sdpa_packed(q, k, v, q_segments, kv_segments=None, *, maxlen=None, scale=None, is_causal=False, q_offset=0,

@@ -268,6 +268,17 @@ sdpa_status sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tens
                      const int32_t* q_offset, int32_t q_offset_all, const int32_t* kv_lengths,
                      int32_t kv_length_all, const int32_t* q_lengths, int32_t q_length_all, int32_t qk_norm,
                      sdpa_tensor* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return sdpa_fwd_lse(q, k, v, bias, mask, mask_info, scale, is_causal, q_offset, q_offset_all, kv_lengths,
+                      kv_length_all, q_lengths, q_length_all, qk_norm, out, nullptr, workspace, workspace_bytes,
+                      stream);
+}
+
+sdpa_status sdpa_fwd_lse(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v, const sdpa_tensor* bias,
+                         const sdpa_tensor* mask, const sdpa_block_mask_info* mask_info, float scale,
+                         int32_t is_causal, const int32_t* q_offset, int32_t q_offset_all,
+                         const int32_t* kv_lengths, int32_t kv_length_all, const int32_t* q_lengths,
+                         int32_t q_length_all, int32_t qk_norm, sdpa_tensor* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (!v || !out) return fail(SDPA_ERR_NULL, "v and out descriptors are required");
   AttnArgs a;
@@ -279,6 +290,9 @@ sdpa_status sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tens
     return fail(SDPA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
   if (a.B == 0 || a.Lq == 0) return SDPA_OK;
   if (!a.q || !a.out || (a.Lkv > 0 && (!a.k || !a.v))) return fail(SDPA_ERR_NULL, "a tensor's data is NULL");
+  a.lse = lse;
+  a.lse_sh = a.Lq;
+  a.lse_sb = (int64_t)a.Hq * a.Lq;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (qk_norm && a.Lkv > 0) {
     a.k_rinv = static_cast<const float*>(workspace);
@@ -289,6 +303,64 @@ sdpa_status sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tens
   }
   if (fwd_mfma_supports(a)) return hip_status(launch_fwd_mfma(a, s), "sdpa_fwd (mfma)");
   return hip_status(launch_fwd_generic(a, s), "sdpa_fwd (generic)");
+}
+
+size_t sdpa_bwd_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v) {
+  (void)k; (void)v;
+  if (!q) return 0;
+  const size_t rows = (size_t)(q->dims[3] * q->dims[1] * q->dims[2]);
+  return 3 * ((rows * sizeof(float) + 255) & ~(size_t)255);
+}
+
+sdpa_status sdpa_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v, const sdpa_tensor* out,
+                     const sdpa_tensor* dout, const float* lse, const sdpa_tensor* mask,
+                     const sdpa_block_mask_info* mask_info, float scale, int32_t is_causal,
+                     const int32_t* q_offset, int32_t q_offset_all, const int32_t* kv_lengths,
+                     int32_t kv_length_all, const int32_t* q_lengths, int32_t q_length_all, sdpa_tensor* dq,
+                     sdpa_tensor* dk, sdpa_tensor* dv, float* dscale, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  g_err.clear();
+  if (!v || !out || !dout || !dq || !dk || !dv)
+    return fail(SDPA_ERR_NULL, "v, out, dout, dq, dk and dv descriptors are required");
+  BwdArgs g;
+  std::memset(&g, 0, sizeof g);
+  sdpa_status st = resolve_attention(q, k, v, nullptr, mask, mask_info, scale, is_causal, q_offset, q_offset_all,
+                                     kv_lengths, kv_length_all, q_lengths, q_length_all, 0, out, g.a);
+  if (st != SDPA_OK) return st;
+  const AttnArgs& a = g.a;
+  auto same = [](const sdpa_tensor* x, const sdpa_tensor* y) {
+    for (int i = 0; i < 4; ++i)
+      if (x->dims[i] != y->dims[i]) return false;
+    return true;
+  };
+  if (!same(dout, out)) return fail(SDPA_ERR_SHAPE, "dout must have the dims of out");
+  if (!same(dq, q) || !same(dk, k) || !same(dv, v)) return fail(SDPA_ERR_SHAPE, "dq, dk, dv must have the dims of q, k, v");
+  if (!dims_ok(dout) || !dims_ok(dq) || !dims_ok(dk) || !dims_ok(dv)) return fail(SDPA_ERR_SHAPE, "a dim is out of range");
+  if (!is_float(dout->dtype) || !is_float(dq->dtype) || !is_float(dk->dtype) || !is_float(dv->dtype))
+    return fail(SDPA_ERR_DTYPE, "dout, dq, dk and dv must be F32, BF16 or F16");
+  if (dout->strides[0] != 1 || dq->strides[0] != 1 || dk->strides[0] != 1 || dv->strides[0] != 1)
+    return fail(SDPA_ERR_SHAPE, "dout, dq, dk and dv need head_dim stride 1");
+  const size_t need = sdpa_bwd_workspace_bytes(q, k, v);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(SDPA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
+  if (rows > 0 && !lse) return fail(SDPA_ERR_NULL, "lse is required");
+  if ((rows > 0 && (!a.q || !a.out || !dout->data || !dq->data)) ||
+      ((int64_t)a.B * a.Lkv > 0 && (!a.k || !a.v || !dk->data || !dv->data)))
+    return fail(SDPA_ERR_NULL, "a tensor's data is NULL");
+  g.dout = dout->data; g.do_sb = dout->strides[3]; g.do_ss = dout->strides[2]; g.do_sh = dout->strides[1];
+  g.do_dtype = dout->dtype;
+  g.lse = lse;
+  g.dq = dq->data; g.dq_sb = dq->strides[3]; g.dq_ss = dq->strides[2]; g.dq_sh = dq->strides[1];
+  g.dk = dk->data; g.dk_sb = dk->strides[3]; g.dk_ss = dk->strides[2]; g.dk_sh = dk->strides[1];
+  g.dv = dv->data; g.dv_sb = dv->strides[3]; g.dv_ss = dv->strides[2]; g.dv_sh = dv->strides[1];
+  g.dq_dtype = dq->dtype; g.dk_dtype = dk->dtype; g.dv_dtype = dv->dtype;
+  g.dscale = dscale;
+  const size_t seg = need / 3;
+  g.w_dsum = static_cast<float*>(workspace);
+  g.w_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + seg);
+  g.w_dsc = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * seg);
+  return hip_status(launch_bwd(g, static_cast<hipStream_t>(stream)), "sdpa_bwd");
 }
 
 size_t sdpa_decode_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k_cache, int32_t num_splits) {

@@ -45,8 +45,10 @@ __global__ __launch_bounds__(kGenThreads) void fwd_generic_kernel(AttnArgs args)
   const int64_t off = batch_causal_offset(a, b);
   const int64_t o_row = b * a.o_sb + (int64_t)i * a.o_ss + h * a.o_sh;
 
-  if (i >= nq) {                                 // past q_lengths: output 0
+  float* lse = a.lse ? a.lse + b * a.lse_sb + h * a.lse_sh + i : nullptr;
+  if (i >= nq) {                                 // past q_lengths: output 0, attends nothing
     for (int d = lane; d < a.Dv; d += 64) store_elem(a.out, o_row + d, a.out_dtype, 0.f);
+    if (lse && lane == 0) *lse = -INFINITY;
     return;
   }
 
@@ -105,6 +107,7 @@ __global__ __launch_bounds__(kGenThreads) void fwd_generic_kernel(AttnArgs args)
   }
 
   const float inv_l = (l > 0.f) ? 1.0f / l : NAN;
+  if (lse && lane == 0) *lse = (l > 0.f) ? m + logf(l) : -INFINITY;
 #pragma unroll
   for (int t = 0; t < kGenMaxD / 64; ++t) {
     const int d = lane + 64 * t;

@@ -675,6 +675,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const bool zero_row = i_me >= nq;
   const float inv = zero_row ? 0.f : (l_tot > 0.f ? 1.0f / l_tot : NAN);
+  if (a.lse && hh == 0) {
+    // m_run and l_run are in log2 units of the full logits (scale and bias included)
+    a.lse[b * a.lse_sb + h * a.lse_sh + i_me] =
+        (zero_row || !(l_tot > 0.f)) ? -INFINITY : (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+  }
   const int64_t orow = b * a.o_sb + (int64_t)i_me * a.o_ss + h * a.o_sh;
 #pragma unroll
   for (int d = 0; d < DB; ++d)

@@ -55,6 +55,10 @@ struct AttnArgs {
   const int32_t* kv_seg;       // [n_seg] lengths along k/v
   int n_seg;
   int seg_maxlen;              // bound on the segment lengths from the caller, or -1 (host use)
+
+  // log-sum-exp output (natural log) of every query row, or nullptr: lse[b*lse_sb + h*lse_sh + i]
+  float* lse;
+  int64_t lse_sb, lse_sh;
 };
 
 struct DecodeArgs {
@@ -83,6 +87,28 @@ struct MaskInfoArgs {
   int32_t* data_next;
   uint32_t* bits;
   int32_t* n_partial;
+};
+
+// The backward pass: the forward's arguments (a.out is the forward output O, read only) plus
+// the output cotangent, the saved log-sum-exp, the gradients and the workspace rows.
+struct BwdArgs {
+  AttnArgs a;
+  const void* dout;            // [B][Lq][Hq][Dv]
+  int64_t do_sb, do_ss, do_sh;
+  int do_dtype;
+  const float* lse;            // [B][Hq][Lq] natural log, from the forward
+  void* dq;                    // [B][Lq][Hq][D]
+  void* dk;                    // [B][Lkv][Hkv][D]
+  void* dv;                    // [B][Lkv][Hkv][Dv]
+  int64_t dq_sb, dq_ss, dq_sh, dk_sb, dk_ss, dk_sh, dv_sb, dv_ss, dv_sh;
+  int dq_dtype, dk_dtype, dv_dtype;
+  float* dscale;               // one float, or nullptr
+  // workspace rows, [B][Hq][Lq] each: rowsum(dO * O) (0 for rows that take no part), the lse of
+  // rows that take part (+inf for the others, so that every weight of such a row is 0), and
+  // each row's share of dscale
+  float* w_dsum;
+  float* w_lse;
+  float* w_dsc;
 };
 
 constexpr float kRmsEps = 1e-6f;
@@ -117,6 +143,7 @@ hipError_t launch_kv_cache_update(void* kc, void* vc, const void* kn, const void
                                   int64_t vn_sb, int64_t vn_ss, int64_t vn_sh,
                                   const int32_t* write_index, hipStream_t s);
 hipError_t launch_mask_info(const MaskInfoArgs& m, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& g, hipStream_t s);
 hipError_t launch_debug_allowed(const AttnArgs& a, uint8_t* out, int64_t sb, int64_t sh, int64_t sq,
                                 int64_t sk, hipStream_t s);
 

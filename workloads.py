@@ -27,7 +27,7 @@ from typing import Optional
 
 import numpy as np
 
-TAG_Q, TAG_K, TAG_V, TAG_KNEW, TAG_VNEW, TAG_KVLEN, TAG_MCLASS, TAG_MBITS, TAG_BIAS = range(9)
+TAG_Q, TAG_K, TAG_V, TAG_KNEW, TAG_VNEW, TAG_KVLEN, TAG_MCLASS, TAG_MBITS, TAG_BIAS, TAG_DOUT = range(10)
 SEED_BASE = 1000
 
 BF16_NAN_BITS = 0x7FC0  # quiet NaN, used to poison cache slots that must never be read
@@ -168,6 +168,12 @@ def random_attention(seed: int, B, Lq, Lkv, Hq, Hkv, D, Dv=None, dtype="f32", *,
     return Attention(name, dtype, q, k, v, scale=scale, is_causal=is_causal, q_offset=q_offset,
                      kv_lengths=kv_lengths, bias=bias, bias_dtype=bias_dtype, mask=mask,
                      qk_norm=qk_norm)
+
+
+def output_cotangent(w: Attention, seed: int) -> np.ndarray:
+    """N(0,1) cotangent of the output of ``w`` ([B][Lq][Hq][Dv]), stored as ``w.dtype``."""
+    B, Lq, _, Hq, _, _, Dv = w.shape
+    return normal_tensor(np.random.default_rng([seed, TAG_DOUT]), (B, Lq, Hq, Dv), w.dtype)
 
 
 # ----------------------------------------------------------------------------------------------
