@@ -52,6 +52,7 @@ def parse_args():
                    help="also run a 1 GiB device copy (for scaling HBM byte counters)")
     p.add_argument("--skip-decode", action="store_true")
     p.add_argument("--skip-mask-info", action="store_true")
+    p.add_argument("--skip-backward", action="store_true")
     return p.parse_args()
 
 
@@ -100,6 +101,34 @@ def oracle_rows_parity(out, w, rows):
                       q_offset=w.q_offset, rows=rows)
     d = got - ref
     return float(np.max(np.abs(d))), float(np.linalg.norm(d) / np.linalg.norm(ref))
+
+
+def backward_parity(w, q, k, v, outb, dout, lse, grads):
+    """The timed gradients of two (batch, head) slices against the fp64 oracle gradient of
+    those slices (each slice is an independent attention: one K/V head per query head)."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+    import transformer_attention_sdpa_amd as sa
+    sa.sdpa_bwd(q, k, v, outb, dout, lse, is_causal=True, scale=w.scale, grads=grads)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy()
+    worst = {}
+    do_np = workloads.widen(workloads.output_cotangent(w, 7), "bf16")
+    for b, h in ((0, 0), (w.q.shape[0] - 1, w.q.shape[2] - 1)):
+        sl = lambda x: x[b:b + 1, :, h:h + 1]
+        ref = oracle.sdpa_grad(sl(w.values("q")), sl(w.values("k")), sl(w.values("v")), sl(do_np),
+                               scale=w.scale, is_causal=True)
+        for n, t in zip(("dq", "dk", "dv"), grads[:3]):
+            got = f(t[b:b + 1, :, h:h + 1])
+            mag = max(1.0, float(np.max(np.abs(ref[n]))))
+            d = got - ref[n]
+            m, r = float(np.max(np.abs(d))) / mag, float(np.linalg.norm(d) / np.linalg.norm(ref[n]))
+            worst[n] = [max(worst.get(n, [0, 0])[0], m), max(worst.get(n, [0, 0])[1], r)]
+    return {"slices_checked": "(b, h) = (0, 0) and (B-1, H-1), every row",
+            **{n: {"max_abs_over_mag": v[0], "rel_l2": v[1]} for n, v in worst.items()},
+            "bar": "max_abs/max(1,|ref|) <= 2e-2, rel_l2 <= 5e-3"}
 
 
 def blas_threads():
@@ -188,6 +217,33 @@ def main():
                    "rel_l2": p_rel, "bar": "max_abs <= 2e-2, rel_l2 <= 5e-3 (bf16 output)"},
         "wall_s_timed_region": round(t_wall, 4),
     }
+    # ---- gradient (sdpa_bwd) of the same causal prefill ------------------------------------
+    # one call: prep (D = rowsum(dO * O)), dK/dV, dQ and the dscale sum. Algorithmic work: the
+    # five products per allowed pair (S again, dP, dV, dK, dQ), 10 * D flops, 2.5x the forward.
+    if not args.skip_backward:
+        out32, lse = sa.sdpa(q, k, v, is_causal=True, scale=w.scale, out_dtype=torch.float32, return_lse=True)
+        outb = out32.to(torch.bfloat16)
+        dout = sa.from_numpy(workloads.output_cotangent(w, 7), "bf16")
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 torch.empty(1, dtype=torch.float32, device="cuda"))
+        bws = torch.empty(sa.bwd_workspace_bytes(q, k, v), dtype=torch.uint8, device="cuda")
+        bstep = lambda: sa.sdpa_bwd(q, k, v, outb, dout, lse, is_causal=True, scale=w.scale, grads=grads,
+                                    workspace=bws)
+        bsteps = max(1, args.steps // 2)
+        t_b, _ = time_steps(bstep, bsteps, max(1, args.warmup // 4), stream)
+        flops_b = 10.0 * D * pairs
+        tf_b = flops_b / (t_b / bsteps) / 1e12
+        result["backward"] = {
+            "metric": "attention gradient TFLOP/s (causal bf16 prefill)", "value": round(tf_b, 2),
+            "unit": "TFLOP/s", "ms_per_step": round(t_b / bsteps * 1e3, 4), "steps": bsteps,
+            "config": {"workload": "causal_prefill", "batch": B, "heads": Hq, "head_dim": D, "q_len": Lq,
+                       "is_causal": True, "grad_dtype": "bf16", "saved_out_dtype": "bf16"},
+            "roofline": {"bound": "mfma", "achieved": round(tf_b, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "traffic": None, "flops_per_call": flops_b,
+                         "kernel": "bwd_prep + bwd_dkdv_mfma_kernel<128> + bwd_dq_mfma_kernel<128> + bwd_dscale"},
+            "parity": backward_parity(w, q, k, v, outb, dout, lse, grads),
+        }
+        del out32, outb, dout, grads, bws, lse
     del q, k, v, out
     torch.cuda.empty_cache()
 

@@ -8,7 +8,7 @@ Entry points (same names as the C ABI): ``sdpa`` (sdpa_fwd, and sdpa_fwd_lse wit
 """
 from ._native import load, SdpaError, header_functions, LIB_PATH
 from .api import (sdpa, sdpa_bwd, sdpa_packed, sdpa_decode, kv_cache_update, build_block_mask_info, BlockMaskInfo, PackedMask,
-                  head_rms_norm, per_head_rms_norm, debug_allowed_mask, decode_workspace_bytes,
+                  head_rms_norm, per_head_rms_norm, debug_allowed_mask, decode_workspace_bytes, bwd_workspace_bytes,
                   desc, from_numpy, to_numpy_f32)
 
 sdpa_fwd = sdpa
@@ -18,5 +18,5 @@ sdpa_fwd_packed = sdpa_packed
 __all__ = ["load", "SdpaError", "header_functions", "LIB_PATH", "sdpa", "sdpa_fwd", "sdpa_fwd_lse", "sdpa_bwd", "sdpa_packed",
            "sdpa_fwd_packed", "sdpa_decode",
            "kv_cache_update", "build_block_mask_info", "BlockMaskInfo", "PackedMask", "head_rms_norm",
-           "per_head_rms_norm", "debug_allowed_mask", "decode_workspace_bytes", "desc",
+           "per_head_rms_norm", "debug_allowed_mask", "decode_workspace_bytes", "bwd_workspace_bytes", "desc",
            "from_numpy", "to_numpy_f32"]

@@ -202,20 +202,25 @@ def sdpa(q, k, v, bias=None, mask=None, *, mask_info: BlockMaskInfo = None, scal
 
 
 def sdpa_bwd(q, k, v, out, dout, lse, mask=None, *, mask_info: BlockMaskInfo = None, scale=None,
-             is_causal=False, q_offset=0, kv_lengths=None, q_lengths=None, grad_dtype=None, stream=None):
+             is_causal=False, q_offset=0, kv_lengths=None, q_lengths=None, grad_dtype=None, grads=None,
+             workspace=None, stream=None):
     """Gradient of ``sdpa`` with respect to q, k, v and scale (sdpa_bwd).
 
     out and lse come from ``sdpa(..., return_lse=True)`` of the same call; dout is the cotangent
     of out. Returns (dq, dk, dv, dscale): dq/dk/dv of q/k/v's shapes in grad_dtype (default
-    q.dtype), dscale a one-element fp32 tensor.
+    q.dtype), dscale a one-element fp32 tensor. ``grads`` may pass those four tensors to be
+    written instead, and ``workspace`` a uint8 device tensor of bwd_workspace_bytes().
     """
     lib = N.load()
     B, Lq, Hq, _ = q.shape
     gd = grad_dtype or q.dtype
-    dq_t = torch.empty(q.shape, dtype=gd, device=q.device)
-    dk_t = torch.empty(k.shape, dtype=gd, device=q.device)
-    dv_t = torch.empty(v.shape, dtype=gd, device=q.device)
-    dscale = torch.empty(1, dtype=torch.float32, device=q.device)
+    if grads is not None:
+        dq_t, dk_t, dv_t, dscale = grads
+    else:
+        dq_t = torch.empty(q.shape, dtype=gd, device=q.device)
+        dk_t = torch.empty(k.shape, dtype=gd, device=q.device)
+        dv_t = torch.empty(v.shape, dtype=gd, device=q.device)
+        dscale = torch.empty(1, dtype=torch.float32, device=q.device)
     tq, tk, tv, to, tdo = desc(q), desc(k), desc(v), desc(out), desc(dout)
     gq, gk, gv = desc(dq_t), desc(dk_t), desc(dv_t)
     m = _mask_u8(mask) if mask_info is None else None
@@ -224,7 +229,9 @@ def sdpa_bwd(q, k, v, out, dout, lse, mask=None, *, mask_info: BlockMaskInfo = N
     kv_ptr, kv_all, kv_keep = _per_batch_arg(kv_lengths, B, q.device, -1)
     ql_ptr, ql_all, ql_keep = _per_batch_arg(q_lengths, B, q.device, -1)
     ws_bytes = lib.sdpa_bwd_workspace_bytes(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv))
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if ws.numel() < ws_bytes:
+        raise ValueError(f"workspace needs {ws_bytes} bytes")
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Lq):
         raise ValueError("lse must be a contiguous fp32 [B][Hq][Lq] tensor")
     s, sp = _stream(stream)
@@ -283,6 +290,13 @@ def sdpa_packed(q, k, v, q_segments, kv_segments=None, *, maxlen=None, scale=Non
             if t is not None:
                 t.record_stream(s)
     return out
+
+
+def bwd_workspace_bytes(q, k, v) -> int:
+    """Bytes of workspace sdpa_bwd needs for these tensors."""
+    lib = N.load()
+    tq, tk, tv = desc(q), desc(k), desc(v)
+    return int(lib.sdpa_bwd_workspace_bytes(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv)))
 
 
 def decode_workspace_bytes(q, k_cache, num_splits=0) -> int:

@@ -309,7 +309,8 @@ size_t sdpa_bwd_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k, cons
   (void)k; (void)v;
   if (!q) return 0;
   const size_t rows = (size_t)(q->dims[3] * q->dims[1] * q->dims[2]);
-  return 3 * ((rows * sizeof(float) + 255) & ~(size_t)255);
+  const size_t chunks = (rows + 4095) / 4096;
+  return 3 * ((rows * sizeof(float) + 255) & ~(size_t)255) + ((chunks * sizeof(double) + 255) & ~(size_t)255);
 }
 
 sdpa_status sdpa_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v, const sdpa_tensor* out,
@@ -356,10 +357,11 @@ sdpa_status sdpa_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tens
   g.dv = dv->data; g.dv_sb = dv->strides[3]; g.dv_ss = dv->strides[2]; g.dv_sh = dv->strides[1];
   g.dq_dtype = dq->dtype; g.dk_dtype = dk->dtype; g.dv_dtype = dv->dtype;
   g.dscale = dscale;
-  const size_t seg = need / 3;
+  const size_t seg = ((size_t)rows * sizeof(float) + 255) & ~(size_t)255;
   g.w_dsum = static_cast<float*>(workspace);
   g.w_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + seg);
   g.w_dsc = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * seg);
+  g.w_dsc2 = reinterpret_cast<double*>(static_cast<char*>(workspace) + 3 * seg);
   return hip_status(launch_bwd(g, static_cast<hipStream_t>(stream)), "sdpa_bwd");
 }
 

@@ -11,7 +11,7 @@
 //   1. prep: D_i, and the lse of the rows that take part (+inf for the others);
 //   2. dK/dV: a key's gradients, summed over the query heads of its group and all queries;
 //   3. dQ: a query's gradient and its row share of dscale;
-//   4. dscale: a fixed-order sum of the row shares.
+//   4. dscale: a fixed-order sum of the row shares, in two stages.
 // Passes 2 and 3 have a matrix-core form for bf16/f16 at head dims 64 and 128 (bwd_mfma.hip);
 // the kernels here take every other case, in fp32 with an accurate expf.
 #include "device_common.h"
@@ -23,27 +23,61 @@ namespace {
 constexpr int kBwdThreads = 256;                 // 4 waves
 constexpr int kBwdMaxD = 256;
 
-// ---- 1. prep: one wave per (b, h, i) ---------------------------------------------------------
-__global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs g) {
+// ---- 1. prep: 16 lanes per (b, h, i) row, 16 rows per workgroup ------------------------------
+// Each lane takes 8 consecutive head-dim elements at a time (one 16-byte load of 16-bit data,
+// two of fp32) when the rows allow vector loads (vec), else single elements.
+__device__ __forceinline__ void load8(const void* base, int64_t idx, int dtype, float* x) {
+  if (dtype == SDPA_F32) {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    return;
+  }
+  const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (dtype == SDPA_BF16) {
+      x[2 * t] = bf16_bits_to_float((uint16_t)w[t]);
+      x[2 * t + 1] = bf16_bits_to_float((uint16_t)(w[t] >> 16));
+    } else {
+      x[2 * t] = f16_bits_to_float((uint16_t)w[t]);
+      x[2 * t + 1] = f16_bits_to_float((uint16_t)(w[t] >> 16));
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs g, int vec) {
   const AttnArgs& a = g.a;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
+  const int l16 = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * (kBwdThreads / 16) + (threadIdx.x >> 4);
   const int64_t n_rows = (int64_t)a.B * a.Hq * a.Lq;
-  if (row >= n_rows) return;
-  const int i = (int)(row % a.Lq);
-  const int h = (int)((row / a.Lq) % a.Hq);
-  const int b = (int)(row / ((int64_t)a.Lq * a.Hq));
-  const float lse = g.lse[row];
-  const bool part = i < batch_q_len(a, b) && lse > -INFINITY && lse < INFINITY;
+  const bool in = row < n_rows;                  // no early exit: the 16-lane sums below use shuffles
+  const int i = in ? (int)(row % a.Lq) : 0;
+  const int h = in ? (int)((row / a.Lq) % a.Hq) : 0;
+  const int b = in ? (int)(row / ((int64_t)a.Lq * a.Hq)) : 0;
+  const float lse = in ? g.lse[row] : 0.f;
+  const bool part = in && i < batch_q_len(a, b) && lse > -INFINITY && lse < INFINITY;
   float acc = 0.f;
   if (part) {
     const int64_t o = b * a.o_sb + (int64_t)i * a.o_ss + h * a.o_sh;
     const int64_t d_ = b * g.do_sb + (int64_t)i * g.do_ss + h * g.do_sh;
-    for (int d = lane; d < a.Dv; d += 64)
-      acc += load_elem(a.out, o + d, a.out_dtype) * load_elem(g.dout, d_ + d, g.do_dtype);
-    acc = wave_sum(acc);
+    if (vec) {
+      for (int d = 8 * l16; d < a.Dv; d += 128) {
+        float x[8], y[8];
+        load8(a.out, o + d, a.out_dtype, x);
+        load8(g.dout, d_ + d, g.do_dtype, y);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc = fmaf(x[t], y[t], acc);
+      }
+    } else {
+      for (int d = l16; d < a.Dv; d += 16)
+        acc += load_elem(a.out, o + d, a.out_dtype) * load_elem(g.dout, d_ + d, g.do_dtype);
+    }
   }
-  if (lane == 0) {
+#pragma unroll
+  for (int m = 8; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (in && l16 == 0) {
     g.w_dsum[row] = part ? acc : 0.f;
     g.w_lse[row] = part ? lse : INFINITY;
   }
@@ -185,18 +219,40 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_generic_kernel(BwdArgs g) 
   }
 }
 
-// ---- 4. dscale: one workgroup, a fixed order of fp64 sums --------------------------------------
-__global__ __launch_bounds__(kBwdThreads) void bwd_dscale_kernel(const float* part, int64_t n, float* out) {
+// ---- 4. dscale: a fixed-order sum in two stages ----------------------------------------------
+// Stage 1: workgroup c sums rows [c * kDscChunk, (c + 1) * kDscChunk) (each thread 16 of them,
+// then a tree in LDS) into part2[c]; stage 2: one workgroup sums part2 the same way. The order
+// of every addition is fixed by the sizes alone, so the result is repeatable.
+constexpr int kDscChunk = kBwdThreads * 16;
+
+__device__ __forceinline__ double block_sum(double acc) {
   __shared__ double red[kBwdThreads];
-  double acc = 0.0;
-  for (int64_t e = threadIdx.x; e < n; e += kBwdThreads) acc += (double)part[e];
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int w = kBwdThreads / 2; w > 0; w >>= 1) {
     if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) *out = (float)red[0];
+  return red[0];
+}
+
+__global__ __launch_bounds__(kBwdThreads) void bwd_dscale_stage1(const float* part, int64_t n, double* part2) {
+  const int64_t base = (int64_t)blockIdx.x * kDscChunk + threadIdx.x;
+  double acc = 0.0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int64_t e = base + (int64_t)u * kBwdThreads;
+    if (e < n) acc += (double)part[e];
+  }
+  const double t = block_sum(acc);
+  if (threadIdx.x == 0) part2[blockIdx.x] = t;
+}
+
+__global__ __launch_bounds__(kBwdThreads) void bwd_dscale_stage2(const double* part2, int64_t n, float* out) {
+  double acc = 0.0;
+  for (int64_t e = threadIdx.x; e < n; e += kBwdThreads) acc += part2[e];
+  const double t = block_sum(acc);
+  if (threadIdx.x == 0) *out = (float)t;
 }
 
 }  // namespace
@@ -210,7 +266,12 @@ hipError_t launch_bwd(const BwdArgs& g, hipStream_t s) {
   const int64_t n_rows = (int64_t)a.B * a.Hq * a.Lq;
   const int rpw = kBwdThreads / 64;
   if (n_rows > 0) {
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((n_rows + rpw - 1) / rpw)), dim3(kBwdThreads), 0, s, g);
+    const int pe = a.out_dtype == SDPA_F32 ? 4 : 8, de = g.do_dtype == SDPA_F32 ? 4 : 8;   // elements per 16 B
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    const int vec = (a.Dv % 8 == 0) && al16(a.out) && al16(g.dout) && ((a.o_sb | a.o_ss | a.o_sh) % pe == 0) &&
+                    ((g.do_sb | g.do_ss | g.do_sh) % de == 0);
+    const int rpb = kBwdThreads / 16;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((n_rows + rpb - 1) / rpb)), dim3(kBwdThreads), 0, s, g, vec);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -237,7 +298,13 @@ hipError_t launch_bwd(const BwdArgs& g, hipStream_t s) {
     }
   }
   if (g.dscale) {
-    hipLaunchKernelGGL(bwd_dscale_kernel, dim3(1), dim3(kBwdThreads), 0, s, g.w_dsc, n_rows, g.dscale);
+    const int64_t n2 = (n_rows + kDscChunk - 1) / kDscChunk;
+    if (n2 > 0) {
+      hipLaunchKernelGGL(bwd_dscale_stage1, dim3((unsigned)n2), dim3(kBwdThreads), 0, s, g.w_dsc, n_rows, g.w_dsc2);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(bwd_dscale_stage2, dim3(1), dim3(kBwdThreads), 0, s, g.w_dsc2, n2, g.dscale);
     return hipGetLastError();
   }
   return hipSuccess;

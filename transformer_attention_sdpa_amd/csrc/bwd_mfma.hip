@@ -1,21 +1,558 @@
-// bwd_mfma.hip -- matrix-core form of the dK/dV and dQ passes of the attention gradient.
-#include "device_common.h"
+// bwd_mfma.hip -- the dK/dV and dQ passes of the attention gradient on the gfx950 matrix cores
+// (bf16 or f16 inputs, head dims 64 and 128, no mask; page "Neural Network primitives from
+// NNlib.jl", section "Fused implementation": the weights are formed again tile by tile from q,
+// k and the saved log-sum-exp, never stored).
+//
+// Both passes use v_mfma_f32_32x32x16 with one operand kept in registers for the whole loop
+// and the other streamed through LDS, and they are mirror images of each other:
+//
+// * dK/dV: a workgroup owns 128 keys of one K/V head (32 per wave, K and V in registers as B
+//   operands) and streams tiles of 64 queries of every query head of the group. Per 32-query
+//   block a wave forms S = Q K^T and dP = dO V^T. Its lanes then hold one key column each, with
+//   16 consecutive queries per lane half, because the A-operand rows of Q and dO are read in the
+//   permuted order perm32. Next P = exp2(S * scale * log2 e - lse * log2 e) and
+//   dS = P (dP - D). Finally P and dS are packed to 16 bits and feed dV^T += dO^T P and
+//   dK^T += Q^T dS directly as B operands; dO^T and Q^T come from transposed LDS reads
+//   (ds_read_b64_tr_b16).
+// * dQ: a workgroup owns 128 queries of one head (Q and dO in registers) and streams tiles of 64
+//   keys. S^T = K Q^T and dP^T = V dO^T leave each lane one query column and 16 consecutive
+//   keys per lane half; dS^T feeds dQ^T += K^T dS^T, with K^T read transposed. The lane also
+//   sums dS * <q, k> for its row's share of dscale.
+//
+// Tiles sit in LDS row-major and unpermuted, 16-byte chunks XOR-swizzled by bswz so that both
+// read patterns are free of bank conflicts: the permuted A-operand reads (rows perm32(0..15) of
+// one chunk) and the transposed reads (4 consecutive rows x 64 bytes). Rows past the arrays
+// arrive as zeros (buffer range checks); rows that take no part carry lse = +inf, so all their
+// weights are 0; keys past kv_lengths and past the causal limit are set to weight 0 per
+// element. No atomics: each workgroup writes its own rows.
+#include <type_traits>
+
+#include "mfma_common.h"
 
 namespace sdpa {
 
+namespace {
+
+constexpr int NTB = 256;          // threads per workgroup (4 waves)
+constexpr int RB = 128;           // rows a workgroup owns: keys (dK/dV) or queries (dQ)
+constexpr int ST = 64;            // keys per streamed tile of the dQ pass
+constexpr int QT_KV = 128;        // queries per streamed tile of the dK/dV pass
+
+// MFMA row r of a 32-row A operand reads tile row perm32(r): accumulator entry 4*i + j of lane
+// half h (MFMA row 8*i + 4*h + j) then belongs to tile row 16*h + 4*i + j.
+__device__ __forceinline__ int perm32(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+
+// Chunk swizzle of tile row `row` (chunk = 16 bytes): logical chunk c sits at position
+// c ^ bswz(row). Bits 0-1 separate the rows perm32 reads together; bits 2-3 (D = 128) or bit
+// 2 with the row's 128-byte half (D = 64) separate 4 consecutive rows for transposed reads.
+template <int D>
+__device__ __forceinline__ int bswz(int row) {
+  const int f = ((row >> 2) & 1) | (((row >> 4) & 1) << 1);
+  return D == 128 ? (((row & 3) << 2) | f) : ((((row >> 1) & 1) << 2) | f);
+}
+
+// Tile loader and readers for ST x D tiles of 16-bit elements in LDS.
+template <int D, bool F16, int ST>
+struct Tiles {
+  using x8 = typename In<F16>::x8;
+  static constexpr int CPR = D / 8;                 // chunks per row
+  static constexpr int SPT = ST * CPR / NTB;        // direct-load instructions per thread
+  static constexpr int DB = D / 32;
+  int doff[SPT];                                    // per-thread source offsets (row bytes applied)
+  int nrow, nsw;                                    // permuted A-operand row of this lane, its swizzle
+  int toff_lo[DB], toff_hi[DB];                     // transposed-read offsets (elements)
+
+  __device__ void init(int row_bytes, int lane, int tid) {
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int sl = NTB * u + tid, row = sl / CPR, pos = sl % CPR;
+      doff[u] = row * row_bytes + (pos ^ bswz<D>(row)) * 16;
+    }
+    nrow = perm32(lane & 31);
+    nsw = bswz<D>(nrow);
+    const int vr = 16 * (lane >> 5) + ((lane & 15) >> 2);
+    const int vc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      const int col = 32 * d + vc;
+      toff_lo[d] = vr * D + ((((col >> 3) ^ bswz<D>(vr)) << 3) | (col & 7));
+      toff_hi[d] = (vr + 4) * D + ((((col >> 3) ^ bswz<D>(vr + 4)) << 3) | (col & 7));
+      asm volatile("" : "+v"(toff_hi[d]));
+    }
+  }
+  // rows [r0, r0 + ST) of the slice at `base` (row stride row_bytes), rows from `valid` on as zeros
+  __device__ void load(const uint16_t* base, int64_t row_elems, int r0, int valid, int row_bytes,
+                       uint16_t* dst, int wave) const {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)r0 * row_elems, (int64_t)(valid - r0) * row_bytes);
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) dma16(r, dst + 8 * (NTB * u + 64 * wave), doff[u]);
+  }
+  // A operand: 32-row block rb, head-dim chunk c (16 elements), rows in perm32 order
+  __device__ x8 arow(const uint16_t* t, int rb, int c, int hh) const {
+    const int row = 32 * rb + nrow;
+    return *reinterpret_cast<const x8*>(t + row * D + (((2 * c + hh) ^ nsw) << 3));
+  }
+  // A operand, transposed: lane L gets tile[32*rb + 16*(L/32) + 8*sh + t][32*d + L%32], t = 0..7
+  __device__ x8 atr(const uint16_t* t, int rb, int sh, int d) const {
+    const int rows = (32 * rb + 8 * sh) * D;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(t + (rows + toff_lo[d])));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(t + (rows + toff_hi[d])));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(x8, v);
+  }
+};
+
+// Workgroup n of a launch over n_t row tiles x HB (batch, head) slices -> (tile rank, slice).
+// Rank-major, so that the heaviest tiles of every slice run first; with remap every XCD (the
+// hardware deals workgroups round-robin over 8) gets a contiguous set of slices.
+__device__ __forceinline__ void wg_map(int n, int HB, int remap, int& rank, int& slice) {
+  if (remap) {
+    const int per_x = HB >> 3, k = n >> 3;
+    rank = k / per_x;
+    slice = (n & 7) * per_x + k % per_x;
+  } else {
+    rank = n / HB;
+    slice = n % HB;
+  }
+}
+
+// 16-bit B operand from 8 fp32 values
+template <bool F16>
+__device__ __forceinline__ typename In<F16>::x8 pack8(const float* x) {
+  using E = In<F16>;
+  const uint4 u = make_uint4(E::pack(x[0], x[1]), E::pack(x[2], x[3]), E::pack(x[4], x[5]), E::pack(x[6], x[7]));
+  return __builtin_bit_cast(typename E::x8, u);
+}
+
+// Four consecutive outputs (fp32, bf16 or f16) at element offset `off`
+__device__ __forceinline__ void store4(void* base, int64_t off, int dtype, float r0, float r1, float r2, float r3) {
+  if (dtype == SDPA_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + off) = make_float4(r0, r1, r2, r3);
+  } else if (dtype == SDPA_F16) {
+    const uint32_t w0 = (uint32_t)float_to_f16_bits(r0) | ((uint32_t)float_to_f16_bits(r1) << 16);
+    const uint32_t w1 = (uint32_t)float_to_f16_bits(r2) | ((uint32_t)float_to_f16_bits(r3) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + off) = make_uint2(w0, w1);
+  } else {
+    const uint32_t w0 = (uint32_t)float_to_bf16_bits(r0) | ((uint32_t)float_to_bf16_bits(r1) << 16);
+    const uint32_t w1 = (uint32_t)float_to_bf16_bits(r2) | ((uint32_t)float_to_bf16_bits(r3) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + off) = make_uint2(w0, w1);
+  }
+}
+
+// ================================ dK / dV ====================================================
+template <int D, bool F16>
+__global__ __launch_bounds__(NTB, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_mfma_kernel(BwdArgs g, int remap) {
+  using E = In<F16>;
+  using x8 = typename E::x8;
+  constexpr int DC = D / 16, DB = D / 32, TILE = QT_KV * D;
+  constexpr int ST = QT_KV, QB = ST / 32;
+  __shared__ __align__(16) uint16_t qbuf0[TILE], qbuf1[TILE], obuf0[TILE], obuf1[TILE];
+  __shared__ __align__(16) float stat[2][2][ST];      // [buffer][lse / scale, D][query]
+  const AttnArgs& a = g.a;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ql = lane & 31, hh = lane >> 5;
+
+  int kt, bg;
+  wg_map(blockIdx.x, a.Hkv * a.B, remap, kt, bg);
+  const int gk = bg % a.Hkv, b = bg / a.Hkv;
+  const int grp = a.Hq / a.Hkv;
+  const int k0 = kt * RB, wk0 = k0 + 32 * wave, key_me = wk0 + ql;
+  const int nkv = batch_kv_len(a, b), nq = batch_q_len(a, b);
+  const int64_t off = batch_causal_offset(a, b);
+  const bool causal = a.causal != SDPA_CAUSAL_NONE;
+  const float c2 = a.scale * LOG2E;
+
+  // queries that may attend a key of this workgroup: i >= k0 - off under the causal rule
+  int64_t i_lo = causal ? (int64_t)k0 - off : 0;
+  i_lo = i_lo < 0 ? 0 : i_lo;
+  const int n_qt = (nq + ST - 1) / ST;
+  const int qt0 = (k0 < nkv && i_lo < nq) ? (int)(i_lo / ST) : n_qt;
+  const int per_head = n_qt - qt0;
+  const int n_it = per_head * grp;
+  // this wave: queries i >= wk0 - off matter, keys from wk0 must lie below nkv
+  const int64_t wi_lo = causal ? (int64_t)wk0 - off : INT64_MIN / 2;
+  const bool wave_live = wk0 < nkv;
+
+  // K and V of this lane's key as B operands (keys past kv_lengths as zeros)
+  x8 kB[DC], vB[DC];
+  {
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + gk * a.k_sh;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + gk * a.v_sh;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, (int64_t)nkv * a.k_ss * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, (int64_t)nkv * a.v_ss * 2);
+    const int ko = key_me * (int)(a.k_ss * 2) + 16 * hh, vo = key_me * (int)(a.v_ss * 2) + 16 * hh;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      kB[c] = __builtin_bit_cast(x8, buf_load16(rk, ko + 32 * c));
+      vB[c] = __builtin_bit_cast(x8, buf_load16(rv, vo + 32 * c));
+    }
+  }
+
+  Tiles<D, F16, ST> tq, to;
+  tq.init((int)(a.q_ss * 2), lane, tid);
+  to.init((int)(g.do_ss * 2), lane, tid);
+  auto it_head = [&](int it) { return gk * grp + it / per_head; };
+  auto it_q0 = [&](int it) { return (qt0 + it % per_head) * ST; };
+  auto load_tiles = [&](int it, uint16_t* qd, uint16_t* od) {
+    const int h = it_head(it), i0 = it_q0(it);
+    tq.load(static_cast<const uint16_t*>(a.q) + b * a.q_sb + h * a.q_sh, a.q_ss, i0, a.Lq, (int)(a.q_ss * 2), qd, wave);
+    to.load(static_cast<const uint16_t*>(g.dout) + b * g.do_sb + h * g.do_sh, g.do_ss, i0, a.Lq, (int)(g.do_ss * 2),
+            od, wave);
+  };
+  // statistics of the tile's queries: thread t < 64 takes lse of query t, 64 <= t < 128 its D
+  auto load_stat = [&](int it) -> float {
+    if (tid >= 2 * ST) return 0.f;
+    const int h = it_head(it), i = it_q0(it) + (tid & (ST - 1));
+    const int64_t row = ((int64_t)b * a.Hq + h) * a.Lq + i;
+    if (tid < ST) return i < nq ? g.w_lse[row] / a.scale : INFINITY;   // +inf: weight 0 (scale > 0)
+    return i < nq ? g.w_dsum[row] : 0.f;
+  };
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dk[d][e] = dv[d][e] = 0.f;
+
+  if (n_it > 0) {
+    load_tiles(0, qbuf0, obuf0);
+    const float st0 = load_stat(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (tid < 2 * ST) stat[0][tid / ST][tid & (ST - 1)] = st0;
+  }
+  __syncthreads();
+
+  // S = Q K^T - lse/scale and dP = dO V^T - D of 32-query block qb start from the row
+  // statistics (the MFMAs' C operands), so that a weight is one multiply and exp2 and dS one
+  // multiply
+  auto init_sdp = [&](const float* st, int qb, f32x16& s, f32x16& dp) {
+    const float4* ls = reinterpret_cast<const float4*>(st + 32 * qb + 16 * hh);
+    const float4* ds = reinterpret_cast<const float4*>(st + ST + 32 * qb + 16 * hh);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 l4 = ls[i], d4 = ds[i];
+      s[4 * i] = -l4.x; s[4 * i + 1] = -l4.y; s[4 * i + 2] = -l4.z; s[4 * i + 3] = -l4.w;
+      dp[4 * i] = -d4.x; dp[4 * i + 1] = -d4.y; dp[4 * i + 2] = -d4.z; dp[4 * i + 3] = -d4.w;
+    }
+  };
+  // One block step. The instruction order is fixed by scheduling barriers, because with one
+  // wave per SIMD nothing else hides latency: in step c the LDS operands of step c + 1 are
+  // requested, the two S/dP MFMAs of the next block are issued with the operands requested one
+  // step earlier, and 16/DC weights of the current block are taken while those MFMAs run. Then
+  // the 16 dV/dK MFMAs of the current block follow, their transposed operands one step ahead.
+  auto block = [&](auto NEXT_, const uint16_t* qs, const uint16_t* os, const float* st, int qb, int e_min,
+                   f32x16& sc, f32x16& dc, f32x16& sn, f32x16& dn) {
+    constexpr bool NEXT = decltype(NEXT_)::value;
+    constexpr int EPS = 16 / DC;                    // weights taken per step
+    float pv[16], sv[16];
+    x8 aq, ao;
+    if constexpr (NEXT) {
+      init_sdp(st, qb + 1, sn, dn);
+      aq = tq.arow(qs, qb + 1, 0, hh);
+      ao = to.arow(os, qb + 1, 0, hh);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      x8 aqn = aq, aon = ao;
+      if constexpr (NEXT) {
+        if (c + 1 < DC) {
+          aqn = tq.arow(qs, qb + 1, c + 1, hh);
+          aon = to.arow(os, qb + 1, c + 1, hh);
+        }
+        sn = E::mfma(aq, kB[c], sn);
+        dn = E::mfma(ao, vB[c], dn);
+      }
+#pragma unroll
+      for (int u = 0; u < EPS; ++u) {
+        const int e = EPS * c + u;
+        // masked entries get exponent -inf (weight 0): a select on the argument, not a branch
+        const float x = sc[e] * c2;
+        const float p = __builtin_amdgcn_exp2f(e >= e_min ? x : -INFINITY);
+        pv[e] = p;
+        sv[e] = p * dc[e];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      aq = aqn;
+      ao = aon;
+    }
+    const x8 pB[2] = {pack8<F16>(pv), pack8<F16>(pv + 8)};
+    const x8 sB[2] = {pack8<F16>(sv), pack8<F16>(sv + 8)};
+    x8 to_c = to.atr(os, qb, 0, 0), tq_c = tq.atr(qs, qb, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 2 * DB; ++k) {
+      const int sh = k / DB, d = k % DB;
+      x8 to_n = to_c, tq_n = tq_c;
+      if (k + 1 < 2 * DB) {
+        to_n = to.atr(os, qb, (k + 1) / DB, (k + 1) % DB);
+        tq_n = tq.atr(qs, qb, (k + 1) / DB, (k + 1) % DB);
+      }
+      dv[d] = E::mfma(to_c, pB[sh], dv[d]);
+      dk[d] = E::mfma(tq_c, sB[sh], dk[d]);
+      __builtin_amdgcn_sched_barrier(0);
+      to_c = to_n;
+      tq_c = tq_n;
+    }
+  };
+  std::integral_constant<bool, false> LAST;
+  std::integral_constant<bool, true> MORE;
+  auto iter = [&](auto PAR_, int it) {
+    constexpr int P = decltype(PAR_)::value;
+    const uint16_t* qs = P ? qbuf1 : qbuf0;
+    const uint16_t* os = P ? obuf1 : obuf0;
+    float st_next = 0.f;
+    if (it + 1 < n_it) {
+      load_tiles(it + 1, P ? qbuf0 : qbuf1, P ? obuf0 : obuf1);
+      st_next = load_stat(it + 1);
+    }
+    const int i0 = it_q0(it);
+    if (wave_live && (int64_t)i0 + ST - 1 >= wi_lo) {
+      const float* st = &stat[P][0][0];
+      f32x16 sa[2], dpa[2];
+      init_sdp(st, 0, sa[0], dpa[0]);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        sa[0] = E::mfma(tq.arow(qs, 0, c, hh), kB[c], sa[0]);
+        dpa[0] = E::mfma(to.arow(os, 0, c, hh), vB[c], dpa[0]);
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        int e_min = 0;                              // entries below: before this key's causal limit
+        if (causal) {
+          const int64_t m = (int64_t)key_me - off - (i0 + 32 * qb + 16 * hh);
+          e_min = m < 0 ? 0 : (m > 16 ? 16 : (int)m);
+        }
+        if (key_me >= nkv) e_min = 16;
+        if (qb + 1 < QB) block(MORE, qs, os, st, qb, e_min, sa[qb & 1], dpa[qb & 1], sa[(qb + 1) & 1], dpa[(qb + 1) & 1]);
+        else block(LAST, qs, os, st, qb, e_min, sa[qb & 1], dpa[qb & 1], sa[(qb + 1) & 1], dpa[(qb + 1) & 1]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (it + 1 < n_it && tid < 2 * ST) stat[1 - P][tid / ST][tid & (ST - 1)] = st_next;
+    __syncthreads();
+  };
+  std::integral_constant<int, 0> I0;
+  std::integral_constant<int, 1> I1;
+  for (int it = 0; it < n_it; it += 2) {
+    iter(I0, it);
+    if (it + 1 >= n_it) break;
+    iter(I1, it + 1);
+  }
+
+  // epilogue: lane owns key key_me; entry 4*i + j of block d is head-dim column 32*d + 8*i + 4*hh + j
+  if (key_me >= a.Lkv) return;
+  const int64_t kr = b * g.dk_sb + (int64_t)key_me * g.dk_ss + gk * g.dk_sh;
+  const int64_t vr = b * g.dv_sb + (int64_t)key_me * g.dv_ss + gk * g.dv_sh;
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = 32 * d + 8 * i + 4 * hh;
+      store4(g.dk, kr + col, g.dk_dtype, dk[d][4 * i] * a.scale, dk[d][4 * i + 1] * a.scale,
+             dk[d][4 * i + 2] * a.scale, dk[d][4 * i + 3] * a.scale);
+      store4(g.dv, vr + col, g.dv_dtype, dv[d][4 * i], dv[d][4 * i + 1], dv[d][4 * i + 2], dv[d][4 * i + 3]);
+    }
+}
+
+// ================================ dQ =========================================================
+template <int D, bool F16>
+__global__ __launch_bounds__(NTB, 1) void bwd_dq_mfma_kernel(BwdArgs g, int n_qt, int remap) {
+  using E = In<F16>;
+  using x8 = typename E::x8;
+  constexpr int DC = D / 16, DB = D / 32, TILE = ST * D;
+  __shared__ __align__(16) uint16_t kbuf0[TILE], kbuf1[TILE], vbuf0[TILE], vbuf1[TILE];
+  const AttnArgs& a = g.a;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ql = lane & 31, hh = lane >> 5;
+
+  int rank, bh;
+  wg_map(blockIdx.x, a.Hq * a.B, remap, rank, bh);
+  const int qt = n_qt - 1 - rank;                 // causal: the last query tiles are the heaviest
+  const int h = bh % a.Hq, b = bh / a.Hq;
+  const int gk = h / (a.Hq / a.Hkv);
+  const int q0 = qt * RB;
+  const int nkv = batch_kv_len(a, b), nq = batch_q_len(a, b);
+  const int64_t off = batch_causal_offset(a, b);
+  const bool causal = a.causal != SDPA_CAUSAL_NONE;
+  const float c2 = a.scale * LOG2E;
+  const int i_me = q0 + 32 * wave + ql;
+  const int64_t wrow = ((int64_t)b * a.Hq + h) * a.Lq + i_me;
+  const float lse2 = i_me < nq ? g.w_lse[wrow] * LOG2E : INFINITY;
+  const float dsum = i_me < nq ? g.w_dsum[wrow] : 0.f;
+
+  // keys the workgroup and this wave visit
+  const int row_end = min(q0 + RB, nq);
+  int64_t k_end = nkv;
+  if (causal) { const int64_t l = off + row_end; if (l < k_end) k_end = l; }
+  if (row_end <= q0 || k_end < 0) k_end = 0;
+  const int w_last = min(q0 + 32 * wave + 31, row_end - 1);
+  int64_t k_end_w = nkv;
+  if (causal) { const int64_t l = off + w_last + 1; if (l < k_end_w) k_end_w = l; }
+  if (w_last < q0 + 32 * wave || k_end_w < 0) k_end_w = 0;
+  const int n_tiles = (int)((k_end + ST - 1) / ST);
+  // per-entry key limit of this lane: keys below kv_lengths and (causal) at most off + i
+  int64_t lim_me = nkv;
+  if (causal) { const int64_t l = off + i_me + 1; if (l < lim_me) lim_me = l; }
+
+  // Q and dO of this lane's query as B operands (rows past Lq as zeros)
+  x8 qB[DC], oB[DC];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(a.q) + b * a.q_sb + h * a.q_sh,
+                                                (int64_t)a.Lq * a.q_ss * 2);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<const uint16_t*>(g.dout) + b * g.do_sb + h * g.do_sh,
+                                                (int64_t)a.Lq * g.do_ss * 2);
+    const int qo = i_me * (int)(a.q_ss * 2) + 16 * hh, oo = i_me * (int)(g.do_ss * 2) + 16 * hh;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      qB[c] = __builtin_bit_cast(x8, buf_load16(rq, qo + 32 * c));
+      oB[c] = __builtin_bit_cast(x8, buf_load16(ro, oo + 32 * c));
+    }
+  }
+
+  Tiles<D, F16, ST> tk, tv;
+  tk.init((int)(a.k_ss * 2), lane, tid);
+  tv.init((int)(a.v_ss * 2), lane, tid);
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + gk * a.k_sh;
+  const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + gk * a.v_sh;
+  auto load_tiles = [&](int t, uint16_t* kd, uint16_t* vd) {
+    tk.load(kp, a.k_ss, t * ST, nkv, (int)(a.k_ss * 2), kd, wave);
+    tv.load(vp, a.v_ss, t * ST, nkv, (int)(a.v_ss * 2), vd, wave);
+  };
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[d][e] = 0.f;
+  float dsc = 0.f;
+
+  if (n_tiles > 0) load_tiles(0, kbuf0, vbuf0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  auto iter = [&](auto PAR_, int t) {
+    constexpr int P = decltype(PAR_)::value;
+    const uint16_t* ks = P ? kbuf1 : kbuf0;
+    const uint16_t* vs = P ? vbuf1 : vbuf0;
+    if (t + 1 < n_tiles) load_tiles(t + 1, P ? kbuf0 : kbuf1, P ? vbuf0 : vbuf1);
+    const int k0 = t * ST;
+    if (k0 < k_end_w) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int jbase = k0 + 32 * kb + 16 * hh;     // entry e of this lane: key jbase + e
+        f32x16 s, dp;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          s = E::mfma(tk.arow(ks, kb, c, hh), qB[c], s);
+          dp = E::mfma(tv.arow(vs, kb, c, hh), oB[c], dp);
+        }
+        int e_end = 16;
+        {
+          const int64_t m = lim_me - jbase;
+          e_end = m < 0 ? 0 : (m > 16 ? 16 : (int)m);
+        }
+        float sv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float x = fmaf(s[e], c2, -lse2);
+          const float p = __builtin_amdgcn_exp2f(e < e_end ? x : -INFINITY);
+          const float d_s = p * (dp[e] - dsum);
+          sv[e] = d_s;
+          dsc = fmaf(d_s, s[e], dsc);
+        }
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          const x8 sB = pack8<F16>(sv + 8 * sh);
+#pragma unroll
+          for (int d = 0; d < DB; ++d) dq[d] = E::mfma(tk.atr(ks, kb, sh, d), sB, dq[d]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  std::integral_constant<int, 0> I0;
+  std::integral_constant<int, 1> I1;
+  for (int t = 0; t < n_tiles; t += 2) {
+    iter(I0, t);
+    if (t + 1 >= n_tiles) break;
+    iter(I1, t + 1);
+  }
+
+  if (i_me >= a.Lq) return;
+  dsc += __shfl_xor(dsc, 32, 64);
+  if (hh == 0) g.w_dsc[wrow] = dsc;
+  const int64_t qr = b * g.dq_sb + (int64_t)i_me * g.dq_ss + h * g.dq_sh;
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = 32 * d + 8 * i + 4 * hh;
+      store4(g.dq, qr + col, g.dq_dtype, dq[d][4 * i] * a.scale, dq[d][4 * i + 1] * a.scale,
+             dq[d][4 * i + 2] * a.scale, dq[d][4 * i + 3] * a.scale);
+    }
+}
+
+bool al(const void* p, int n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+template <int D, bool F16>
+hipError_t launch_dkdv_t(const BwdArgs& g, hipStream_t s) {
+  const AttnArgs& a = g.a;
+  const int n_kt = (a.Lkv + RB - 1) / RB;
+  const int HB = a.Hkv * a.B;
+  hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<D, F16>), dim3((unsigned)((int64_t)n_kt * HB)), dim3(NTB), 0, s, g,
+                     HB % 8 == 0 ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <int D, bool F16>
+hipError_t launch_dq_t(const BwdArgs& g, hipStream_t s) {
+  const AttnArgs& a = g.a;
+  const int n_qt = (a.Lq + RB - 1) / RB;
+  const int HB = a.Hq * a.B;
+  hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, F16>), dim3((unsigned)((int64_t)n_qt * HB)), dim3(NTB), 0, s, g, n_qt,
+                     HB % 8 == 0 ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 bool bwd_mfma_supports(const BwdArgs& g) {
-  (void)g;
-  return false;
+  const AttnArgs& a = g.a;
+  if ((a.in_dtype != SDPA_BF16 && a.in_dtype != SDPA_F16) || a.D != a.Dv || (a.D != 64 && a.D != 128)) return false;
+  if (g.do_dtype != a.in_dtype) return false;            // dO streams through the same 16-bit tiles
+  if (a.mask || a.bm_class || a.bias || a.qk_norm || a.q_seg) return false;
+  if (!(a.scale > 0.f)) return false;    // the dK/dV pass folds lse / scale into its MFMAs
+  if (!al(a.q, 16) || !al(a.k, 16) || !al(a.v, 16) || !al(g.dout, 16)) return false;
+  if ((a.q_sb | a.q_ss | a.q_sh | a.k_sb | a.k_ss | a.k_sh | a.v_sb | a.v_ss | a.v_sh | g.do_sb | g.do_ss | g.do_sh) & 7)
+    return false;
+  const int64_t eq = g.dq_dtype == SDPA_F32 ? 4 : 2, ek = g.dk_dtype == SDPA_F32 ? 4 : 2, ev = g.dv_dtype == SDPA_F32 ? 4 : 2;
+  if (!al(g.dq, (int)(4 * eq)) || !al(g.dk, (int)(4 * ek)) || !al(g.dv, (int)(4 * ev))) return false;
+  if ((g.dq_sb | g.dq_ss | g.dq_sh | g.dk_sb | g.dk_ss | g.dk_sh | g.dv_sb | g.dv_ss | g.dv_sh) & 3) return false;
+  if (a.q_ss < a.D || a.k_ss < a.D || a.v_ss < a.D || g.do_ss < a.D) return false;
+  if ((int64_t)a.Lq * a.q_ss * 2 > INT32_MAX || (int64_t)a.Lkv * a.k_ss * 2 > INT32_MAX ||
+      (int64_t)a.Lkv * a.v_ss * 2 > INT32_MAX || (int64_t)a.Lq * g.do_ss * 2 > INT32_MAX)
+    return false;
+  const int64_t n1 = (int64_t)((a.Lkv + RB - 1) / RB) * a.Hkv * a.B, n2 = (int64_t)((a.Lq + RB - 1) / RB) * a.Hq * a.B;
+  return n1 < (int64_t)INT32_MAX && n2 < (int64_t)INT32_MAX;
 }
 
 hipError_t launch_bwd_mfma_dkdv(const BwdArgs& g, hipStream_t s) {
-  (void)g; (void)s;
-  return hipErrorInvalidValue;
+  const bool f16 = g.a.in_dtype == SDPA_F16;
+  if (g.a.D == 128) return f16 ? launch_dkdv_t<128, true>(g, s) : launch_dkdv_t<128, false>(g, s);
+  return f16 ? launch_dkdv_t<64, true>(g, s) : launch_dkdv_t<64, false>(g, s);
 }
 
 hipError_t launch_bwd_mfma_dq(const BwdArgs& g, hipStream_t s) {
-  (void)g; (void)s;
-  return hipErrorInvalidValue;
+  const bool f16 = g.a.in_dtype == SDPA_F16;
+  if (g.a.D == 128) return f16 ? launch_dq_t<128, true>(g, s) : launch_dq_t<128, false>(g, s);
+  return f16 ? launch_dq_t<64, true>(g, s) : launch_dq_t<64, false>(g, s);
 }
 
 }  // namespace sdpa

@@ -109,6 +109,7 @@ struct BwdArgs {
   float* w_dsum;
   float* w_lse;
   float* w_dsc;
+  double* w_dsc2;              // [ceil(B*Hq*Lq / 4096)]: first-stage sums of w_dsc
 };
 
 constexpr float kRmsEps = 1e-6f;
