@@ -239,19 +239,23 @@ void bwd_dkdv_mfma_kernel(BwdArgs g, int remap) {
   };
   // One block step. The instruction order is fixed by scheduling barriers, because with one
   // wave per SIMD nothing else hides latency: in step c the LDS operands of step c + 1 are
-  // requested, the two S/dP MFMAs of the next block are issued with the operands requested one
-  // step earlier, and 16/DC weights of the current block are taken while those MFMAs run. Then
-  // the 16 dV/dK MFMAs of the current block follow, their transposed operands one step ahead.
-  auto block = [&](auto NEXT_, const uint16_t* qs, const uint16_t* os, const float* st, int qb, int e_min,
+  // requested, the two S/dP MFMAs of the next block (qb2 of the tile at qs2/os2) are issued
+  // with the operands requested one step earlier, and 16/DC weights of the current block are
+  // taken while those MFMAs run. Then the 16 dV/dK MFMAs of the current block follow, their
+  // transposed operands one step ahead. NEXT: a next block is formed; FIN: the current block
+  // is finished.
+  auto block = [&](auto NEXT_, auto FIN_, const uint16_t* qs, const uint16_t* os, int qb, int e_min,
+                   const uint16_t* qs2, const uint16_t* os2, const float* st2, int qb2,
                    f32x16& sc, f32x16& dc, f32x16& sn, f32x16& dn) {
     constexpr bool NEXT = decltype(NEXT_)::value;
+    constexpr bool FIN = decltype(FIN_)::value;
     constexpr int EPS = 16 / DC;                    // weights taken per step
     float pv[16], sv[16];
     x8 aq, ao;
     if constexpr (NEXT) {
-      init_sdp(st, qb + 1, sn, dn);
-      aq = tq.arow(qs, qb + 1, 0, hh);
-      ao = to.arow(os, qb + 1, 0, hh);
+      init_sdp(st2, qb2, sn, dn);
+      aq = tq.arow(qs2, qb2, 0, hh);
+      ao = to.arow(os2, qb2, 0, hh);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -259,79 +263,105 @@ void bwd_dkdv_mfma_kernel(BwdArgs g, int remap) {
       x8 aqn = aq, aon = ao;
       if constexpr (NEXT) {
         if (c + 1 < DC) {
-          aqn = tq.arow(qs, qb + 1, c + 1, hh);
-          aon = to.arow(os, qb + 1, c + 1, hh);
+          aqn = tq.arow(qs2, qb2, c + 1, hh);
+          aon = to.arow(os2, qb2, c + 1, hh);
         }
         sn = E::mfma(aq, kB[c], sn);
         dn = E::mfma(ao, vB[c], dn);
       }
+      if constexpr (FIN) {
 #pragma unroll
-      for (int u = 0; u < EPS; ++u) {
-        const int e = EPS * c + u;
-        // masked entries get exponent -inf (weight 0): a select on the argument, not a branch
-        const float x = sc[e] * c2;
-        const float p = __builtin_amdgcn_exp2f(e >= e_min ? x : -INFINITY);
-        pv[e] = p;
-        sv[e] = p * dc[e];
+        for (int u = 0; u < EPS; ++u) {
+          const int e = EPS * c + u;
+          // masked entries get exponent -inf (weight 0): a select on the argument, not a branch
+          const float x = sc[e] * c2;
+          const float p = __builtin_amdgcn_exp2f(e >= e_min ? x : -INFINITY);
+          pv[e] = p;
+          sv[e] = p * dc[e];
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       aq = aqn;
       ao = aon;
     }
-    const x8 pB[2] = {pack8<F16>(pv), pack8<F16>(pv + 8)};
-    const x8 sB[2] = {pack8<F16>(sv), pack8<F16>(sv + 8)};
-    x8 to_c = to.atr(os, qb, 0, 0), tq_c = tq.atr(qs, qb, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < 2 * DB; ++k) {
-      const int sh = k / DB, d = k % DB;
-      x8 to_n = to_c, tq_n = tq_c;
-      if (k + 1 < 2 * DB) {
-        to_n = to.atr(os, qb, (k + 1) / DB, (k + 1) % DB);
-        tq_n = tq.atr(qs, qb, (k + 1) / DB, (k + 1) % DB);
-      }
-      dv[d] = E::mfma(to_c, pB[sh], dv[d]);
-      dk[d] = E::mfma(tq_c, sB[sh], dk[d]);
+    if constexpr (FIN) {
+      const x8 pB[2] = {pack8<F16>(pv), pack8<F16>(pv + 8)};
+      const x8 sB[2] = {pack8<F16>(sv), pack8<F16>(sv + 8)};
+      x8 to_c = to.atr(os, qb, 0, 0), tq_c = tq.atr(qs, qb, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      to_c = to_n;
-      tq_c = tq_n;
+#pragma unroll
+      for (int k = 0; k < 2 * DB; ++k) {
+        const int sh = k / DB, d = k % DB;
+        x8 to_n = to_c, tq_n = tq_c;
+        if (k + 1 < 2 * DB) {
+          to_n = to.atr(os, qb, (k + 1) / DB, (k + 1) % DB);
+          tq_n = tq.atr(qs, qb, (k + 1) / DB, (k + 1) % DB);
+        }
+        dv[d] = E::mfma(to_c, pB[sh], dv[d]);
+        dk[d] = E::mfma(tq_c, sB[sh], dk[d]);
+        __builtin_amdgcn_sched_barrier(0);
+        to_c = to_n;
+        tq_c = tq_n;
+      }
     }
   };
-  std::integral_constant<bool, false> LAST;
-  std::integral_constant<bool, true> MORE;
+  std::integral_constant<bool, false> NO;
+  std::integral_constant<bool, true> YES;
+  // the wave has work in tile it when some query of the tile may attend one of its keys
+  auto has_work = [&](int it) { return wave_live && (int64_t)it_q0(it) + ST - 1 >= wi_lo; };
+  auto e_min_of = [&](int i0, int qb) {              // entries below: before this key's causal limit
+    int e_min = 0;
+    if (causal) {
+      const int64_t m = (int64_t)key_me - off - (i0 + 32 * qb + 16 * hh);
+      e_min = m < 0 ? 0 : (m > 16 ? 16 : (int)m);
+    }
+    return key_me >= nkv ? 16 : e_min;
+  };
+  // S/dP of block 0 of the first tile (buffer 0); every later first block is formed during the
+  // last block of the tile before
+  f32x16 sa[2], dpa[2];
+  if (n_it > 0 && has_work(0)) {
+    init_sdp(&stat[0][0][0], 0, sa[0], dpa[0]);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      sa[0] = E::mfma(tq.arow(qbuf0, 0, c, hh), kB[c], sa[0]);
+      dpa[0] = E::mfma(to.arow(obuf0, 0, c, hh), vB[c], dpa[0]);
+    }
+  }
+  // Tile it sits in buffer P = it & 1; tile it + 1 is loaded into the other buffer while blocks
+  // 0 .. QB-2 of tile it are worked. A barrier then makes tile it + 1 visible, and the last
+  // block of tile it is finished while block 0 of tile it + 1 is formed. A second barrier ends
+  // every read of buffer P before the next iteration refills it.
   auto iter = [&](auto PAR_, int it) {
     constexpr int P = decltype(PAR_)::value;
     const uint16_t* qs = P ? qbuf1 : qbuf0;
     const uint16_t* os = P ? obuf1 : obuf0;
+    uint16_t* qsn = P ? qbuf0 : qbuf1;
+    uint16_t* osn = P ? obuf0 : obuf1;
     float st_next = 0.f;
     if (it + 1 < n_it) {
-      load_tiles(it + 1, P ? qbuf0 : qbuf1, P ? obuf0 : obuf1);
+      load_tiles(it + 1, qsn, osn);
       st_next = load_stat(it + 1);
     }
     const int i0 = it_q0(it);
-    if (wave_live && (int64_t)i0 + ST - 1 >= wi_lo) {
-      const float* st = &stat[P][0][0];
-      f32x16 sa[2], dpa[2];
-      init_sdp(st, 0, sa[0], dpa[0]);
+    const bool w_cur = has_work(it);
+    const float* st = &stat[P][0][0];
+    if (w_cur) {
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        sa[0] = E::mfma(tq.arow(qs, 0, c, hh), kB[c], sa[0]);
-        dpa[0] = E::mfma(to.arow(os, 0, c, hh), vB[c], dpa[0]);
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        int e_min = 0;                              // entries below: before this key's causal limit
-        if (causal) {
-          const int64_t m = (int64_t)key_me - off - (i0 + 32 * qb + 16 * hh);
-          e_min = m < 0 ? 0 : (m > 16 ? 16 : (int)m);
-        }
-        if (key_me >= nkv) e_min = 16;
-        if (qb + 1 < QB) block(MORE, qs, os, st, qb, e_min, sa[qb & 1], dpa[qb & 1], sa[(qb + 1) & 1], dpa[(qb + 1) & 1]);
-        else block(LAST, qs, os, st, qb, e_min, sa[qb & 1], dpa[qb & 1], sa[(qb + 1) & 1], dpa[(qb + 1) & 1]);
-      }
+      for (int qb = 0; qb + 1 < QB; ++qb)
+        block(YES, YES, qs, os, qb, e_min_of(i0, qb), qs, os, st, qb + 1, sa[qb & 1], dpa[qb & 1],
+              sa[(qb + 1) & 1], dpa[(qb + 1) & 1]);
     }
     __builtin_amdgcn_s_waitcnt(0);
     if (it + 1 < n_it && tid < 2 * ST) stat[1 - P][tid / ST][tid & (ST - 1)] = st_next;
+    __syncthreads();
+    const bool w_next = it + 1 < n_it && has_work(it + 1);
+    const float* stn = &stat[1 - P][0][0];
+    constexpr int L = QB - 1;
+    const int em = e_min_of(i0, L);
+    if (w_cur && w_next) block(YES, YES, qs, os, L, em, qsn, osn, stn, 0, sa[L & 1], dpa[L & 1], sa[0], dpa[0]);
+    else if (w_cur) block(NO, YES, qs, os, L, em, qsn, osn, stn, 0, sa[L & 1], dpa[L & 1], sa[0], dpa[0]);
+    else if (w_next) block(YES, NO, qs, os, L, em, qsn, osn, stn, 0, sa[L & 1], dpa[L & 1], sa[0], dpa[0]);
     __syncthreads();
   };
   std::integral_constant<int, 0> I0;
