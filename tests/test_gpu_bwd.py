@@ -148,3 +148,15 @@ def test_grad_degenerate_lengths(lib, Lq, Lkv):
     for n in ("dq", "dk", "dv"):
         np.testing.assert_allclose(got[n], ref[n], atol=2e-2, rtol=0)
     assert abs(got["dscale"] - ref["dscale"]) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_grad_gqa_ragged_several_tiles(lib, dtype, D):
+    # several 128-key and 128-query tiles with ragged tails, 4 query heads per K/V head,
+    # bottom-right causal with per-batch kv_lengths
+    w = workloads.random_attention(2700 + D, 2, 300, 777, 8, 2, D, dtype=dtype, is_causal="bottom_right",
+                                   kv_lengths=np.array([700, 777], dtype=np.int32))
+    dout = workloads.output_cotangent(w, 3700)
+    say(f"grad GQA ragged {dtype} D={D}")
+    check(run_bwd(w, dout), run_ref(w, dout), dtype, "gqa ragged")

@@ -106,3 +106,32 @@ def test_chunked_prefill_b1_hq32_hkv8_kv131072(lib):
     rows = [0, 1, 127, 128, 1024, 2046, 2047]
     ref = _rows_oracle(w, rows)
     assert_close(out[:, rows].cpu().numpy(), ref, "bf16", "chunked prefill rows")
+
+
+def test_causal_prefill_gradient_b4_h16_d128_l4096(lib):
+    # the gradient in the benchmark's configuration (bf16 inputs, saved output and gradients in
+    # bf16): every row of two whole (batch, head) slices against the fp64 oracle gradient of the
+    # slice (one K/V head per query head, so a slice is an independent attention); every entry
+    # of all slices finite
+    say("full size: gradient of the causal prefill B4 H16 D128 L4096")
+    from gpu_util import assert_grad_close
+    w = workloads.causal_prefill()
+    t = gpu_inputs(w)
+    out, lse = sa.sdpa(t["q"], t["k"], t["v"], is_causal=True, scale=w.scale, out_dtype=torch.float32,
+                       return_lse=True)
+    dout_np = workloads.output_cotangent(w, 7)
+    dq, dk, dv, dsc = sa.sdpa_bwd(t["q"], t["k"], t["v"], out.to(torch.bfloat16), dev(dout_np, "bf16"), lse,
+                                  is_causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq.float()).all() and torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all()
+    do64 = workloads.widen(dout_np, "bf16")
+    for b, h in ((0, 0), (3, 15)):
+        sl = lambda x: x[b:b + 1, :, h:h + 1]
+        ref = oracle.sdpa_grad(sl(w.values("q")), sl(w.values("k")), sl(w.values("v")), sl(do64),
+                               scale=w.scale, is_causal=True)
+        for n, g_ in (("dq", dq), ("dk", dk), ("dv", dv)):
+            assert_grad_close(g_[b:b + 1, :, h:h + 1].float().cpu().numpy(), ref[n], "bf16", f"({b},{h}) {n}")
+        # the lse of the slice
+        lref = oracle.sdpa_lse(sl(w.values("q")), sl(w.values("k")), sl(w.values("v")), scale=w.scale,
+                               is_causal=True)
+        assert_close(lse[b:b + 1, h:h + 1].cpu().numpy(), lref, "bf16", f"({b},{h}) lse")
