@@ -14,6 +14,10 @@ The same run times the GQA decode step (batch 64, 32 query heads over 8 K/V head
 sdpa_decode. Its metric is KV-read GB/s: the algorithmic bytes are the K and V rows of the
 attended keys, sum_b kv_len_b * Hkv * D * 2 bytes * 2, plus q and the output.
 
+It also times the gradient of the same prefill (sdpa_bwd: dq, dk, dv and dscale from the saved
+output and log-sum-exp), in TFLOP/s over 10 * D flops per allowed pair, and the block info of
+the 8192 x 8192 runtime mask from bytes and from packed bits.
+
 Printed: one JSON line (rank 0) with the contract fields, a ``roofline`` object for the
 prefill kernel (achieved = algorithmic flops per launch / average launch time measured with
 HIP events on the launch stream; peak = 2500 TFLOP/s bf16 dense MFMA), a ``decode`` object with
@@ -37,6 +41,8 @@ PREFILL_COUNTERS = (os.path.join(ROOT, "profiles", "fwd_mfma_causal_b4h16d128l40
                     os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc", "fwd_mfma.hip"))
 DECODE_COUNTERS = (os.path.join(ROOT, "profiles", "decode_gqa_b64h32kv8d128_counters.txt"),
                    os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc", "decode.hip"))
+BACKWARD_COUNTERS = (os.path.join(ROOT, "profiles", "bwd_causal_b4h16d128l4096_counters.txt"),
+                     os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc", "bwd_mfma.hip"))
 
 
 def parse_args():
@@ -239,7 +245,8 @@ def main():
             "config": {"workload": "causal_prefill", "batch": B, "heads": Hq, "head_dim": D, "q_len": Lq,
                        "is_causal": True, "grad_dtype": "bf16", "saved_out_dtype": "bf16"},
             "roofline": {"bound": "mfma", "achieved": round(tf_b, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "traffic": None, "flops_per_call": flops_b,
+                         "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "traffic": counters_traffic(BACKWARD_COUNTERS),
+                         "flops_per_call": flops_b,
                          "kernel": "bwd_prep + bwd_dkdv_mfma_kernel<128> + bwd_dq_mfma_kernel<128> + bwd_dscale"},
             "parity": backward_parity(w, q, k, v, outb, dout, lse, grads),
         }
