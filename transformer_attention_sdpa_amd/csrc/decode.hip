@@ -441,26 +441,33 @@ __device__ __forceinline__ bool mf_locate(const DecodeArgs& a, int item, int& b,
 // (query head, token) column groups of 16 per K/V head
 __host__ __device__ __forceinline__ int mf_groups(const DecodeArgs& a) { return ((a.Hq / a.Hkv) * a.T + 15) / 16; }
 
-// One workgroup (one wave) per (K/V head, column group, split, sequence): blockIdx.x = Hkv *
-// (groups * i + cg) + g. LINEAR: i is an item of mf_locate; else i is the split and the
-// sequence is blockIdx.y, and splits past a sequence's length exit at once.
+// One workgroup (one wave) per (K/V head g, column group cg, split, sequence). The hardware
+// deals consecutive workgroups round-robin over the 8 XCDs, so workgroup n runs on XCD n % 8;
+// n is laid out so that each XCD takes all (head, group) pairs of one item back to back:
+// hg = g + Hkv * cg = (n / 8) % HG and i = n % 8 + 8 * (n / (8 * HG)). The heads of one key
+// range then leave one XCD close together, as whole 2 KB cache rows rather than 256-byte
+// pieces at a 2 KB stride. LINEAR: i is an item of mf_locate; else i is the split and the
+// sequence is blockIdx.y. Items past the end (the grid is padded to whole groups of 8) and
+// splits past a sequence's length exit at once.
 template <bool LINEAR, bool F16>
 __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   __shared__ __align__(16) uint16_t k0s[kMfTileElems], k1s[kMfTileElems], k2s[kMfTileElems];
   __shared__ __align__(16) uint16_t v0s[kMfTileElems], v1s[kMfTileElems], v2s[kMfTileElems];
   const int r = a.Hq / a.Hkv;
   const int ng = mf_groups(a);
-  const int g = blockIdx.x % a.Hkv;
-  const int rest = blockIdx.x / a.Hkv;
-  const int cg = rest % ng;
+  const int HG = a.Hkv * ng;
+  const int xk = blockIdx.x >> 3;
+  const int hg = xk % HG;
+  const int g = hg % a.Hkv, cg = hg / a.Hkv;
+  const int item = (blockIdx.x & 7) + 8 * (xk / HG);
   int b, split, nkv;
   if constexpr (LINEAR) {
-    if (!mf_locate(a, rest / ng, b, split, nkv)) return;
+    if (!mf_locate(a, item, b, split, nkv)) return;
     b = __builtin_amdgcn_readfirstlane(b);
     split = __builtin_amdgcn_readfirstlane(split);
     nkv = __builtin_amdgcn_readfirstlane(nkv);
   } else {
-    split = rest / ng;
+    split = item;
     b = blockIdx.y;
     nkv = clampi(a.kv_lengths[b], 0, a.cap);
   }
@@ -560,9 +567,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int r = a.Hq / a.Hkv;
   dim3 grid(a.Hkv * a.max_splits, a.B);
   if (decode_mfma_supports(a)) {
-    const int64_t per_seq = (int64_t)a.Hkv * mf_groups(a) * a.max_splits;
-    const bool lin = a.B <= kLinMaxB && per_seq * a.B <= INT32_MAX;
-    const dim3 g1((unsigned)(per_seq * a.B)), g2((unsigned)per_seq, a.B);
+    // grids padded to whole groups of 8 items per (head, group) pair (see the kernel)
+    const int64_t hg = (int64_t)a.Hkv * mf_groups(a);
+    const int64_t per_seq = hg * a.max_splits;
+    const bool lin = a.B <= kLinMaxB && (per_seq * a.B + 8 * hg) <= INT32_MAX;
+    const int64_t n_lin = hg * 8 * (((int64_t)a.max_splits * a.B + 7) / 8);
+    const int64_t n_2d = hg * 8 * (((int64_t)a.max_splits + 7) / 8);
+    const dim3 g1((unsigned)n_lin), g2((unsigned)n_2d, a.B);
     if (a.in_dtype == SDPA_F16) {
       if (lin) hipLaunchKernelGGL((decode_split_mfma_kernel<true, true>), g1, dim3(64), 0, s, a);
       else hipLaunchKernelGGL((decode_split_mfma_kernel<false, true>), g2, dim3(64), 0, s, a);
