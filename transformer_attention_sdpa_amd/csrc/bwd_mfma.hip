@@ -1,5 +1,5 @@
 // bwd_mfma.hip -- the dK/dV and dQ passes of the attention gradient on the gfx950 matrix cores
-// (bf16 or f16 inputs, head dims 64 and 128, no mask; page "Neural Network primitives from
+// (bf16 or f16 inputs, head dims 64 and 128, no mask, scale > 0; page "Neural Network primitives from
 // NNlib.jl", section "Fused implementation": the weights are formed again tile by tile from q,
 // k and the saved log-sum-exp, never stored).
 //
@@ -7,13 +7,14 @@
 // and the other streamed through LDS, and they are mirror images of each other:
 //
 // * dK/dV: a workgroup owns 128 keys of one K/V head (32 per wave, K and V in registers as B
-//   operands) and streams tiles of 64 queries of every query head of the group. Per 32-query
-//   block a wave forms S = Q K^T and dP = dO V^T. Its lanes then hold one key column each, with
-//   16 consecutive queries per lane half, because the A-operand rows of Q and dO are read in the
-//   permuted order perm32. Next P = exp2(S * scale * log2 e - lse * log2 e) and
-//   dS = P (dP - D). Finally P and dS are packed to 16 bits and feed dV^T += dO^T P and
-//   dK^T += Q^T dS directly as B operands; dO^T and Q^T come from transposed LDS reads
-//   (ds_read_b64_tr_b16).
+//   operands) and streams tiles of 128 queries of every query head of the group. Per 32-query
+//   block a wave forms S = Q K^T - lse/scale and dP = dO V^T - D, the row statistics being the
+//   MFMAs' starting values. Its lanes then hold one key column each, with 16 consecutive
+//   queries per lane half, because the A-operand rows of Q and dO are read in the permuted
+//   order perm32. Next P = exp2(scale * log2 e * S) and dS = P dP. Finally P and dS are packed
+//   to 16 bits and feed dV^T += dO^T P and dK^T += Q^T dS directly as B operands; dO^T and Q^T
+//   come from transposed LDS reads (ds_read_b64_tr_b16). One wave per SIMD fits, so the
+//   instruction order is set by hand (see the block steps).
 // * dQ: a workgroup owns 128 queries of one head (Q and dO in registers) and streams tiles of 64
 //   keys. S^T = K Q^T and dP^T = V dO^T leave each lane one query column and 16 consecutive
 //   keys per lane half; dS^T feeds dQ^T += K^T dS^T, with K^T read transposed. The lane also
