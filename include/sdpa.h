@@ -158,6 +158,8 @@ SDPA_API sdpa_status sdpa_fwd_lse(const sdpa_tensor* q, const sdpa_tensor* k, co
  *      forward call (no bias and no qk_norm: the page sends a call with a bias to the
  *      materialized path, whose gradient is not this one).
  * out  the forward output {Dv, Hq, Lq, B}; dout its cotangent, same dims; each F32, BF16 or F16.
+ *      dout must be finite everywhere, also on rows that take no part: the matrix-core kernels
+ *      multiply it by their zero weights, and a NaN or Inf there would reach dk and dv.
  * lse  device fp32 [B][Hq][Lq] as written by sdpa_fwd_lse for this call.
  * dq {D, Hq, Lq, B}, dk {D, Hkv, Lkv, B}, dv {Dv, Hkv, Lkv, B}: outputs, each F32, BF16 or F16,
  *      head_dim stride 1; every element is written (0 for keys that no query attends).
