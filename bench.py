@@ -14,7 +14,9 @@ The same run times the GQA decode step (batch 64, 32 query heads over 8 K/V head
 sdpa_decode. Its metric is KV-read GB/s: the algorithmic bytes are the K and V rows of the
 attended keys, sum_b kv_len_b * Hkv * D * 2 bytes * 2, plus q and the output.
 
-It also times the gradient of the same prefill (sdpa_bwd: dq, dk, dv and dscale from the saved
+It also times the bias + block-sparse mask workload (B2 H16 D64 L8192, 2 GiB ALiBi bias, mask
+through block info) and the long-context chunk (32/8 heads, 2048 queries at offset 129024 over
+131072 keys), the gradient of the same prefill (sdpa_bwd: dq, dk, dv and dscale from the saved
 output and log-sum-exp), in TFLOP/s over 10 * D flops per allowed pair, and the block info of
 the 8192 x 8192 runtime mask from bytes and from packed bits.
 
@@ -59,6 +61,7 @@ def parse_args():
     p.add_argument("--skip-decode", action="store_true")
     p.add_argument("--skip-mask-info", action="store_true")
     p.add_argument("--skip-backward", action="store_true")
+    p.add_argument("--skip-extra", action="store_true", help="skip the bias + block-mask and long-context timings")
     return p.parse_args()
 
 
@@ -324,6 +327,61 @@ def main():
         result["mask_info"] = {"workload": "bias_block_mask mask, 1 x 1 x 8192 x 8192, 128 x 128 blocks",
                                "n_partial": int(infos["u8"]["n_partial"]), "u1_equals_u8": bool(same), **mi}
         del mu8, mu1
+        torch.cuda.empty_cache()
+
+    # ---- bias + block-sparse mask (B2 H16 D64 L8192) and the long-context chunk ------------
+    # bias + mask: ALiBi bias [1][16][8192][8192] bf16 (2 GiB) and the runtime mask through its
+    # block info; algorithmic work counts the non-empty 128 x 128 blocks (4 * D flops per pair of
+    # such a block), and the bias bytes of those blocks read once. Long context: B1, 32 query
+    # heads over 8 K/V heads, 2048 queries at offset 129024 over 131072 keys, causal; exact pairs.
+    if not args.skip_extra:
+        w4 = workloads.bias_block_mask()
+        B4_, Lq4, _, Hq4, _, D4, _ = w4.shape
+        q4, k4, v4 = (sa.from_numpy(getattr(w4, n), "bf16") for n in ("q", "k", "v"))
+        bias4 = sa.from_numpy(w4.bias, "bf16")
+        info4 = sa.build_block_mask_info(sa.from_numpy(w4.mask, "u8"), 128, 128)
+        nonempty = int(np.count_nonzero(info4.to_numpy()["block_mask"]))
+        out4 = torch.empty((B4_, Lq4, Hq4, D4), dtype=torch.bfloat16, device="cuda")
+        st4 = lambda: sa.sdpa(q4, k4, v4, bias4, None, mask_info=info4, scale=w4.scale, out=out4)
+        n4 = max(2, args.steps // 5)
+        t4, _ = time_steps(st4, n4, max(2, args.warmup // 10), stream)
+        fl4 = float(nonempty) * B4_ * Hq4 * 4.0 * 128 * 128 * D4
+        bias_bytes = float(nonempty) * Hq4 * 128 * 128 * 2
+        per4 = t4 / n4
+        result["bias_block_mask"] = {
+            "metric": "attention TFLOP/s over non-empty blocks", "value": round(fl4 / per4 / 1e12, 2),
+            "unit": "TFLOP/s", "ms_per_step": round(per4 * 1e3, 4), "steps": n4,
+            "config": {"workload": "bias_block_mask", "batch": B4_, "heads": Hq4, "head_dim": D4, "q_len": Lq4,
+                       "bias": "ALiBi bf16 [1][16][8192][8192]", "mask_blocks_nonempty": nonempty,
+                       "mask_blocks_total": int(info4.to_numpy()["block_mask"].size)},
+            "roofline": {"bound": "mixed: MFMA and the bias stream", "mfma_frac": round(fl4 / per4 / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "bias_GB_per_s": round(bias_bytes / per4 / 1e9, 1),
+                         "bias_frac_of_hbm": round(bias_bytes / per4 / 1e9 / PEAK_HBM_GBS, 4),
+                         "note": "bias bytes of the non-empty blocks counted once (the batch shares them)"},
+        }
+        del q4, k4, v4, bias4, info4, out4
+        torch.cuda.empty_cache()
+        w5 = workloads.chunked_prefill()
+        B5, Lq5, Lkv5, Hq5, Hkv5, D5, _ = w5.shape
+        q5, k5, v5 = (sa.from_numpy(getattr(w5, n), "bf16") for n in ("q", "k", "v"))
+        out5 = torch.empty((B5, Lq5, Hq5, D5), dtype=torch.bfloat16, device="cuda")
+        qo5 = int(w5.q_offset)
+        st5 = lambda: sa.sdpa(q5, k5, v5, is_causal=True, q_offset=qo5, scale=w5.scale, out=out5)
+        n5 = max(2, args.steps // 5)
+        t5, _ = time_steps(st5, n5, max(2, args.warmup // 10), stream)
+        pairs5 = float(Lq5) * qo5 + Lq5 * (Lq5 + 1) / 2
+        fl5 = 4.0 * D5 * pairs5 * Hq5 * B5
+        per5 = t5 / n5
+        result["chunked_prefill"] = {
+            "metric": "attention TFLOP/s (long-context chunk)", "value": round(fl5 / per5 / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(per5 * 1e3, 4), "steps": n5,
+            "config": {"workload": "chunked_prefill", "batch": B5, "q_heads": Hq5, "kv_heads": Hkv5, "head_dim": D5,
+                       "q_len": Lq5, "kv_len": Lkv5, "q_offset": qo5, "is_causal": True},
+            "roofline": {"bound": "mfma", "achieved": round(fl5 / per5 / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(fl5 / per5 / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "flops_per_launch": fl5},
+        }
+        del q5, k5, v5, out5
         torch.cuda.empty_cache()
 
     # ---- CPU baseline (rank 0, N = 1 only) ------------------------------------------------
