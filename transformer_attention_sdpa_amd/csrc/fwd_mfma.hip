@@ -354,8 +354,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     if (k0 < k_end_w) {
       // -- element masking, only on tiles that need it --------------------------------------
       // lane (ql, hh) holds, in s_cur[kb][e], the key k0 + 32*kb + 16*hh + e of query i_me
-      bool need_mask = (k0 + BN > nkv) || (causal && (int64_t)k0 + BN - 1 > off + wave_first) ||
-                       (MASK == MASK_DENSE);
+      // edge: some key of the tile lies past kv_lengths or past the causal limit of the wave's
+      // first row (wave-uniform)
+      const bool edge = (k0 + BN > nkv) || (causal && (int64_t)k0 + BN - 1 > off + wave_first);
+      bool need_mask = edge || (MASK == MASK_DENSE);
       int blk_cls = 2;
       int64_t blk_id = 0;
       if constexpr (MASK == MASK_INFO) {
@@ -451,12 +453,23 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
               }
             }
           }
-          const int64_t lim = causal ? off + i_me : (int64_t)INT32_MAX;
+          if (edge) {
+            const int64_t lim = causal ? off + i_me : (int64_t)INT32_MAX;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int j = jb + e;
-            const bool ok = (j < nkv) && ((int64_t)j <= lim) && ((bits >> e) & 1u);
-            s_cur[kb][e] = ok ? s_cur[kb][e] : -INFINITY;
+            for (int e = 0; e < 16; ++e) {
+              const int j = jb + e;
+              const bool ok = (j < nkv) && ((int64_t)j <= lim) && ((bits >> e) & 1u);
+              s_cur[kb][e] = ok ? s_cur[kb][e] : -INFINITY;
+            }
+          } else {
+            // inside kv_lengths and the causal limit: only the mask bit decides. Bit e
+            // sign-extended is all ones (keep the score) or zero (take -inf), one bit select
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const uint32_t keep = (uint32_t)((int32_t)(bits << (31 - e)) >> 31);
+              const uint32_t x = __float_as_uint(s_cur[kb][e]);
+              s_cur[kb][e] = __uint_as_float((x & keep) | (0xff800000u & ~keep));
+            }
           }
         }
       }
