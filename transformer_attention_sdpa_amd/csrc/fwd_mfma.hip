@@ -37,7 +37,9 @@
 //   the arithmetic (0 * NaN would).
 // * Grid: every XCD (the hardware deals consecutive workgroups round-robin over the 8 XCDs; each
 //   has its own L2) gets a contiguous set of heads. Non-causal launches run one head's tiles
-//   back to back (K/V reuse in L2); causal launches run longest tile first across all heads.
+//   back to back (K/V reuse in L2), or, with a bias broadcast over the batch, the batches of one
+//   head and tile back to back (bias reuse in L2); causal launches run longest tile first
+//   across all heads.
 #include <type_traits>
 
 #include "mfma_common.h"
@@ -77,7 +79,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int SPT = BN * CPR / NT; // direct-load instructions per thread per tile (K or V)
   constexpr int TILE = BN * D;       // elements of one K or V tile in LDS
-  constexpr bool FUSED = (BIAS == BIAS_NONE) && !NORM;   // logits = scale*log2e * q.k only
+  // FUSED: scale*log2e is folded into Q and each S MFMA chain starts from -m_run (plus
+  // log2e*bias for a bf16 bias at D = 64, FBIAS), so a probability is one exp2 of the
+  // accumulator. Otherwise the logits are scaled (and biased) per element.
+  constexpr bool FBIAS = BIAS == BIAS_BF16 && D == 64 && !NORM;
+  constexpr bool FUSED = (BIAS == BIAS_NONE || FBIAS) && !NORM;
   // Four statically distinct tile buffers, so that the compiler's wait-count tracking can tell a
   // read of one from a direct load in flight into another.
   __shared__ __align__(16) uint16_t kbuf0[TILE], kbuf1[TILE], vbuf0[TILE], vbuf1[TILE];
@@ -93,6 +99,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   // concurrently running workgroups of an XCD share few K/V heads. order 1 (rank-major, for
   // causal launches): all heads' heaviest tiles first, then the next rank -- longest work first
   // across the whole launch, so no heavy tile starts at the end and leaves the chip idle.
+  // order 2: order 0 with the batch innermost (a bias shared by the batches).
   // PACKED: workgroup Hq * i + h takes query tile i of the segments (seg_locate) for head h,
   // and the segment is then a batch of one.
   AttnArgs a = args;
@@ -119,8 +126,16 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       const int per = gridDim.x >> 3;
       n = (n & 7) * per + (n >> 3);
     }
-    qt = n_qt - 1 - (n % n_qt);
-    bh = n / n_qt;
+    if (order == 2) {
+      // batch innermost: the batches' workgroups of one (head, query tile) run back to back on
+      // one XCD, so a bias shared by the batches is read from HBM once and then from L2
+      const int bb = n % a.B, r = n / a.B;
+      qt = n_qt - 1 - (r % n_qt);
+      bh = bb * a.Hq + r / n_qt;
+    } else {
+      qt = n_qt - 1 - (n % n_qt);
+      bh = n / n_qt;
+    }
   }
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
@@ -147,23 +162,42 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   // tiles to visit: all tiles below k_end, or the non-empty blocks of the mask info
   int n_tiles = 0, csr_begin = 0, sub_per_blk = 1;
   int64_t info_row = 0;
+  // MASK_INFO: lane l holds entry l of the row's CSR (its kv block and that block's class), so
+  // the tile loop reads them with readlane instead of scalar loads, which would share their
+  // wait counter with the LDS reads. Entries from 64 on are loaded where they are used.
+  int dn_lane = 0, cls_lane = 0;
   if constexpr (MASK == MASK_INFO) {
     const int mb = a.bm_batch > 1 ? b : 0, mh = a.bm_heads > 1 ? h : 0;
     info_row = ((int64_t)mb * a.bm_heads + mh) * a.bm_nqb + qt;
     csr_begin = a.bm_row_ptr[info_row];
     const int csr_end = a.bm_row_ptr[info_row + 1];
     sub_per_blk = a.bm_bkv / BN;
-    int cnt = 0;
-    for (int e = csr_begin; e < csr_end; ++e) {
-      if ((int64_t)a.bm_data_next[e] * a.bm_bkv >= k_end) break;   // ascending: the rest lie past k_end
-      ++cnt;
+    const bool in_row = csr_begin + lane < csr_end;
+    if (in_row) {
+      dn_lane = a.bm_data_next[csr_begin + lane];
+      cls_lane = a.bm_class[info_row * a.bm_nkb + dn_lane];
+    }
+    // the entries are ascending: those below k_end are a prefix
+    int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(in_row && (int64_t)dn_lane * a.bm_bkv < k_end));
+    if (cnt == 64) {
+      for (int e = csr_begin + 64; e < csr_end; ++e) {
+        if ((int64_t)a.bm_data_next[e] * a.bm_bkv >= k_end) break;
+        ++cnt;
+      }
     }
     n_tiles = cnt * sub_per_blk;
   } else {
     n_tiles = (int)((k_end + BN - 1) / BN);
   }
+  // kv block of the idx-th non-empty block of the row, and its class (MASK_INFO)
+  auto blk_at = [&](int idx) -> int {
+    return idx < 64 ? __builtin_amdgcn_readlane(dn_lane, idx) : a.bm_data_next[csr_begin + idx];
+  };
+  auto cls_at = [&](int idx, int blk) -> int {
+    return idx < 64 ? __builtin_amdgcn_readlane(cls_lane, idx) : (int)a.bm_class[info_row * a.bm_nkb + blk];
+  };
   auto tile_k0 = [&](int t) -> int {
-    if constexpr (MASK == MASK_INFO) return a.bm_data_next[csr_begin + t / sub_per_blk] * a.bm_bkv + (t % sub_per_blk) * BN;
+    if constexpr (MASK == MASK_INFO) return blk_at(t / sub_per_blk) * a.bm_bkv + (t % sub_per_blk) * BN;
     else return t * BN;
   };
   // staging runs ahead of the last tile without branches: past the end it reloads the last tile
@@ -254,11 +288,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     return *reinterpret_cast<const bf16x8*>(ks + row * D + (((2 * c + hh) ^ k_swz<D>(row)) << 3));
   };
   // S^T = K Q^T for two 32-key blocks (two independent MFMA chains, interleaved)
-  auto compute_s = [&](const uint16_t* ks, f32x16 (&sacc)[2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+  auto compute_s = [&](const uint16_t* ks, f32x16 (&sacc)[2]) {   // sacc holds the start values
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
 #pragma unroll
@@ -313,10 +343,63 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   const int64_t mask_row = (MASK == MASK_DENSE && i_me < a.Lq)
                                ? b * a.mask_sb + h * a.mask_sh + (int64_t)i_me * a.mask_sq : -1;
 
+  // ---- FBIAS: the bias of tile u as raw bf16, in register set u & 1, loaded two tiles ahead:
+  // the loads of tile t + 2 are issued as tile t starts and are used by the S(t+1) MFMAs of
+  // tile t + 1 (lane: query i_me, keys k0 + 32*kb + 16*hh + 0..15)
+  uint4 braw[2][2][2];                                   // [set][kb][8 keys]
+  auto load_bias = [&](int k0t, uint4 (&dst)[2][2]) {
+    if constexpr (FBIAS) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int jb = k0t + 32 * kb + 16 * hh;
+        if (bias_row >= 0 && a.bias_vec && jb + 16 <= a.Lkv) {
+          const uint4* bp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.bias) + bias_row + jb);
+          dst[kb][0] = bp[0];
+          dst[kb][1] = bp[1];
+        } else {
+          uint32_t w[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j0 = jb + 2 * e, j1 = j0 + 1;
+            const uint32_t lo = (bias_row >= 0 && j0 < a.Lkv)
+                                    ? static_cast<const uint16_t*>(a.bias)[bias_row + (int64_t)j0 * a.bias_sk] : 0u;
+            const uint32_t hi = (bias_row >= 0 && j1 < a.Lkv)
+                                    ? static_cast<const uint16_t*>(a.bias)[bias_row + (int64_t)j1 * a.bias_sk] : 0u;
+            w[e] = lo | (hi << 16);
+          }
+          dst[kb][0] = make_uint4(w[0], w[1], w[2], w[3]);
+          dst[kb][1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+      }
+    }
+  };
+  // start values of an S chain: log2e*bias - m (FBIAS), -m (other FUSED), 0
+  auto s_start = [&](const uint4 (&src)[2][2], float m, f32x16 (&c)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if constexpr (FBIAS) {
+        const uint32_t w[8] = {src[kb][0].x, src[kb][0].y, src[kb][0].z, src[kb][0].w,
+                               src[kb][1].x, src[kb][1].y, src[kb][1].z, src[kb][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          c[kb][2 * e] = fmaf(__uint_as_float(w[e] << 16), LOG2E, -m);
+          c[kb][2 * e + 1] = fmaf(__uint_as_float(w[e] & 0xffff0000u), LOG2E, -m);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) c[kb][e] = FUSED ? -m : 0.f;
+      }
+    }
+  };
+
   // ---- pipeline prologue: K0, V0, K1 in LDS; S(0) formed ----------------------------------
   // K(t) lives in buffer t & 1, V(t) in buffer t & 1; S(t) in s_even (FUSED: s_odd for odd t).
   f32x16 s_even[2], s_odd[2];
   if (n_tiles > 0) {
+    if constexpr (FBIAS) {
+      load_bias(tile_k0(0), braw[0]);
+      load_bias(tile_k0c(1), braw[1]);
+    }
     dma_k(tile_k0(0), kbuf0);
     dma_v(tile_k0(0), vbuf0);
     dma_k(tile_k0c(1), kbuf1);
@@ -327,7 +410,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     }
   }
   __syncthreads();
-  if (n_tiles > 0 && tile_k0(0) < k_end_w) compute_s(kbuf0, s_even);   // m_run = 0: from zero
+  if (n_tiles > 0 && tile_k0(0) < k_end_w) {            // m_run = 0: from zero (or the bias)
+    s_start(braw[0], 0.f, s_even);
+    compute_s(kbuf0, s_even);
+  }
   __syncthreads();                                       // K buffer 0 is refilled in iteration 0
 
   // ---- one tile; P = t & 1 fixes every buffer's role at compile time -----------------------
@@ -350,6 +436,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     dma_k(tile_k0c(t + 2), kfree);
     dma_v(tile_k0c(t + 1), vfree);
     load_krv(tile_k0c(t + 1));
+    if constexpr (FBIAS) {
+      if (t + 2 < n_tiles) load_bias(tile_k0(t + 2), braw[P]);   // set P held tile t's bias
+    }
     const int k0 = tile_k0(t);
     if (k0 < k_end_w) {
       // -- element masking, only on tiles that need it --------------------------------------
@@ -361,9 +450,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       int blk_cls = 2;
       int64_t blk_id = 0;
       if constexpr (MASK == MASK_INFO) {
-        const int kb_blk = a.bm_data_next[csr_begin + t / sub_per_blk];
+        const int kb_blk = blk_at(t / sub_per_blk);
         blk_id = info_row * a.bm_nkb + kb_blk;
-        blk_cls = a.bm_class[blk_id];
+        blk_cls = cls_at(t / sub_per_blk, kb_blk);
         if (blk_cls == 1) need_mask = true;
       }
       // logits in the exp2 domain. FUSED: s stays raw (the max is taken on raw scores, scaled
@@ -556,12 +645,18 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       bf16x8 kf[PF + 1][2];
       // the C operand that starts S(t+1): zero, or -m_run broadcast (FUSED). Built here from an
       // opaque copy of m_run, so that its 16 registers live only until the first two MFMAs.
-      f32x16 c0;
+      // FBIAS: one start vector per 32-key block (the bias of tile t + 1 is in set 1 - P);
+      // otherwise a single vector serves both blocks
+      f32x16 c0[FBIAS ? 2 : 1];
       {
-        float m0 = FUSED ? -m_run : 0.f;
+        float m0 = m_run;
         if constexpr (FUSED) asm volatile("" : "+v"(m0));
+        if constexpr (FBIAS) {
+          s_start(braw[1 - P], m0, c0);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) c0[e] = m0;
+          for (int e = 0; e < 16; ++e) c0[0][e] = FUSED ? -m0 : 0.f;
+        }
       }
 #pragma unroll
       for (int c = 0; c < PF; ++c) {
@@ -580,7 +675,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (c == 0) {
-            s_next[kb] = E::mfma(kf[0][kb], qB[0], c0);
+            s_next[kb] = E::mfma(kf[0][kb], qB[0], c0[FBIAS ? kb : 0]);
           } else {
             s_next[kb] = E::mfma(kf[c % (PF + 1)][kb], qB[c], s_next[kb]);
           }
@@ -668,7 +763,9 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   }
   const int n_qt = (a.Lq + BM - 1) / BM;
   const int64_t nwg = (int64_t)n_qt * a.Hq * a.B;
-  const int order = a.causal != SDPA_CAUSAL_NONE ? 1 : 0;
+  // causal: longest tiles first across heads; a bias broadcast over several batches: batch
+  // innermost (L2 sharing of the bias); otherwise one head's tiles back to back
+  const int order = a.causal != SDPA_CAUSAL_NONE ? 1 : ((a.bias && a.bias_sb == 0 && a.B > 1) ? 2 : 0);
   const int remap = order == 1 ? ((a.Hq * a.B) % 8 == 0 ? 1 : 0) : (nwg % 8) == 0 ? 1 : 0;
   hipLaunchKernelGGL((fwd_mfma_kernel<D, BIAS, MASK, NORM, F16, false>), dim3((unsigned)nwg), dim3(NT), 0, s, a, n_qt,
                      remap, order);
