@@ -221,3 +221,15 @@ def test_f16_bias_and_f16_output(lib, D):
     out = run_gpu(w2, out_dtype=torch.float16)
     assert out.dtype == torch.float16
     assert_close(out.float().cpu().numpy(), run_oracle(w2), "f16", "f16 out")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("bias_shape", [(2, 4, 130, 150), (1, 4, 130, 150), (2, 1, 1, 150)])
+def test_bf16_bias_fused_path_d64(lib, dtype, bias_shape):
+    # a bf16 bias at head dim 64 enters the q.k MFMAs as their start value; 150 keys leave a
+    # ragged 6-key tail whose bias is loaded element by element; with block info as well
+    w = workloads.random_attention(4100 + bias_shape[0] + bias_shape[2], 2, 130, 150, 4, 2, 64, dtype=dtype,
+                                   bias_shape=bias_shape, bias_dtype="bf16", mask_shape=(1, 1, 130, 150))
+    say(f"bf16 bias fused D=64 {dtype} {bias_shape}")
+    assert_close(run_gpu(w).cpu().numpy(), run_oracle(w), dtype, "bias dense mask")
+    assert_close(run_gpu(w, use_mask_info=True, bq=128, bkv=64).cpu().numpy(), run_oracle(w), dtype, "bias info")
