@@ -53,11 +53,11 @@ __device__ __forceinline__ int bswz(int row) {
 }
 
 // Tile loader and readers for ST x D tiles of 16-bit elements in LDS.
-template <int D, bool F16, int ST>
+template <int D, bool F16, int ST, int NTH = NTB>
 struct Tiles {
   using x8 = typename In<F16>::x8;
   static constexpr int CPR = D / 8;                 // chunks per row
-  static constexpr int SPT = ST * CPR / NTB;        // direct-load instructions per thread
+  static constexpr int SPT = ST * CPR / NTH;        // direct-load instructions per thread
   static constexpr int DB = D / 32;
   int doff[SPT];                                    // per-thread source offsets (row bytes applied)
   int nrow, nsw;                                    // permuted A-operand row of this lane, its swizzle
@@ -66,7 +66,7 @@ struct Tiles {
   __device__ void init(int row_bytes, int lane, int tid) {
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
-      const int sl = NTB * u + tid, row = sl / CPR, pos = sl % CPR;
+      const int sl = NTH * u + tid, row = sl / CPR, pos = sl % CPR;
       doff[u] = row * row_bytes + (pos ^ bswz<D>(row)) * 16;
     }
     nrow = perm32(lane & 31);
@@ -86,7 +86,7 @@ struct Tiles {
                        uint16_t* dst, int wave) const {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)r0 * row_elems, (int64_t)(valid - r0) * row_bytes);
 #pragma unroll
-    for (int u = 0; u < SPT; ++u) dma16(r, dst + 8 * (NTB * u + 64 * wave), doff[u]);
+    for (int u = 0; u < SPT; ++u) dma16(r, dst + 8 * (NTH * u + 64 * wave), doff[u]);
   }
   // A operand: 32-row block rb, head-dim chunk c (16 elements), rows in perm32 order
   __device__ x8 arow(const uint16_t* t, int rb, int c, int hh) const {
@@ -388,6 +388,210 @@ void bwd_dkdv_mfma_kernel(BwdArgs g, int remap) {
     }
 }
 
+// ============================ dK / dV, two waves per SIMD ======================================
+// The same products as bwd_dkdv_mfma_kernel with eight waves: waves w and w + 4 own the same 32
+// keys and take the two 32-query blocks of each 64-query tile, so each holds only its
+// accumulators and the S/dP pair, and two waves share every SIMD. K and V stay in LDS for the
+// whole kernel (rows swizzled by kvswz for the B-operand reads, 16 consecutive rows per read)
+// instead of in registers. At the end the two waves of a key block add their partial dK/dV
+// through LDS.
+constexpr int NT8 = 512;
+constexpr int QT8 = 64;
+
+// chunk swizzle of the K/V rows read as B operands (16 consecutive rows, one chunk each)
+template <int D>
+__device__ __forceinline__ int kvswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+
+template <int D, bool F16>
+__global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap) {
+  using E = In<F16>;
+  using x8 = typename E::x8;
+  constexpr int DC = D / 16, DB = D / 32, CPR = D / 8, TILE = QT8 * D;
+  constexpr int KVSPT = RB * CPR / NT8;              // direct loads per thread for K (and V)
+  __shared__ __align__(16) uint16_t kbuf[RB * D], vbuf[RB * D];
+  __shared__ __align__(16) uint16_t qbuf0[TILE], qbuf1[TILE], obuf0[TILE], obuf1[TILE];
+  __shared__ __align__(16) float stat[2][2][QT8];    // [buffer][lse / scale, D][query]
+  const AttnArgs& a = g.a;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 3, qp = wave >> 2;           // key block, query block of each tile
+  const int ql = lane & 31, hh = lane >> 5;
+
+  int kt, bg;
+  wg_map(blockIdx.x, a.Hkv * a.B, remap, kt, bg);
+  const int gk = bg % a.Hkv, b = bg / a.Hkv;
+  const int grp = a.Hq / a.Hkv;
+  const int k0 = kt * RB, wk0 = k0 + 32 * kw, key_me = wk0 + ql;
+  const int nkv = batch_kv_len(a, b), nq = batch_q_len(a, b);
+  const int64_t off = batch_causal_offset(a, b);
+  const bool causal = a.causal != SDPA_CAUSAL_NONE;
+  const float c2 = a.scale * LOG2E;
+
+  int64_t i_lo = causal ? (int64_t)k0 - off : 0;
+  i_lo = i_lo < 0 ? 0 : i_lo;
+  const int n_qt = (nq + QT8 - 1) / QT8;
+  const int qt0 = (k0 < nkv && i_lo < nq) ? (int)(i_lo / QT8) : n_qt;
+  const int per_head = n_qt - qt0;
+  const int n_it = per_head * grp;
+  const int64_t wi_lo = causal ? (int64_t)wk0 - off : INT64_MIN / 2;
+  const bool wave_live = wk0 < nkv;
+
+  // K and V of the workgroup's 128 keys into LDS once (keys past kv_lengths as zeros)
+  {
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + gk * a.k_sh + (int64_t)k0 * a.k_ss;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + gk * a.v_sh + (int64_t)k0 * a.v_ss;
+    const int kbytes = (int)(a.k_ss * 2), vbytes = (int)(a.v_ss * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, (int64_t)(nkv - k0) * kbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, (int64_t)(nkv - k0) * vbytes);
+#pragma unroll
+    for (int u = 0; u < KVSPT; ++u) {
+      const int sl = NT8 * u + tid, row = sl / CPR, pos = sl % CPR;
+      const int c = pos ^ kvswz<D>(row);
+      dma16(rk, kbuf + 8 * (NT8 * u + 64 * wave), row * kbytes + c * 16);
+      dma16(rv, vbuf + 8 * (NT8 * u + 64 * wave), row * vbytes + c * 16);
+    }
+  }
+  // B operand from the K or V rows of this wave's keys: key column ql, head-dim chunk c
+  const int kvrow = 32 * kw + ql, kvsw = kvswz<D>(kvrow);
+  auto bkv = [&](const uint16_t* t, int c) -> x8 {
+    return *reinterpret_cast<const x8*>(t + kvrow * D + (((2 * c + hh) ^ kvsw) << 3));
+  };
+
+  Tiles<D, F16, QT8, NT8> tq, to;
+  tq.init((int)(a.q_ss * 2), lane, tid);
+  to.init((int)(g.do_ss * 2), lane, tid);
+  auto it_head = [&](int it) { return gk * grp + it / per_head; };
+  auto it_q0 = [&](int it) { return (qt0 + it % per_head) * QT8; };
+  auto load_tiles = [&](int it, uint16_t* qd, uint16_t* od) {
+    const int h = it_head(it), i0 = it_q0(it);
+    tq.load(static_cast<const uint16_t*>(a.q) + b * a.q_sb + h * a.q_sh, a.q_ss, i0, a.Lq, (int)(a.q_ss * 2), qd, wave);
+    to.load(static_cast<const uint16_t*>(g.dout) + b * g.do_sb + h * g.do_sh, g.do_ss, i0, a.Lq, (int)(g.do_ss * 2),
+            od, wave);
+  };
+  // statistics of the tile's queries: thread t < 64 takes lse / scale of query t, 64 <= t < 128 its D
+  auto load_stat = [&](int it) -> float {
+    if (tid >= 2 * QT8) return 0.f;
+    const int h = it_head(it), i = it_q0(it) + (tid & (QT8 - 1));
+    const int64_t row = ((int64_t)b * a.Hq + h) * a.Lq + i;
+    if (tid < QT8) return i < nq ? g.w_lse[row] / a.scale : INFINITY;   // +inf: weight 0 (scale > 0)
+    return i < nq ? g.w_dsum[row] : 0.f;
+  };
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dk[d][e] = dv[d][e] = 0.f;
+
+  if (n_it > 0) {
+    load_tiles(0, qbuf0, obuf0);
+    const float st0 = load_stat(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (tid < 2 * QT8) stat[0][tid / QT8][tid & (QT8 - 1)] = st0;
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+
+  auto iter = [&](auto PAR_, int it) {
+    constexpr int P = decltype(PAR_)::value;
+    const uint16_t* qs = P ? qbuf1 : qbuf0;
+    const uint16_t* os = P ? obuf1 : obuf0;
+    float st_next = 0.f;
+    if (it + 1 < n_it) {
+      load_tiles(it + 1, P ? qbuf0 : qbuf1, P ? obuf0 : obuf1);
+      st_next = load_stat(it + 1);
+    }
+    const int i0 = it_q0(it);
+    // this wave's block: queries i0 + 32 * qp .. + 31 against keys wk0 .. wk0 + 31
+    if (wave_live && (int64_t)i0 + 32 * qp + 31 >= wi_lo) {
+      const float* st = &stat[P][0][0];
+      f32x16 s, dp;
+      const float4* ls = reinterpret_cast<const float4*>(st + 32 * qp + 16 * hh);
+      const float4* ds = reinterpret_cast<const float4*>(st + QT8 + 32 * qp + 16 * hh);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 l4 = ls[i], d4 = ds[i];
+        s[4 * i] = -l4.x; s[4 * i + 1] = -l4.y; s[4 * i + 2] = -l4.z; s[4 * i + 3] = -l4.w;
+        dp[4 * i] = -d4.x; dp[4 * i + 1] = -d4.y; dp[4 * i + 2] = -d4.z; dp[4 * i + 3] = -d4.w;
+      }
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        s = E::mfma(tq.arow(qs, qp, c, hh), bkv(kbuf, c), s);
+        dp = E::mfma(to.arow(os, qp, c, hh), bkv(vbuf, c), dp);
+      }
+      int e_min = 0;                                  // entries below: before this key's causal limit
+      if (causal) {
+        const int64_t m = (int64_t)key_me - off - (i0 + 32 * qp + 16 * hh);
+        e_min = m < 0 ? 0 : (m > 16 ? 16 : (int)m);
+      }
+      if (key_me >= nkv) e_min = 16;
+      float pv[16], sv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float x = s[e] * c2;
+        const float p = __builtin_amdgcn_exp2f(e >= e_min ? x : -INFINITY);
+        pv[e] = p;
+        sv[e] = p * dp[e];
+      }
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        const x8 pB = pack8<F16>(pv + 8 * sh), sB = pack8<F16>(sv + 8 * sh);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          dv[d] = E::mfma(to.atr(os, qp, sh, d), pB, dv[d]);
+          dk[d] = E::mfma(tq.atr(qs, qp, sh, d), sB, dk[d]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (it + 1 < n_it && tid < 2 * QT8) stat[1 - P][tid / QT8][tid & (QT8 - 1)] = st_next;
+    __syncthreads();
+  };
+  std::integral_constant<int, 0> I0;
+  std::integral_constant<int, 1> I1;
+  for (int it = 0; it < n_it; it += 2) {
+    iter(I0, it);
+    if (it + 1 >= n_it) break;
+    iter(I1, it + 1);
+  }
+
+  // the two waves of a key block add their partial sums: the second wave writes dV (then dK)
+  // to LDS, lane-contiguous, and the first adds it to its own. Key blocks 0-1 use kbuf, 2-3 vbuf
+  // (every read of K and V ended at the last barrier of the loop).
+  float* xb = reinterpret_cast<float*>(kw < 2 ? kbuf : vbuf) + (kw & 1) * (DB * 16 * 64);
+  auto merge = [&](f32x16 (&acc)[DB]) {
+    if (qp == 1) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xb[(d * 16 + e) * 64 + lane] = acc[d][e];
+    }
+    __syncthreads();
+    if (qp == 0) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[d][e] += xb[(d * 16 + e) * 64 + lane];
+    }
+    __syncthreads();
+  };
+  merge(dv);
+  merge(dk);
+  if (qp == 1 || key_me >= a.Lkv) return;
+  const int64_t kr = b * g.dk_sb + (int64_t)key_me * g.dk_ss + gk * g.dk_sh;
+  const int64_t vr = b * g.dv_sb + (int64_t)key_me * g.dv_ss + gk * g.dv_sh;
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = 32 * d + 8 * i + 4 * hh;
+      store4(g.dk, kr + col, g.dk_dtype, dk[d][4 * i] * a.scale, dk[d][4 * i + 1] * a.scale,
+             dk[d][4 * i + 2] * a.scale, dk[d][4 * i + 3] * a.scale);
+      store4(g.dv, vr + col, g.dv_dtype, dv[d][4 * i], dv[d][4 * i + 1], dv[d][4 * i + 2], dv[d][4 * i + 3]);
+    }
+}
+
 // ================================ dQ =========================================================
 template <int D, bool F16>
 __global__ __launch_bounds__(NTB, 1) void bwd_dq_mfma_kernel(BwdArgs g, int n_qt, int remap) {
@@ -574,8 +778,24 @@ bool bwd_mfma_supports(const BwdArgs& g) {
   return n1 < (int64_t)INT32_MAX && n2 < (int64_t)INT32_MAX;
 }
 
+template <int D, bool F16>
+hipError_t launch_dkdv8_t(const BwdArgs& g, hipStream_t s) {
+  const AttnArgs& a = g.a;
+  const int n_kt = (a.Lkv + RB - 1) / RB;
+  const int HB = a.Hkv * a.B;
+  hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16>), dim3((unsigned)((int64_t)n_kt * HB)), dim3(NT8), 0, s, g,
+                     HB % 8 == 0 ? 1 : 0);
+  return hipGetLastError();
+}
+
+int kDkdvEightWaves = 1;
+
 hipError_t launch_bwd_mfma_dkdv(const BwdArgs& g, hipStream_t s) {
   const bool f16 = g.a.in_dtype == SDPA_F16;
+  if (kDkdvEightWaves) {
+    if (g.a.D == 128) return f16 ? launch_dkdv8_t<128, true>(g, s) : launch_dkdv8_t<128, false>(g, s);
+    return f16 ? launch_dkdv8_t<64, true>(g, s) : launch_dkdv8_t<64, false>(g, s);
+  }
   if (g.a.D == 128) return f16 ? launch_dkdv_t<128, true>(g, s) : launch_dkdv_t<128, false>(g, s);
   return f16 ? launch_dkdv_t<64, true>(g, s) : launch_dkdv_t<64, false>(g, s);
 }
