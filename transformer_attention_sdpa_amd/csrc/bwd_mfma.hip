@@ -6,15 +6,17 @@
 // Both passes use v_mfma_f32_32x32x16 with one operand kept in registers for the whole loop
 // and the other streamed through LDS, and they are mirror images of each other:
 //
-// * dK/dV: a workgroup owns 128 keys of one K/V head (32 per wave, K and V in registers as B
-//   operands) and streams tiles of 128 queries of every query head of the group. Per 32-query
-//   block a wave forms S = Q K^T - lse/scale and dP = dO V^T - D, the row statistics being the
-//   MFMAs' starting values. Its lanes then hold one key column each, with 16 consecutive
-//   queries per lane half, because the A-operand rows of Q and dO are read in the permuted
-//   order perm32. Next P = exp2(scale * log2 e * S) and dS = P dP. Finally P and dS are packed
-//   to 16 bits and feed dV^T += dO^T P and dK^T += Q^T dS directly as B operands; dO^T and Q^T
-//   come from transposed LDS reads (ds_read_b64_tr_b16). One wave per SIMD fits, so the
-//   instruction order is set by hand (see the block steps).
+// * dK/dV: a workgroup of 8 waves owns 128 keys of one K/V head; K and V sit in LDS for the
+//   whole kernel and are read as B operands. Waves w and w + 4 own the same 32 keys and take
+//   the two 32-query blocks of each 64-query tile streamed from every query head of the group,
+//   so each wave holds only its own accumulators and two waves share every SIMD. Per block a
+//   wave forms S = Q K^T - lse/scale and dP = dO V^T - D, the row statistics being the MFMAs'
+//   starting values. Its lanes then hold one key column each, with 16 consecutive queries per
+//   lane half, because the A-operand rows of Q and dO are read in the permuted order perm32.
+//   Next P = exp2(scale * log2 e * S) and dS = P dP. Finally P and dS are packed to 16 bits and
+//   feed dV^T += dO^T P and dK^T += Q^T dS directly as B operands; dO^T and Q^T come from
+//   transposed LDS reads (ds_read_b64_tr_b16). The two waves of a key block add their sums
+//   through LDS at the end.
 // * dQ: a workgroup owns 128 queries of one head (Q and dO in registers) and streams tiles of 64
 //   keys. S^T = K Q^T and dP^T = V dO^T leave each lane one query column and 16 consecutive
 //   keys per lane half; dS^T feeds dQ^T += K^T dS^T, with K^T read transposed. The lane also
@@ -37,7 +39,6 @@ namespace {
 constexpr int NTB = 256;          // threads per workgroup (4 waves)
 constexpr int RB = 128;           // rows a workgroup owns: keys (dK/dV) or queries (dQ)
 constexpr int ST = 64;            // keys per streamed tile of the dQ pass
-constexpr int QT_KV = 128;        // queries per streamed tile of the dK/dV pass
 
 // MFMA row r of a 32-row A operand reads tile row perm32(r): accumulator entry 4*i + j of lane
 // half h (MFMA row 8*i + 4*h + j) then belongs to tile row 16*h + 4*i + j.
@@ -141,260 +142,11 @@ __device__ __forceinline__ void store4(void* base, int64_t off, int dtype, float
 }
 
 // ================================ dK / dV ====================================================
-template <int D, bool F16>
-__global__ __launch_bounds__(NTB, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_mfma_kernel(BwdArgs g, int remap) {
-  using E = In<F16>;
-  using x8 = typename E::x8;
-  constexpr int DC = D / 16, DB = D / 32, TILE = QT_KV * D;
-  constexpr int ST = QT_KV, QB = ST / 32;
-  __shared__ __align__(16) uint16_t qbuf0[TILE], qbuf1[TILE], obuf0[TILE], obuf1[TILE];
-  __shared__ __align__(16) float stat[2][2][ST];      // [buffer][lse / scale, D][query]
-  const AttnArgs& a = g.a;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ql = lane & 31, hh = lane >> 5;
-
-  int kt, bg;
-  wg_map(blockIdx.x, a.Hkv * a.B, remap, kt, bg);
-  const int gk = bg % a.Hkv, b = bg / a.Hkv;
-  const int grp = a.Hq / a.Hkv;
-  const int k0 = kt * RB, wk0 = k0 + 32 * wave, key_me = wk0 + ql;
-  const int nkv = batch_kv_len(a, b), nq = batch_q_len(a, b);
-  const int64_t off = batch_causal_offset(a, b);
-  const bool causal = a.causal != SDPA_CAUSAL_NONE;
-  const float c2 = a.scale * LOG2E;
-
-  // queries that may attend a key of this workgroup: i >= k0 - off under the causal rule
-  int64_t i_lo = causal ? (int64_t)k0 - off : 0;
-  i_lo = i_lo < 0 ? 0 : i_lo;
-  const int n_qt = (nq + ST - 1) / ST;
-  const int qt0 = (k0 < nkv && i_lo < nq) ? (int)(i_lo / ST) : n_qt;
-  const int per_head = n_qt - qt0;
-  const int n_it = per_head * grp;
-  // this wave: queries i >= wk0 - off matter, keys from wk0 must lie below nkv
-  const int64_t wi_lo = causal ? (int64_t)wk0 - off : INT64_MIN / 2;
-  const bool wave_live = wk0 < nkv;
-
-  // K and V of this lane's key as B operands (keys past kv_lengths as zeros)
-  x8 kB[DC], vB[DC];
-  {
-    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + gk * a.k_sh;
-    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + gk * a.v_sh;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, (int64_t)nkv * a.k_ss * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, (int64_t)nkv * a.v_ss * 2);
-    const int ko = key_me * (int)(a.k_ss * 2) + 16 * hh, vo = key_me * (int)(a.v_ss * 2) + 16 * hh;
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      kB[c] = __builtin_bit_cast(x8, buf_load16(rk, ko + 32 * c));
-      vB[c] = __builtin_bit_cast(x8, buf_load16(rv, vo + 32 * c));
-    }
-  }
-
-  Tiles<D, F16, ST> tq, to;
-  tq.init((int)(a.q_ss * 2), lane, tid);
-  to.init((int)(g.do_ss * 2), lane, tid);
-  auto it_head = [&](int it) { return gk * grp + it / per_head; };
-  auto it_q0 = [&](int it) { return (qt0 + it % per_head) * ST; };
-  auto load_tiles = [&](int it, uint16_t* qd, uint16_t* od) {
-    const int h = it_head(it), i0 = it_q0(it);
-    tq.load(static_cast<const uint16_t*>(a.q) + b * a.q_sb + h * a.q_sh, a.q_ss, i0, a.Lq, (int)(a.q_ss * 2), qd, wave);
-    to.load(static_cast<const uint16_t*>(g.dout) + b * g.do_sb + h * g.do_sh, g.do_ss, i0, a.Lq, (int)(g.do_ss * 2),
-            od, wave);
-  };
-  // statistics of the tile's queries: thread t < 64 takes lse of query t, 64 <= t < 128 its D
-  auto load_stat = [&](int it) -> float {
-    if (tid >= 2 * ST) return 0.f;
-    const int h = it_head(it), i = it_q0(it) + (tid & (ST - 1));
-    const int64_t row = ((int64_t)b * a.Hq + h) * a.Lq + i;
-    if (tid < ST) return i < nq ? g.w_lse[row] / a.scale : INFINITY;   // +inf: weight 0 (scale > 0)
-    return i < nq ? g.w_dsum[row] : 0.f;
-  };
-
-  f32x16 dk[DB], dv[DB];
-#pragma unroll
-  for (int d = 0; d < DB; ++d)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) dk[d][e] = dv[d][e] = 0.f;
-
-  if (n_it > 0) {
-    load_tiles(0, qbuf0, obuf0);
-    const float st0 = load_stat(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    if (tid < 2 * ST) stat[0][tid / ST][tid & (ST - 1)] = st0;
-  }
-  __syncthreads();
-
-  // S = Q K^T - lse/scale and dP = dO V^T - D of 32-query block qb start from the row
-  // statistics (the MFMAs' C operands), so that a weight is one multiply and exp2 and dS one
-  // multiply
-  auto init_sdp = [&](const float* st, int qb, f32x16& s, f32x16& dp) {
-    const float4* ls = reinterpret_cast<const float4*>(st + 32 * qb + 16 * hh);
-    const float4* ds = reinterpret_cast<const float4*>(st + ST + 32 * qb + 16 * hh);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 l4 = ls[i], d4 = ds[i];
-      s[4 * i] = -l4.x; s[4 * i + 1] = -l4.y; s[4 * i + 2] = -l4.z; s[4 * i + 3] = -l4.w;
-      dp[4 * i] = -d4.x; dp[4 * i + 1] = -d4.y; dp[4 * i + 2] = -d4.z; dp[4 * i + 3] = -d4.w;
-    }
-  };
-  // One block step. The instruction order is fixed by scheduling barriers, because with one
-  // wave per SIMD nothing else hides latency: in step c the LDS operands of step c + 1 are
-  // requested, the two S/dP MFMAs of the next block (qb2 of the tile at qs2/os2) are issued
-  // with the operands requested one step earlier, and 16/DC weights of the current block are
-  // taken while those MFMAs run. Then the 16 dV/dK MFMAs of the current block follow, their
-  // transposed operands one step ahead. NEXT: a next block is formed; FIN: the current block
-  // is finished.
-  auto block = [&](auto NEXT_, auto FIN_, const uint16_t* qs, const uint16_t* os, int qb, int e_min,
-                   const uint16_t* qs2, const uint16_t* os2, const float* st2, int qb2,
-                   f32x16& sc, f32x16& dc, f32x16& sn, f32x16& dn) {
-    constexpr bool NEXT = decltype(NEXT_)::value;
-    constexpr bool FIN = decltype(FIN_)::value;
-    constexpr int EPS = 16 / DC;                    // weights taken per step
-    float pv[16], sv[16];
-    x8 aq, ao;
-    if constexpr (NEXT) {
-      init_sdp(st2, qb2, sn, dn);
-      aq = tq.arow(qs2, qb2, 0, hh);
-      ao = to.arow(os2, qb2, 0, hh);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      x8 aqn = aq, aon = ao;
-      if constexpr (NEXT) {
-        if (c + 1 < DC) {
-          aqn = tq.arow(qs2, qb2, c + 1, hh);
-          aon = to.arow(os2, qb2, c + 1, hh);
-        }
-        sn = E::mfma(aq, kB[c], sn);
-        dn = E::mfma(ao, vB[c], dn);
-      }
-      if constexpr (FIN) {
-#pragma unroll
-        for (int u = 0; u < EPS; ++u) {
-          const int e = EPS * c + u;
-          // masked entries get exponent -inf (weight 0): a select on the argument, not a branch
-          const float x = sc[e] * c2;
-          const float p = __builtin_amdgcn_exp2f(e >= e_min ? x : -INFINITY);
-          pv[e] = p;
-          sv[e] = p * dc[e];
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      aq = aqn;
-      ao = aon;
-    }
-    if constexpr (FIN) {
-      const x8 pB[2] = {pack8<F16>(pv), pack8<F16>(pv + 8)};
-      const x8 sB[2] = {pack8<F16>(sv), pack8<F16>(sv + 8)};
-      x8 to_c = to.atr(os, qb, 0, 0), tq_c = tq.atr(qs, qb, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int k = 0; k < 2 * DB; ++k) {
-        const int sh = k / DB, d = k % DB;
-        x8 to_n = to_c, tq_n = tq_c;
-        if (k + 1 < 2 * DB) {
-          to_n = to.atr(os, qb, (k + 1) / DB, (k + 1) % DB);
-          tq_n = tq.atr(qs, qb, (k + 1) / DB, (k + 1) % DB);
-        }
-        dv[d] = E::mfma(to_c, pB[sh], dv[d]);
-        dk[d] = E::mfma(tq_c, sB[sh], dk[d]);
-        __builtin_amdgcn_sched_barrier(0);
-        to_c = to_n;
-        tq_c = tq_n;
-      }
-    }
-  };
-  std::integral_constant<bool, false> NO;
-  std::integral_constant<bool, true> YES;
-  // the wave has work in tile it when some query of the tile may attend one of its keys
-  auto has_work = [&](int it) { return wave_live && (int64_t)it_q0(it) + ST - 1 >= wi_lo; };
-  auto e_min_of = [&](int i0, int qb) {              // entries below: before this key's causal limit
-    int e_min = 0;
-    if (causal) {
-      const int64_t m = (int64_t)key_me - off - (i0 + 32 * qb + 16 * hh);
-      e_min = m < 0 ? 0 : (m > 16 ? 16 : (int)m);
-    }
-    return key_me >= nkv ? 16 : e_min;
-  };
-  // S/dP of block 0 of the first tile (buffer 0); every later first block is formed during the
-  // last block of the tile before
-  f32x16 sa[2], dpa[2];
-  if (n_it > 0 && has_work(0)) {
-    init_sdp(&stat[0][0][0], 0, sa[0], dpa[0]);
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      sa[0] = E::mfma(tq.arow(qbuf0, 0, c, hh), kB[c], sa[0]);
-      dpa[0] = E::mfma(to.arow(obuf0, 0, c, hh), vB[c], dpa[0]);
-    }
-  }
-  // Tile it sits in buffer P = it & 1; tile it + 1 is loaded into the other buffer while blocks
-  // 0 .. QB-2 of tile it are worked. A barrier then makes tile it + 1 visible, and the last
-  // block of tile it is finished while block 0 of tile it + 1 is formed. A second barrier ends
-  // every read of buffer P before the next iteration refills it.
-  auto iter = [&](auto PAR_, int it) {
-    constexpr int P = decltype(PAR_)::value;
-    const uint16_t* qs = P ? qbuf1 : qbuf0;
-    const uint16_t* os = P ? obuf1 : obuf0;
-    uint16_t* qsn = P ? qbuf0 : qbuf1;
-    uint16_t* osn = P ? obuf0 : obuf1;
-    float st_next = 0.f;
-    if (it + 1 < n_it) {
-      load_tiles(it + 1, qsn, osn);
-      st_next = load_stat(it + 1);
-    }
-    const int i0 = it_q0(it);
-    const bool w_cur = has_work(it);
-    const float* st = &stat[P][0][0];
-    if (w_cur) {
-#pragma unroll
-      for (int qb = 0; qb + 1 < QB; ++qb)
-        block(YES, YES, qs, os, qb, e_min_of(i0, qb), qs, os, st, qb + 1, sa[qb & 1], dpa[qb & 1],
-              sa[(qb + 1) & 1], dpa[(qb + 1) & 1]);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    if (it + 1 < n_it && tid < 2 * ST) stat[1 - P][tid / ST][tid & (ST - 1)] = st_next;
-    __syncthreads();
-    const bool w_next = it + 1 < n_it && has_work(it + 1);
-    const float* stn = &stat[1 - P][0][0];
-    constexpr int L = QB - 1;
-    const int em = e_min_of(i0, L);
-    if (w_cur && w_next) block(YES, YES, qs, os, L, em, qsn, osn, stn, 0, sa[L & 1], dpa[L & 1], sa[0], dpa[0]);
-    else if (w_cur) block(NO, YES, qs, os, L, em, qsn, osn, stn, 0, sa[L & 1], dpa[L & 1], sa[0], dpa[0]);
-    else if (w_next) block(YES, NO, qs, os, L, em, qsn, osn, stn, 0, sa[L & 1], dpa[L & 1], sa[0], dpa[0]);
-    __syncthreads();
-  };
-  std::integral_constant<int, 0> I0;
-  std::integral_constant<int, 1> I1;
-  for (int it = 0; it < n_it; it += 2) {
-    iter(I0, it);
-    if (it + 1 >= n_it) break;
-    iter(I1, it + 1);
-  }
-
-  // epilogue: lane owns key key_me; entry 4*i + j of block d is head-dim column 32*d + 8*i + 4*hh + j
-  if (key_me >= a.Lkv) return;
-  const int64_t kr = b * g.dk_sb + (int64_t)key_me * g.dk_ss + gk * g.dk_sh;
-  const int64_t vr = b * g.dv_sb + (int64_t)key_me * g.dv_ss + gk * g.dv_sh;
-#pragma unroll
-  for (int d = 0; d < DB; ++d)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int col = 32 * d + 8 * i + 4 * hh;
-      store4(g.dk, kr + col, g.dk_dtype, dk[d][4 * i] * a.scale, dk[d][4 * i + 1] * a.scale,
-             dk[d][4 * i + 2] * a.scale, dk[d][4 * i + 3] * a.scale);
-      store4(g.dv, vr + col, g.dv_dtype, dv[d][4 * i], dv[d][4 * i + 1], dv[d][4 * i + 2], dv[d][4 * i + 3]);
-    }
-}
-
-// ============================ dK / dV, two waves per SIMD ======================================
-// The same products as bwd_dkdv_mfma_kernel with eight waves: waves w and w + 4 own the same 32
-// keys and take the two 32-query blocks of each 64-query tile, so each holds only its
-// accumulators and the S/dP pair, and two waves share every SIMD. K and V stay in LDS for the
-// whole kernel (rows swizzled by kvswz for the B-operand reads, 16 consecutive rows per read)
-// instead of in registers. At the end the two waves of a key block add their partial dK/dV
-// through LDS.
+// Eight waves: waves w and w + 4 own the same 32 keys and take the two 32-query blocks of each
+// 64-query tile, so each holds only its accumulators and the S/dP pair, and two waves share
+// every SIMD. K and V stay in LDS for the whole kernel (rows swizzled by kvswz for the B-operand
+// reads, 16 consecutive rows per read). At the end the two waves of a key block add their
+// partial dK/dV through LDS.
 constexpr int NT8 = 512;
 constexpr int QT8 = 64;
 
@@ -737,16 +489,6 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dq_mfma_kernel(BwdArgs g, int n_qt
 bool al(const void* p, int n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 template <int D, bool F16>
-hipError_t launch_dkdv_t(const BwdArgs& g, hipStream_t s) {
-  const AttnArgs& a = g.a;
-  const int n_kt = (a.Lkv + RB - 1) / RB;
-  const int HB = a.Hkv * a.B;
-  hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<D, F16>), dim3((unsigned)((int64_t)n_kt * HB)), dim3(NTB), 0, s, g,
-                     HB % 8 == 0 ? 1 : 0);
-  return hipGetLastError();
-}
-
-template <int D, bool F16>
 hipError_t launch_dq_t(const BwdArgs& g, hipStream_t s) {
   const AttnArgs& a = g.a;
   const int n_qt = (a.Lq + RB - 1) / RB;
@@ -788,16 +530,10 @@ hipError_t launch_dkdv8_t(const BwdArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-int kDkdvEightWaves = 1;
-
 hipError_t launch_bwd_mfma_dkdv(const BwdArgs& g, hipStream_t s) {
   const bool f16 = g.a.in_dtype == SDPA_F16;
-  if (kDkdvEightWaves) {
-    if (g.a.D == 128) return f16 ? launch_dkdv8_t<128, true>(g, s) : launch_dkdv8_t<128, false>(g, s);
-    return f16 ? launch_dkdv8_t<64, true>(g, s) : launch_dkdv8_t<64, false>(g, s);
-  }
-  if (g.a.D == 128) return f16 ? launch_dkdv_t<128, true>(g, s) : launch_dkdv_t<128, false>(g, s);
-  return f16 ? launch_dkdv_t<64, true>(g, s) : launch_dkdv_t<64, false>(g, s);
+  if (g.a.D == 128) return f16 ? launch_dkdv8_t<128, true>(g, s) : launch_dkdv8_t<128, false>(g, s);
+  return f16 ? launch_dkdv8_t<64, true>(g, s) : launch_dkdv8_t<64, false>(g, s);
 }
 
 hipError_t launch_bwd_mfma_dq(const BwdArgs& g, hipStream_t s) {
