@@ -433,11 +433,13 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     const uint16_t* const knext = P ? kbuf0 : kbuf1;
     uint16_t* const vfree = P ? vbuf0 : vbuf1;
     const uint16_t* const vcur = P ? vbuf1 : vbuf0;
-    dma_k(tile_k0c(t + 2), kfree);
-    dma_v(tile_k0c(t + 1), vfree);
-    load_krv(tile_k0c(t + 1));
+    // first keys of tiles t + 1 and t + 2 (with block info each is a CSR lookup): once each
+    const int k1 = tile_k0c(t + 1), k2 = tile_k0c(t + 2);
+    dma_k(k2, kfree);
+    dma_v(k1, vfree);
+    load_krv(k1);
     if constexpr (FBIAS) {
-      if (t + 2 < n_tiles) load_bias(tile_k0(t + 2), braw[P]);   // set P held tile t's bias
+      if (t + 2 < n_tiles) load_bias(k2, braw[P]);     // set P held tile t's bias
     }
     const int k0 = tile_k0(t);
     if (k0 < k_end_w) {
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       int blk_cls = 2;
       int64_t blk_id = 0;
       if constexpr (MASK == MASK_INFO) {
-        const int kb_blk = blk_at(t / sub_per_blk);
+        const int kb_blk = (k0 - (t % sub_per_blk) * BN) / a.bm_bkv;   // the block tile t lies in
         blk_id = info_row * a.bm_nkb + kb_blk;
         blk_cls = cls_at(t / sub_per_blk, kb_blk);
         if (blk_cls == 1) need_mask = true;
