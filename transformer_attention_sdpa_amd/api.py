@@ -143,14 +143,22 @@ class BlockMaskInfo:
         }
 
 
-def build_block_mask_info(mask: torch.Tensor, bq: int = 128, bkv: int = 128, stream=None) -> BlockMaskInfo:
-    """Block info of a runtime device mask [Mb][Mh][Lq][Lkv] (bool or uint8, or a PackedMask)."""
+def build_block_mask_info(mask: torch.Tensor, bq: int = 128, bkv: int = 128, stream=None,
+                          storage: torch.Tensor = None) -> BlockMaskInfo:
+    """Block info of a runtime device mask [Mb][Mh][Lq][Lkv] (bool or uint8, or a PackedMask).
+
+    ``storage``: a uint8 device tensor of at least sdpa_block_mask_info_bytes() to write into
+    (allocated here when None); the returned info points into it.
+    """
     lib = N.load()
     m = _mask_u8(mask)
     dm = _mask_desc(m)
     nbytes = ctypes.c_size_t()
     N.check(lib.sdpa_block_mask_info_bytes(ctypes.byref(dm), bq, bkv, ctypes.byref(nbytes)))
-    storage = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=mask.device)
+    if storage is None:
+        storage = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=mask.device)
+    elif storage.numel() < int(nbytes.value):
+        raise ValueError(f"storage needs {int(nbytes.value)} bytes")
     info = N.BlockMaskInfoC()
     s, sp = _stream(stream)
     N.check(lib.build_block_mask_info(ctypes.byref(dm), bq, bkv, ctypes.c_void_p(storage.data_ptr()),

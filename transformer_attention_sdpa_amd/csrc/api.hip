@@ -488,6 +488,10 @@ sdpa_status build_block_mask_info(const sdpa_tensor* mask, int32_t bq, int32_t b
   m.mask = static_cast<const uint8_t*>(mask->data);
   m.u1 = mask->dtype == SDPA_U1;
   m.sb = mask->strides[3]; m.sh = mask->strides[2]; m.sq = mask->strides[1]; m.sk = mask->dims[0] == 1 ? 0 : mask->strides[0];
+  // 16-byte loads of U8 rows: unit column stride, aligned base, and every row start aligned
+  m.vec16 = !m.u1 && m.sk == 1 && (reinterpret_cast<uintptr_t>(m.mask) & 15) == 0 &&
+            ((mask->dims[3] <= 1 || m.sb % 16 == 0) && (mask->dims[2] <= 1 || m.sh % 16 == 0) &&
+             (mask->dims[1] <= 1 || m.sq % 16 == 0));
   m.Mb = info->mask_batch; m.Mh = info->mask_heads; m.Lq = info->q_len; m.Lkv = info->kv_len;
   m.bq = bq; m.bkv = bkv; m.n_qb = info->n_qb; m.n_kb = info->n_kb;
   m.cls = info->block_mask; m.next = info->mask_next; m.row_ptr = info->row_ptr; m.data_next = info->data_next;

@@ -80,6 +80,7 @@ struct MaskInfoArgs {
   const uint8_t* mask;
   int64_t sb, sh, sq, sk;      // U1: sb/sh/sq in 32-bit words, sk 0 or 1 (bits)
   int u1;                      // 1: U1 bits, 0: U8 bytes
+  int vec16;                   // U8 rows allow 16-byte loads (aligned base and strides, unit column stride)
   int Mb, Mh, Lq, Lkv, bq, bkv, n_qb, n_kb;
   int8_t* cls;
   int32_t* next;

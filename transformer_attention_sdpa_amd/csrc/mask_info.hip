@@ -8,11 +8,14 @@
 // block is stored as bits.
 //
 // Three stream-ordered passes, all deterministic:
-//   1. classify: one workgroup per block counts the allowed in-range elements;
+//   1. classify: one workgroup per block counts the allowed in-range elements (16 mask bytes
+//      per load where the rows allow it);
 //   2. scan: one workgroup walks the blocks in flat order (mask batch, mask head, q-block,
-//      kv-block) with an exclusive scan, writing row_ptr, data_next, mask_next and n_partial;
-//   3. pack: one workgroup per partial block turns each row into bits with wave ballots and
-//      writes them at its compacted index.
+//      kv-block), 4 consecutive blocks per thread and round, with an exclusive scan, writing
+//      row_ptr, data_next, mask_next and n_partial;
+//   3. pack: one workgroup per partial block turns each row into bits (16 bytes to 16 bits per
+//      thread, or with wave ballots where rows do not allow 16-byte loads) and writes them at
+//      its compacted index.
 #include "device_common.h"
 
 namespace sdpa {
@@ -27,6 +30,15 @@ __device__ __forceinline__ void block_coords(const MaskInfoArgs& m, int64_t blk,
   hh = (int)(bh % m.Mh);
   bb = (int)(bh / m.Mh);
 }
+
+// U8 16-byte paths: a byte's high bit in ((x & 0x7f7f7f7f) + 0x7f7f7f7f) | x is set exactly
+// when the byte is nonzero.
+__device__ __forceinline__ uint32_t nonzero_bytes_hi(uint32_t x) {
+  return (((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u;
+}
+// the four byte flags of a word as a nibble (bit k = byte k nonzero): the multiply moves bit
+// 7 + 8k to bit 28 + k, and no other product lands in bits 28..31
+__device__ __forceinline__ uint32_t nonzero_nibble(uint32_t x) { return (nonzero_bytes_hi(x) * 0x00204081u) >> 28; }
 
 __global__ __launch_bounds__(256) void mask_classify_kernel(MaskInfoArgs m) {
   __shared__ int partial_counts[4];
@@ -49,6 +61,16 @@ __global__ __launch_bounds__(256) void mask_classify_kernel(MaskInfoArgs m) {
       uint32_t bits = w0[(int64_t)r * m.sq + w];
       if (tail && w == nw - 1) bits &= (1u << tail) - 1u;
       count += __builtin_popcount(bits);
+    }
+  } else if (m.vec16 && (nc & 15) == 0) {
+    // 16 bytes per load: rows of nc / 16 chunks
+    const int cpr = nc >> 4;
+    const uint8_t* b0 = m.mask + row0 + c0;
+    for (int e = threadIdx.x; e < nr * cpr; e += blockDim.x) {
+      const int r = e / cpr, ch = e - r * cpr;
+      const uint4 x = *reinterpret_cast<const uint4*>(b0 + (int64_t)r * m.sq + 16 * ch);
+      count += __builtin_popcount(nonzero_bytes_hi(x.x)) + __builtin_popcount(nonzero_bytes_hi(x.y)) +
+               __builtin_popcount(nonzero_bytes_hi(x.z)) + __builtin_popcount(nonzero_bytes_hi(x.w));
     }
   } else {
     for (int e = threadIdx.x; e < n; e += blockDim.x) {
@@ -92,21 +114,37 @@ __device__ __forceinline__ void block_scan2(int a, int b, int& a_ex, int& b_ex, 
   __syncthreads();                                     // wa/wb reused by the next call
 }
 
+constexpr int kScanPer = 4;                          // consecutive blocks per thread and round
+
 __global__ __launch_bounds__(kScanThreads) void mask_scan_kernel(MaskInfoArgs m) {
   const int64_t nblk = (int64_t)m.Mb * m.Mh * m.n_qb * m.n_kb;
   int run_ne = 0, run_pa = 0;
-  for (int64_t base = 0; base < nblk; base += kScanThreads) {
-    const int64_t idx = base + threadIdx.x;
-    const int c = idx < nblk ? m.cls[idx] : 0;
-    const int ne = c != 0, pa = c == 1;
+  for (int64_t base = 0; base < nblk; base += (int64_t)kScanThreads * kScanPer) {
+    // each thread sums its kScanPer blocks, the workgroup scans the sums, and each thread then
+    // walks its blocks from its own starting offsets
+    const int64_t i0 = base + (int64_t)threadIdx.x * kScanPer;
+    int cl[kScanPer], ne_sum = 0, pa_sum = 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      cl[j] = i0 + j < nblk ? m.cls[i0 + j] : 0;
+      ne_sum += cl[j] != 0;
+      pa_sum += cl[j] == 1;
+    }
     int ne_ex, pa_ex, ne_tot, pa_tot;
-    block_scan2(ne, pa, ne_ex, pa_ex, ne_tot, pa_tot);
-    if (idx < nblk) {
-      const int kb = (int)(idx % m.n_kb);
-      const int64_t row = idx / m.n_kb;
-      if (kb == 0) m.row_ptr[row] = run_ne + ne_ex;
-      if (ne) m.data_next[run_ne + ne_ex] = kb;
-      m.next[idx] = pa ? run_pa + pa_ex : 0;
+    block_scan2(ne_sum, pa_sum, ne_ex, pa_ex, ne_tot, pa_tot);
+    int ne_at = run_ne + ne_ex, pa_at = run_pa + pa_ex;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int64_t idx = i0 + j;
+      if (idx < nblk) {
+        const int kb = (int)(idx % m.n_kb);
+        const int64_t row = idx / m.n_kb;
+        if (kb == 0) m.row_ptr[row] = ne_at;
+        if (cl[j] != 0) m.data_next[ne_at] = kb;
+        m.next[idx] = cl[j] == 1 ? pa_at : 0;
+        ne_at += cl[j] != 0;
+        pa_at += cl[j] == 1;
+      }
     }
     run_ne += ne_tot;
     run_pa += pa_tot;
@@ -131,14 +169,31 @@ __global__ __launch_bounds__(256) void mask_pack_kernel(MaskInfoArgs m) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (m.u1 && m.sk == 1) {
     // the block's words as they are, bits past the mask cleared; one word per lane
+    // every thread takes (row, word) pairs, so all lanes load at once
     const uint32_t* w0 = reinterpret_cast<const uint32_t*>(m.mask) + row0 + (c0 >> 5);
     const int nw = (nc + 31) >> 5, tail = nc & 31;
-    for (int r = wave; r < m.bq; r += blockDim.x >> 6) {
-      for (int w = lane; w < words; w += 64) {
-        uint32_t bits = (r < nr && w < nw) ? w0[(int64_t)r * m.sq + w] : 0u;
-        if (tail && w == nw - 1) bits &= (1u << tail) - 1u;
-        dst[(int64_t)r * words + w] = bits;
+    for (int e = threadIdx.x; e < m.bq * words; e += blockDim.x) {
+      const int r = e / words, w = e - r * words;
+      uint32_t bits = (r < nr && w < nw) ? w0[(int64_t)r * m.sq + w] : 0u;
+      if (tail && w == nw - 1) bits &= (1u << tail) - 1u;
+      dst[(int64_t)r * words + w] = bits;
+    }
+    return;
+  }
+  if (m.vec16 && (nc & 15) == 0) {
+    // 16 bytes -> 16 bits per thread, written as the low or high half of a word
+    const int cpr = m.bkv >> 4;                        // 16-column chunks of a stored row
+    const uint8_t* b0 = m.mask + row0 + c0;
+    uint16_t* dst16 = reinterpret_cast<uint16_t*>(dst);
+    for (int e = threadIdx.x; e < m.bq * cpr; e += blockDim.x) {
+      const int r = e / cpr, ch = e - r * cpr;
+      uint32_t bits = 0;
+      if (r < nr && 16 * ch < nc) {
+        const uint4 x = *reinterpret_cast<const uint4*>(b0 + (int64_t)r * m.sq + 16 * ch);
+        bits = nonzero_nibble(x.x) | (nonzero_nibble(x.y) << 4) | (nonzero_nibble(x.z) << 8) |
+               (nonzero_nibble(x.w) << 12);
       }
+      dst16[(int64_t)r * words * 2 + ch] = (uint16_t)bits;
     }
     return;
   }
