@@ -386,6 +386,64 @@ def main():
         del q5, k5, v5, out5
         torch.cuda.empty_cache()
 
+    # ---- widened paths: packed sequences, several decode tokens, f16 ------------------------
+    # packed: causal prefill over documents packed in one sequence (16 heads, D 128, segment
+    # lengths ~ U{256..4096} up to 32768 tokens), exact in-segment causal pairs; decode: the GQA
+    # decode cache with 4 new query tokens per sequence (KV bytes as for one token: each K/V row
+    # is read once for all 4); f16: the causal prefill with f16 inputs (the bf16 values, exact in f16)
+    if not args.skip_extra:
+        nx = {}
+        rng = np.random.default_rng([1007, 11])
+        lens = []
+        while sum(lens) < 32768:
+            lens.append(int(rng.integers(256, 4097)))
+        lens[-1] -= sum(lens) - 32768
+        lens = [t for t in lens if t > 0]
+        tot = sum(lens)
+        Hp, Dp = 16, 128
+        qp_, kp_, vp_ = (sa.from_numpy(workloads.normal_tensor(np.random.default_rng([1007, tag]), (tot, Hp, Dp), "bf16"),
+                                       "bf16") for tag in (0, 1, 2))
+        segs = sa.from_numpy(np.array(lens, dtype=np.int32), "i32")
+        outp = torch.empty((tot, Hp, Dp), dtype=torch.bfloat16, device="cuda")
+        stp = lambda: sa.sdpa_packed(qp_, kp_, vp_, segs, is_causal=True, maxlen=max(lens), out=outp)
+        n_p = max(2, args.steps // 5)
+        t_p, _ = time_steps(stp, n_p, max(2, args.warmup // 10), stream)
+        fl_p = 4.0 * Dp * Hp * sum(t * (t + 1) / 2 for t in lens)
+        nx["packed_causal_prefill"] = {"segments": len(lens), "total_tokens": tot, "heads": Hp, "head_dim": Dp,
+                                       "ms": round(t_p / n_p * 1e3, 4),
+                                       "TFLOP_per_s": round(fl_p / (t_p / n_p) / 1e12, 2),
+                                       "frac_of_2500": round(fl_p / (t_p / n_p) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del qp_, kp_, vp_, outp
+        d4 = workloads.gqa_decode(q_len=4)
+        q4 = sa.from_numpy(d4.q, "bf16")
+        kc4, vc4 = sa.from_numpy(d4.k_cache, "bf16"), sa.from_numpy(d4.v_cache, "bf16")
+        sa.kv_cache_update(kc4, vc4, sa.from_numpy(d4.k_new, "bf16"), sa.from_numpy(d4.v_new, "bf16"),
+                           sa.from_numpy(d4.write_index, "i32"))
+        kvl4 = sa.from_numpy(d4.kv_lengths, "i32")
+        B4d, T4, Hq4d, D4d = d4.q.shape
+        o4 = torch.empty((B4d, T4, Hq4d, D4d), dtype=torch.bfloat16, device="cuda")
+        ws4 = torch.empty(sa.decode_workspace_bytes(q4, kc4, 0), dtype=torch.uint8, device="cuda")
+        std = lambda: sa.sdpa_decode(q4, kc4, vc4, kvl4, scale=d4.scale, out=o4, workspace=ws4)
+        t_d4, _ = time_steps(std, args.steps, args.warmup, stream)
+        by4 = float(np.sum(d4.kv_lengths.astype(np.int64))) * d4.k_cache.shape[2] * D4d * 2 * 2 + \
+            2.0 * B4d * T4 * Hq4d * D4d * 2
+        nx["decode_4_tokens"] = {"batch": B4d, "q_tokens": T4, "q_heads": Hq4d, "kv_heads": int(d4.k_cache.shape[2]),
+                                 "ms": round(t_d4 / args.steps * 1e3, 4),
+                                 "GB_per_s": round(by4 / (t_d4 / args.steps) / 1e9, 1),
+                                 "frac_of_8000": round(by4 / (t_d4 / args.steps) / 1e9 / PEAK_HBM_GBS, 4)}
+        del q4, kc4, vc4, o4, ws4
+        torch.cuda.empty_cache()
+        q16, k16, v16 = (sa.from_numpy(getattr(w, n), "bf16").to(torch.float16) for n in ("q", "k", "v"))
+        o16 = torch.empty((B, Lq, Hq, D), dtype=torch.float16, device="cuda")
+        st16 = lambda: sa.sdpa(q16, k16, v16, is_causal=True, scale=w.scale, out=o16)
+        t16, _ = time_steps(st16, args.steps, args.warmup, stream)
+        nx["f16_causal_prefill"] = {"workload": "causal_prefill in f16", "ms": round(t16 / args.steps * 1e3, 4),
+                                    "TFLOP_per_s": round(flops / (t16 / args.steps) / 1e12, 2),
+                                    "frac_of_2500": round(flops / (t16 / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del q16, k16, v16, o16
+        torch.cuda.empty_cache()
+        result["widened"] = nx
+
     # ---- CPU baseline (rank 0, N = 1 only) ------------------------------------------------
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_seconds)
