@@ -345,8 +345,8 @@ def main():
         nonempty = int(np.count_nonzero(info4.to_numpy()["block_mask"]))
         out4 = torch.empty((B4_, Lq4, Hq4, D4), dtype=torch.bfloat16, device="cuda")
         st4 = lambda: sa.sdpa(q4, k4, v4, bias4, None, mask_info=info4, scale=w4.scale, out=out4)
-        n4 = max(2, args.steps // 5)
-        t4, _ = time_steps(st4, n4, max(2, args.warmup // 10), stream)
+        n4 = max(2, args.steps // 2)
+        t4, _ = time_steps(st4, n4, max(2, args.warmup // 3), stream)
         fl4 = float(nonempty) * B4_ * Hq4 * 4.0 * 128 * 128 * D4
         bias_bytes = float(nonempty) * Hq4 * 128 * 128 * 2
         per4 = t4 / n4
@@ -406,8 +406,8 @@ def main():
         segs = sa.from_numpy(np.array(lens, dtype=np.int32), "i32")
         outp = torch.empty((tot, Hp, Dp), dtype=torch.bfloat16, device="cuda")
         stp = lambda: sa.sdpa_packed(qp_, kp_, vp_, segs, is_causal=True, maxlen=max(lens), out=outp)
-        n_p = max(2, args.steps // 5)
-        t_p, _ = time_steps(stp, n_p, max(2, args.warmup // 10), stream)
+        n_p = max(2, args.steps // 2)
+        t_p, _ = time_steps(stp, n_p, max(2, args.warmup), stream)
         fl_p = 4.0 * Dp * Hp * sum(t * (t + 1) / 2 for t in lens)
         nx["packed_causal_prefill"] = {"segments": len(lens), "total_tokens": tot, "heads": Hp, "head_dim": Dp,
                                        "ms": round(t_p / n_p * 1e3, 4),

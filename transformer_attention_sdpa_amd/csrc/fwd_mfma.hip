@@ -109,7 +109,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     SegView sv;
     if (!seg_locate(args, (int)(blockIdx.x / args.Hq), BM, sv)) return;     // workgroup-uniform
     a = seg_args(args, sv);
-    qt = sv.tile;
+    // causal: a segment's last tiles attend the most keys, so they go first
+    qt = args.causal != SDPA_CAUSAL_NONE ? (sv.q_len + BM - 1) / BM - 1 - sv.tile : sv.tile;
     bh = blockIdx.x % args.Hq;
   } else if (order == 1) {
     if (remap) {                                  // HB % 8 == 0
