@@ -524,10 +524,16 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
             } else if (mask_row >= 0) {
               const uint8_t* mp = a.mask + mask_row + (int64_t)jb * a.mask_sk;
               if (a.mask_vec && jb + 16 <= a.Lkv) {
+                // 16 mask bytes -> 16 bits: in a word x the high bit of each byte of
+                // ((x & 0x7f7f7f7f) + 0x7f7f7f7f) | x is set exactly for the nonzero bytes (no
+                // byte's sum carries), and the multiply gathers those 4 bits into bits 28..31
                 const uint4 m4 = *reinterpret_cast<const uint4*>(mp);
                 const uint32_t w[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
-                for (int e = 0; e < 16; ++e) bits |= (((w[e >> 2] >> (8 * (e & 3))) & 0xffu) != 0) << e;
+                for (int t4 = 0; t4 < 4; ++t4) {
+                  const uint32_t hi8 = (((w[t4] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[t4]) & 0x80808080u;
+                  bits |= ((hi8 * 0x00204081u) >> 28) << (4 * t4);
+                }
               } else {
                 for (int e = 0; e < 16; ++e)
                   if (jb + e < a.Lkv) bits |= (mp[(int64_t)e * a.mask_sk] != 0) << e;
