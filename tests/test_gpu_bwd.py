@@ -19,8 +19,10 @@ pytestmark = pytest.mark.gpu
 
 
 def run_bwd(w, dout, q_lengths=None, grad_dtype=torch.float32, use_mask_info=False, bq=128, bkv=128,
-            out_dtype=torch.float32):
+            out_dtype=torch.float32, mask=None):
     t = gpu_inputs(w)
+    if mask is not None:
+        t["mask"] = mask
     info = sa.build_block_mask_info(t["mask"], bq, bkv) if use_mask_info and t["mask"] is not None else None
     kw = dict(scale=w.scale, is_causal=w.is_causal, q_offset=per_batch(w.q_offset),
               kv_lengths=per_batch(w.kv_lengths), q_lengths=per_batch(q_lengths))
@@ -117,6 +119,31 @@ def test_grad_mask_info_and_bits_equal_dense(lib):
     for n in ("dq", "dk", "dv"):
         np.testing.assert_array_equal(info[n], dense[n])
     check(dense, run_ref(w, dout), "bf16", "dense mask")
+
+
+@pytest.mark.parametrize("kind", ["u8", "u1"])
+@pytest.mark.parametrize("dtype,D,mshape,causal", [("bf16", 128, (2, 8), False), ("f16", 64, (1, 1), "bottom_right"),
+                                                   ("bf16", 64, (2, 1), True), ("f16", 128, (1, 8), True)])
+def test_grad_mask_matrix_tiles(lib, kind, dtype, D, mshape, causal):
+    # masks whose rows suit the 16-bit matrix-core kernels (496 keys: 31 16-byte runs of bytes,
+    # 16 words of bits) over several query and key tiles, ragged tails, GQA, per-batch kv_lengths,
+    # and rows left with no allowed key; U1 padding bits are set, so a read of one would show
+    w = workloads.random_attention(2800 + D, 2, 300, 496, 8, 2, D, dtype=dtype, is_causal=causal,
+                                   mask_shape=mshape + (300, 496), mask_p=0.6,
+                                   kv_lengths=np.array([496, 431], dtype=np.int32))
+    w.mask[..., 7, :] = 0
+    w.mask[0, ..., 150:260, 200:330] = 0
+    dout = workloads.output_cotangent(w, 3800)
+    m = None
+    if kind == "u1":
+        m = sa.PackedMask(torch.as_tensor(workloads.pack_mask_bits(w.mask, 1), device="cuda"), w.mask.shape[-1])
+    say(f"grad mask {kind} {dtype} D={D} mask {mshape} causal={causal}")
+    got = run_bwd(w, dout, mask=m)
+    check(got, run_ref(w, dout), dtype, f"mask {kind}")
+    if kind == "u1":
+        dense = run_bwd(w, dout)
+        for n in ("dq", "dk", "dv"):
+            np.testing.assert_array_equal(got[n], dense[n])
 
 
 @pytest.mark.parametrize("gdt", [torch.bfloat16, torch.float16])

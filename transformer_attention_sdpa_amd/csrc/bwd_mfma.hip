@@ -141,6 +141,34 @@ __device__ __forceinline__ void store4(void* base, int64_t off, int dtype, float
   }
 }
 
+// Masked variants: the mask tile of each step travels to LDS with the K/V or Q/dO tiles
+// (direct loads, no registers held across the step). U8: one byte per key; U1: 32 keys a word.
+constexpr int MK_NONE = 0, MK_U8 = 1, MK_U1 = 2;
+
+// Buffer resource over the mask rows of (b, h): loads past its last row read 0
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mask_rsrc(const AttnArgs& a, int b, int h) {
+  const int64_t eb = a.mask_u1 ? 4 : 1;
+  const int64_t row_bytes = a.mask_u1 ? (int64_t)((a.Lkv + 31) / 32) * 4 : a.Lkv;
+  const uint8_t* base = a.mask + (b * a.mask_sb + h * a.mask_sh) * eb;
+  return make_rsrc(base, (int64_t)(a.Lq - 1) * a.mask_sq * eb + row_bytes);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
+}
+// 4 mask bytes to 4 bits (bit t: byte t nonzero). The high bit of ((x & 0x7f7f7f7f) + 0x7f7f7f7f)
+// | x is set exactly in the nonzero bytes (no byte's sum carries into the next); the multiply
+// moves the four flags, bits 7, 15, 23 and 31, to bits 28 .. 31 without overlapping carries.
+__device__ __forceinline__ uint32_t nonzero_nibble4(uint32_t x) {
+  const uint32_t hi = (((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u;
+  return (hi * 0x00204081u) >> 28;
+}
+
+// weight argument x where bit e of the 16-bit set `valid` is set, else -inf (a bit select)
+__device__ __forceinline__ float keep_or_ninf(uint32_t valid, int e, float x) {
+  const uint32_t keep = (uint32_t)((int32_t)(valid << (31 - e)) >> 31);
+  return __uint_as_float((__float_as_uint(x) & keep) | (0xff800000u & ~keep));
+}
+
 // ================================ dK / dV ====================================================
 // Eight waves: waves w and w + 4 own the same 32 keys and take the two 32-query blocks of each
 // 64-query tile, so each holds only its accumulators and the S/dP pair, and two waves share
@@ -154,7 +182,7 @@ constexpr int QT8 = 64;
 template <int D>
 __device__ __forceinline__ int kvswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
 
-template <int D, bool F16>
+template <int D, bool F16, int MK>
 __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap) {
   using E = In<F16>;
   using x8 = typename E::x8;
@@ -163,6 +191,8 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
   __shared__ __align__(16) uint16_t kbuf[RB * D], vbuf[RB * D];
   __shared__ __align__(16) uint16_t qbuf0[TILE], qbuf1[TILE], obuf0[TILE], obuf1[TILE];
   __shared__ __align__(16) float stat[2][2][QT8];    // [buffer][lse / scale, D][query]
+  // mask tile [buffer][query][key]: U8 128 bytes a query, U1 4 words a query
+  __shared__ __align__(16) uint8_t mraw[MK ? 2 : 1][MK == MK_U1 ? QT8 * 16 : (MK ? QT8 * RB : 16)];
   const AttnArgs& a = g.a;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -228,6 +258,19 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
     if (tid < QT8) return i < nq ? g.w_lse[row] / a.scale : INFINITY;   // +inf: weight 0 (scale > 0)
     return i < nq ? g.w_dsum[row] : 0.f;
   };
+  // mask rows of step it (queries it_q0 .. + 63, keys k0 .. k0 + 127) into mraw[buf]
+  auto load_mask = [&](int it, int buf) {
+    if constexpr (MK != MK_NONE) {
+      const __amdgpu_buffer_rsrc_t rm = mask_rsrc(a, b, it_head(it));
+      const int64_t i0 = it_q0(it);
+      if constexpr (MK == MK_U8) {                   // 16 bytes a thread: row 8 * wave + lane / 8
+        const int64_t i = i0 + 8 * wave + (lane >> 3);
+        dma16(rm, reinterpret_cast<uint16_t*>(mraw[buf] + 1024 * wave), (int)(i * a.mask_sq) + k0 + 16 * (lane & 7));
+      } else if (wave == 0) {                        // 4 words a lane: row lane
+        dma16(rm, reinterpret_cast<uint16_t*>(mraw[buf]), (int)(((i0 + lane) * a.mask_sq + (k0 >> 5)) * 4));
+      }
+    }
+  };
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -238,6 +281,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
   if (n_it > 0) {
     load_tiles(0, qbuf0, obuf0);
     const float st0 = load_stat(0);
+    load_mask(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     if (tid < 2 * QT8) stat[0][tid / QT8][tid & (QT8 - 1)] = st0;
   } else {
@@ -253,6 +297,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
     if (it + 1 < n_it) {
       load_tiles(it + 1, P ? qbuf0 : qbuf1, P ? obuf0 : obuf1);
       st_next = load_stat(it + 1);
+      load_mask(it + 1, 1 - P);
     }
     const int i0 = it_q0(it);
     // this wave's block: queries i0 + 32 * qp .. + 31 against keys wk0 .. wk0 + 31
@@ -278,11 +323,27 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
         e_min = m < 0 ? 0 : (m > 16 ? 16 : (int)m);
       }
       if (key_me >= nkv) e_min = 16;
+      uint32_t valid = 0;                             // masked: bit e set where query e keeps this key
+      if constexpr (MK != MK_NONE) {
+        const int r0 = 32 * qp + 16 * hh;
+        if constexpr (MK == MK_U8) {
+          const uint8_t* mp = mraw[P] + r0 * RB + 32 * kw + ql;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) valid |= (uint32_t)(mp[e * RB] != 0) << e;
+        } else {
+          const uint32_t* mp = reinterpret_cast<const uint32_t*>(mraw[P]) + 4 * r0 + kw;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) valid |= ((mp[4 * e] >> ql) & 1u) << e;
+        }
+        valid &= 0xffffu << e_min;
+      }
       float pv[16], sv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float x = s[e] * c2;
-        const float p = __builtin_amdgcn_exp2f(e >= e_min ? x : -INFINITY);
+        float p;
+        if constexpr (MK != MK_NONE) p = __builtin_amdgcn_exp2f(keep_or_ninf(valid, e, x));
+        else p = __builtin_amdgcn_exp2f(e >= e_min ? x : -INFINITY);
         pv[e] = p;
         sv[e] = p * dp[e];
       }
@@ -345,12 +406,14 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
 }
 
 // ================================ dQ =========================================================
-template <int D, bool F16>
-__global__ __launch_bounds__(NTB, 1) void bwd_dq_mfma_kernel(BwdArgs g, int n_qt, int remap) {
+template <int D, bool F16, int MK>
+__global__ __launch_bounds__(NTB, MK == MK_NONE ? 1 : 2) void bwd_dq_mfma_kernel(BwdArgs g, int n_qt, int remap) {
   using E = In<F16>;
   using x8 = typename E::x8;
   constexpr int DC = D / 16, DB = D / 32, TILE = ST * D;
   __shared__ __align__(16) uint16_t kbuf0[TILE], kbuf1[TILE], vbuf0[TILE], vbuf1[TILE];
+  // mask tile [buffer][query][key]: U8 64 bytes a query, U1 2 words a query
+  __shared__ __align__(16) uint8_t mraw[MK ? 2 : 1][MK == MK_U1 ? RB * 8 : (MK ? RB * ST : 16)];
   const AttnArgs& a = g.a;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -416,8 +479,28 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dq_mfma_kernel(BwdArgs g, int n_qt
 #pragma unroll
     for (int e = 0; e < 16; ++e) dq[d][e] = 0.f;
   float dsc = 0.f;
+  // mask rows of tile t (queries q0 .. q0 + 127, keys t * 64 .. + 63) into mraw[buf]
+  auto load_mask = [&](int t, int buf) {
+    if constexpr (MK != MK_NONE) {
+      const __amdgpu_buffer_rsrc_t rm = mask_rsrc(a, b, h);
+      if constexpr (MK == MK_U8) {                   // 16 bytes a thread and pass: row 64u + 16 * wave + lane / 4
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int64_t i = q0 + 64 * u + 16 * wave + (lane >> 2);
+          dma16(rm, reinterpret_cast<uint16_t*>(mraw[buf] + 4096 * u + 1024 * wave),
+                (int)(i * a.mask_sq) + t * ST + 16 * (lane & 3));
+        }
+      } else {                                       // one word a thread: row tid / 2, word tid % 2
+        const int64_t i = q0 + (tid >> 1);
+        dma4(rm, mraw[buf] + 256 * wave, (int)((i * a.mask_sq + 2 * t + (tid & 1)) * 4));
+      }
+    }
+  };
 
-  if (n_tiles > 0) load_tiles(0, kbuf0, vbuf0);
+  if (n_tiles > 0) {
+    load_tiles(0, kbuf0, vbuf0);
+    load_mask(0, 0);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -425,7 +508,10 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dq_mfma_kernel(BwdArgs g, int n_qt
     constexpr int P = decltype(PAR_)::value;
     const uint16_t* ks = P ? kbuf1 : kbuf0;
     const uint16_t* vs = P ? vbuf1 : vbuf0;
-    if (t + 1 < n_tiles) load_tiles(t + 1, P ? kbuf0 : kbuf1, P ? vbuf0 : vbuf1);
+    if (t + 1 < n_tiles) {
+      load_tiles(t + 1, P ? kbuf0 : kbuf1, P ? vbuf0 : vbuf1);
+      load_mask(t + 1, 1 - P);
+    }
     const int k0 = t * ST;
     if (k0 < k_end_w) {
 #pragma unroll
@@ -444,11 +530,22 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dq_mfma_kernel(BwdArgs g, int n_qt
           const int64_t m = lim_me - jbase;
           e_end = m < 0 ? 0 : (m > 16 ? 16 : (int)m);
         }
+        uint32_t valid = 0;                           // masked: bit e set where key jbase + e is kept
+        if constexpr (MK == MK_U8) {
+          const uint4 x = *reinterpret_cast<const uint4*>(mraw[P] + (32 * wave + ql) * ST + 32 * kb + 16 * hh);
+          valid = nonzero_nibble4(x.x) | (nonzero_nibble4(x.y) << 4) | (nonzero_nibble4(x.z) << 8) |
+                  (nonzero_nibble4(x.w) << 12);
+        } else if constexpr (MK == MK_U1) {
+          valid = reinterpret_cast<const uint32_t*>(mraw[P])[2 * (32 * wave + ql) + kb] >> (16 * hh);
+        }
+        if constexpr (MK != MK_NONE) valid &= (1u << e_end) - 1u;
         float sv[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float x = fmaf(s[e], c2, -lse2);
-          const float p = __builtin_amdgcn_exp2f(e < e_end ? x : -INFINITY);
+          float p;
+          if constexpr (MK != MK_NONE) p = __builtin_amdgcn_exp2f(keep_or_ninf(valid, e, x));
+          else p = __builtin_amdgcn_exp2f(e < e_end ? x : -INFINITY);
           const float d_s = p * (dp[e] - dsum);
           sv[e] = d_s;
           dsc = fmaf(d_s, s[e], dsc);
@@ -493,10 +590,17 @@ hipError_t launch_dq_t(const BwdArgs& g, hipStream_t s) {
   const AttnArgs& a = g.a;
   const int n_qt = (a.Lq + RB - 1) / RB;
   const int HB = a.Hq * a.B;
-  hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, F16>), dim3((unsigned)((int64_t)n_qt * HB)), dim3(NTB), 0, s, g, n_qt,
-                     HB % 8 == 0 ? 1 : 0);
+  const dim3 grid((unsigned)((int64_t)n_qt * HB));
+  const int remap = HB % 8 == 0 ? 1 : 0;
+  if (!a.mask)
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, F16, MK_NONE>), grid, dim3(NTB), 0, s, g, n_qt, remap);
+  else if (a.mask_u1)
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, F16, MK_U1>), grid, dim3(NTB), 0, s, g, n_qt, remap);
+  else
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, F16, MK_U8>), grid, dim3(NTB), 0, s, g, n_qt, remap);
   return hipGetLastError();
 }
+
 
 }  // namespace
 
@@ -504,7 +608,15 @@ bool bwd_mfma_supports(const BwdArgs& g) {
   const AttnArgs& a = g.a;
   if ((a.in_dtype != SDPA_BF16 && a.in_dtype != SDPA_F16) || a.D != a.Dv || (a.D != 64 && a.D != 128)) return false;
   if (g.do_dtype != a.in_dtype) return false;            // dO streams through the same 16-bit tiles
-  if (a.mask || a.bm_class || a.bias || a.qk_norm || a.q_seg) return false;
+  if (a.bias || a.qk_norm || a.q_seg || a.bm_class) return false;   // block info: the generic kernels
+  if (a.mask) {
+    // 16-byte rows of the mask tiles: unit key stride, 16-byte aligned row starts; 32-bit offsets
+    const int64_t eb = a.mask_u1 ? 4 : 1, q = 16 / eb;
+    if (a.mask_sk != 1 || !al(a.mask, 16) || (a.mask_sb % q) || (a.mask_sh % q) || (a.mask_sq % q)) return false;
+    if (a.mask_sb < 0 || a.mask_sh < 0 || a.mask_sq < 0) return false;
+    const int64_t row_bytes = a.mask_u1 ? (int64_t)((a.Lkv + 31) / 32) * 4 : a.Lkv;
+    if (((int64_t)a.Lq + 2 * RB) * a.mask_sq * eb + row_bytes + 2 * RB > INT32_MAX) return false;
+  }
   if (!(a.scale > 0.f)) return false;    // the dK/dV pass folds lse / scale into its MFMAs
   if (!al(a.q, 16) || !al(a.k, 16) || !al(a.v, 16) || !al(g.dout, 16)) return false;
   if ((a.q_sb | a.q_ss | a.q_sh | a.k_sb | a.k_ss | a.k_sh | a.v_sb | a.v_ss | a.v_sh | g.do_sb | g.do_ss | g.do_sh) & 7)
@@ -525,8 +637,14 @@ hipError_t launch_dkdv8_t(const BwdArgs& g, hipStream_t s) {
   const AttnArgs& a = g.a;
   const int n_kt = (a.Lkv + RB - 1) / RB;
   const int HB = a.Hkv * a.B;
-  hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16>), dim3((unsigned)((int64_t)n_kt * HB)), dim3(NT8), 0, s, g,
-                     HB % 8 == 0 ? 1 : 0);
+  const dim3 grid((unsigned)((int64_t)n_kt * HB));
+  const int remap = HB % 8 == 0 ? 1 : 0;
+  if (!a.mask)
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_NONE>), grid, dim3(NT8), 0, s, g, remap);
+  else if (a.mask_u1)
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_U1>), grid, dim3(NT8), 0, s, g, remap);
+  else
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_U8>), grid, dim3(NT8), 0, s, g, remap);
   return hipGetLastError();
 }
 
