@@ -250,7 +250,7 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(tf_b, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "traffic": counters_traffic(BACKWARD_COUNTERS),
                          "flops_per_call": flops_b,
-                         "kernel": "bwd_prep + bwd_dkdv_mfma_kernel<128> + bwd_dq_mfma_kernel<128> + bwd_dscale"},
+                         "kernel": "bwd_prep + bwd_dkdv8_kernel<128> + bwd_dq_mfma_kernel<128> + bwd_dscale"},
             "parity": backward_parity(w, q, k, v, outb, dout, lse, grads),
         }
         del out32, outb, dout, grads, bws, lse
