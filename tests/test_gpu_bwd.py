@@ -109,16 +109,41 @@ def test_grad_value_head_dim_differs(lib, dtype):
     check(run_bwd(w, dout), run_ref(w, dout), dtype, "dv=32")
 
 
-def test_grad_mask_info_and_bits_equal_dense(lib):
-    w = workloads.random_attention(2300, 2, 200, 260, 4, 2, 128, dtype="bf16", mask_shape=(1, 4, 200, 260),
-                                   is_causal="bottom_right")
+@pytest.mark.parametrize("Lkv,bq,bkv,D", [(272, 128, 64, 128), (272, 32, 32, 64), (496, 100, 96, 128), (496, 200, 160, 64)])
+def test_grad_mask_info_equals_dense(lib, Lkv, bq, bkv, D):
+    # byte rows of 16-byte runs: the dense mask and its block info both take the matrix-core
+    # kernels and must agree bit for bit; blocks of every class, block edges off the 64-query and
+    # 128-key steps of the kernels, ragged tails
+    w = workloads.random_attention(2300 + bq, 2, 200, Lkv, 4, 2, D, dtype="bf16",
+                                   mask_shape=(1, 4, 200, Lkv), is_causal="bottom_right")
+    w.mask[..., :bq, :bkv] = 1                    # a full block
+    w.mask[:, 1, bq:, :] = 0                      # empty blocks
     dout = workloads.output_cotangent(w, 3300)
-    say("grad with block info")
-    dense = run_bwd(w, dout)
-    info = run_bwd(w, dout, use_mask_info=True, bq=128, bkv=64)
-    for n in ("dq", "dk", "dv"):
-        np.testing.assert_array_equal(info[n], dense[n])
-    check(dense, run_ref(w, dout), "bf16", "dense mask")
+    say(f"grad with block info Lkv={Lkv} bq={bq} bkv={bkv} D={D}")
+    # one forward (its rounding depends on the tiles it visits) feeds both gradients
+    t = gpu_inputs(w)
+    kw = dict(scale=w.scale, is_causal=w.is_causal)
+    out, lse = sa.sdpa(t["q"], t["k"], t["v"], None, t["mask"], return_lse=True, out_dtype=torch.float32, **kw)
+    d_o = dev(dout, w.dtype)
+    info = sa.build_block_mask_info(t["mask"], bq, bkv)
+    g_dense = sa.sdpa_bwd(t["q"], t["k"], t["v"], out, d_o, lse, t["mask"], **kw)
+    g_info = sa.sdpa_bwd(t["q"], t["k"], t["v"], out, d_o, lse, None, mask_info=info, **kw)
+    torch.cuda.synchronize()
+    for n, x, y in zip(("dq", "dk", "dv", "dscale"), g_info, g_dense):
+        np.testing.assert_array_equal(x.float().cpu().numpy(), y.float().cpu().numpy(), err_msg=n)
+    check(run_bwd(w, dout, use_mask_info=True, bq=bq, bkv=bkv), run_ref(w, dout), "bf16", "block info")
+
+
+def test_grad_mask_info_unaligned_dense(lib):
+    # 260-key byte rows take the generic kernels; the block info of the same mask the matrix-core
+    # ones: both against the oracle
+    w = workloads.random_attention(2350, 2, 200, 260, 4, 2, 128, dtype="bf16", mask_shape=(1, 4, 200, 260),
+                                   is_causal="bottom_right")
+    dout = workloads.output_cotangent(w, 3350)
+    say("grad with block info, unaligned dense mask")
+    ref = run_ref(w, dout)
+    check(run_bwd(w, dout), ref, "bf16", "dense mask")
+    check(run_bwd(w, dout, use_mask_info=True, bq=128, bkv=64), ref, "bf16", "block info")
 
 
 @pytest.mark.parametrize("kind", ["u8", "u1"])

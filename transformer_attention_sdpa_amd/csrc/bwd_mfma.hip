@@ -143,7 +143,7 @@ __device__ __forceinline__ void store4(void* base, int64_t off, int dtype, float
 
 // Masked variants: the mask tile of each step travels to LDS with the K/V or Q/dO tiles
 // (direct loads, no registers held across the step). U8: one byte per key; U1: 32 keys a word.
-constexpr int MK_NONE = 0, MK_U8 = 1, MK_U1 = 2;
+constexpr int MK_NONE = 0, MK_U8 = 1, MK_U1 = 2, MK_BI = 3;
 
 // Buffer resource over the mask rows of (b, h): loads past its last row read 0
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t mask_rsrc(const AttnArgs& a, int b, int h) {
@@ -155,6 +155,53 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mask_rsrc(const AttnArgs& a, i
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
 }
+// Block info (MK_BI): each of 256 threads owns one 32-key word of every step's mask tile, laid
+// out in LDS as U1 words. The class and partial index of the word's block are loaded two steps
+// ahead (bi_fetch), turned into the word's source one step ahead (bi_source: a byte offset into
+// the partial bits, -1 for an empty block, -2 for a full one), and the word arrives by a direct
+// 4-byte load; empty and full blocks load from past the end of the range, which writes 0, and a
+// full block's word is set to all ones once the step's loads have landed. No load result is
+// used before the step's own wait, so the tile prefetch is never stalled.
+constexpr int kBiNone = 0x7ffffff0;               // past every partial-bits range (at most 2^30 bytes)
+__device__ __forceinline__ void bi_fetch(const AttnArgs& a, int b, int h, int i, int j, int& cls, int& nxt) {
+  cls = 0;
+  nxt = 0;
+  if (i < a.Lq && j < a.Lkv) {
+    const int mb = a.bm_batch > 1 ? b : 0, mh = a.bm_heads > 1 ? h : 0;
+    const int64_t blk = (((int64_t)mb * a.bm_heads + mh) * a.bm_nqb + i / a.bm_bq) * a.bm_nkb + j / a.bm_bkv;
+    cls = a.bm_class[blk];
+    nxt = a.bm_next[blk];
+  }
+}
+__device__ __forceinline__ int bi_source(const AttnArgs& a, int cls, int nxt, int i, int j) {
+  if (cls == 1) {
+    const int r = i % a.bm_bq, c = j % a.bm_bkv;
+    return (int)((((int64_t)nxt * a.bm_bq + r) * (a.bm_bkv >> 5) + (c >> 5)) * 4);
+  }
+  return cls == 2 ? -2 : -1;
+}
+// Block info: some block meeting rows [i0, i1) x keys [j0, j1) of head h is not empty.
+// Rectangles of more than 16 blocks count as live without a look.
+__device__ __forceinline__ bool bi_rect_live(const AttnArgs& a, int b, int h, int i0, int i1, int j0, int j1) {
+  i1 = min(i1, a.Lq);
+  j1 = min(j1, a.Lkv);
+  if (i0 >= i1 || j0 >= j1) return false;
+  const int qb0 = i0 / a.bm_bq, qb1 = (i1 - 1) / a.bm_bq, kb0 = j0 / a.bm_bkv, kb1 = (j1 - 1) / a.bm_bkv;
+  if ((qb1 - qb0 + 1) * (kb1 - kb0 + 1) > 16) return true;
+  const int mb = a.bm_batch > 1 ? b : 0, mh = a.bm_heads > 1 ? h : 0;
+  const int64_t base = ((int64_t)mb * a.bm_heads + mh) * a.bm_nqb;
+  for (int qb = qb0; qb <= qb1; ++qb)
+    for (int kb = kb0; kb <= kb1; ++kb)
+      if (a.bm_class[(base + qb) * a.bm_nkb + kb] != 0) return true;
+  return false;
+}
+// Steps a workgroup can skip through its LDS bitmask of live steps (more: every step is visited)
+constexpr int kLiveWords = 128;
+
+__host__ __device__ __forceinline__ int64_t bi_bits_bytes(const AttnArgs& a) {
+  return (int64_t)a.bm_batch * a.bm_heads * a.bm_nqb * a.bm_nkb * a.bm_bq * (a.bm_bkv / 32) * 4;
+}
+
 // 4 mask bytes to 4 bits (bit t: byte t nonzero). The high bit of ((x & 0x7f7f7f7f) + 0x7f7f7f7f)
 // | x is set exactly in the nonzero bytes (no byte's sum carries into the next); the multiply
 // moves the four flags, bits 7, 15, 23 and 31, to bits 28 .. 31 without overlapping carries.
@@ -192,7 +239,8 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
   __shared__ __align__(16) uint16_t qbuf0[TILE], qbuf1[TILE], obuf0[TILE], obuf1[TILE];
   __shared__ __align__(16) float stat[2][2][QT8];    // [buffer][lse / scale, D][query]
   // mask tile [buffer][query][key]: U8 128 bytes a query, U1 4 words a query
-  __shared__ __align__(16) uint8_t mraw[MK ? 2 : 1][MK == MK_U1 ? QT8 * 16 : (MK ? QT8 * RB : 16)];
+  __shared__ __align__(16) uint8_t mraw[MK ? 2 : 1][MK == MK_U8 ? QT8 * RB : QT8 * 16];
+  __shared__ uint64_t live_bits[MK == MK_BI ? kLiveWords : 1];   // block info: bit s, step s is not empty
   const AttnArgs& a = g.a;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -260,7 +308,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
   };
   // mask rows of step it (queries it_q0 .. + 63, keys k0 .. k0 + 127) into mraw[buf]
   auto load_mask = [&](int it, int buf) {
-    if constexpr (MK != MK_NONE) {
+    if constexpr (MK == MK_U8 || MK == MK_U1) {
       const __amdgpu_buffer_rsrc_t rm = mask_rsrc(a, b, it_head(it));
       const int64_t i0 = it_q0(it);
       if constexpr (MK == MK_U8) {                   // 16 bytes a thread: row 8 * wave + lane / 8
@@ -272,32 +320,95 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
     }
   };
 
+  // block info: thread t < 256 owns word t % 4 of query row t / 4 of each step
+  int bi_cls = 0, bi_nxt = 0, bi_src = -1;
+  auto bi_load_raw = [&](int it) {
+    if constexpr (MK == MK_BI) {
+      if (tid < 256 && it < n_it) bi_fetch(a, b, it_head(it), it_q0(it) + (tid >> 2), k0 + 32 * (tid & 3), bi_cls, bi_nxt);
+    }
+  };
+  auto bi_advance = [&](int it) {
+    if constexpr (MK == MK_BI) {
+      if (tid < 256) bi_src = bi_source(a, bi_cls, bi_nxt, it_q0(it) + (tid >> 2), k0 + 32 * (tid & 3));
+    }
+  };
+  auto bi_dma = [&](int buf) {
+    if constexpr (MK == MK_BI) {
+      if (tid < 256) dma4(make_rsrc(a.bm_bits, bi_bits_bytes(a)), mraw[buf] + 256 * wave, bi_src >= 0 ? bi_src : kBiNone);
+    }
+  };
+  auto bi_fix = [&](int buf) {
+    if constexpr (MK == MK_BI) {
+      if (tid < 256 && bi_src == -2) reinterpret_cast<uint32_t*>(mraw[buf])[tid] = 0xffffffffu;
+    }
+  };
+  // block info: the steps that meet a non-empty block, found before the loop, and the loop
+  // visits only those (the others would add exact zeros); other masks: every step
+  bool scan = false;
+  if constexpr (MK == MK_BI) {
+    scan = n_it <= kLiveWords * 64;
+    if (scan) {
+      for (int s0 = 64 * wave; s0 < n_it; s0 += 64 * (NT8 / 64)) {
+        const int st = s0 + lane;
+        const bool lv = st < n_it && bi_rect_live(a, b, it_head(st), it_q0(st), it_q0(st) + QT8, k0, k0 + RB);
+        const uint64_t m = __builtin_amdgcn_ballot_w64(lv);
+        if (lane == 0) live_bits[s0 >> 6] = m;
+      }
+      __syncthreads();
+    }
+  }
+  auto next_step = [&](int st) -> int {     // the first visited step after st, or n_it
+    if constexpr (MK == MK_BI) {
+      if (scan) {
+        for (++st; st < n_it; st = (st | 63) + 1) {
+          const uint64_t m = live_bits[st >> 6] >> (st & 63);
+          if (m) return st + (int)__builtin_ctzll(m);
+        }
+        return n_it;
+      }
+    }
+    return min(st + 1, n_it);
+  };
+
   f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) dk[d][e] = dv[d][e] = 0.f;
 
-  if (n_it > 0) {
-    load_tiles(0, qbuf0, obuf0);
-    const float st0 = load_stat(0);
-    load_mask(0, 0);
+  const int first = next_step(-1), second = next_step(first);
+  if (first < n_it) {
+    load_tiles(first, qbuf0, obuf0);
+    const float st0 = load_stat(first);
+    load_mask(first, 0);
+    if constexpr (MK == MK_BI) {
+      bi_load_raw(first);
+      __builtin_amdgcn_s_waitcnt(0);
+      bi_advance(first);
+      bi_dma(0);
+      bi_load_raw(second);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     if (tid < 2 * QT8) stat[0][tid / QT8][tid & (QT8 - 1)] = st0;
+    bi_fix(0);
+    bi_advance(second);
   } else {
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
 
-  auto iter = [&](auto PAR_, int it) {
+  // step it in buffer P; nx: the next visited step (prefetched here), nn: the one after it
+  auto iter = [&](auto PAR_, int it, int nx, int nn) {
     constexpr int P = decltype(PAR_)::value;
     const uint16_t* qs = P ? qbuf1 : qbuf0;
     const uint16_t* os = P ? obuf1 : obuf0;
     float st_next = 0.f;
-    if (it + 1 < n_it) {
-      load_tiles(it + 1, P ? qbuf0 : qbuf1, P ? obuf0 : obuf1);
-      st_next = load_stat(it + 1);
-      load_mask(it + 1, 1 - P);
+    if (nx < n_it) {
+      load_tiles(nx, P ? qbuf0 : qbuf1, P ? obuf0 : obuf1);
+      st_next = load_stat(nx);
+      load_mask(nx, 1 - P);
+      bi_dma(1 - P);
+      bi_load_raw(nn);
     }
     const int i0 = it_q0(it);
     // this wave's block: queries i0 + 32 * qp .. + 31 against keys wk0 .. wk0 + 31
@@ -358,15 +469,25 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
-    if (it + 1 < n_it && tid < 2 * QT8) stat[1 - P][tid / QT8][tid & (QT8 - 1)] = st_next;
+    if (nx < n_it && tid < 2 * QT8) stat[1 - P][tid / QT8][tid & (QT8 - 1)] = st_next;
+    if (nx < n_it) {
+      bi_fix(1 - P);
+      bi_advance(nn);
+    }
     __syncthreads();
   };
   std::integral_constant<int, 0> I0;
   std::integral_constant<int, 1> I1;
-  for (int it = 0; it < n_it; it += 2) {
-    iter(I0, it);
-    if (it + 1 >= n_it) break;
-    iter(I1, it + 1);
+  for (int it = first, nx = second; it < n_it;) {
+    int nn = next_step(nx);
+    iter(I0, it, nx, nn);
+    it = nx;
+    nx = nn;
+    if (it >= n_it) break;
+    nn = next_step(nx);
+    iter(I1, it, nx, nn);
+    it = nx;
+    nx = nn;
   }
 
   // the two waves of a key block add their partial sums: the second wave writes dV (then dK)
@@ -413,7 +534,8 @@ __global__ __launch_bounds__(NTB, MK == MK_NONE ? 1 : 2) void bwd_dq_mfma_kernel
   constexpr int DC = D / 16, DB = D / 32, TILE = ST * D;
   __shared__ __align__(16) uint16_t kbuf0[TILE], kbuf1[TILE], vbuf0[TILE], vbuf1[TILE];
   // mask tile [buffer][query][key]: U8 64 bytes a query, U1 2 words a query
-  __shared__ __align__(16) uint8_t mraw[MK ? 2 : 1][MK == MK_U1 ? RB * 8 : (MK ? RB * ST : 16)];
+  __shared__ __align__(16) uint8_t mraw[MK ? 2 : 1][MK == MK_U8 ? RB * ST : RB * 8];
+  __shared__ uint64_t live_bits[MK == MK_BI ? kLiveWords : 1];   // block info: bit t, tile t is not empty
   const AttnArgs& a = g.a;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -481,7 +603,7 @@ __global__ __launch_bounds__(NTB, MK == MK_NONE ? 1 : 2) void bwd_dq_mfma_kernel
   float dsc = 0.f;
   // mask rows of tile t (queries q0 .. q0 + 127, keys t * 64 .. + 63) into mraw[buf]
   auto load_mask = [&](int t, int buf) {
-    if constexpr (MK != MK_NONE) {
+    if constexpr (MK == MK_U8 || MK == MK_U1) {
       const __amdgpu_buffer_rsrc_t rm = mask_rsrc(a, b, h);
       if constexpr (MK == MK_U8) {                   // 16 bytes a thread and pass: row 64u + 16 * wave + lane / 4
 #pragma unroll
@@ -497,20 +619,81 @@ __global__ __launch_bounds__(NTB, MK == MK_NONE ? 1 : 2) void bwd_dq_mfma_kernel
     }
   };
 
-  if (n_tiles > 0) {
-    load_tiles(0, kbuf0, vbuf0);
-    load_mask(0, 0);
+  // block info: thread t owns word t % 2 of query row t / 2 of each tile
+  int bi_cls = 0, bi_nxt = 0, bi_src = -1;
+  auto bi_load_raw = [&](int t) {
+    if constexpr (MK == MK_BI) {
+      if (t < n_tiles) bi_fetch(a, b, h, q0 + (tid >> 1), t * ST + 32 * (tid & 1), bi_cls, bi_nxt);
+    }
+  };
+  auto bi_advance = [&](int t) {
+    if constexpr (MK == MK_BI) bi_src = bi_source(a, bi_cls, bi_nxt, q0 + (tid >> 1), t * ST + 32 * (tid & 1));
+  };
+  auto bi_dma = [&](int buf) {
+    if constexpr (MK == MK_BI)
+      dma4(make_rsrc(a.bm_bits, bi_bits_bytes(a)), mraw[buf] + 256 * wave, bi_src >= 0 ? bi_src : kBiNone);
+  };
+  auto bi_fix = [&](int buf) {
+    if constexpr (MK == MK_BI) {
+      if (bi_src == -2) reinterpret_cast<uint32_t*>(mraw[buf])[tid] = 0xffffffffu;
+    }
+  };
+  // block info: the tiles that meet a non-empty block (the loop visits only those)
+  bool scan = false;
+  if constexpr (MK == MK_BI) {
+    scan = n_tiles <= kLiveWords * 64;
+    if (scan) {
+      for (int s0 = 64 * wave; s0 < n_tiles; s0 += 64 * (NTB / 64)) {
+        const int st = s0 + lane;
+        const bool lv = st < n_tiles && bi_rect_live(a, b, h, q0, q0 + RB, st * ST, st * ST + ST);
+        const uint64_t m = __builtin_amdgcn_ballot_w64(lv);
+        if (lane == 0) live_bits[s0 >> 6] = m;
+      }
+      __syncthreads();
+    }
+  }
+  auto next_step = [&](int st) -> int {     // the first visited tile after st, or n_tiles
+    if constexpr (MK == MK_BI) {
+      if (scan) {
+        for (++st; st < n_tiles; st = (st | 63) + 1) {
+          const uint64_t m = live_bits[st >> 6] >> (st & 63);
+          if (m) return st + (int)__builtin_ctzll(m);
+        }
+        return n_tiles;
+      }
+    }
+    return min(st + 1, n_tiles);
+  };
+
+  const int first = next_step(-1), second = next_step(first);
+  if (first < n_tiles) {
+    load_tiles(first, kbuf0, vbuf0);
+    load_mask(first, 0);
+    if constexpr (MK == MK_BI) {
+      bi_load_raw(first);
+      __builtin_amdgcn_s_waitcnt(0);
+      bi_advance(first);
+      bi_dma(0);
+      bi_load_raw(second);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
+  if (first < n_tiles) {
+    bi_fix(0);
+    bi_advance(second);
+  }
   __syncthreads();
 
-  auto iter = [&](auto PAR_, int t) {
+  // tile t in buffer P; nx: the next visited tile (prefetched here), nn: the one after it
+  auto iter = [&](auto PAR_, int t, int nx, int nn) {
     constexpr int P = decltype(PAR_)::value;
     const uint16_t* ks = P ? kbuf1 : kbuf0;
     const uint16_t* vs = P ? vbuf1 : vbuf0;
-    if (t + 1 < n_tiles) {
-      load_tiles(t + 1, P ? kbuf0 : kbuf1, P ? vbuf0 : vbuf1);
-      load_mask(t + 1, 1 - P);
+    if (nx < n_tiles) {
+      load_tiles(nx, P ? kbuf0 : kbuf1, P ? vbuf0 : vbuf1);
+      load_mask(nx, 1 - P);
+      bi_dma(1 - P);
+      bi_load_raw(nn);
     }
     const int k0 = t * ST;
     if (k0 < k_end_w) {
@@ -535,7 +718,7 @@ __global__ __launch_bounds__(NTB, MK == MK_NONE ? 1 : 2) void bwd_dq_mfma_kernel
           const uint4 x = *reinterpret_cast<const uint4*>(mraw[P] + (32 * wave + ql) * ST + 32 * kb + 16 * hh);
           valid = nonzero_nibble4(x.x) | (nonzero_nibble4(x.y) << 4) | (nonzero_nibble4(x.z) << 8) |
                   (nonzero_nibble4(x.w) << 12);
-        } else if constexpr (MK == MK_U1) {
+        } else if constexpr (MK == MK_U1 || MK == MK_BI) {
           valid = reinterpret_cast<const uint32_t*>(mraw[P])[2 * (32 * wave + ql) + kb] >> (16 * hh);
         }
         if constexpr (MK != MK_NONE) valid &= (1u << e_end) - 1u;
@@ -559,14 +742,24 @@ __global__ __launch_bounds__(NTB, MK == MK_NONE ? 1 : 2) void bwd_dq_mfma_kernel
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
+    if (nx < n_tiles) {
+      bi_fix(1 - P);
+      bi_advance(nn);
+    }
     __syncthreads();
   };
   std::integral_constant<int, 0> I0;
   std::integral_constant<int, 1> I1;
-  for (int t = 0; t < n_tiles; t += 2) {
-    iter(I0, t);
-    if (t + 1 >= n_tiles) break;
-    iter(I1, t + 1);
+  for (int t = first, nx = second; t < n_tiles;) {
+    int nn = next_step(nx);
+    iter(I0, t, nx, nn);
+    t = nx;
+    nx = nn;
+    if (t >= n_tiles) break;
+    nn = next_step(nx);
+    iter(I1, t, nx, nn);
+    t = nx;
+    nx = nn;
   }
 
   if (i_me >= a.Lq) return;
@@ -592,7 +785,9 @@ hipError_t launch_dq_t(const BwdArgs& g, hipStream_t s) {
   const int HB = a.Hq * a.B;
   const dim3 grid((unsigned)((int64_t)n_qt * HB));
   const int remap = HB % 8 == 0 ? 1 : 0;
-  if (!a.mask)
+  if (a.bm_class)
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, F16, MK_BI>), grid, dim3(NTB), 0, s, g, n_qt, remap);
+  else if (!a.mask)
     hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, F16, MK_NONE>), grid, dim3(NTB), 0, s, g, n_qt, remap);
   else if (a.mask_u1)
     hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, F16, MK_U1>), grid, dim3(NTB), 0, s, g, n_qt, remap);
@@ -608,7 +803,8 @@ bool bwd_mfma_supports(const BwdArgs& g) {
   const AttnArgs& a = g.a;
   if ((a.in_dtype != SDPA_BF16 && a.in_dtype != SDPA_F16) || a.D != a.Dv || (a.D != 64 && a.D != 128)) return false;
   if (g.do_dtype != a.in_dtype) return false;            // dO streams through the same 16-bit tiles
-  if (a.bias || a.qk_norm || a.q_seg || a.bm_class) return false;   // block info: the generic kernels
+  if (a.bias || a.qk_norm || a.q_seg) return false;
+  if (a.bm_class && (bi_bits_bytes(a) > (1 << 30) || !al(a.bm_bits, 4))) return false;
   if (a.mask) {
     // 16-byte rows of the mask tiles: unit key stride, 16-byte aligned row starts; 32-bit offsets
     const int64_t eb = a.mask_u1 ? 4 : 1, q = 16 / eb;
@@ -639,7 +835,9 @@ hipError_t launch_dkdv8_t(const BwdArgs& g, hipStream_t s) {
   const int HB = a.Hkv * a.B;
   const dim3 grid((unsigned)((int64_t)n_kt * HB));
   const int remap = HB % 8 == 0 ? 1 : 0;
-  if (!a.mask)
+  if (a.bm_class)
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_BI>), grid, dim3(NT8), 0, s, g, remap);
+  else if (!a.mask)
     hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_NONE>), grid, dim3(NT8), 0, s, g, remap);
   else if (a.mask_u1)
     hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_U1>), grid, dim3(NT8), 0, s, g, remap);
