@@ -39,7 +39,7 @@
 //   has its own L2) gets a contiguous set of heads. Non-causal launches run one head's tiles
 //   back to back (K/V reuse in L2), or, with a bias broadcast over the batch, the batches of one
 //   head and tile back to back (bias reuse in L2); causal launches run longest tile first
-//   across all heads.
+//   within groups of 4 heads per XCD.
 #include <type_traits>
 
 #include "mfma_common.h"
@@ -67,6 +67,10 @@ template <int D>
 __device__ __forceinline__ int k_swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
 template <int D>
 __device__ __forceinline__ int v_swz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
+// Heads an XCD runs together in a causal launch: 4 heads' K/V (8 MB at L4096 D128) against 8,
+// 0.9% faster at the causal prefill than all of an XCD's heads at once, 2 heads slightly slower
+constexpr int kGroupHeads = 4;
 
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units: the running max moves only when a row's max grows by more
 
@@ -97,8 +101,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   // 8 XCDs (each with its own L2), so with remap every XCD gets a contiguous set of heads.
   // order 0 (head-major): one head's tiles back to back, heaviest causal tile first, so the
   // concurrently running workgroups of an XCD share few K/V heads. order 1 (rank-major, for
-  // causal launches): all heads' heaviest tiles first, then the next rank -- longest work first
-  // across the whole launch, so no heavy tile starts at the end and leaves the chip idle.
+  // causal launches): heaviest tiles first, then the next rank, so no heavy tile starts at the
+  // end and leaves the chip idle; an XCD takes its heads kGroupHeads at a time (all ranks of one
+  // group, then the next group), which keeps fewer heads' K/V live in its L2 at once.
   // order 2: order 0 with the batch innermost (a bias shared by the batches).
   // PACKED: workgroup Hq * i + h takes query tile i of the segments (seg_locate) for head h,
   // and the segment is then a batch of one.
@@ -113,7 +118,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     qt = args.causal != SDPA_CAUSAL_NONE ? (sv.q_len + BM - 1) / BM - 1 - sv.tile : sv.tile;
     bh = blockIdx.x % args.Hq;
   } else if (order == 1) {
-    if (remap) {                                  // HB % 8 == 0
+    if (remap && ((HB >> 3) % kGroupHeads) == 0) {   // HB % 8 == 0, groups of kGroupHeads heads
+      const int per_x = HB >> 3, k = blockIdx.x >> 3, gs = kGroupHeads * n_qt;
+      const int g = k / gs, r = k % gs;
+      qt = n_qt - 1 - r / kGroupHeads;
+      bh = (blockIdx.x & 7) * per_x + g * kGroupHeads + r % kGroupHeads;
+    } else if (remap) {                           // HB % 8 == 0
       const int per_x = HB >> 3, k = blockIdx.x >> 3;
       qt = n_qt - 1 - k / per_x;
       bh = (blockIdx.x & 7) * per_x + k % per_x;
