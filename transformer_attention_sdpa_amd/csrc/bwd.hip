@@ -47,39 +47,74 @@ __device__ __forceinline__ void load8(const void* base, int64_t idx, int dtype, 
   }
 }
 
+constexpr int kPrepRows = 4;                     // rows per 16-lane group
+
 __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs g, int vec) {
   const AttnArgs& a = g.a;
   const int l16 = threadIdx.x & 15;
-  const int64_t row = (int64_t)blockIdx.x * (kBwdThreads / 16) + (threadIdx.x >> 4);
-  const int64_t n_rows = (int64_t)a.B * a.Hq * a.Lq;
-  const bool in = row < n_rows;                  // no early exit: the 16-lane sums below use shuffles
-  const int i = in ? (int)(row % a.Lq) : 0;
-  const int h = in ? (int)((row / a.Lq) % a.Hq) : 0;
-  const int b = in ? (int)(row / ((int64_t)a.Lq * a.Hq)) : 0;
-  const float lse = in ? g.lse[row] : 0.f;
-  const bool part = in && i < batch_q_len(a, b) && lse > -INFINITY && lse < INFINITY;
-  float acc = 0.f;
-  if (part) {
-    const int64_t o = b * a.o_sb + (int64_t)i * a.o_ss + h * a.o_sh;
-    const int64_t d_ = b * g.do_sb + (int64_t)i * g.do_ss + h * g.do_sh;
-    if (vec) {
-      for (int d = 8 * l16; d < a.Dv; d += 128) {
-        float x[8], y[8];
-        load8(a.out, o + d, a.out_dtype, x);
-        load8(g.dout, d_ + d, g.do_dtype, y);
+  // grid: x = head * n_ib + block of kPrepRows * 16 queries, y = batch (a scalar division per
+  // workgroup, none per row); rows of the stats are [b][h][i]
+  const int n_ib = (a.Lq + kPrepRows * (kBwdThreads / 16) - 1) / (kPrepRows * (kBwdThreads / 16));
+  const int h = (int)blockIdx.x / n_ib, ib = (int)blockIdx.x - h * n_ib, b = blockIdx.y;
+  const int i0 = (ib * (kBwdThreads / 16) + (threadIdx.x >> 4)) * kPrepRows;
+  const int64_t row0 = ((int64_t)b * a.Hq + h) * a.Lq + i0;
+  const int nq = batch_q_len(a, b);
+  // O and dO are read for every row in range, in parallel with lse, and for the group's rows
+  // together (one memory latency for all of them); a row that takes no part discards its sum
+  // (the 16-lane sums stay within one row). No early exit: shuffles below.
+  float lse[kPrepRows], acc[kPrepRows];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc = fmaf(x[t], y[t], acc);
+  for (int r = 0; r < kPrepRows; ++r) {
+    lse[r] = i0 + r < a.Lq ? g.lse[row0 + r] : 0.f;
+    acc[r] = 0.f;
+  }
+  const int64_t ob = b * a.o_sb + h * a.o_sh, db = b * g.do_sb + h * g.do_sh;
+  if (vec && a.Dv <= 128) {                        // one 8-element run per lane and row
+    float x[kPrepRows][8], y[kPrepRows][8];
+#pragma unroll
+    for (int r = 0; r < kPrepRows; ++r) {
+      if (i0 + r < a.Lq && 8 * l16 < a.Dv) {
+        load8(a.out, ob + (int64_t)(i0 + r) * a.o_ss + 8 * l16, a.out_dtype, x[r]);
+        load8(g.dout, db + (int64_t)(i0 + r) * g.do_ss + 8 * l16, g.do_dtype, y[r]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[r][t] = y[r][t] = 0.f;
       }
-    } else {
-      for (int d = l16; d < a.Dv; d += 16)
-        acc += load_elem(a.out, o + d, a.out_dtype) * load_elem(g.dout, d_ + d, g.do_dtype);
+    }
+#pragma unroll
+    for (int r = 0; r < kPrepRows; ++r)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[r] = fmaf(x[r][t], y[r][t], acc[r]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < kPrepRows; ++r) {
+      if (i0 + r >= a.Lq) continue;
+      const int64_t o = ob + (int64_t)(i0 + r) * a.o_ss;
+      const int64_t d_ = db + (int64_t)(i0 + r) * g.do_ss;
+      if (vec) {
+        for (int d = 8 * l16; d < a.Dv; d += 128) {
+          float x[8], y[8];
+          load8(a.out, o + d, a.out_dtype, x);
+          load8(g.dout, d_ + d, g.do_dtype, y);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) acc[r] = fmaf(x[t], y[t], acc[r]);
+        }
+      } else {
+        for (int d = l16; d < a.Dv; d += 16)
+          acc[r] += load_elem(a.out, o + d, a.out_dtype) * load_elem(g.dout, d_ + d, g.do_dtype);
+      }
     }
   }
 #pragma unroll
-  for (int m = 8; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (in && l16 == 0) {
-    g.w_dsum[row] = part ? acc : 0.f;
-    g.w_lse[row] = part ? lse : INFINITY;
+  for (int r = 0; r < kPrepRows; ++r) {
+#pragma unroll
+    for (int m = 8; m > 0; m >>= 1) acc[r] += __shfl_xor(acc[r], m, 64);
+    const bool in = i0 + r < a.Lq;
+    const bool part = in && i0 + r < nq && lse[r] > -INFINITY && lse[r] < INFINITY;
+    if (in && l16 == 0) {
+      g.w_dsum[row0 + r] = part ? acc[r] : 0.f;
+      g.w_lse[row0 + r] = part ? lse[r] : INFINITY;
+    }
   }
 }
 
@@ -270,8 +305,9 @@ hipError_t launch_bwd(const BwdArgs& g, hipStream_t s) {
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     const int vec = (a.Dv % 8 == 0) && al16(a.out) && al16(g.dout) && ((a.o_sb | a.o_ss | a.o_sh) % pe == 0) &&
                     ((g.do_sb | g.do_ss | g.do_sh) % de == 0);
-    const int rpb = kBwdThreads / 16;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((n_rows + rpb - 1) / rpb)), dim3(kBwdThreads), 0, s, g, vec);
+    const int rpb = kBwdThreads / 16 * kPrepRows;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((int64_t)((a.Lq + rpb - 1) / rpb) * a.Hq), (unsigned)a.B),
+                       dim3(kBwdThreads), 0, s, g, vec);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
