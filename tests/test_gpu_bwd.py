@@ -171,6 +171,20 @@ def test_grad_mask_matrix_tiles(lib, kind, dtype, D, mshape, causal):
             np.testing.assert_array_equal(got[n], dense[n])
 
 
+@pytest.mark.parametrize("kind", ["u8", "u1"])
+def test_grad_key_padding_mask(lib, kind):
+    # a key-padding mask [B][1][1][Lkv] (query stride 0) in the matrix-core kernels, GQA, D 128
+    w = workloads.random_attention(2900, 2, 260, 496, 8, 2, 128, dtype="bf16", mask_shape=(2, 1, 1, 496))
+    w.mask[0, ..., 400:] = 0
+    w.mask[1, ..., :37] = 0
+    dout = workloads.output_cotangent(w, 3900)
+    m = None
+    if kind == "u1":
+        m = sa.PackedMask(torch.as_tensor(workloads.pack_mask_bits(w.mask, 1), device="cuda"), w.mask.shape[-1])
+    say(f"grad key-padding mask {kind}")
+    check(run_bwd(w, dout, mask=m), run_ref(w, dout), "bf16", f"key padding {kind}")
+
+
 @pytest.mark.parametrize("gdt", [torch.bfloat16, torch.float16])
 def test_grad_16bit_outputs(lib, gdt):
     # 16-bit gradients from a 16-bit saved output (the forward's own dtype)
