@@ -1,7 +1,10 @@
 // bwd_mfma.hip -- the dK/dV and dQ passes of the attention gradient on the gfx950 matrix cores
-// (bf16 or f16 inputs, head dims 64 and 128, no mask, scale > 0; page "Neural Network primitives from
-// NNlib.jl", section "Fused implementation": the weights are formed again tile by tile from q,
-// k and the saved log-sum-exp, never stored).
+// (bf16 or f16 inputs, head dims 64 and 128, no bias, scale > 0; page "Neural Network primitives
+// from NNlib.jl", section "Fused implementation": the weights are formed again tile by tile from
+// q, k and the saved log-sum-exp, never stored). A boolean mask comes as U8 bytes, U1 bits or
+// block info (the block-sparse scheme of the splash-attention pull request "Support dynamic
+// masks in splash attention #25213"); each step's mask tile is staged in LDS next to the
+// streamed tiles, and with block info only the steps that meet a non-empty block are visited.
 //
 // Both passes use v_mfma_f32_32x32x16 with one operand kept in registers for the whole loop
 // and the other streamed through LDS, and they are mirror images of each other:
@@ -26,8 +29,8 @@
 // read patterns are free of bank conflicts: the permuted A-operand reads (rows perm32(0..15) of
 // one chunk) and the transposed reads (4 consecutive rows x 64 bytes). Rows past the arrays
 // arrive as zeros (buffer range checks); rows that take no part carry lse = +inf, so all their
-// weights are 0; keys past kv_lengths and past the causal limit are set to weight 0 per
-// element. No atomics: each workgroup writes its own rows.
+// weights are 0; keys past kv_lengths, past the causal limit and masked out are set to weight
+// 0 per element. No atomics: each workgroup writes its own rows.
 #include <type_traits>
 
 #include "mfma_common.h"
