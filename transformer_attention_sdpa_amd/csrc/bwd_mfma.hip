@@ -461,14 +461,22 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
         pv[e] = p;
         sv[e] = p * dp[e];
       }
+      // the four B operands packed first (the fp32 probabilities end here), then each pair of
+      // transposed A operands read one MFMA pair ahead of its use
+      const x8 pB[2] = {pack8<F16>(pv), pack8<F16>(pv + 8)}, sB[2] = {pack8<F16>(sv), pack8<F16>(sv + 8)};
+      x8 ao = to.atr(os, qp, 0, 0), aq = tq.atr(qs, qp, 0, 0);
 #pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        const x8 pB = pack8<F16>(pv + 8 * sh), sB = pack8<F16>(sv + 8 * sh);
-#pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          dv[d] = E::mfma(to.atr(os, qp, sh, d), pB, dv[d]);
-          dk[d] = E::mfma(tq.atr(qs, qp, sh, d), sB, dk[d]);
+      for (int n = 0; n < 2 * DB; ++n) {
+        const int sh = n / DB, d = n % DB;
+        x8 ao_n = ao, aq_n = aq;
+        if (n + 1 < 2 * DB) {
+          ao_n = to.atr(os, qp, (n + 1) / DB, (n + 1) % DB);
+          aq_n = tq.atr(qs, qp, (n + 1) / DB, (n + 1) % DB);
         }
+        dv[d] = E::mfma(ao, pB[sh], dv[d]);
+        dk[d] = E::mfma(aq, sB[sh], dk[d]);
+        ao = ao_n;
+        aq = aq_n;
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
