@@ -744,11 +744,25 @@ __global__ __launch_bounds__(NTB, MK == MK_NONE ? 1 : 2) void bwd_dq_mfma_kernel
           sv[e] = d_s;
           dsc = fmaf(d_s, s[e], dsc);
         }
+        if constexpr (D == 128) {
+          // dS packed first, then each transposed K fragment read one MFMA ahead of its use
+          // (at D = 64 the extra registers would cost a wave per SIMD)
+          const x8 sB[2] = {pack8<F16>(sv), pack8<F16>(sv + 8)};
+          x8 ak = tk.atr(ks, kb, 0, 0);
 #pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          const x8 sB = pack8<F16>(sv + 8 * sh);
+          for (int n = 0; n < 2 * DB; ++n) {
+            x8 ak_n = ak;
+            if (n + 1 < 2 * DB) ak_n = tk.atr(ks, kb, (n + 1) / DB, (n + 1) % DB);
+            dq[n % DB] = E::mfma(ak, sB[n / DB], dq[n % DB]);
+            ak = ak_n;
+          }
+        } else {
 #pragma unroll
-          for (int d = 0; d < DB; ++d) dq[d] = E::mfma(tk.atr(ks, kb, sh, d), sB, dq[d]);
+          for (int sh = 0; sh < 2; ++sh) {
+            const x8 sB = pack8<F16>(sv + 8 * sh);
+#pragma unroll
+            for (int d = 0; d < DB; ++d) dq[d] = E::mfma(tk.atr(ks, kb, sh, d), sB, dq[d]);
+          }
         }
       }
     }
