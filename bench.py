@@ -20,6 +20,21 @@ through block info) and the long-context chunk (32/8 heads, 2048 queries at offs
 output and log-sum-exp), in TFLOP/s over 10 * D flops per allowed pair, and the block info of
 the 8192 x 8192 runtime mask from bytes and from packed bits.
 
+Timing. The GPU's clocks take some 10-20 ms of sustained work to ramp up after the idle
+seconds of input generation. Before the counted --warmup launches of every section, the same
+step therefore runs for --prewarm-ms milliseconds of wall time (default 200); the count and the
+time are reported (``timing.prewarm_ms``, ``timing.prewarm_launches``). The timed region is
+exactly --steps launches back to back between two device synchronizations, with an event
+recorded on the launch stream after each launch, so the line also carries the per-launch
+median and the mean of the first and the last quarter of the window. The prefill section also
+times launches one at a time with 512 MiB written between them (the 256 MiB last-level cache
+flushed), reported as ``timing.mall_flushed_median_ms`` beside the back-to-back figure.
+
+Measured peaks. Two probes of the library (sdpa_measure_mfma_bf16: only bf16 MFMAs, two waves
+per SIMD; sdpa_measure_stream_read: a 4 GiB streaming read) give the rates the chip sustains;
+every roofline carries its fraction of the vendor peak (``frac``) and of the measured one
+(``frac_of_measured``).
+
 Printed: one JSON line (rank 0) with the contract fields, a ``roofline`` object for the
 prefill kernel (achieved = algorithmic flops per launch / average launch time measured with
 HIP events on the launch stream; peak = 2500 TFLOP/s bf16 dense MFMA), a ``decode`` object with
@@ -50,10 +65,12 @@ BACKWARD_COUNTERS = (os.path.join(ROOT, "profiles", "bwd_causal_b4h16d128l4096_c
 def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    # the GPU's clocks take some 10-20 ms of sustained work to ramp up after the idle seconds of
-    # input generation: 100 untimed launches (about 30 ms of prefill) reach the steady state
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    # the clocks ramp up over 10-20 ms of sustained work: every section first runs its own step
+    # for this much wall time (reported in the line), then the counted warm-up launches
+    p.add_argument("--prewarm-ms", type=float, default=200.0)
+    p.add_argument("--skip-peaks", action="store_true", help="skip the measured-peak probes")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU budget of the oracle baseline")
     p.add_argument("--copy-calibration", action="store_true",
@@ -85,21 +102,115 @@ def counters_traffic(counters):
     return float(m_bytes.group(1))
 
 
-def time_steps(fn, steps, warmup, stream):
+PREWARM_MS = 200.0          # set from --prewarm-ms in main()
+TIMINGS = {}                # section -> per-launch statistics of its timed window
+
+
+def prewarm(fn, ms):
+    """Run fn back to back until `ms` of wall time have passed (the clocks ramp up under load)."""
     import torch
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) * 1e3
+        if el >= ms:
+            return n, el
+
+
+def time_steps(fn, steps, warmup, stream, label=None):
+    """--prewarm-ms of fn, `warmup` counted launches, then exactly `steps` timed launches back to
+    back on `stream`, with an event after each. Returns (seconds for all steps, wall seconds);
+    the per-launch statistics go to TIMINGS[label]."""
+    import torch
+    pw_n, pw_ms = prewarm(fn, PREWARM_MS)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         fn()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / 1e3, wall
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    q = max(1, steps // 4)
+    if label:
+        TIMINGS[label] = {"prewarm_ms": round(pw_ms, 1), "prewarm_launches": pw_n, "warmup": warmup,
+                          "median_ms": round(float(sorted(per)[len(per) // 2]), 4),
+                          "first_quarter_ms": round(sum(per[:q]) / q, 4),
+                          "last_quarter_ms": round(sum(per[-q:]) / q, 4)}
+    return ev[0].elapsed_time(ev[-1]) / 1e3, wall
+
+
+def time_flushed(fn, n, stream, flush_bytes=512 << 20):
+    """Median milliseconds of `n` single launches, each after `flush_bytes` written to a scratch
+    buffer (more than the 256 MiB last-level cache holds), timed by events around the launch."""
+    import torch
+    buf = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):                      # queued back to back: the GPU never idles in between
+        buf.fill_(i & 255)
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    times = [e0.elapsed_time(e1) for e0, e1 in ev]
+    del buf
+    return float(sorted(times)[n // 2])
+
+
+def measured_peaks(stream):
+    """The bf16 MFMA rate and the HBM streaming-read rate this GPU sustains, from the library's
+    two probes (median of 5 timed launches each, after a time-based warm-up)."""
+    import torch
+    import transformer_attention_sdpa_amd as sa
+    res = {}
+    wgs, iters = 512, 20000                        # 2 workgroups per CU: two waves per SIMD
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    flops = [0.0]
+
+    def mf():
+        flops[0] = sa.measure_mfma_bf16(wgs, iters, sink)
+    prewarm(mf, PREWARM_MS)
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        mf()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3)
+    t = sorted(ts)[2]
+    res["mfma_bf16_tflops"] = round(flops[0] / t / 1e12, 1)
+    res["mfma_probe"] = f"{wgs} workgroups x 4 waves x {iters} x 4 v_mfma_f32_32x32x16_bf16, median of 5"
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    ssink = torch.empty(2048 * 4, dtype=torch.int32, device="cuda")
+    nb = [0]
+
+    def rd():
+        nb[0] = sa.measure_stream_read(buf, 2048, ssink)
+    prewarm(rd, PREWARM_MS)
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3)
+    t = sorted(ts)[2]
+    res["hbm_read_gbs"] = round(nb[0] / t / 1e9, 1)
+    res["read_probe"] = "4 GiB streaming read, 16-byte loads, 2048 workgroups of 256, median of 5"
+    del buf, ssink, sink
+    torch.cuda.empty_cache()
+    return res
 
 
 def oracle_rows_parity(out, w, rows):
@@ -140,6 +251,17 @@ def backward_parity(w, q, k, v, outb, dout, lse, grads):
             "bar": "max_abs/max(1,|ref|) <= 2e-2, rel_l2 <= 5e-3"}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -168,7 +290,9 @@ def cpu_baseline_prefill(w, budget_s):
     flops = 4.0 * D * (Lq * (Lq + 1) / 2) * done
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
             "sample": f"{done} of {B * Hq} (batch, head) pairs, all {Lq} query rows each, fp64 numpy",
-            "seconds": round(t_total, 2)}
+            "seconds": round(t_total, 2), "cpu_model": cpu_model(),
+            "affinity_cores": len(os.sched_getaffinity(0)),
+            "cores_note": "cores = the BLAS threads the oracle's matrix products ran on"}
 
 
 def main():
@@ -181,9 +305,15 @@ def main():
     import workloads
     import transformer_attention_sdpa_amd as sa
 
+    global PREWARM_MS
+    PREWARM_MS = args.prewarm_ms
     sa.load()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    peaks = None if args.skip_peaks else measured_peaks(stream)
+
+    def frac_measured(achieved, key):
+        return round(achieved / peaks[key], 4) if peaks else None
 
     # ---- causal prefill -------------------------------------------------------------------
     w = workloads.causal_prefill()
@@ -197,7 +327,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     step = lambda: sa.sdpa(q, k, v, is_causal=True, scale=w.scale, out=out)
-    t_gpu, t_wall = time_steps(step, args.steps, args.warmup, stream)
+    t_gpu, t_wall = time_steps(step, args.steps, args.warmup, stream, "prefill")
+    TIMINGS["prefill"]["mall_flushed_median_ms"] = round(time_flushed(step, 10, stream), 4)
     pairs = B * Hq * Lq * (Lq + 1) / 2
     flops = 4.0 * D * pairs
     per_launch = t_gpu / args.steps
@@ -221,7 +352,11 @@ def main():
                    "kv_len": Lkv, "is_causal": True, "scale": w.scale, "out_dtype": "bf16"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": counters_traffic(PREFILL_COUNTERS),
-                     "kernel": "fwd_mfma_kernel<128,0,0>", "flops_per_launch": flops},
+                     "kernel": "fwd_mfma_kernel<128,0,0>", "flops_per_launch": flops,
+                     "measured_peak": peaks["mfma_bf16_tflops"] if peaks else None,
+                     "frac_of_measured": frac_measured(tflops, "mfma_bf16_tflops")},
+        "timing": TIMINGS["prefill"],
+        "measured_peaks": peaks,
         "parity": {"rows_checked": f"{len(rows)} query rows x {B * Hq} (batch, head)", "max_abs": p_max,
                    "rel_l2": p_rel, "bar": "max_abs <= 2e-2, rel_l2 <= 5e-3 (bf16 output)"},
         "wall_s_timed_region": round(t_wall, 4),
@@ -239,7 +374,7 @@ def main():
         bstep = lambda: sa.sdpa_bwd(q, k, v, outb, dout, lse, is_causal=True, scale=w.scale, grads=grads,
                                     workspace=bws)
         bsteps = max(1, args.steps // 2)
-        t_b, _ = time_steps(bstep, bsteps, max(1, args.warmup // 4), stream)
+        t_b, _ = time_steps(bstep, bsteps, max(1, args.warmup // 2), stream, "backward")
         flops_b = 10.0 * D * pairs
         tf_b = flops_b / (t_b / bsteps) / 1e12
         result["backward"] = {
@@ -249,9 +384,10 @@ def main():
                        "is_causal": True, "grad_dtype": "bf16", "saved_out_dtype": "bf16"},
             "roofline": {"bound": "mfma", "achieved": round(tf_b, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "traffic": counters_traffic(BACKWARD_COUNTERS),
-                         "flops_per_call": flops_b,
+                         "flops_per_call": flops_b, "frac_of_measured": frac_measured(tf_b, "mfma_bf16_tflops"),
                          "kernel": "bwd_prep + bwd_dkdv8_kernel<128> + bwd_dq_mfma_kernel<128> + bwd_dscale"},
             "parity": backward_parity(w, q, k, v, outb, dout, lse, grads),
+            "timing": TIMINGS["backward"],
         }
         del out32, outb, dout, grads, bws, lse
     del q, k, v, out
@@ -274,9 +410,9 @@ def main():
             sa.kv_cache_update(kc, vc, kn, vn, widx)
             sa.sdpa_decode(qd, kc, vc, kvl, scale=d.scale, out=od, workspace=ws)
 
-        td, _ = time_steps(dstep, args.steps, args.warmup, stream)
+        td, _ = time_steps(dstep, args.steps, args.warmup, stream, "decode_with_update")
         tdec, _ = time_steps(lambda: sa.sdpa_decode(qd, kc, vc, kvl, scale=d.scale, out=od, workspace=ws),
-                             args.steps, args.warmup, stream)
+                             args.steps, args.warmup, stream, "decode")
         kv_bytes = float(np.sum(d.kv_lengths.astype(np.int64))) * Hkvd * Dd * 2 * 2
         io_bytes = float(Bd * Hqd * Dd * 2 * 2)
         gbs = (kv_bytes + io_bytes) / (tdec / args.steps) / 1e9
@@ -300,7 +436,10 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counters_traffic(DECODE_COUNTERS),
                          "bytes_per_step": kv_bytes + io_bytes,
+                         "measured_peak": peaks["hbm_read_gbs"] if peaks else None,
+                         "frac_of_measured": frac_measured(gbs, "hbm_read_gbs"),
                          "note": "split + combine kernels together (one sdpa_decode call)"},
+            "timing": TIMINGS["decode"], "timing_with_update": TIMINGS["decode_with_update"],
             "parity": {"sequences_checked": sel, "max_abs": float(np.max(np.abs(diff))),
                        "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(np.stack(refs)))},
         }
@@ -319,7 +458,7 @@ def main():
         for name, m in (("u8", mu8), ("u1", mu1)):
             store = sa.build_block_mask_info(m, 128, 128).storage          # reused by the timed calls
             t_mi, _ = time_steps(lambda m=m, st=store: sa.build_block_mask_info(m, 128, 128, storage=st),
-                                 args.steps, args.warmup, stream)
+                                 args.steps, args.warmup, stream, "mask_info_" + name)
             infos[name] = sa.build_block_mask_info(m, 128, 128).to_numpy()
             mask_bytes = mask.size if name == "u8" else mask.size / 8
             mi[name] = {"ms": round(t_mi / args.steps * 1e3, 4),
@@ -346,7 +485,7 @@ def main():
         out4 = torch.empty((B4_, Lq4, Hq4, D4), dtype=torch.bfloat16, device="cuda")
         st4 = lambda: sa.sdpa(q4, k4, v4, bias4, None, mask_info=info4, scale=w4.scale, out=out4)
         n4 = max(2, args.steps // 2)
-        t4, _ = time_steps(st4, n4, max(2, args.warmup // 3), stream)
+        t4, _ = time_steps(st4, n4, max(2, args.warmup // 2), stream, "bias_block_mask")
         fl4 = float(nonempty) * B4_ * Hq4 * 4.0 * 128 * 128 * D4
         bias_bytes = float(nonempty) * Hq4 * 128 * 128 * 2
         per4 = t4 / n4
@@ -359,7 +498,9 @@ def main():
             "roofline": {"bound": "mixed: MFMA and the bias stream", "mfma_frac": round(fl4 / per4 / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "bias_GB_per_s": round(bias_bytes / per4 / 1e9, 1),
                          "bias_frac_of_hbm": round(bias_bytes / per4 / 1e9 / PEAK_HBM_GBS, 4),
+                         "mfma_frac_of_measured": frac_measured(fl4 / per4 / 1e12, "mfma_bf16_tflops"),
                          "note": "bias bytes of the non-empty blocks counted once (the batch shares them)"},
+            "timing": TIMINGS["bias_block_mask"],
         }
         del q4, k4, v4, bias4, info4, out4
         torch.cuda.empty_cache()
@@ -370,7 +511,7 @@ def main():
         qo5 = int(w5.q_offset)
         st5 = lambda: sa.sdpa(q5, k5, v5, is_causal=True, q_offset=qo5, scale=w5.scale, out=out5)
         n5 = max(2, args.steps // 5)
-        t5, _ = time_steps(st5, n5, max(2, args.warmup // 10), stream)
+        t5, _ = time_steps(st5, n5, max(2, args.warmup // 5), stream, "chunked_prefill")
         pairs5 = float(Lq5) * qo5 + Lq5 * (Lq5 + 1) / 2
         fl5 = 4.0 * D5 * pairs5 * Hq5 * B5
         per5 = t5 / n5
@@ -381,7 +522,8 @@ def main():
                        "q_len": Lq5, "kv_len": Lkv5, "q_offset": qo5, "is_causal": True},
             "roofline": {"bound": "mfma", "achieved": round(fl5 / per5 / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(fl5 / per5 / 1e12 / PEAK_BF16_TFLOPS, 4),
-                         "flops_per_launch": fl5},
+                         "flops_per_launch": fl5, "frac_of_measured": frac_measured(fl5 / per5 / 1e12, "mfma_bf16_tflops")},
+            "timing": TIMINGS["chunked_prefill"],
         }
         del q5, k5, v5, out5
         torch.cuda.empty_cache()

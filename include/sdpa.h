@@ -278,6 +278,27 @@ SDPA_API sdpa_status sdpa_debug_allowed_mask(const sdpa_tensor* q, const sdpa_te
                                     const int32_t* q_lengths, int32_t q_length_all,
                                     sdpa_tensor* allowed, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Measurement probes. They are not part of the attention operation: they measure the two
+ * roofline denominators (the bf16 matrix-core rate and the HBM streaming-read rate) on the
+ * device the library runs on, so that a kernel's fraction can be stated against the measured
+ * rates as well as against the vendor's published peaks.
+ *
+ * sdpa_measure_mfma_bf16: `workgroups` workgroups of 256 threads (two per CU at most); every
+ *   wave issues iters x 4 v_mfma_f32_32x32x16_bf16 on four independent accumulator chains and
+ *   nothing else. Work = workgroups * 4 * iters * 4 * 32768 flops. sink: device float array of
+ *   at least workgroups * 256 elements, overwritten with meaningless sums.
+ * sdpa_measure_stream_read: reads `bytes` of device memory at src (16-byte aligned, bytes a
+ *   multiple of 16) once, with 16-byte loads spread over `workgroups` workgroups of 256
+ *   threads. sink: device uint32 array of at least workgroups * 4 elements, overwritten.
+ * Both are asynchronous on `stream`; host-detectable errors: NULL pointers (NULL), sizes out of
+ *   range or a misaligned src (SHAPE), a sink too small (WORKSPACE).
+ * ------------------------------------------------------------------------------------- */
+SDPA_API sdpa_status sdpa_measure_mfma_bf16(int32_t workgroups, int32_t iters, float* sink, size_t sink_bytes,
+                                            void* stream);
+SDPA_API sdpa_status sdpa_measure_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
+                                              size_t sink_bytes, void* stream);
+
 /* Status text; detail of the last non-OK status on this thread (empty if none). */
 SDPA_API const char* sdpa_status_string(int32_t status);
 SDPA_API const char* sdpa_last_error(void);

@@ -5,7 +5,9 @@ Bar (floating point): fp32 inputs max-abs <= 1e-5; bf16 inputs (fp32 accumulate)
 <= 2e-2 and relative L2 <= 5e-3, both over the finite entries; NaN positions must match
 exactly. Integer/byte results are compared bit for bit.
 """
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -104,3 +106,22 @@ def assert_grad_close(got, ref, dtype, label=""):
     assert max_abs <= tol["max_abs"], f"{label}: max-abs/mag {max_abs:.3e} > {tol['max_abs']}"
     if tol["rel_l2"] is not None:
         assert rel <= tol["rel_l2"], f"{label}: rel-L2 {rel:.3e} > {tol['rel_l2']}"
+
+
+def oracle_pool(jobs, workers=None):
+    """Results of the zero-argument oracle calls ``jobs``, run on a thread pool with one BLAS
+    thread per worker (numpy releases the GIL in its matrix products and element loops). The
+    pool is sized to the host's cores, at most 16."""
+    from threadpoolctl import threadpool_limits
+    n = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    with threadpool_limits(limits=1, user_api="blas"):
+        with ThreadPoolExecutor(n) as ex:
+            return list(ex.map(lambda f: f(), jobs))
+
+
+def nan_like(shape, dtype, device="cuda"):
+    """A tensor filled with NaN (floating dtypes) or 0xFF bytes (uint8), to poison an output or a
+    workspace: any element a kernel fails to write stays NaN and fails the comparison."""
+    if dtype == torch.uint8:
+        return torch.full(shape, 0xFF, dtype=dtype, device=device)
+    return torch.full(shape, float("nan"), dtype=dtype, device=device)

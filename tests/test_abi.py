@@ -244,3 +244,23 @@ def test_bwd_workspace_bytes(lib):
     n = lib.sdpa_bwd_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v))
     rows = 3 * 8 * 5
     assert n == 3 * ((rows * 4 + 255) // 256 * 256) + 256      # + one chunk of first-stage dscale sums
+
+
+def test_decode_per_batch_lengths_are_checked_on_the_host(lib):
+    # the kernels read kv_lengths[b] (and write_index[b]) for every batch element: a shorter
+    # array is refused before anything reaches the device; an int or one entry broadcasts
+    import numpy as np
+    import torch
+    from transformer_attention_sdpa_amd.api import _per_batch_tensor
+    q = torch.zeros((3, 1, 4, 128), dtype=torch.bfloat16)
+    kc = torch.zeros((3, 16, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="kv_lengths needs one entry per batch element"):
+        sa.sdpa_decode(q, kc, kc, [5, 6])
+    with pytest.raises(ValueError, match="kv_lengths needs one entry per batch element"):
+        sa.sdpa_decode(q, kc, kc, np.array([5, 6, 7, 8], dtype=np.int32))
+    with pytest.raises(ValueError, match="write_index needs one entry per batch element"):
+        sa.kv_cache_update(kc, kc, q[:, :, :2], q[:, :, :2], [0, 1])
+    assert _per_batch_tensor(5, 3, "cpu", "x").tolist() == [5, 5, 5]
+    assert _per_batch_tensor([7], 3, "cpu", "x").tolist() == [7, 7, 7]
+    assert _per_batch_tensor(np.array([1, 2, 3]), 3, "cpu", "x").dtype == torch.int32
+

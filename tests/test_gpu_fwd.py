@@ -233,3 +233,74 @@ def test_bf16_bias_fused_path_d64(lib, dtype, bias_shape):
     say(f"bf16 bias fused D=64 {dtype} {bias_shape}")
     assert_close(run_gpu(w).cpu().numpy(), run_oracle(w), dtype, "bias dense mask")
     assert_close(run_gpu(w, use_mask_info=True, bq=128, bkv=64).cpu().numpy(), run_oracle(w), dtype, "bias info")
+
+
+@pytest.mark.parametrize("D,dtype,bias_dtype", [(64, "bf16", "bf16"), (128, "bf16", "bf16"), (64, "bf16", "f32"),
+                                                (128, "f16", "f32"), (32, "bf16", "bf16")])
+def test_bias_at_dtype_minimum_is_finite(lib, D, dtype, bias_dtype):
+    # an additive mask filled with the bias dtype's most negative finite value: the logits stay
+    # finite ("Arguments": the bias is added to the logits), so a row whose every key carries it
+    # is the mean of the values, and such keys get no weight in a row that also has ordinary
+    # keys. Covers the fused bias (D 64, bf16), the per-element bias (D 128, f32 bias) and the
+    # general kernel (D 32); a -inf bias stays a masked key
+    say(f"bias at the dtype minimum D={D} {dtype} bias {bias_dtype}")
+    w = workloads.random_attention(4200 + D, 2, 130, 150, 4, 2, D, dtype=dtype, bias_shape=(2, 4, 130, 150),
+                                   bias_dtype=bias_dtype, is_causal=True, q_offset=20)
+    lo = np.finfo(np.float32).min if bias_dtype == "f32" else None
+    if bias_dtype == "bf16":
+        w.bias[0, :, 3, :] = 0xFF7F                           # bf16 -3.39e38: the whole row
+        w.bias[1, :, 70, :75] = 0xFF7F                        # half of a row
+        w.bias[1, 2, 100, :] = 0xFF80                         # -inf: the whole row is masked
+    else:
+        w.bias[0, :, 3, :] = lo
+        w.bias[1, :, 70, :75] = lo
+        w.bias[1, 2, 100, :] = -np.inf
+    ref = run_oracle(w)
+    assert np.isfinite(ref[0, 3]).all() and np.isnan(ref[1, 100, 2]).all()
+    assert_close(run_gpu(w).cpu().numpy(), ref, dtype, "bias at the dtype minimum")
+
+
+@pytest.mark.parametrize("shape", [(2, 16, 16), (4, 8, 2)])
+def test_causal_grouped_head_order_whole_output(lib, shape):
+    # a causal launch with B * Hq a multiple of 32 takes the grouped order (every XCD runs its
+    # heads four at a time, longest query tile first), as the full-size causal prefill does;
+    # every element against the oracle, with 640 queries (five 128-row tiles)
+    B, Hq, Hkv = shape
+    say(f"causal grouped order B{B} Hq{Hq} Hkv{Hkv} D128 L640")
+    w = workloads.random_attention(4300 + Hq, B, 640, 640, Hq, Hkv, 128, dtype="bf16", is_causal=True)
+    t = gpu_inputs(w)
+    out = torch.full((B, 640, Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    sa.sdpa(t["q"], t["k"], t["v"], is_causal=True, out=out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), run_oracle(w), "bf16", "grouped causal order")
+
+
+def test_side_stream(lib):
+    # a call on a side stream: the binding's temporaries (per-batch lengths from a host list,
+    # the workspace, the default output) are made on that stream, so the result equals the same
+    # call on the current stream
+    say("side stream")
+    w = workloads.random_attention(4400, 3, 130, 150, 4, 2, 128, dtype="bf16", is_causal="bottom_right",
+                                   kv_lengths=np.array([150, 77, 9], dtype=np.int32))
+    t = gpu_inputs(w)
+    ref = sa.sdpa(t["q"], t["k"], t["v"], is_causal="bottom_right", kv_lengths=[150, 77, 9], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    got = sa.sdpa(t["q"], t["k"], t["v"], is_causal="bottom_right", kv_lengths=[150, 77, 9], out_dtype=torch.float32,
+                  stream=s)
+    d = workloads.gqa_decode(B=3, Hq=8, Hkv=2, D=128, capacity=300, kv_min=50, kv_max=300, base=4401)
+    kc, vc = dev(d.k_cache, "bf16"), dev(d.v_cache, "bf16")
+    qd = dev(d.q, "bf16")
+    torch.cuda.synchronize()
+    sa.kv_cache_update(kc, vc, dev(d.k_new, "bf16"), dev(d.v_new, "bf16"), d.write_index.tolist(), stream=s)
+    od = sa.sdpa_decode(qd, kc, vc, d.kv_lengths.tolist(), scale=d.scale, out_dtype=torch.float32, stream=s)
+    s.synchronize()
+    # rows of the third sequence before its 9 keys attend nothing: NaN in both
+    assert torch.equal(torch.isnan(got), torch.isnan(ref)) and torch.isnan(got).any()
+    assert torch.equal(torch.nan_to_num(got, nan=5.0), torch.nan_to_num(ref, nan=5.0))
+    assert_close(got.cpu().numpy(), run_oracle(w), "bf16", "side stream prefill")
+    ekc, evc = oracle.kv_cache_update(d.k_cache, d.v_cache, d.k_new, d.v_new, d.write_index)
+    f = workloads.bf16_to_f32
+    refd = np.stack([oracle.sdpa(f(d.q[b:b + 1]), f(ekc[b:b + 1, :d.kv_lengths[b]]), f(evc[b:b + 1, :d.kv_lengths[b]]),
+                                 scale=d.scale, is_causal="bottom_right")[0] for b in range(3)])
+    assert_close(od.cpu().numpy(), refd, "bf16", "side stream decode")

@@ -70,6 +70,8 @@ PROTOTYPES = {
     "head_rms_norm": (I32, [T, T, ctypes.c_float, VP]),
     "sdpa_debug_allowed_mask": (I32, [T, T, T, ctypes.POINTER(BlockMaskInfoC), I32, I32P, I32, I32P, I32,
                                       I32P, I32, T, VP]),
+    "sdpa_measure_mfma_bf16": (I32, [I32, I32, VP, SZ, VP]),
+    "sdpa_measure_stream_read": (I32, [VP, SZ, I32, VP, SZ, VP]),
     "sdpa_status_string": (ctypes.c_char_p, [I32]),
     "sdpa_last_error": (ctypes.c_char_p, []),
     "sdpa_version": (ctypes.c_char_p, []),

@@ -6,8 +6,16 @@ column-major (head_dim, heads, seq, batch) with the dims reversed, so each descr
 to the library is the torch shape and strides read backwards. Every computation runs in the
 HIP library on the caller's current stream; nothing here computes on the host or falls back
 to another implementation.
+
+``stream=``: every entry point takes an optional torch stream. The call then runs as if that
+stream were current: the binding's own temporaries (int32 casts of per-batch arguments, the
+workspace, a default output) are made on it, so the kernels never read a temporary that another
+stream is still writing. Inputs the caller made on another stream are the caller's to order, as
+with any torch operation.
 """
+import contextlib
 import ctypes
+import functools
 import math
 
 import numpy as np
@@ -44,9 +52,21 @@ def desc(t: torch.Tensor) -> N.SdpaTensor:
     return d
 
 
-def _stream(stream):
+def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return s, ctypes.c_void_p(s.cuda_stream)
+
+
+def _on_stream(fn):
+    """Run ``fn`` with ``stream`` (a keyword argument, default the current stream) made current,
+    so that every tensor the binding creates for the call is made on the stream the kernels run
+    on."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        ctx = torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+        with ctx:
+            return fn(*args, **kwargs)
+    return wrapper
 
 
 def _per_batch_arg(x, B, device, none_value):
@@ -62,6 +82,21 @@ def _per_batch_arg(x, B, device, none_value):
     if t.numel() != B:
         raise ValueError("per-batch argument needs one entry per batch element")
     return t.data_ptr(), 0, t
+
+
+def _per_batch_tensor(x, B, device, name):
+    """An int, a one-element or a [B] array/tensor -> contiguous int32 [B] device tensor. The
+    count is checked before anything moves to the device: the kernels read entry b of every
+    batch element b, so a shorter array would be read past its end."""
+    if isinstance(x, (int, np.integer)):
+        return torch.full((B,), int(x), dtype=torch.int32, device=device)
+    t = x if isinstance(x, torch.Tensor) else torch.as_tensor(np.asarray(x, dtype=np.int32))
+    t = t.reshape(-1)
+    if t.numel() == 1:
+        t = t.expand(B)
+    if t.numel() != B:
+        raise ValueError(f"{name} needs one entry per batch element ({B}), got {t.numel()}")
+    return t.to(device=device, dtype=torch.int32).contiguous()
 
 
 class PackedMask:
@@ -143,7 +178,8 @@ class BlockMaskInfo:
         }
 
 
-def build_block_mask_info(mask: torch.Tensor, bq: int = 128, bkv: int = 128, stream=None,
+@_on_stream
+def build_block_mask_info(mask: torch.Tensor, bq: int = 128, bkv: int = 128,
                           storage: torch.Tensor = None) -> BlockMaskInfo:
     """Block info of a runtime device mask [Mb][Mh][Lq][Lkv] (bool or uint8, or a PackedMask).
 
@@ -160,17 +196,15 @@ def build_block_mask_info(mask: torch.Tensor, bq: int = 128, bkv: int = 128, str
     elif storage.numel() < int(nbytes.value):
         raise ValueError(f"storage needs {int(nbytes.value)} bytes")
     info = N.BlockMaskInfoC()
-    s, sp = _stream(stream)
+    s, sp = _stream()
     N.check(lib.build_block_mask_info(ctypes.byref(dm), bq, bkv, ctypes.c_void_p(storage.data_ptr()),
                                       storage.numel(), ctypes.byref(info), sp))
-    if stream is not None:
-        storage.record_stream(s)
     return BlockMaskInfo(storage, info, m.shape)
 
 
+@_on_stream
 def sdpa(q, k, v, bias=None, mask=None, *, mask_info: BlockMaskInfo = None, scale=None, is_causal=False,
-         q_offset=0, kv_lengths=None, q_lengths=None, qk_norm=False, out=None, out_dtype=None, stream=None,
-         return_lse=False):
+         q_offset=0, kv_lengths=None, q_lengths=None, qk_norm=False, out=None, out_dtype=None, return_lse=False):
     """Scaled dot-product attention. q [B][Lq][Hq][D], k [B][Lkv][Hkv][D], v [B][Lkv][Hkv][Dv].
 
     is_causal: False, True or "bottom_right". q_offset, kv_lengths, q_lengths: int, None or a
@@ -191,7 +225,7 @@ def sdpa(q, k, v, bias=None, mask=None, *, mask_info: BlockMaskInfo = None, scal
     ql_ptr, ql_all, ql_keep = _per_batch_arg(q_lengths, B, q.device, -1)
     ws_bytes = lib.sdpa_fwd_workspace_bytes(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(bool(qk_norm)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
-    s, sp = _stream(stream)
+    s, sp = _stream()
     lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
     st = lib.sdpa_fwd_lse(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
                           ctypes.byref(db) if db is not None else None,
@@ -202,16 +236,13 @@ def sdpa(q, k, v, bias=None, mask=None, *, mask_info: BlockMaskInfo = None, scal
                           ctypes.byref(do), ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
                           ctypes.c_void_p(ws.data_ptr()) if ws is not None else None, ws_bytes, sp)
     N.check(st)
-    if stream is not None:
-        for t in (ws, qo_keep, kv_keep, ql_keep):
-            if t is not None:
-                t.record_stream(s)
     return (out, lse) if return_lse else out
 
 
+@_on_stream
 def sdpa_bwd(q, k, v, out, dout, lse, mask=None, *, mask_info: BlockMaskInfo = None, scale=None,
              is_causal=False, q_offset=0, kv_lengths=None, q_lengths=None, grad_dtype=None, grads=None,
-             workspace=None, stream=None):
+             workspace=None):
     """Gradient of ``sdpa`` with respect to q, k, v and scale (sdpa_bwd).
 
     out and lse come from ``sdpa(..., return_lse=True)`` of the same call; dout is the cotangent
@@ -242,7 +273,7 @@ def sdpa_bwd(q, k, v, out, dout, lse, mask=None, *, mask_info: BlockMaskInfo = N
         raise ValueError(f"workspace needs {ws_bytes} bytes")
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Lq):
         raise ValueError("lse must be a contiguous fp32 [B][Hq][Lq] tensor")
-    s, sp = _stream(stream)
+    s, sp = _stream()
     st = lib.sdpa_bwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(to), ctypes.byref(tdo),
                       ctypes.c_void_p(lse.data_ptr()), ctypes.byref(dm) if dm is not None else None,
                       ctypes.byref(mask_info.c) if mask_info is not None else None,
@@ -251,15 +282,12 @@ def sdpa_bwd(q, k, v, out, dout, lse, mask=None, *, mask_info: BlockMaskInfo = N
                       ctypes.byref(gq), ctypes.byref(gk), ctypes.byref(gv), ctypes.c_void_p(dscale.data_ptr()),
                       ctypes.c_void_p(ws.data_ptr()), ws_bytes, sp)
     N.check(st)
-    if stream is not None:
-        for t in (ws, qo_keep, kv_keep, ql_keep):
-            if t is not None:
-                t.record_stream(s)
     return dq_t, dk_t, dv_t, dscale
 
 
+@_on_stream
 def sdpa_packed(q, k, v, q_segments, kv_segments=None, *, maxlen=None, scale=None, is_causal=False, q_offset=0,
-                kv_lengths=None, q_lengths=None, qk_norm=False, out=None, out_dtype=None, stream=None):
+                kv_lengths=None, q_lengths=None, qk_norm=False, out=None, out_dtype=None):
     """Attention over packed sequences. q [Lq_total][Hq][D], k [Lkv_total][Hkv][D], v [Lkv_total][Hkv][Dv]
     hold the segments one after the other; q_segments / kv_segments (device int32 tensors, kv =
     q when None) give their lengths. Segment s of q attends segment s of k/v only; is_causal,
@@ -283,7 +311,7 @@ def sdpa_packed(q, k, v, q_segments, kv_segments=None, *, maxlen=None, scale=Non
     ql_ptr, ql_all, ql_keep = _per_batch_arg(q_lengths, S, q.device, -1)
     ws_bytes = lib.sdpa_fwd_workspace_bytes(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(bool(qk_norm)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
-    s, sp = _stream(stream)
+    s, sp = _stream()
     st = lib.sdpa_fwd_packed(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
                              ctypes.c_void_p(qs.data_ptr()) if S else None,
                              ctypes.c_void_p(ks.data_ptr()) if ks is not None and S else None, S,
@@ -293,10 +321,6 @@ def sdpa_packed(q, k, v, q_segments, kv_segments=None, *, maxlen=None, scale=Non
                              ctypes.byref(do), ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
                              ws_bytes, sp)
     N.check(st)
-    if stream is not None:
-        for t in (ws, qs, ks, qo_keep, kv_keep, ql_keep):
-            if t is not None:
-                t.record_stream(s)
     return out
 
 
@@ -313,50 +337,47 @@ def decode_workspace_bytes(q, k_cache, num_splits=0) -> int:
     return int(lib.sdpa_decode_workspace_bytes(ctypes.byref(dq), ctypes.byref(dk), int(num_splits)))
 
 
+@_on_stream
 def sdpa_decode(q, k_cache, v_cache, kv_lengths, *, scale=None, num_splits=0, out=None, out_dtype=None,
-                workspace=None, stream=None):
+                workspace=None):
     """The newest T queries of each sequence, q [B][T][Hq][D], against caches [B][cap][Hkv][D]:
-    query t attends keys [0, kv_lengths[b] - T + t] (bottom-right causal)."""
+    query t attends keys [0, kv_lengths[b] - T + t] (bottom-right causal). kv_lengths: an int,
+    or one entry per sequence (a one-element array broadcasts)."""
     lib = N.load()
     B, T, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, T, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
     dq, dk, dv, do = desc(q), desc(k_cache), desc(v_cache), desc(out)
-    kv = torch.as_tensor(kv_lengths, dtype=torch.int32, device=q.device).contiguous()
+    kv = _per_batch_tensor(kv_lengths, B, q.device, "kv_lengths")
     need = int(lib.sdpa_decode_workspace_bytes(ctypes.byref(dq), ctypes.byref(dk), int(num_splits)))
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    s, sp = _stream(stream)
+    s, sp = _stream()
     N.check(lib.sdpa_decode(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.c_void_p(kv.data_ptr()),
                             float("nan") if scale is None else float(scale), int(num_splits), ctypes.byref(do),
                             ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), sp))
-    if stream is not None:
-        ws.record_stream(s)
-        kv.record_stream(s)
     return out
 
 
-def kv_cache_update(k_cache, v_cache, k_new, v_new, write_index, stream=None):
+@_on_stream
+def kv_cache_update(k_cache, v_cache, k_new, v_new, write_index):
     """In place: cache[b][write_index[b] + t] = new[b][t] for k and v (rows outside the cache skipped)."""
     lib = N.load()
     B = k_cache.shape[0]
-    wi = torch.as_tensor(write_index, dtype=torch.int32, device=k_cache.device).contiguous()
-    if wi.numel() != B:
-        raise ValueError("write_index needs one entry per batch element")
+    wi = _per_batch_tensor(write_index, B, k_cache.device, "write_index")
     dkc, dvc, dkn, dvn = desc(k_cache), desc(v_cache), desc(k_new), desc(v_new)
-    s, sp = _stream(stream)
+    s, sp = _stream()
     N.check(lib.kv_cache_update(ctypes.byref(dkc), ctypes.byref(dvc), ctypes.byref(dkn), ctypes.byref(dvn),
                                 ctypes.c_void_p(wi.data_ptr()), sp))
-    if stream is not None:
-        wi.record_stream(s)
     return k_cache, v_cache
 
 
-def head_rms_norm(x, eps=1e-6, out=None, stream=None):
+@_on_stream
+def head_rms_norm(x, eps=1e-6, out=None):
     """x [B][T][H][Dh] -> every head vector divided by sqrt(mean(v^2) + eps)."""
     lib = N.load()
     y = torch.empty_like(x) if out is None else out
     dx, dy = desc(x), desc(y)
-    _, sp = _stream(stream)
+    _, sp = _stream()
     N.check(lib.head_rms_norm(ctypes.byref(dx), ctypes.byref(dy), float(eps), sp))
     return y
 
@@ -373,8 +394,9 @@ def per_head_rms_norm(x, num_heads: int, eps=1e-6) -> dict:
     return {"heads": heads, "merged": merged}
 
 
+@_on_stream
 def debug_allowed_mask(q, k, mask=None, *, mask_info=None, is_causal=False, q_offset=0, kv_lengths=None,
-                       q_lengths=None, stream=None):
+                       q_lengths=None):
     """uint8 [B][Hq][Lq][Lkv]: 1 where the kernels let query i attend key j."""
     lib = N.load()
     B, Lq, Hq, _ = q.shape
@@ -386,7 +408,7 @@ def debug_allowed_mask(q, k, mask=None, *, mask_info=None, is_causal=False, q_of
     qo_ptr, qo_all, _k1 = _per_batch_arg(q_offset, B, q.device, 0)
     kv_ptr, kv_all, _k2 = _per_batch_arg(kv_lengths, B, q.device, -1)
     ql_ptr, ql_all, _k3 = _per_batch_arg(q_lengths, B, q.device, -1)
-    _, sp = _stream(stream)
+    _, sp = _stream()
     N.check(lib.sdpa_debug_allowed_mask(ctypes.byref(dq), ctypes.byref(dk),
                                         ctypes.byref(dm) if dm is not None else None,
                                         ctypes.byref(mask_info.c) if mask_info is not None else None,
@@ -417,3 +439,30 @@ def from_numpy(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
 def to_numpy_f32(t: torch.Tensor) -> np.ndarray:
     """Device tensor -> float32 numpy (bf16 widened exactly; a copy, no other arithmetic)."""
     return t.detach().float().cpu().numpy()
+
+
+@_on_stream
+def measure_mfma_bf16(workgroups: int, iters: int, sink: torch.Tensor = None) -> float:
+    """Launch the matrix-core rate probe (sdpa_measure_mfma_bf16) on the current stream; returns
+    the flops it executes: workgroups * 4 waves * iters * 4 MFMAs * 32768."""
+    lib = N.load()
+    if sink is None:
+        sink = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+    _, sp = _stream()
+    N.check(lib.sdpa_measure_mfma_bf16(int(workgroups), int(iters), ctypes.c_void_p(sink.data_ptr()),
+                                       sink.numel() * 4, sp))
+    return float(workgroups) * 4 * iters * 4 * 32768
+
+
+@_on_stream
+def measure_stream_read(buf: torch.Tensor, workgroups: int = 2048, sink: torch.Tensor = None) -> int:
+    """Launch the streaming-read probe (sdpa_measure_stream_read) over the bytes of ``buf``;
+    returns the bytes it reads."""
+    lib = N.load()
+    nbytes = (buf.numel() * buf.element_size()) & ~15
+    if sink is None:
+        sink = torch.empty(workgroups * 4, dtype=torch.int32, device=buf.device)
+    _, sp = _stream()
+    N.check(lib.sdpa_measure_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, int(workgroups),
+                                         ctypes.c_void_p(sink.data_ptr()), sink.numel() * 4, sp))
+    return nbytes

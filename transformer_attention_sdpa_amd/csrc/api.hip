@@ -219,6 +219,29 @@ const char* sdpa_last_error(void) { return g_err.c_str(); }
 
 const char* sdpa_version(void) { return "sdpa_mi355x 0.1 gfx950"; }
 
+sdpa_status sdpa_measure_mfma_bf16(int32_t workgroups, int32_t iters, float* sink, size_t sink_bytes, void* stream) {
+  g_err.clear();
+  if (!sink) return fail(SDPA_ERR_NULL, "sink is required");
+  if (workgroups < 1 || iters < 1) return fail(SDPA_ERR_SHAPE, "workgroups and iters must be positive");
+  if (sink_bytes < (size_t)workgroups * 256 * sizeof(float))
+    return fail(SDPA_ERR_WORKSPACE, "sink needs %zu bytes", (size_t)workgroups * 256 * sizeof(float));
+  return hip_status(launch_measure_mfma(workgroups, iters, sink, static_cast<hipStream_t>(stream)),
+                    "sdpa_measure_mfma_bf16");
+}
+
+sdpa_status sdpa_measure_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
+                                     size_t sink_bytes, void* stream) {
+  g_err.clear();
+  if (!src || !sink) return fail(SDPA_ERR_NULL, "src and sink are required");
+  if (workgroups < 1 || bytes == 0 || bytes % 16 || (reinterpret_cast<uintptr_t>(src) & 15))
+    return fail(SDPA_ERR_SHAPE, "need workgroups >= 1, bytes a positive multiple of 16, src 16-byte aligned");
+  if (sink_bytes < (size_t)workgroups * 4 * sizeof(uint32_t))
+    return fail(SDPA_ERR_WORKSPACE, "sink needs %zu bytes", (size_t)workgroups * 4 * sizeof(uint32_t));
+  return hip_status(launch_stream_read(src, bytes, sink, workgroups, static_cast<hipStream_t>(stream)),
+                    "sdpa_measure_stream_read");
+}
+
+
 sdpa_status sdpa_fwd_packed(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
                             const int32_t* q_segments, const int32_t* kv_segments, int32_t n_segments, int32_t maxlen,
                             float scale, int32_t is_causal, const int32_t* q_offset, int32_t q_offset_all,

@@ -73,6 +73,11 @@ __device__ __forceinline__ int v_swz(int row) { return D == 128 ? 4 * (row & 3) 
 constexpr int kGroupHeads = 4;
 
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units: the running max moves only when a row's max grows by more
+// The fused bias path forms the logits against m_s = m_run clamped to [-kStartLim, kStartLim]
+// (natural units): a start value of that size keeps q.k to within 2^-10 in the accumulator,
+// while a row max far outside it (a bias at the dtype's most negative value) would absorb q.k
+// into the start value entirely.
+constexpr float kStartLim = 16384.0f;
 
 template <int D, int BIAS, int MASK, bool NORM, bool F16, bool PACKED>
 __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt, int remap, int order) {
@@ -83,11 +88,18 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int SPT = BN * CPR / NT; // direct-load instructions per thread per tile (K or V)
   constexpr int TILE = BN * D;       // elements of one K or V tile in LDS
-  // FUSED: scale*log2e is folded into Q and each S MFMA chain starts from -m_run (plus
-  // log2e*bias for a bf16 bias at D = 64, FBIAS), so a probability is one exp2 of the
-  // accumulator. Otherwise the logits are scaled (and biased) per element.
+  // FUSED: the scale is folded into Q and each S MFMA chain starts from -m_run (plus the bias
+  // for a bf16 bias at D = 64, FBIAS), so the accumulator holds the logit minus the running
+  // max. Otherwise the logits are scaled (and biased) per element.
+  // NAT: with a bias the logits are kept in natural units and turned into log2 units only
+  // after the running max is subtracted. A finite bias below -FLT_MAX/log2(e) (an additive mask
+  // filled with the dtype's most negative value) then stays finite, as the definition has it,
+  // instead of overflowing to -inf and passing for a masked key. Without a bias the logits are
+  // in log2 units from the start (scale*log2e folded into Q, or into the per-element scale).
   constexpr bool FBIAS = BIAS == BIAS_BF16 && D == 64 && !NORM;
   constexpr bool FUSED = (BIAS == BIAS_NONE || FBIAS) && !NORM;
+  constexpr bool NAT = BIAS != BIAS_NONE;
+  constexpr float SLACK = NAT ? RESCALE_SLACK * LN2 : RESCALE_SLACK;   // in the logits' units
   // Four statically distinct tile buffers, so that the compiler's wait-count tracking can tell a
   // read of one from a direct load in flight into another.
   __shared__ __align__(16) uint16_t kbuf0[TILE], kbuf1[TILE], vbuf0[TILE], vbuf1[TILE];
@@ -220,7 +232,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
 
   // ---- Q^T operand (stays in registers); rows past Lq load as zeros ------------------------
   bf16x8 qB[DC];
-  float c_lane = a.scale * LOG2E;
+  float c_lane = NAT ? a.scale : a.scale * LOG2E;
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(a.q) + b * a.q_sb + h * a.q_sh,
                                                 (int64_t)a.Lq * a.q_ss * 2);
@@ -230,8 +242,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     for (int c = 0; c < DC; ++c) {
       uint4 x = buf_load16(rq, qoff + 32 * c);
       if constexpr (FUSED) {
-        // scale*log2e folded into Q (rounded to bf16 once): the q.k MFMAs then emit logits in
-        // the exp2 domain, and the softmax needs no multiply per score
+        // the scale (times log2e without a bias) folded into Q, rounded to 16 bits once: the
+        // q.k MFMAs then emit the logits, and the softmax needs no multiply per score
         uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -338,15 +350,15 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   for (int d = 0; d < DB; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
-  // Running max m_run (log2 units) and row sum l_run.
+  // Running max m_run (in the logits' units, see NAT) and row sum l_run.
   //  * FUSED: the scores are kept relative to the running max -- the q.k MFMAs start from
-  //    -m_run instead of zero, so they emit scale*log2e*q.k - m_run and a
-  //    probability is one exp2. m_run starts at 0 with threshold thr = -inf: the first tile
-  //    holding an allowed key of a row sets the row's max outright; after that the max moves
-  //    only when it grows by more than RESCALE_SLACK.
-  //  * otherwise: finite start, so exp2 of (masked -inf) - m_run is 0, and any finite score
-  //    grows it at once.
-  float m_run = FUSED ? 0.f : -1.0e30f, l_run = 0.f;
+  //    -m_run instead of zero, so they emit the logit minus m_run and a probability is one
+  //    exp2 (NAT: of that times log2e). m_run starts at 0 with threshold thr = -inf: the first
+  //    tile holding an allowed key of a row sets the row's max outright; after that the max
+  //    moves only when it grows by more than SLACK.
+  //  * otherwise: m_run starts at -inf; any finite logit grows it at once, and until one has
+  //    come the probabilities are taken against 0 (every logit so far is -inf).
+  float m_run = FUSED ? 0.f : -INFINITY, l_run = 0.f;
   float thr = -INFINITY;
 
   const int64_t bias_row = (BIAS != BIAS_NONE && i_me < a.Lq)
@@ -384,7 +396,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       }
     }
   };
-  // start values of an S chain: log2e*bias - m (FBIAS), -m (other FUSED), 0
+  // start values of an S chain: bias - m (FBIAS), -m (other FUSED), 0
   auto s_start = [&](const uint4 (&src)[2][2], float m, f32x16 (&c)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -393,8 +405,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
                                src[kb][1].x, src[kb][1].y, src[kb][1].z, src[kb][1].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          c[kb][2 * e] = fmaf(__uint_as_float(w[e] << 16), LOG2E, -m);
-          c[kb][2 * e + 1] = fmaf(__uint_as_float(w[e] & 0xffff0000u), LOG2E, -m);
+          c[kb][2 * e] = __uint_as_float(w[e] << 16) - m;
+          c[kb][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u) - m;
         }
       } else {
 #pragma unroll
@@ -468,8 +480,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
         blk_cls = cls_at(t / sub_per_blk, kb_blk);
         if (blk_cls == 1) need_mask = true;
       }
-      // logits in the exp2 domain. FUSED: s stays raw (the max is taken on raw scores, scaled
-      // once per row); else s becomes scale*log2e*r_q*r_k*s + log2e*bias.
+      // logits. FUSED: s is already the logit minus m_run; else s becomes
+      // c*r_q*r_k*s + bias, with c = scale (NAT) or scale*log2e.
       if constexpr (!FUSED) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -494,26 +506,25 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
                   const uint32_t w[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
                   for (int e = 0; e < 8; ++e) {
-                    s_cur[kb][2 * e] = fmaf(__uint_as_float(w[e] << 16), LOG2E, s_cur[kb][2 * e]);
-                    s_cur[kb][2 * e + 1] = fmaf(__uint_as_float(w[e] & 0xffff0000u), LOG2E, s_cur[kb][2 * e + 1]);
+                    s_cur[kb][2 * e] += __uint_as_float(w[e] << 16);
+                    s_cur[kb][2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
                   }
                 } else {
                   const float4* bp = reinterpret_cast<const float4*>(static_cast<const float*>(a.bias) + bias_row + jb);
 #pragma unroll
                   for (int v4 = 0; v4 < 4; ++v4) {
                     const float4 f = bp[v4];
-                    s_cur[kb][4 * v4 + 0] = fmaf(f.x, LOG2E, s_cur[kb][4 * v4 + 0]);
-                    s_cur[kb][4 * v4 + 1] = fmaf(f.y, LOG2E, s_cur[kb][4 * v4 + 1]);
-                    s_cur[kb][4 * v4 + 2] = fmaf(f.z, LOG2E, s_cur[kb][4 * v4 + 2]);
-                    s_cur[kb][4 * v4 + 3] = fmaf(f.w, LOG2E, s_cur[kb][4 * v4 + 3]);
+                    s_cur[kb][4 * v4 + 0] += f.x;
+                    s_cur[kb][4 * v4 + 1] += f.y;
+                    s_cur[kb][4 * v4 + 2] += f.z;
+                    s_cur[kb][4 * v4 + 3] += f.w;
                   }
                 }
               } else {
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
                   if (jb + e < a.Lkv)
-                    s_cur[kb][e] = fmaf(load_elem(a.bias, bias_row + (int64_t)(jb + e) * a.bias_sk, a.bias_dtype),
-                                        LOG2E, s_cur[kb][e]);
+                    s_cur[kb][e] += load_elem(a.bias, bias_row + (int64_t)(jb + e) * a.bias_sk, a.bias_dtype);
               }
             }
           }
@@ -593,7 +604,33 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s_cur[kb][e]);
-      if constexpr (FUSED) {
+      if constexpr (FUSED && NAT) {
+        // s_cur holds logits minus m_s, the clamped m_run the start values of S(t) were formed
+        // with; off = m_run - m_s is 0 unless the row max lies beyond the clamp. mt - off is the
+        // growth of the row max (thr: see above). With off != 0 every tile takes this branch and
+        // moves its scores to m_run (or to the new max) explicitly.
+        const float m_s = fminf(fmaxf(m_run, -kStartLim), kStartLim);
+        const float off = m_run - m_s;
+        if (__builtin_amdgcn_ballot_w64(mt - off > thr || off != 0.f)) {
+          mt = fmaxf(mt, __shfl_xor(mt, 32, 64));        // row max over both halves
+          const bool grow = mt - off > thr;              // thr and off are the same for both halves
+          const float dlt = grow ? mt : off;             // the scores become relative to m_new
+          const float m_new = grow ? m_s + mt : m_run;
+          // a row's first keys: nothing accumulated yet (and the exp2 may overflow)
+          const float alpha = thr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * LOG2E);
+          l_run *= alpha;
+#pragma unroll
+          for (int d = 0; d < DB; ++d)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s_cur[kb][e] -= dlt;
+          m_run = m_new;
+          if (grow) thr = SLACK;
+        }
+      } else if constexpr (FUSED) {
         // s_cur holds scores minus m_run: mt is the growth of the row max (thr: see above)
         if (__builtin_amdgcn_ballot_w64(mt > thr)) {
           mt = fmaxf(mt, __shfl_xor(mt, 32, 64));        // row max over both halves
@@ -611,13 +648,14 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
 #pragma unroll
             for (int e = 0; e < 16; ++e) s_cur[kb][e] -= dlt;
           m_run += dlt;
-          if (grow) thr = RESCALE_SLACK;
+          if (grow) thr = SLACK;
         }
-      } else if (__builtin_amdgcn_ballot_w64(mt > m_run + RESCALE_SLACK)) {
+      } else if (__builtin_amdgcn_ballot_w64(mt > m_run + SLACK)) {
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));          // row max over both halves
-        const bool grow = mt > m_run + RESCALE_SLACK;
+        const bool grow = mt > m_run + SLACK;
         const float m_new = grow ? mt : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on a row's first keys
+        // 0 on a row's first finite logit (m_run = -inf)
+        const float alpha = __builtin_amdgcn_exp2f(NAT ? (m_run - m_new) * LOG2E : m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int d = 0; d < DB; ++d)
@@ -625,7 +663,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
           for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
         m_run = m_new;
       }
-      const float m_use = m_run;
+      // no finite logit yet: every logit so far is -inf, and exp2(-inf - 0) = 0 (not NaN)
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
       // -- the tile body, in chunks the compiler may not reorder across ---------------------
       // The matrix cores and the VALU only run side by side when their instructions alternate
@@ -642,7 +681,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       uint32_t pw[16];                                   // the same, packed as bf16 pairs
       auto prob = [&](int f) {                           // element f = 16*kb + 8*sh + e
         const float xe = s_cur[f >> 4][f & 15];
-        pf[f] = FUSED ? __builtin_amdgcn_exp2f(xe) : __builtin_amdgcn_exp2f(xe - m_use);
+        // NAT: the max is subtracted in natural units first (no overflow), then scaled
+        float x2;
+        if constexpr (FUSED) x2 = NAT ? xe * LOG2E : xe;
+        else x2 = NAT ? (xe - m_use) * LOG2E : xe - m_use;
+        pf[f] = __builtin_amdgcn_exp2f(x2);
         if (f & 1) {
           pw[f >> 1] = E::pack(pf[f - 1], pf[f]);
           // row sum of the same 16-bit probabilities the MFMA consumes
@@ -664,11 +707,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       bf16x8 kf[PF + 1][2];
       // the C operand that starts S(t+1): zero, or -m_run broadcast (FUSED). Built here from an
       // opaque copy of m_run, so that its 16 registers live only until the first two MFMAs.
-      // FBIAS: one start vector per 32-key block (the bias of tile t + 1 is in set 1 - P);
-      // otherwise a single vector serves both blocks
+      // FBIAS: one start vector per 32-key block (the bias of tile t + 1 is in set 1 - P),
+      // against m_run clamped to [-kStartLim, kStartLim]; otherwise a single vector serves both
+      // blocks
       f32x16 c0[FBIAS ? 2 : 1];
       {
-        float m0 = m_run;
+        float m0 = FBIAS ? fminf(fmaxf(m_run, -kStartLim), kStartLim) : m_run;
         if constexpr (FUSED) asm volatile("" : "+v"(m0));
         if constexpr (FBIAS) {
           s_start(braw[1 - P], m0, c0);
@@ -742,9 +786,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   const bool zero_row = i_me >= nq;
   const float inv = zero_row ? 0.f : (l_tot > 0.f ? 1.0f / l_tot : NAN);
   if (a.lse && hh == 0) {
-    // m_run and l_run are in log2 units of the full logits (scale and bias included)
+    // m_run is in the logits' units (natural with a bias, else log2), l_run relative to it
     a.lse[b * a.lse_sb + h * a.lse_sh + i_me] =
-        (zero_row || !(l_tot > 0.f)) ? -INFINITY : (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+        (zero_row || !(l_tot > 0.f)) ? -INFINITY
+                                     : (NAT ? m_run + __log2f(l_tot) * LN2 : (m_run + __log2f(l_tot)) * LN2);
   }
   const int64_t orow = b * a.o_sb + (int64_t)i_me * a.o_ss + h * a.o_sh;
 #pragma unroll
