@@ -235,6 +235,23 @@ SDPA_API sdpa_status sdpa_decode(const sdpa_tensor* q, const sdpa_tensor* k_cach
 SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k_cache, int32_t num_splits);
 
 /* ---------------------------------------------------------------------------------------
+ * sdpa_decode_noalloc -- sdpa_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation). Same arguments,
+ * result and kernels as sdpa_decode, minus the workspace: the split partials go to a device
+ * array the library holds, sdpa_decode_noalloc_max_scratch_bytes() bytes (32 MiB) on every GPU
+ * the library runs on, kept until the process ends. A call whose partials need more
+ * (sdpa_decode_workspace_bytes() of the same arguments) returns SDPA_ERR_WORKSPACE without
+ * launching anything. The call allocates nothing. All calls on one GPU share its array, so
+ * calls that overlap on one GPU (on different streams, or from different threads without
+ * ordering) race; calls ordered on one stream do not. Nothing in the array needs clearing
+ * between calls: every partial a call reads it has written first.
+ * ------------------------------------------------------------------------------------- */
+SDPA_API sdpa_status sdpa_decode_noalloc(const sdpa_tensor* q, const sdpa_tensor* k_cache, const sdpa_tensor* v_cache,
+                                         const int32_t* kv_lengths, float scale, int32_t num_splits,
+                                         sdpa_tensor* out, void* stream);
+SDPA_API size_t sdpa_decode_noalloc_max_scratch_bytes(void);
+
+/* ---------------------------------------------------------------------------------------
  * kv_cache_update -- writes row t of k_new/v_new of batch b at cache position
  * write_index[b] + t (keras issue: a cache-update index says where new keys/values go; Flax
  * discussion: the cache grows one position per decode step). A bit-exact copy. Rows whose

@@ -264,3 +264,19 @@ def test_decode_per_batch_lengths_are_checked_on_the_host(lib):
     assert _per_batch_tensor([7], 3, "cpu", "x").tolist() == [7, 7, 7]
     assert _per_batch_tensor(np.array([1, 2, 3]), 3, "cpu", "x").dtype == torch.int32
 
+
+def test_decode_noalloc_refuses_more_than_its_scratch(lib):
+    # 64 sequences x 32 query heads x 128 splits of a 65536-slot cache need 136 MB of partials,
+    # more than the 32 MiB scratch: refused on the host, before any launch
+    import torch
+    assert sa.decode_noalloc_max_scratch_bytes() == 32 << 20
+    q = torch.zeros(128, dtype=torch.bfloat16).expand(64, 1, 32, 128)
+    kc = torch.zeros(128, dtype=torch.bfloat16).expand(64, 65536, 8, 128)
+    out = torch.zeros(128, dtype=torch.float32).expand(64, 1, 32, 128)
+    kvl = torch.zeros(64, dtype=torch.int32)
+    dq, dk, do = sa.desc(q), sa.desc(kc), sa.desc(out)
+    st = lib.sdpa_decode_noalloc(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dk), ctypes.c_void_p(kvl.data_ptr()),
+                                 math.nan, 0, ctypes.byref(do), None)
+    assert st == N.SDPA_ERR_WORKSPACE
+    assert "device scratch holds" in lib.sdpa_last_error().decode()
+    assert sa.decode_workspace_bytes(q, kc, 0) > sa.decode_noalloc_max_scratch_bytes()

@@ -64,6 +64,8 @@ PROTOTYPES = {
     "sdpa_fwd_workspace_bytes": (SZ, [T, T, T, I32]),
     "sdpa_decode": (I32, [T, T, T, I32P, ctypes.c_float, I32, T, VP, SZ, VP]),
     "sdpa_decode_workspace_bytes": (SZ, [T, T, I32]),
+    "sdpa_decode_noalloc": (I32, [T, T, T, I32P, ctypes.c_float, I32, T, VP]),
+    "sdpa_decode_noalloc_max_scratch_bytes": (SZ, []),
     "kv_cache_update": (I32, [T, T, T, T, I32P, VP]),
     "sdpa_block_mask_info_bytes": (I32, [T, I32, I32, ctypes.POINTER(SZ)]),
     "build_block_mask_info": (I32, [T, I32, I32, VP, SZ, ctypes.POINTER(BlockMaskInfoC), VP]),

@@ -359,6 +359,31 @@ def sdpa_decode(q, k_cache, v_cache, kv_lengths, *, scale=None, num_splits=0, ou
 
 
 @_on_stream
+def sdpa_decode_noalloc(q, k_cache, v_cache, kv_lengths, out, *, scale=None, num_splits=0):
+    """sdpa_decode without a workspace (sdpa_decode_noalloc): the split partials go to the
+    library's device scratch of sdpa_decode_noalloc_max_scratch_bytes(). Allocates nothing:
+    ``kv_lengths`` must already be a contiguous int32 [B] device tensor and ``out`` is required.
+    Calls that overlap on one GPU race on the shared scratch."""
+    lib = N.load()
+    B = q.shape[0]
+    if not (isinstance(kv_lengths, torch.Tensor) and kv_lengths.dtype == torch.int32 and kv_lengths.is_contiguous()
+            and kv_lengths.numel() == B and kv_lengths.device == q.device):
+        raise ValueError("kv_lengths must be a contiguous int32 device tensor with one entry per sequence")
+    dq, dk, dv, do = desc(q), desc(k_cache), desc(v_cache), desc(out)
+    _, sp = _stream()
+    N.check(lib.sdpa_decode_noalloc(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                                    ctypes.c_void_p(kv_lengths.data_ptr()),
+                                    float("nan") if scale is None else float(scale), int(num_splits),
+                                    ctypes.byref(do), sp))
+    return out
+
+
+def decode_noalloc_max_scratch_bytes() -> int:
+    """Bytes of the device scratch sdpa_decode_noalloc holds on each GPU."""
+    return int(N.load().sdpa_decode_noalloc_max_scratch_bytes())
+
+
+@_on_stream
 def kv_cache_update(k_cache, v_cache, k_new, v_new, write_index):
     """In place: cache[b][write_index[b] + t] = new[b][t] for k and v (rows outside the cache skipped)."""
     lib = N.load()

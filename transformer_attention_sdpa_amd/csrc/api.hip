@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "internal.h"
@@ -241,7 +242,6 @@ sdpa_status sdpa_measure_stream_read(const void* src, size_t bytes, int32_t work
                     "sdpa_measure_stream_read");
 }
 
-
 sdpa_status sdpa_fwd_packed(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
                             const int32_t* q_segments, const int32_t* kv_segments, int32_t n_segments, int32_t maxlen,
                             float scale, int32_t is_causal, const int32_t* q_offset, int32_t q_offset_all,
@@ -397,10 +397,64 @@ size_t sdpa_decode_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k_ca
   return (size_t)(q->dims[3] * T * q->dims[1] * max_splits * (q->dims[0] + 2)) * sizeof(float);
 }
 
+namespace {
+
+// ---- the allocation-free decode's device scratch -------------------------------------------
+// One array per GPU (each device that loads the code object holds its own copy, at its own
+// address, until the process ends). Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, taken once per device with that device
+// current, and kept here.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+sdpa_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SDPA_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SDPA_OK;
+}
+
+// sdpa_decode and sdpa_decode_noalloc: with use_scratch the split partials go to the device
+// scratch instead of the caller's workspace.
+sdpa_status decode_call(const sdpa_tensor* q, const sdpa_tensor* kc, const sdpa_tensor* vc, const int32_t* kv_lengths,
+                        float scale, int32_t num_splits, sdpa_tensor* out, void* workspace, size_t workspace_bytes,
+                        void* stream, bool use_scratch);
+
+}  // namespace
+
 sdpa_status sdpa_decode(const sdpa_tensor* q, const sdpa_tensor* kc, const sdpa_tensor* vc, const int32_t* kv_lengths,
                         float scale, int32_t num_splits, sdpa_tensor* out, void* workspace, size_t workspace_bytes,
                         void* stream) {
   g_err.clear();
+  return decode_call(q, kc, vc, kv_lengths, scale, num_splits, out, workspace, workspace_bytes, stream, false);
+}
+
+sdpa_status sdpa_decode_noalloc(const sdpa_tensor* q, const sdpa_tensor* kc, const sdpa_tensor* vc,
+                                const int32_t* kv_lengths, float scale, int32_t num_splits, sdpa_tensor* out,
+                                void* stream) {
+  g_err.clear();
+  return decode_call(q, kc, vc, kv_lengths, scale, num_splits, out, nullptr, 0, stream, true);
+}
+
+size_t sdpa_decode_noalloc_max_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+namespace {
+
+sdpa_status decode_call(const sdpa_tensor* q, const sdpa_tensor* kc, const sdpa_tensor* vc, const int32_t* kv_lengths,
+                        float scale, int32_t num_splits, sdpa_tensor* out, void* workspace, size_t workspace_bytes,
+                        void* stream, bool use_scratch) {
   if (!q || !kc || !vc || !out) return fail(SDPA_ERR_NULL, "q, k_cache, v_cache and out are required");
   if (!kv_lengths) return fail(SDPA_ERR_NULL, "kv_lengths is required for decode");
   if (q->dims[2] < 0 || q->dims[2] > kc->dims[2])
@@ -413,9 +467,20 @@ sdpa_status sdpa_decode(const sdpa_tensor* q, const sdpa_tensor* kc, const sdpa_
                                      nullptr, 0, kv_lengths, -1, nullptr, -1, 0, out, a);
   if (st != SDPA_OK) return st;
   const size_t need = sdpa_decode_workspace_bytes(q, kc, num_splits);
-  if (workspace_bytes < need || (need && !workspace))
+  if (use_scratch) {
+    if (need > kNoAllocScratchBytes)
+      return fail(SDPA_ERR_WORKSPACE,
+                  "sdpa_decode_noalloc: this call needs %zu bytes of split partials; the device scratch holds %zu "
+                  "(fewer sequences, query heads, tokens or splits fit; sdpa_decode takes any size)",
+                  need, kNoAllocScratchBytes);
+  } else if (workspace_bytes < need || (need && !workspace)) {
     return fail(SDPA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  }
   if (a.B == 0 || a.Lq == 0) return SDPA_OK;
+  if (use_scratch && need) {
+    st = scratch_address(&workspace);
+    if (st != SDPA_OK) return st;
+  }
   if (!a.q || !a.out || (a.Lkv > 0 && (!a.k || !a.v))) return fail(SDPA_ERR_NULL, "a tensor's data is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -439,6 +504,8 @@ sdpa_status sdpa_decode(const sdpa_tensor* q, const sdpa_tensor* kc, const sdpa_
   // any other shape: the general kernel at these T queries, bottom-right causal, these kv_lengths
   return hip_status(launch_fwd_generic(a, s), "sdpa_decode (generic)");
 }
+
+}  // namespace
 
 sdpa_status kv_cache_update(sdpa_tensor* kc, sdpa_tensor* vc, const sdpa_tensor* kn, const sdpa_tensor* vn,
                             const int32_t* write_index, void* stream) {
