@@ -31,7 +31,8 @@ times launches one at a time with 512 MiB written between them (the 256 MiB last
 flushed), reported as ``timing.mall_flushed_median_ms`` beside the back-to-back figure.
 
 Measured peaks. Two probes of the library (sdpa_measure_mfma_bf16: only bf16 MFMAs, two waves
-per SIMD; sdpa_measure_stream_read: a 4 GiB streaming read) give the rates the chip sustains;
+per SIMD; sdpa_measure_stream_read: a 4 GiB nontemporal streaming read) give the rates the chip
+sustains;
 every roofline carries its fraction of the vendor peak (``frac``) and of the measured one
 (``frac_of_measured``).
 
@@ -191,11 +192,11 @@ def measured_peaks(stream):
     res["mfma_probe"] = f"{wgs} workgroups x 4 waves x {iters} x 4 v_mfma_f32_32x32x16_bf16, median of 5"
     buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
-    ssink = torch.empty(2048 * 4, dtype=torch.int32, device="cuda")
+    ssink = torch.empty(16384 * 4, dtype=torch.int32, device="cuda")
     nb = [0]
 
     def rd():
-        nb[0] = sa.measure_stream_read(buf, 2048, ssink)
+        nb[0] = sa.measure_stream_read(buf, 16384, ssink)
     prewarm(rd, PREWARM_MS)
     ts = []
     for _ in range(5):
@@ -207,7 +208,7 @@ def measured_peaks(stream):
         ts.append(e0.elapsed_time(e1) / 1e3)
     t = sorted(ts)[2]
     res["hbm_read_gbs"] = round(nb[0] / t / 1e9, 1)
-    res["read_probe"] = "4 GiB streaming read, 16-byte loads, 2048 workgroups of 256, median of 5"
+    res["read_probe"] = "4 GiB streaming read, 16-byte nontemporal loads, 16384 workgroups of 256, median of 5"
     del buf, ssink, sink
     torch.cuda.empty_cache()
     return res

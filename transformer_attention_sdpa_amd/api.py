@@ -480,7 +480,7 @@ def measure_mfma_bf16(workgroups: int, iters: int, sink: torch.Tensor = None) ->
 
 
 @_on_stream
-def measure_stream_read(buf: torch.Tensor, workgroups: int = 2048, sink: torch.Tensor = None) -> int:
+def measure_stream_read(buf: torch.Tensor, workgroups: int = 16384, sink: torch.Tensor = None) -> int:
     """Launch the streaming-read probe (sdpa_measure_stream_read) over the bytes of ``buf``;
     returns the bytes it reads."""
     lib = N.load()
