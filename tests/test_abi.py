@@ -135,12 +135,12 @@ def test_workspace_sizes(lib):
     assert lib.sdpa_fwd_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 1) == 3 * 7 * 2 * 4
     qd = T([128, 32, 1, 64])
     kc = T([128, 8, 8192, 64])
-    # 512 keys per split by default -> 16 splits; (D + 2) floats per (b, head, split)
-    assert lib.sdpa_decode_workspace_bytes(ctypes.byref(qd), ctypes.byref(kc), 0) == 64 * 32 * 16 * 130 * 4
+    # 1024 keys per split by default -> 8 splits; (D + 2) floats per (b, head, split)
+    assert lib.sdpa_decode_workspace_bytes(ctypes.byref(qd), ctypes.byref(kc), 0) == 64 * 32 * 8 * 130 * 4
     assert lib.sdpa_decode_workspace_bytes(ctypes.byref(qd), ctypes.byref(kc), 4) == 64 * 32 * 4 * 130 * 4
     # T query tokens: one partial per (b, token, head, split)
     q3 = T([128, 32, 3, 64])
-    assert lib.sdpa_decode_workspace_bytes(ctypes.byref(q3), ctypes.byref(kc), 0) == 64 * 3 * 32 * 16 * 130 * 4
+    assert lib.sdpa_decode_workspace_bytes(ctypes.byref(q3), ctypes.byref(kc), 0) == 64 * 3 * 32 * 8 * 130 * 4
 
 
 def test_decode_validation(lib):

@@ -85,7 +85,7 @@ def test_decode_equals_fwd_bottom_right(lib):
     ref = sa.sdpa(q, kc, vc, is_causal="bottom_right", kv_lengths=kvl, scale=d.scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
     # same operation, but the two kernels round differently (the forward kernel folds the scale
-    # into bf16 Q and sums over 64-key tiles, decode sums bf16 P over 512-key splits and merges
+    # into bf16 Q and sums over 64-key tiles, decode sums bf16 P over 1024-key splits and merges
     # them), so they agree to the bf16 bar rather than bit for bit
     assert_close(out.cpu().numpy(), ref.cpu().numpy(), "bf16", "decode vs fwd")
     assert_close(out.cpu().numpy(), oracle_decode(d), "bf16", "decode vs oracle")
@@ -153,11 +153,12 @@ def test_head_rms_norm_random_vs_oracle(lib):
 
 @pytest.mark.parametrize("hq,hkv", [(16, 16), (16, 8), (32, 8), (32, 4), (32, 2), (16, 1)])
 def test_decode_tile_and_split_edges(lib, hq, hkv):
-    # the matrix-core decode works in 32-key tiles and 512-key splits: lengths on and around
+    # the matrix-core decode works in 32-key tiles and 1024-key splits: lengths on and around
     # both edges, every query-heads-per-K/V-head ratio it takes (1..16), default splits
-    lens = np.array([1, 2, 31, 32, 33, 63, 511, 512, 513, 1024, 1025, 1040], dtype=np.int32)
+    lens = np.array([1, 2, 31, 32, 33, 63, 511, 512, 513, 1023, 1024, 1025, 1040, 2047, 2048, 2080],
+                    dtype=np.int32)
     say(f"decode edges hq={hq} hkv={hkv}")
-    d = decode_case(len(lens), hq, hkv, 128, 1040, 1040, 1040, base=700 + hq + hkv)
+    d = decode_case(len(lens), hq, hkv, 128, 2080, 2080, 2080, base=700 + hq + hkv)
     d.kv_lengths = lens                                   # rows past each length are never read
     out, _, _ = run_decode(d)
     got = out.cpu().numpy()

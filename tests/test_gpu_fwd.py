@@ -304,3 +304,25 @@ def test_side_stream(lib):
     refd = np.stack([oracle.sdpa(f(d.q[b:b + 1]), f(ekc[b:b + 1, :d.kv_lengths[b]]), f(evc[b:b + 1, :d.kv_lengths[b]]),
                                  scale=d.scale, is_causal="bottom_right")[0] for b in range(3)])
     assert_close(od.cpu().numpy(), refd, "bf16", "side stream decode")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_logit_jumps_move_the_running_max(lib, dtype, D, causal):
+    # keys 0..63 give logits near 1 (log2 units), keys 64..191 near 130 and keys 192.. near 260:
+    # the running max set by the first tile is far below the later logits, whose exponentials
+    # would overflow against it; the kernels must move the max before those reach P.V
+    say(f"logit jumps D={D} {dtype} causal={causal}")
+    B, L, H = 1, 300, 2
+    rng = np.random.default_rng(77 + D)
+    q = np.ones((B, L, H, D), dtype=np.float32)
+    k = np.empty((B, L, H, D), dtype=np.float32)
+    lvl = np.where(np.arange(L) < 64, 0.1, np.where(np.arange(L) < 192, 8.0, 16.0)) * math.sqrt(128 / D)
+    k[:] = (lvl[None, :, None, None] * (1.0 + 0.002 * (np.arange(L) % 7))[None, :, None, None])
+    v = rng.standard_normal((B, L, H, D), dtype=np.float32)
+    w = workloads.Attention("jumps", dtype, workloads.to_storage(q, dtype), workloads.to_storage(k, dtype),
+                            workloads.to_storage(v, dtype), scale=1.0 / math.sqrt(D), is_causal=causal)
+    ref = run_oracle(w)
+    assert np.isfinite(ref).all()
+    assert_close(run_gpu(w).cpu().numpy(), ref, dtype, "logit jumps")

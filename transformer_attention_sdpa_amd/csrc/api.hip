@@ -157,7 +157,7 @@ sdpa_status resolve_attention(const sdpa_tensor* q, const sdpa_tensor* k, const 
 }
 
 int decode_split_len(int64_t cap, int32_t num_splits) {
-  int64_t len = 512;                                   // library choice: 512 keys per split
+  int64_t len = 1024;                                  // library choice: 1024 keys per split
   if (num_splits > 0) len = (cap + num_splits - 1) / num_splits;
   len = ((len + 63) / 64) * 64;
   if (len < 64) len = 64;

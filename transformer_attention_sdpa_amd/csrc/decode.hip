@@ -12,8 +12,8 @@
 //     that shares g (grouped-query attention) from the same K/V tiles and writes the split's
 //     running max m, sum l and unnormalised output o in fp32. The online softmax is kept in
 //     the exp2 domain (logits pre-multiplied by scale*log2 e).
-//     - decode_split_mfma (head dim 128, 512-key splits, up to 16 query heads per K/V head):
-//       one wave streams 32-key tiles through a three-stage LDS ring filled by direct global ->
+//     - decode_split_mfma (head dim 128, 1024-key splits, up to 16 query heads per K/V head):
+//       one wave streams 32-key tiles through a two-stage LDS ring filled by direct global ->
 //       LDS loads and does q.k and p.V on the matrix cores (see that kernel). Its grid is
 //       linear: all full splits first, then the partial ones, then idle workgroups (mf_locate).
 //     - decode_split (the other bf16 shapes): 256 threads stream 64-key tiles through LDS with
@@ -171,12 +171,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
 }
 
 // ---- matrix-core variant of pass 1 --------------------------------------------------------
-// One wave per (K/V head g, 512-key split, sequence b). The split streams through LDS in
-// 32-key tiles, filled by direct global -> LDS loads into a ring of three stages, so that two
-// tiles are in flight while one is computed; there are no staging registers and no LDS stores.
-// The 16 tiles of a split are unrolled into straight-line code: every stage is a distinct LDS
-// array, which lets the compiler's wait-count tracking tell a read of one stage from a load in
-// flight into another.
+// One wave per (K/V head g, 1024-key split, sequence b). The split streams through LDS in
+// 32-key tiles, filled by direct global -> LDS loads into a ring of two stages, so that one
+// tile is in flight while the other is computed; there are no staging registers and no LDS
+// stores. The 32 tiles of a split are unrolled into straight-line code: every stage is a
+// distinct LDS array, which lets the compiler's wait-count tracking tell a read of one stage
+// from a load in flight into another.
+// Ring depth and split length were measured at the GQA decode workload once the loads carried
+// the nontemporal policy (alternating builds, us per sdpa_decode call): 3 stages / 512 keys
+// 237.8, 2 / 512 233.1, 4 / 512 247.0, 3 / 1024 235.5, 2 / 1024 229.9, 3 / 256 262.2, 2 / 768
+// 233.8, 2 / 1536 240.3. Two stages of 16 KB let five waves share a CU's LDS instead of three.
 //   S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (or _f16): A = 16 keys x 32 head-dim values of K, B = Q^T with
 //     the group's r query heads as columns (padded to 16 with zeros).
 //   The 16x16 accumulator gives lane l the scores of keys 4*(l/16) + i (i = 0..3) of a 16-key
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
 //   Softmax in the exp2 domain as in pass 1 above; row sums of the bf16 probabilities the
 //     MFMA consumes.
 constexpr int kMfTile = 32;                    // keys per tile
-constexpr int kMfSplit = 512;                  // keys per split (16 tiles)
+constexpr int kMfSplit = 1024;                 // keys per split (32 tiles)
 constexpr int kMfTileElems = kMfTile * kDecD;  // 4096 bf16 = 8 KB
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -456,8 +460,8 @@ __host__ __device__ __forceinline__ int mf_groups(const DecodeArgs& a) { return 
 // splits past a sequence's length exit at once.
 template <bool LINEAR, bool F16>
 __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
-  __shared__ __align__(16) uint16_t k0s[kMfTileElems], k1s[kMfTileElems], k2s[kMfTileElems];
-  __shared__ __align__(16) uint16_t v0s[kMfTileElems], v1s[kMfTileElems], v2s[kMfTileElems];
+  __shared__ __align__(16) uint16_t k0s[kMfTileElems], k1s[kMfTileElems];
+  __shared__ __align__(16) uint16_t v0s[kMfTileElems], v1s[kMfTileElems];
   const int r = a.Hq / a.Hkv;
   const int ng = mf_groups(a);
   const int HG = a.Hkv * ng;
@@ -482,21 +486,20 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   MfWave w;
   mf_init(w, a);
   mf_begin(w, a, b, g, r, cg, nkv, j_end);
-  uint16_t* const kst[3] = {k0s, k1s, k2s};
-  uint16_t* const vst[3] = {v0s, v1s, v2s};
+  uint16_t* const kst[2] = {k0s, k1s};
+  uint16_t* const vst[2] = {v0s, v1s};
   mf_load(w, a, b, g, j_begin, j_end, kst[0], vst[0]);
-  mf_load(w, a, b, g, j_begin + kMfTile, j_end, kst[1], vst[1]);
 #pragma unroll
-  for (int t = 0; t < kMfTiles; ++t) {              // three stages: two tiles in flight
-    if (t + 2 < kMfTiles) {
+  for (int t = 0; t < kMfTiles; ++t) {              // two stages: one tile in flight
+    if (t + 1 < kMfTiles) {
       // the stage refilled here was read for tile t-1: those LDS reads must be complete before
       // the direct loads that overwrite it are issued (the compiler orders a direct load only
       // before later reads of its data, not after earlier reads of what it replaces)
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_sched_barrier(0);
-      mf_load(w, a, b, g, j_begin + kMfTile * (t + 2), j_end, kst[(t + 2) % 3], vst[(t + 2) % 3]);
+      mf_load(w, a, b, g, j_begin + kMfTile * (t + 1), j_end, kst[(t + 1) % 2], vst[(t + 1) % 2]);
     }
-    if (j_begin + kMfTile * t < j_end) mf_tile<F16>(w, a, j_begin + kMfTile * t, j_end, kst[t % 3], vst[t % 3]);
+    if (j_begin + kMfTile * t < j_end) mf_tile<F16>(w, a, j_begin + kMfTile * t, j_end, kst[t % 2], vst[t % 2]);
   }
   __builtin_amdgcn_s_waitcnt(0);                    // no direct load may land after the wave ends
   mf_store(w, a, b, g, r, split);
@@ -541,7 +544,7 @@ __global__ __launch_bounds__(kDecD) void decode_combine_kernel(DecodeArgs a) {
 
 }  // namespace
 
-// The matrix-core pass 1: 512-key splits, up to 16 query tokens and 8 column groups, 16-byte
+// The matrix-core pass 1: 1024-key splits, up to 16 query tokens and 8 column groups, 16-byte
 // aligned query rows (the K/V conditions of decode_fast_supports hold as well).
 constexpr int kMfMaxT = 16, kMfMaxGroups = 8;
 static bool decode_mfma_supports(const DecodeArgs& a) {

@@ -72,6 +72,12 @@ __device__ __forceinline__ int v_swz(int row) { return D == 128 ? 4 * (row & 3) 
 // 0.9% faster at the causal prefill than all of an XCD's heads at once, 2 heads slightly slower
 constexpr int kGroupHeads = 4;
 
+// Without a bias, once every row of a wave has its running max (the first tile holding one of
+// its keys sets it), the per-tile row max is no longer taken: the max moves only when a tile's
+// probabilities grow past kLazyBound, which the tile's probability sum shows (inf included)
+// before any of them reaches the P.V products. Probabilities up to 2^64, sums of them over
+// every key and the O accumulators all stay far inside fp32 and bf16 range.
+constexpr float kLazyBound = 18446744073709551616.0f;   // 2^64
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units: the running max moves only when a row's max grows by more
 // The fused bias path forms the logits against m_s = m_run clamped to [-kStartLim, kStartLim]
 // (natural units): a start value of that size keeps q.k to within 2^-10 in the accumulator,
@@ -360,6 +366,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   //    come the probabilities are taken against 0 (every logit so far is -inf).
   float m_run = FUSED ? 0.f : -INFINITY, l_run = 0.f;
   float thr = -INFINITY;
+  bool est = false;                                      // LAZY: every row of the wave has its max
 
   const int64_t bias_row = (BIAS != BIAS_NONE && i_me < a.Lq)
                                ? b * a.bias_sb + h * a.bias_sh + (int64_t)i_me * a.bias_sq : -1;
@@ -599,7 +606,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       // fp32 sums and bf16 probabilities hold without loss. Each lane first tests its own 32
       // scores; only when some lane exceeds the slack do the halves exchange maxima (a
       // cross-lane exchange goes through the LDS queue and would drain it every tile).
+      // LAZY (fused, no bias): once the wave is established the max is left to the check of
+      // the tile's probability sum below (kLazyBound)
+      constexpr bool LAZY = FUSED && !NAT;
       float mt = -INFINITY;
+      if (!LAZY || !est) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -663,6 +674,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
           for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
         m_run = m_new;
       }
+      if constexpr (LAZY) est = __builtin_amdgcn_ballot_w64(thr == -INFINITY) == 0;
+      }
       // no finite logit yet: every logit so far is -inf, and exp2(-inf - 0) = 0 (not NaN)
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
@@ -676,7 +689,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       //      V(t+1) into LDS and the loads of K(t+3), V(t+2)
       // Each chunk also issues the LDS fragment read of the next chunk.
       constexpr int NA = DC, NB = 2 * DB;
-      constexpr int EL_A = 24, EL_B = 32 - EL_A;
+      // LAZY: all 32 probabilities in block A, so that the tile's sum is checked before B1
+      constexpr int EL_A = LAZY ? 32 : 24, EL_B = 32 - EL_A;
+      float l_tile = 0.f;                                // LAZY: this tile's share of l_run
       float pf[32];                                      // probabilities of this lane's 32 keys
       uint32_t pw[16];                                   // the same, packed as bf16 pairs
       auto prob = [&](int f) {                           // element f = 16*kb + 8*sh + e
@@ -689,7 +704,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
         if (f & 1) {
           pw[f >> 1] = E::pack(pf[f - 1], pf[f]);
           // row sum of the same 16-bit probabilities the MFMA consumes
-          l_run = E::sum2(pw[f >> 1], l_run);
+          if constexpr (LAZY) l_tile = E::sum2(pw[f >> 1], l_tile);
+          else l_run = E::sum2(pw[f >> 1], l_run);
         }
       };
       auto pb = [&](int kb, int sh) -> bf16x8 {
@@ -745,6 +761,41 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
         }
 #pragma unroll
         for (int f = c * EL_A / NA; f < (c + 1) * EL_A / NA; ++f) prob(f);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (LAZY) {
+        // an established row's max moves only when a probability of this tile grew past 2^64
+        // (the tile's sum shows it, inf included); the tile is then taken again against the
+        // new max before its probabilities reach the P.V products, and S(t+1) is moved too
+        if (est && __builtin_amdgcn_ballot_w64(!(l_tile <= kLazyBound))) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s_cur[kb][e]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const float lt_row = l_tile + __shfl_xor(l_tile, 32, 64);
+          const float dlt = !(lt_row <= kLazyBound) ? mx : 0.f;
+          const float alpha = __builtin_amdgcn_exp2f(-dlt);
+          l_run *= alpha;
+#pragma unroll
+          for (int d = 0; d < DB; ++d)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+          // S(t+1), formed in block A, started from the old max: it moves with it
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              s_cur[kb][e] -= dlt;
+              s_next[kb][e] -= dlt;
+            }
+          m_run += dlt;
+          l_tile = 0.f;
+#pragma unroll
+          for (int f = 0; f < 32; ++f) prob(f);
+        }
+        l_run += l_tile;
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
