@@ -80,7 +80,21 @@ def parse_args():
     p.add_argument("--skip-mask-info", action="store_true")
     p.add_argument("--skip-backward", action="store_true")
     p.add_argument("--skip-extra", action="store_true", help="skip the bias + block-mask and long-context timings")
-    return p.parse_args()
+    p.add_argument("--sections", default="all",
+                   help="comma list of the sections to run besides the headline prefill (backward, decode, "
+                        "mask_info, bias_block_mask, chunked_prefill, widened), or 'all'")
+    a = p.parse_args()
+    if a.sections != "all":
+        want = set(a.sections.split(","))
+        a.skip_backward = a.skip_backward or "backward" not in want
+        a.skip_decode = a.skip_decode or "decode" not in want
+        a.skip_mask_info = a.skip_mask_info or "mask_info" not in want
+        a.skip_bias_mask = a.skip_extra or "bias_block_mask" not in want
+        a.skip_chunked = a.skip_extra or "chunked_prefill" not in want
+        a.skip_widened = a.skip_extra or "widened" not in want
+    else:
+        a.skip_bias_mask = a.skip_chunked = a.skip_widened = a.skip_extra
+    return a
 
 
 def source_hash(path):
@@ -476,7 +490,7 @@ def main():
     # block info; algorithmic work counts the non-empty 128 x 128 blocks (4 * D flops per pair of
     # such a block), and the bias bytes of those blocks read once. Long context: B1, 32 query
     # heads over 8 K/V heads, 2048 queries at offset 129024 over 131072 keys, causal; exact pairs.
-    if not args.skip_extra:
+    if not args.skip_bias_mask:
         w4 = workloads.bias_block_mask()
         B4_, Lq4, _, Hq4, _, D4, _ = w4.shape
         q4, k4, v4 = (sa.from_numpy(getattr(w4, n), "bf16") for n in ("q", "k", "v"))
@@ -505,6 +519,7 @@ def main():
         }
         del q4, k4, v4, bias4, info4, out4
         torch.cuda.empty_cache()
+    if not args.skip_chunked:
         w5 = workloads.chunked_prefill()
         B5, Lq5, Lkv5, Hq5, Hkv5, D5, _ = w5.shape
         q5, k5, v5 = (sa.from_numpy(getattr(w5, n), "bf16") for n in ("q", "k", "v"))
@@ -534,7 +549,7 @@ def main():
     # lengths ~ U{256..4096} up to 32768 tokens), exact in-segment causal pairs; decode: the GQA
     # decode cache with 4 new query tokens per sequence (KV bytes as for one token: each K/V row
     # is read once for all 4); f16: the causal prefill with f16 inputs (the bf16 values, exact in f16)
-    if not args.skip_extra:
+    if not args.skip_widened:
         nx = {}
         rng = np.random.default_rng([1007, 11])
         lens = []

@@ -52,8 +52,14 @@ constexpr int BM = 128;            // query rows per workgroup
 constexpr int BN = 64;             // keys per tile
 constexpr int NT = 256;            // threads per workgroup
 
+// BIAS_F32: an fp32 bias, or a bf16 bias the fused path cannot stage (read element by element)
 enum { BIAS_NONE = 0, BIAS_BF16 = 1, BIAS_F32 = 2 };
-enum { MASK_NONE = 0, MASK_DENSE = 1, MASK_INFO = 2 };
+// MASK_INFO: block info whose rows hold at most 64 blocks (the host knows n_kb), every CSR
+// entry of a row in the lanes of one register; MASK_INFO_LONG: longer rows, entries from 64 on
+// loaded from memory where they are used. (With such a load in one arm of a lookup, the
+// compiler makes the common arm wait for every load in flight, prefetches included, so the
+// short form has no such arm at all.)
+enum { MASK_NONE = 0, MASK_DENSE = 1, MASK_INFO = 2, MASK_INFO_LONG = 3 };
 
 // Key held by LDS row r (0..31) of a 32-key block of K: the A operand of S^T = K Q^T takes row
 // r, and this order makes accumulator entry 4*i + j of lane half h hold key 16*h + 4*i + j.
@@ -77,6 +83,10 @@ constexpr int kGroupHeads = 4;
 // probabilities grow past kLazyBound, which the tile's probability sum shows (inf included)
 // before any of them reaches the P.V products. Probabilities up to 2^64, sums of them over
 // every key and the O accumulators all stay far inside fp32 and bf16 range.
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8): lgkmcnt(0) only;
+// vmcnt(4) and lgkmcnt(0)
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
+constexpr int kWaitVm4Lgkm0 = 0x4 | (0x7 << 4) | (0x0 << 8);
 constexpr float kLazyBound = 18446744073709551616.0f;   // 2^64
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units: the running max moves only when a row's max grows by more
 // The fused bias path forms the logits against m_s = m_run clamped to [-kStartLim, kStartLim]
@@ -102,6 +112,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   // filled with the dtype's most negative value) then stays finite, as the definition has it,
   // instead of overflowing to -inf and passing for a masked key. Without a bias the logits are
   // in log2 units from the start (scale*log2e folded into Q, or into the per-element scale).
+  constexpr bool MI = MASK == MASK_INFO || MASK == MASK_INFO_LONG;
   constexpr bool FBIAS = BIAS == BIAS_BF16 && D == 64 && !NORM;
   constexpr bool FUSED = (BIAS == BIAS_NONE || FBIAS) && !NORM;
   constexpr bool NAT = BIAS != BIAS_NONE;
@@ -110,6 +121,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   // read of one from a direct load in flight into another.
   __shared__ __align__(16) uint16_t kbuf0[TILE], kbuf1[TILE], vbuf0[TILE], vbuf1[TILE];
   __shared__ __align__(16) float krv_s[NORM ? 2 * BN : 1];
+  // FBIAS: the bias of a tile (BM rows x BN keys) reaches LDS by direct loads, two tiles ahead
+  // like K, in two buffers. MASK_INFO: the mask words of a partial block's tile, one tile ahead
+  // like V, each wave its own 32 rows x 2 words, in two buffers.
+  __shared__ __align__(16) uint16_t bbuf0[FBIAS ? BM * BN : 8], bbuf1[FBIAS ? BM * BN : 8];
+  __shared__ __align__(16) uint32_t mbuf0[MI ? NT : 1], mbuf1[MI ? NT : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -191,11 +207,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   // tiles to visit: all tiles below k_end, or the non-empty blocks of the mask info
   int n_tiles = 0, csr_begin = 0, sub_per_blk = 1;
   int64_t info_row = 0;
-  // MASK_INFO: lane l holds entry l of the row's CSR (its kv block and that block's class), so
-  // the tile loop reads them with readlane instead of scalar loads, which would share their
-  // wait counter with the LDS reads. Entries from 64 on are loaded where they are used.
-  int dn_lane = 0, cls_lane = 0;
-  if constexpr (MASK == MASK_INFO) {
+  // MASK_INFO: lane l holds entry l of the row's CSR (its kv block, that block's class and, for a
+  // partial block, its index among the partial blocks), so the tile loop reads them with
+  // readlane instead of scalar loads, which would share their wait counter with the LDS reads.
+  // Entries from 64 on are loaded where they are used.
+  int dn_lane = 0, cls_lane = 0, nx_lane = 0;
+  if constexpr (MI) {
     const int mb = a.bm_batch > 1 ? b : 0, mh = a.bm_heads > 1 ? h : 0;
     info_row = ((int64_t)mb * a.bm_heads + mh) * a.bm_nqb + qt;
     csr_begin = a.bm_row_ptr[info_row];
@@ -205,10 +222,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     if (in_row) {
       dn_lane = a.bm_data_next[csr_begin + lane];
       cls_lane = a.bm_class[info_row * a.bm_nkb + dn_lane];
+      if (cls_lane == 1) nx_lane = a.bm_next[info_row * a.bm_nkb + dn_lane];
     }
     // the entries are ascending: those below k_end are a prefix
     int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(in_row && (int64_t)dn_lane * a.bm_bkv < k_end));
-    if (cnt == 64) {
+    if (MASK == MASK_INFO_LONG && cnt == 64) {
       for (int e = csr_begin + 64; e < csr_end; ++e) {
         if ((int64_t)a.bm_data_next[e] * a.bm_bkv >= k_end) break;
         ++cnt;
@@ -220,13 +238,19 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   }
   // kv block of the idx-th non-empty block of the row, and its class (MASK_INFO)
   auto blk_at = [&](int idx) -> int {
+    if constexpr (MASK == MASK_INFO) return __builtin_amdgcn_readlane(dn_lane, idx);
     return idx < 64 ? __builtin_amdgcn_readlane(dn_lane, idx) : a.bm_data_next[csr_begin + idx];
   };
   auto cls_at = [&](int idx, int blk) -> int {
+    if constexpr (MASK == MASK_INFO) return __builtin_amdgcn_readlane(cls_lane, idx);
     return idx < 64 ? __builtin_amdgcn_readlane(cls_lane, idx) : (int)a.bm_class[info_row * a.bm_nkb + blk];
   };
+  auto next_at = [&](int idx, int blk) -> int {
+    if constexpr (MASK == MASK_INFO) return __builtin_amdgcn_readlane(nx_lane, idx);
+    return idx < 64 ? __builtin_amdgcn_readlane(nx_lane, idx) : a.bm_next[info_row * a.bm_nkb + blk];
+  };
   auto tile_k0 = [&](int t) -> int {
-    if constexpr (MASK == MASK_INFO) return blk_at(t / sub_per_blk) * a.bm_bkv + (t % sub_per_blk) * BN;
+    if constexpr (MI) return blk_at(t / sub_per_blk) * a.bm_bkv + (t % sub_per_blk) * BN;
     else return t * BN;
   };
   // staging runs ahead of the last tile without branches: past the end it reloads the last tile
@@ -373,38 +397,64 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   const int64_t mask_row = (MASK == MASK_DENSE && i_me < a.Lq)
                                ? b * a.mask_sb + h * a.mask_sh + (int64_t)i_me * a.mask_sq : -1;
 
-  // ---- FBIAS: the bias of tile u as raw bf16, in register set u & 1, loaded two tiles ahead:
-  // the loads of tile t + 2 are issued as tile t starts and are used by the S(t+1) MFMAs of
-  // tile t + 1 (lane: query i_me, keys k0 + 32*kb + 16*hh + 0..15)
-  uint4 braw[2][2][2];                                   // [set][kb][8 keys]
-  auto load_bias = [&](int k0t, uint4 (&dst)[2][2]) {
+  // ---- FBIAS: the bias of a tile through LDS ---------------------------------------------
+  // LDS row r holds the tile's 64 keys of query q0 + r, 16-byte chunk c at position c ^ (r & 7),
+  // so that the reads below (lanes on consecutive rows, one chunk) hit distinct banks. Each wave
+  // loads its own 32 rows (slot 64*u + lane of its 256, u < 4), so it can refill a buffer as
+  // soon as its own reads of it are done, without waiting for the other waves: the bias of tile
+  // t + 3 is requested in tile t, right after the bias of tile t + 1 has been read, and the
+  // end-of-tile wait leaves those four loads in flight. Loads stop at the last element of the
+  // last valid row (the buffer range), so rows past Lq and keys past the end read zeros; keys
+  // past kv_len in other rows read the next row, and are masked like any key past kv_len.
+  int bdoff[FBIAS ? 4 : 1];
+  const int bias_row_bytes = (int)(a.bias_sq * 2);
+  if constexpr (FBIAS) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sl = 64 * u + lane, row = 32 * wave + (sl >> 3), pos = sl & 7;
+      bdoff[u] = row * bias_row_bytes + ((pos ^ (row & 7)) << 4);
+    }
+  }
+  const int rows_valid = min(BM, a.Lq - q0);
+  auto dma_bias = [&](int k0t, uint16_t* dst) {
     if constexpr (FBIAS) {
+      const uint16_t* base = static_cast<const uint16_t*>(a.bias) + b * a.bias_sb + h * a.bias_sh +
+                             (int64_t)q0 * a.bias_sq + k0t;
+      const __amdgpu_buffer_rsrc_t rb =
+          make_rsrc(base, (int64_t)(rows_valid - 1) * bias_row_bytes + (int64_t)(a.Lkv - k0t) * 2);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int jb = k0t + 32 * kb + 16 * hh;
-        if (bias_row >= 0 && a.bias_vec && jb + 16 <= a.Lkv) {
-          const uint4* bp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.bias) + bias_row + jb);
-          dst[kb][0] = bp[0];
-          dst[kb][1] = bp[1];
-        } else {
-          uint32_t w[8];
+      for (int u = 0; u < 4; ++u) dma16(rb, dst + 8 * (256 * wave + 64 * u), bdoff[u]);
+    }
+  };
+  // the lane's bias of a tile from LDS: query i_me, keys 32*kb + 16*hh + 0..15 (two chunks)
+  auto bias_lds = [&](const uint16_t* bb, uint4 (&x)[2][2]) {
+    const int row = 32 * wave + ql;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j0 = jb + 2 * e, j1 = j0 + 1;
-            const uint32_t lo = (bias_row >= 0 && j0 < a.Lkv)
-                                    ? static_cast<const uint16_t*>(a.bias)[bias_row + (int64_t)j0 * a.bias_sk] : 0u;
-            const uint32_t hi = (bias_row >= 0 && j1 < a.Lkv)
-                                    ? static_cast<const uint16_t*>(a.bias)[bias_row + (int64_t)j1 * a.bias_sk] : 0u;
-            w[e] = lo | (hi << 16);
-          }
-          dst[kb][0] = make_uint4(w[0], w[1], w[2], w[3]);
-          dst[kb][1] = make_uint4(w[4], w[5], w[6], w[7]);
-        }
+    for (int kb = 0; kb < 2; ++kb) {
+      const int c = 4 * kb + 2 * hh;
+      x[kb][0] = *reinterpret_cast<const uint4*>(bb + row * BN + ((c ^ (row & 7)) << 3));
+      x[kb][1] = *reinterpret_cast<const uint4*>(bb + row * BN + (((c + 1) ^ (row & 7)) << 3));
+    }
+  };
+  // ---- MASK_INFO: the mask words of a partial tile through LDS ------------------------------
+  // Wave w's region of a buffer holds, in word ql + 32*k, word k of the tile in row 32*w + ql of
+  // the block (its keys 32*k .. 32*k + 31); lane l loads word l of the region.
+  auto dma_bits = [&](int u, uint32_t* dst) {
+    if constexpr (MI) {
+      const int idx = u / sub_per_blk;
+      const int blk = blk_at(idx);
+      if (cls_at(idx, blk) == 1) {                       // wave-uniform
+        const int wpr = a.bm_bkv / 32;                   // words per block row
+        const uint32_t* base = a.bm_bits + (int64_t)next_at(idx, blk) * a.bm_bq * wpr;
+        const __amdgpu_buffer_rsrc_t rm = make_rsrc(base, (int64_t)a.bm_bq * wpr * 4);
+        const int row = 32 * wave + (lane & 31);
+        const int word = (u % sub_per_blk) * (BN / 32) + (lane >> 5);
+        dma4(rm, dst + 64 * wave, (row * wpr + word) * 4);
       }
     }
   };
   // start values of an S chain: bias - m (FBIAS), -m (other FUSED), 0
-  auto s_start = [&](const uint4 (&src)[2][2], float m, f32x16 (&c)[2]) {
+  auto s_start = [&](const uint4 (&src)[2][2], float m, f32x16 (&c)[2]) {   // src: the lane's raw bias
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if constexpr (FBIAS) {
@@ -426,10 +476,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   // K(t) lives in buffer t & 1, V(t) in buffer t & 1; S(t) in s_even (FUSED: s_odd for odd t).
   f32x16 s_even[2], s_odd[2];
   if (n_tiles > 0) {
-    if constexpr (FBIAS) {
-      load_bias(tile_k0(0), braw[0]);
-      load_bias(tile_k0c(1), braw[1]);
-    }
+    dma_bias(tile_k0(0), bbuf0);
+    dma_bias(tile_k0c(1), bbuf1);
+    dma_bits(0, mbuf0);
     dma_k(tile_k0(0), kbuf0);
     dma_v(tile_k0(0), vbuf0);
     dma_k(tile_k0c(1), kbuf1);
@@ -440,9 +489,19 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     }
   }
   __syncthreads();
-  if (n_tiles > 0 && tile_k0(0) < k_end_w) {            // m_run = 0: from zero (or the bias)
-    s_start(braw[0], 0.f, s_even);
-    compute_s(kbuf0, s_even);
+  {
+    uint4 bx[2][2];
+    if constexpr (FBIAS) {
+      if (n_tiles > 0) {
+        bias_lds(bbuf0, bx);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);          // this wave's reads of buffer 0 are done
+        dma_bias(tile_k0c(2), bbuf0);                    // the bias of tile 2
+      }
+    }
+    if (n_tiles > 0 && tile_k0(0) < k_end_w) {          // m_run = 0: from zero (or the bias)
+      s_start(bx, 0.f, s_even);
+      compute_s(kbuf0, s_even);
+    }
   }
   __syncthreads();                                       // K buffer 0 is refilled in iteration 0
 
@@ -468,8 +527,14 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     dma_k(k2, kfree);
     dma_v(k1, vfree);
     load_krv(k1);
+    if (t + 1 < n_tiles) dma_bits(t + 1, P ? mbuf0 : mbuf1);   // the buffer tile t - 1's words were read from
+    // the bias of tile t + 1 for the start values of S(t+1), requested in tile t - 2; once this
+    // wave's reads of it are done, the buffer takes the bias of tile t + 3
+    uint4 bx[2][2];
     if constexpr (FBIAS) {
-      if (t + 2 < n_tiles) load_bias(k2, braw[P]);     // set P held tile t's bias
+      bias_lds(P ? bbuf0 : bbuf1, bx);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      dma_bias(tile_k0c(t + 3), P ? bbuf0 : bbuf1);
     }
     const int k0 = tile_k0(t);
     if (k0 < k_end_w) {
@@ -480,10 +545,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       const bool edge = (k0 + BN > nkv) || (causal && (int64_t)k0 + BN - 1 > off + wave_first);
       bool need_mask = edge || (MASK == MASK_DENSE);
       int blk_cls = 2;
-      int64_t blk_id = 0;
-      if constexpr (MASK == MASK_INFO) {
+      if constexpr (MI) {
         const int kb_blk = (k0 - (t % sub_per_blk) * BN) / a.bm_bkv;   // the block tile t lies in
-        blk_id = info_row * a.bm_nkb + kb_blk;
         blk_cls = cls_at(t / sub_per_blk, kb_blk);
         if (blk_cls == 1) need_mask = true;
       }
@@ -567,16 +630,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
                   if (jb + e < a.Lkv) bits |= (mp[(int64_t)e * a.mask_sk] != 0) << e;
               }
             }
-          } else if constexpr (MASK == MASK_INFO) {
+          } else if constexpr (MI) {
             if (blk_cls == 1) {
-              bits = 0;
-              const int r_in = i_me - qt * BM;
-              if (r_in < a.bm_bq && i_me < a.Lq) {
-                const int col = jb - (int)(blk_id % a.bm_nkb) * a.bm_bkv;
-                const uint32_t w =
-                    a.bm_bits[((int64_t)a.bm_next[blk_id] * a.bm_bq + r_in) * (a.bm_bkv / 32) + (col >> 5)];
-                bits = (w >> (col & 31)) & 0xffffu;
-              }
+              // the tile's words arrived in LDS with the previous iteration's loads
+              const uint32_t w = (P ? mbuf1 : mbuf0)[64 * wave + ql + 32 * kb];
+              bits = (w >> (16 * hh)) & 0xffffu;
             }
           }
           if (edge) {
@@ -606,9 +664,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       // fp32 sums and bf16 probabilities hold without loss. Each lane first tests its own 32
       // scores; only when some lane exceeds the slack do the halves exchange maxima (a
       // cross-lane exchange goes through the LDS queue and would drain it every tile).
-      // LAZY (fused, no bias): once the wave is established the max is left to the check of
-      // the tile's probability sum below (kLazyBound)
-      constexpr bool LAZY = FUSED && !NAT;
+      // LAZY (fused, no bias, no mask): once the wave is established the max is left to the
+      // check of the tile's probability sum below (kLazyBound)
+      // (not with a mask: at D = 128 its registers would spill)
+      constexpr bool LAZY = FUSED && !NAT && MASK == MASK_NONE;
       float mt = -INFINITY;
       if (!LAZY || !est) {
 #pragma unroll
@@ -731,7 +790,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
         float m0 = FBIAS ? fminf(fmaxf(m_run, -kStartLim), kStartLim) : m_run;
         if constexpr (FUSED) asm volatile("" : "+v"(m0));
         if constexpr (FBIAS) {
-          s_start(braw[1 - P], m0, c0);
+          s_start(bx, m0, c0);
         } else {
 #pragma unroll
           for (int e = 0; e < 16; ++e) c0[0][e] = FUSED ? -m0 : 0.f;
@@ -817,11 +876,19 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
         for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_next[kb];
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);                       // this wave's loads have landed
-    if constexpr (NORM) {
-      if (tid < BN) krv_s[(1 - P) * BN + tid] = krv;
+    // this wave's loads have landed, except (FBIAS) the four bias loads of tile t + 3, issued
+    // after all others of this tile (a load's count retires in issue order); with those in
+    // flight the barrier is a bare s_barrier, since a fenced one waits for every load
+    if constexpr (FBIAS) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm4Lgkm0);
+      __builtin_amdgcn_s_barrier();
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+      if constexpr (NORM) {
+        if (tid < BN) krv_s[(1 - P) * BN + tid] = krv;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   };
   std::integral_constant<int, 0> I0;
   std::integral_constant<int, 1> I1;
@@ -830,6 +897,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     if (t + 1 >= n_tiles) break;
     iter(I1, t + 1);
   }
+  // FBIAS: the last bias loads are still in flight; no direct load may land in LDS after the
+  // workgroup has ended
+  if constexpr (FBIAS) __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogue: O / l; NaN for rows without keys; 0 past q_lengths -------------------------
   if (i_me >= a.Lq) return;
@@ -901,16 +971,28 @@ hipError_t launch_norm(const AttnArgs& a, hipStream_t s) {
 
 template <int D, int BIAS>
 hipError_t launch_mask(const AttnArgs& a, hipStream_t s) {
-  if (a.bm_class) return launch_norm<D, BIAS, MASK_INFO>(a, s);
+  if (a.bm_class) {
+    if (a.bm_nkb <= 64) return launch_norm<D, BIAS, MASK_INFO>(a, s);
+    return launch_norm<D, BIAS, MASK_INFO_LONG>(a, s);
+  }
   if (a.mask) return launch_norm<D, BIAS, MASK_DENSE>(a, s);
   return launch_norm<D, BIAS, MASK_NONE>(a, s);
 }
 
 template <int D>
-hipError_t launch_bias(const AttnArgs& a, hipStream_t s) {
-  if (!a.bias) return launch_mask<D, BIAS_NONE>(a, s);
-  if (a.bias_dtype == SDPA_BF16) return launch_mask<D, BIAS_BF16>(a, s);
-  return launch_mask<D, BIAS_F32>(a, s);
+hipError_t launch_bias(const AttnArgs& args, hipStream_t s) {
+  if (!args.bias) return launch_mask<D, BIAS_NONE>(args, s);
+  if (args.bias_dtype == SDPA_BF16) {
+    // the fused bias at D = 64 (no QK-norm) reaches LDS by direct loads: it needs rows of
+    // 16-byte runs and a 128-row span within 32-bit offsets; any other bf16 bias is read element
+    // by element (the per-element path, which takes any dtype)
+    const bool dma_ok = args.bias_vec && (int64_t)(BM - 1) * args.bias_sq * 2 + (int64_t)args.Lkv * 2 <= INT32_MAX;
+    if (D != 64 || args.qk_norm || dma_ok) return launch_mask<D, BIAS_BF16>(args, s);
+    AttnArgs a = args;
+    a.bias_vec = 0;
+    return launch_mask<D, BIAS_F32>(a, s);
+  }
+  return launch_mask<D, BIAS_F32>(args, s);
 }
 
 bool al(const void* p, int n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }

@@ -59,6 +59,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, i
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
 
+// The same with one 32-bit word per lane: lane l copies 4 bytes from byte offset voff of r into
+// lds + 4*l.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
+}
+
 // Buffer resource over `bytes` bytes from `base`: loads past the end return 0 (the hardware's
 // range check), which zero-fills ragged tails without branches.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
