@@ -54,9 +54,9 @@ constexpr int NT = 256;            // threads per workgroup
 
 // BIAS_F32: an fp32 bias, or a bf16 bias the fused path cannot stage (read element by element)
 enum { BIAS_NONE = 0, BIAS_BF16 = 1, BIAS_F32 = 2 };
-// MASK_INFO: block info whose rows hold at most 64 blocks (the host knows n_kb), every CSR
-// entry of a row in the lanes of one register; MASK_INFO_LONG: longer rows, entries from 64 on
-// loaded from memory where they are used. (With such a load in one arm of a lookup, the
+// MASK_INFO: block info whose rows hold at most 64 blocks (the host knows n_kb) of a power-of-two
+// number of 64-key tiles, every CSR entry of a row in the lanes of one register; MASK_INFO_LONG:
+// any other block info, entries from 64 on loaded from memory where they are used. (With such a load in one arm of a lookup, the
 // compiler makes the common arm wait for every load in flight, prefetches included, so the
 // short form has no such arm at all.)
 enum { MASK_NONE = 0, MASK_DENSE = 1, MASK_INFO = 2, MASK_INFO_LONG = 3 };
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   if (wave_last < wave_first || k_end_w < 0) k_end_w = 0;
 
   // tiles to visit: all tiles below k_end, or the non-empty blocks of the mask info
-  int n_tiles = 0, csr_begin = 0, sub_per_blk = 1;
+  int n_tiles = 0, csr_begin = 0, sub_per_blk = 1, sub_shift = 0;
   int64_t info_row = 0;
   // MASK_INFO: lane l holds entry l of the row's CSR (its kv block, that block's class and, for a
   // partial block, its index among the partial blocks), so the tile loop reads them with
@@ -218,6 +218,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     csr_begin = a.bm_row_ptr[info_row];
     const int csr_end = a.bm_row_ptr[info_row + 1];
     sub_per_blk = a.bm_bkv / BN;
+    if constexpr (MASK == MASK_INFO) sub_shift = __builtin_ctz(sub_per_blk);   // a power of two (host)
     const bool in_row = csr_begin + lane < csr_end;
     if (in_row) {
       dn_lane = a.bm_data_next[csr_begin + lane];
@@ -236,6 +237,16 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   } else {
     n_tiles = (int)((k_end + BN - 1) / BN);
   }
+  // the CSR entry of tile t and the tile's place in that block (shifts in the short form,
+  // where the host has made bkv / BN a power of two)
+  auto tile_entry = [&](int t) -> int {
+    if constexpr (MASK == MASK_INFO) return t >> sub_shift;
+    return t / sub_per_blk;
+  };
+  auto tile_sub = [&](int t) -> int {
+    if constexpr (MASK == MASK_INFO) return t & (sub_per_blk - 1);
+    return t % sub_per_blk;
+  };
   // kv block of the idx-th non-empty block of the row, and its class (MASK_INFO)
   auto blk_at = [&](int idx) -> int {
     if constexpr (MASK == MASK_INFO) return __builtin_amdgcn_readlane(dn_lane, idx);
@@ -250,7 +261,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     return idx < 64 ? __builtin_amdgcn_readlane(nx_lane, idx) : a.bm_next[info_row * a.bm_nkb + blk];
   };
   auto tile_k0 = [&](int t) -> int {
-    if constexpr (MI) return blk_at(t / sub_per_blk) * a.bm_bkv + (t % sub_per_blk) * BN;
+    if constexpr (MI) return blk_at(tile_entry(t)) * a.bm_bkv + tile_sub(t) * BN;
     else return t * BN;
   };
   // staging runs ahead of the last tile without branches: past the end it reloads the last tile
@@ -441,14 +452,14 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   // the block (its keys 32*k .. 32*k + 31); lane l loads word l of the region.
   auto dma_bits = [&](int u, uint32_t* dst) {
     if constexpr (MI) {
-      const int idx = u / sub_per_blk;
+      const int idx = tile_entry(u);
       const int blk = blk_at(idx);
       if (cls_at(idx, blk) == 1) {                       // wave-uniform
         const int wpr = a.bm_bkv / 32;                   // words per block row
         const uint32_t* base = a.bm_bits + (int64_t)next_at(idx, blk) * a.bm_bq * wpr;
         const __amdgpu_buffer_rsrc_t rm = make_rsrc(base, (int64_t)a.bm_bq * wpr * 4);
         const int row = 32 * wave + (lane & 31);
-        const int word = (u % sub_per_blk) * (BN / 32) + (lane >> 5);
+        const int word = tile_sub(u) * (BN / 32) + (lane >> 5);
         dma4(rm, dst + 64 * wave, (row * wpr + word) * 4);
       }
     }
@@ -546,8 +557,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       bool need_mask = edge || (MASK == MASK_DENSE);
       int blk_cls = 2;
       if constexpr (MI) {
-        const int kb_blk = (k0 - (t % sub_per_blk) * BN) / a.bm_bkv;   // the block tile t lies in
-        blk_cls = cls_at(t / sub_per_blk, kb_blk);
+        const int kb_blk = blk_at(tile_entry(t));          // the block tile t lies in
+        blk_cls = cls_at(tile_entry(t), kb_blk);
         if (blk_cls == 1) need_mask = true;
       }
       // logits. FUSED: s is already the logit minus m_run; else s becomes
@@ -972,7 +983,8 @@ hipError_t launch_norm(const AttnArgs& a, hipStream_t s) {
 template <int D, int BIAS>
 hipError_t launch_mask(const AttnArgs& a, hipStream_t s) {
   if (a.bm_class) {
-    if (a.bm_nkb <= 64) return launch_norm<D, BIAS, MASK_INFO>(a, s);
+    const int sub = a.bm_bkv / BN;
+    if (a.bm_nkb <= 64 && (sub & (sub - 1)) == 0) return launch_norm<D, BIAS, MASK_INFO>(a, s);
     return launch_norm<D, BIAS, MASK_INFO_LONG>(a, s);
   }
   if (a.mask) return launch_norm<D, BIAS, MASK_DENSE>(a, s);
