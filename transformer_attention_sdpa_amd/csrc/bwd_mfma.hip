@@ -301,14 +301,19 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
     to.load(static_cast<const uint16_t*>(g.dout) + b * g.do_sb + h * g.do_sh, g.do_ss, i0, a.Lq, (int)(g.do_ss * 2),
             od, wave);
   };
-  // statistics of the tile's queries: thread t < 64 takes lse / scale of query t, 64 <= t < 128 its D
-  auto load_stat = [&](int it) -> float {
-    if (tid >= 2 * QT8) return 0.f;
-    const int h = it_head(it), i = it_q0(it) + (tid & (QT8 - 1));
-    const int64_t row = ((int64_t)b * a.Hq + h) * a.Lq + i;
-    if (tid < QT8) return i < nq ? g.w_lse[row] / a.scale : INFINITY;   // +inf: weight 0 (scale > 0)
-    return i < nq ? g.w_dsum[row] : 0.f;
+  // statistics of the step's queries into stat[buf] by direct loads, like the tiles: wave 0 the
+  // lse of queries it_q0 .. + 63, wave 1 their D. The prep pass wrote +inf and 0 for rows that
+  // take no part; rows past Lq read 0 (buffer range), harmless there since their Q and dO tiles
+  // are zeros too. (Loaded into registers instead, the values made the compiler wait for every
+  // load in flight where the branches on the thread index met, or spill.)
+  auto dma_stat = [&](int it, int buf) {
+    if (wave < 2) {
+      const int i0 = it_q0(it);
+      const float* src = (wave == 0 ? g.w_lse : g.w_dsum) + ((int64_t)b * a.Hq + it_head(it)) * a.Lq + i0;
+      dma4(make_rsrc(src, (int64_t)(a.Lq - i0) * 4), reinterpret_cast<uint32_t*>(&stat[buf][wave][0]), lane * 4);
+    }
   };
+  const float neg_inv_scale = -1.0f / a.scale;          // scale > 0 on this path
   // mask rows of step it (queries it_q0 .. + 63, keys k0 .. k0 + 127) into mraw[buf]
   auto load_mask = [&](int it, int buf) {
     if constexpr (MK == MK_U8 || MK == MK_U1) {
@@ -381,8 +386,8 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
 
   const int first = next_step(-1), second = next_step(first);
   if (first < n_it) {
+    dma_stat(first, 0);
     load_tiles(first, qbuf0, obuf0);
-    const float st0 = load_stat(first);
     load_mask(first, 0);
     if constexpr (MK == MK_BI) {
       bi_load_raw(first);
@@ -392,7 +397,6 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
       bi_load_raw(second);
     }
     __builtin_amdgcn_s_waitcnt(0);
-    if (tid < 2 * QT8) stat[0][tid / QT8][tid & (QT8 - 1)] = st0;
     bi_fix(0);
     bi_advance(second);
   } else {
@@ -405,10 +409,9 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
     constexpr int P = decltype(PAR_)::value;
     const uint16_t* qs = P ? qbuf1 : qbuf0;
     const uint16_t* os = P ? obuf1 : obuf0;
-    float st_next = 0.f;
     if (nx < n_it) {
+      dma_stat(nx, 1 - P);
       load_tiles(nx, P ? qbuf0 : qbuf1, P ? obuf0 : obuf1);
-      st_next = load_stat(nx);
       load_mask(nx, 1 - P);
       bi_dma(1 - P);
       bi_load_raw(nn);
@@ -423,7 +426,8 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 l4 = ls[i], d4 = ds[i];
-        s[4 * i] = -l4.x; s[4 * i + 1] = -l4.y; s[4 * i + 2] = -l4.z; s[4 * i + 3] = -l4.w;
+        s[4 * i] = l4.x * neg_inv_scale; s[4 * i + 1] = l4.y * neg_inv_scale;
+        s[4 * i + 2] = l4.z * neg_inv_scale; s[4 * i + 3] = l4.w * neg_inv_scale;
         dp[4 * i] = -d4.x; dp[4 * i + 1] = -d4.y; dp[4 * i + 2] = -d4.z; dp[4 * i + 3] = -d4.w;
       }
 #pragma unroll
@@ -480,7 +484,6 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
-    if (nx < n_it && tid < 2 * QT8) stat[1 - P][tid / QT8][tid & (QT8 - 1)] = st_next;
     if (nx < n_it) {
       bi_fix(1 - P);
       bi_advance(nn);
