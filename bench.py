@@ -59,6 +59,8 @@ PREFILL_COUNTERS = (os.path.join(ROOT, "profiles", "fwd_mfma_causal_b4h16d128l40
                     os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc", "fwd_mfma.hip"))
 DECODE_COUNTERS = (os.path.join(ROOT, "profiles", "decode_gqa_b64h32kv8d128_counters.txt"),
                    os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc", "decode.hip"))
+BIAS_MASK_COUNTERS = (os.path.join(ROOT, "profiles", "fwd_mfma_bias_block_mask_b2h16d64l8192.md"),
+                      os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc", "fwd_mfma.hip"))
 BACKWARD_COUNTERS = (os.path.join(ROOT, "profiles", "bwd_causal_b4h16d128l4096_counters.txt"),
                      os.path.join(ROOT, "transformer_attention_sdpa_amd", "csrc", "bwd_mfma.hip"))
 
@@ -310,6 +312,11 @@ def cpu_baseline_prefill(w, budget_s):
             "cores_note": "cores = the BLAS threads the oracle's matrix products ran on"}
 
 
+def progress(msg):
+    """One line on stderr per finished section: the JSON result stays the only stdout line."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -326,6 +333,7 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     peaks = None if args.skip_peaks else measured_peaks(stream)
+    progress("measured peaks done" if peaks else "measured peaks skipped")
 
     def frac_measured(achieved, key):
         return round(achieved / peaks[key], 4) if peaks else None
@@ -376,6 +384,7 @@ def main():
                    "rel_l2": p_rel, "bar": "max_abs <= 2e-2, rel_l2 <= 5e-3 (bf16 output)"},
         "wall_s_timed_region": round(t_wall, 4),
     }
+    progress("prefill timed")
     # ---- gradient (sdpa_bwd) of the same causal prefill ------------------------------------
     # one call: prep (D = rowsum(dO * O)), dK/dV, dQ and the dscale sum. Algorithmic work: the
     # five products per allowed pair (S again, dP, dV, dK, dQ), 10 * D flops, 2.5x the forward.
@@ -408,6 +417,7 @@ def main():
     del q, k, v, out
     torch.cuda.empty_cache()
 
+    progress("gradient section done")
     # ---- GQA decode -----------------------------------------------------------------------
     if not args.skip_decode:
         d = workloads.gqa_decode()
@@ -461,6 +471,7 @@ def main():
         del qd, kc, vc, od, ws
         torch.cuda.empty_cache()
 
+    progress("decode section done")
     # ---- block info of a runtime mask: bytes (U8) and packed bits (U1) --------------------
     # the 8192 x 8192 mask of the bias + block-sparse workload, 128 x 128 blocks; the bound is
     # reading the mask (64 MiB as bytes, 8 MiB as bits) plus writing the partial blocks' bits
@@ -485,6 +496,7 @@ def main():
         del mu8, mu1
         torch.cuda.empty_cache()
 
+    progress("block info section done")
     # ---- bias + block-sparse mask (B2 H16 D64 L8192) and the long-context chunk ------------
     # bias + mask: ALiBi bias [1][16][8192][8192] bf16 (2 GiB) and the runtime mask through its
     # block info; algorithmic work counts the non-empty 128 x 128 blocks (4 * D flops per pair of
@@ -514,6 +526,8 @@ def main():
                          "bias_GB_per_s": round(bias_bytes / per4 / 1e9, 1),
                          "bias_frac_of_hbm": round(bias_bytes / per4 / 1e9 / PEAK_HBM_GBS, 4),
                          "mfma_frac_of_measured": frac_measured(fl4 / per4 / 1e12, "mfma_bf16_tflops"),
+                         "traffic": counters_traffic(BIAS_MASK_COUNTERS),
+                         "algorithmic_bytes": float(bias_bytes + 4.0 * B4_ * Lq4 * Hq4 * D4 * 2),
                          "note": "bias bytes of the non-empty blocks counted once (the batch shares them)"},
             "timing": TIMINGS["bias_block_mask"],
         }
@@ -544,6 +558,7 @@ def main():
         del q5, k5, v5, out5
         torch.cuda.empty_cache()
 
+    progress("bias + block mask and long-context sections done")
     # ---- widened paths: packed sequences, several decode tokens, f16 ------------------------
     # packed: causal prefill over documents packed in one sequence (16 heads, D 128, segment
     # lengths ~ U{256..4096} up to 32768 tokens), exact in-segment causal pairs; decode: the GQA
@@ -602,6 +617,7 @@ def main():
         torch.cuda.empty_cache()
         result["widened"] = nx
 
+    progress("widened sections done")
     # ---- CPU baseline (rank 0, N = 1 only) ------------------------------------------------
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_seconds)
