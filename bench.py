@@ -563,7 +563,8 @@ def main():
     # packed: causal prefill over documents packed in one sequence (16 heads, D 128, segment
     # lengths ~ U{256..4096} up to 32768 tokens), exact in-segment causal pairs; decode: the GQA
     # decode cache with 4 new query tokens per sequence (KV bytes as for one token: each K/V row
-    # is read once for all 4); f16: the causal prefill with f16 inputs (the bf16 values, exact in f16)
+    # is read once for all 4); f16: the causal prefill with f16 inputs (the bf16 values, exact in f16);
+    # non-causal: the causal prefill's tensors with every pair allowed
     if not args.skip_widened:
         nx = {}
         rng = np.random.default_rng([1007, 11])
@@ -614,6 +615,17 @@ def main():
                                     "TFLOP_per_s": round(flops / (t16 / args.steps) / 1e12, 2),
                                     "frac_of_2500": round(flops / (t16 / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del q16, k16, v16, o16
+        torch.cuda.empty_cache()
+        # the same tensors without the causal limit: every (query, key) pair, 4 * D flops each
+        qn, kn, vn = (sa.from_numpy(getattr(w, n), "bf16") for n in ("q", "k", "v"))
+        ond = torch.empty((B, Lq, Hq, D), dtype=torch.bfloat16, device="cuda")
+        stn = lambda: sa.sdpa(qn, kn, vn, is_causal=False, scale=w.scale, out=ond)
+        tnd, _ = time_steps(stn, args.steps, args.warmup, stream)
+        fl_nd = 4.0 * D * B * Hq * Lq * Lkv
+        nx["noncausal_prefill"] = {"workload": "causal_prefill shapes, is_causal false", "ms": round(tnd / args.steps * 1e3, 4),
+                                   "TFLOP_per_s": round(fl_nd / (tnd / args.steps) / 1e12, 2),
+                                   "frac_of_2500": round(fl_nd / (tnd / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del qn, kn, vn, ond
         torch.cuda.empty_cache()
         result["widened"] = nx
 
