@@ -89,10 +89,10 @@ constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
 constexpr int kWaitVm4Lgkm0 = 0x4 | (0x7 << 4) | (0x0 << 8);
 constexpr float kLazyBound = 18446744073709551616.0f;   // 2^64
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units: the running max moves only when a row's max grows by more
-// The fused bias path forms the logits against m_s = m_run clamped to [-kStartLim, kStartLim]
-// (natural units): a start value of that size keeps q.k to within 2^-10 in the accumulator,
-// while a row max far outside it (a bias at the dtype's most negative value) would absorb q.k
-// into the start value entirely.
+// The fused bias path takes its probabilities against m_s = m_run clamped to [-kStartLim,
+// kStartLim] (natural units), so that m_s * log2e is finite and one fma per score turns a logit
+// into the exponent; a row max beyond the clamp (a bias at the dtype's most negative value) is
+// handled by moving the scores explicitly.
 constexpr float kStartLim = 16384.0f;
 
 template <int D, int BIAS, int MASK, bool NORM, bool F16, bool PACKED>
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       }
     }
   };
-  // start values of an S chain: bias - m (FBIAS), -m (other FUSED), 0
+  // start values of an S chain: the bias (FBIAS), -m (other FUSED), 0
   auto s_start = [&](const uint4 (&src)[2][2], float m, f32x16 (&c)[2]) {   // src: the lane's raw bias
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -473,8 +473,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
                                src[kb][1].x, src[kb][1].y, src[kb][1].z, src[kb][1].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          c[kb][2 * e] = __uint_as_float(w[e] << 16) - m;
-          c[kb][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u) - m;
+          c[kb][2 * e] = __uint_as_float(w[e] << 16);
+          c[kb][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
         }
       } else {
 #pragma unroll
@@ -680,18 +680,24 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       // (not with a mask: at D = 128 its registers would spill)
       constexpr bool LAZY = FUSED && !NAT && MASK == MASK_NONE;
       float mt = -INFINITY;
+      float mL = 0.f;                                    // FBIAS: -m_s * log2e, see below
       if (!LAZY || !est) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s_cur[kb][e]);
       if constexpr (FUSED && NAT) {
-        // s_cur holds logits minus m_s, the clamped m_run the start values of S(t) were formed
-        // with; off = m_run - m_s is 0 unless the row max lies beyond the clamp. mt - off is the
-        // growth of the row max (thr: see above). With off != 0 every tile takes this branch and
-        // moves its scores to m_run (or to the new max) explicitly.
+        // s_cur holds the logits themselves (the chains start from the bias). Probabilities are
+        // taken against m_s, m_run clamped to [-kStartLim, kStartLim], with one fma per score,
+        // exp2(s * log2e - m_s * log2e), whose constant is finite because m_s is. off = m_run -
+        // m_s is 0 unless the row max lies beyond the clamp; then every tile takes the branch
+        // below and moves its scores by off (or to the new max), so that s - m_s is the logit
+        // minus m_run. mt (after subtracting m_s) - off is the growth of the row max (thr: see
+        // above).
         const float m_s = fminf(fmaxf(m_run, -kStartLim), kStartLim);
         const float off = m_run - m_s;
+        mL = -m_s * LOG2E;
+        mt -= m_s;
         if (__builtin_amdgcn_ballot_w64(mt - off > thr || off != 0.f)) {
           mt = fmaxf(mt, __shfl_xor(mt, 32, 64));        // row max over both halves
           const bool grow = mt - off > thr;              // thr and off are the same for both halves
@@ -768,7 +774,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
         const float xe = s_cur[f >> 4][f & 15];
         // NAT: the max is subtracted in natural units first (no overflow), then scaled
         float x2;
-        if constexpr (FUSED) x2 = NAT ? xe * LOG2E : xe;
+        if constexpr (FUSED) x2 = NAT ? fmaf(xe, LOG2E, mL) : xe;
         else x2 = NAT ? (xe - m_use) * LOG2E : xe - m_use;
         pf[f] = __builtin_amdgcn_exp2f(x2);
         if (f & 1) {
@@ -791,14 +797,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       // LDS fragments are read PF chunks ahead of the MFMA that consumes them
       constexpr int PF = 2;
       bf16x8 kf[PF + 1][2];
-      // the C operand that starts S(t+1): zero, or -m_run broadcast (FUSED). Built here from an
-      // opaque copy of m_run, so that its 16 registers live only until the first two MFMAs.
-      // FBIAS: one start vector per 32-key block (the bias of tile t + 1 is in set 1 - P),
-      // against m_run clamped to [-kStartLim, kStartLim]; otherwise a single vector serves both
-      // blocks
+      // the C operand that starts S(t+1): zero, -m_run broadcast (FUSED), or the bias (FBIAS:
+      // one start vector per 32-key block, the bias of tile t + 1). Built here from an opaque
+      // copy of m_run, so that its 16 registers live only until the first two MFMAs.
       f32x16 c0[FBIAS ? 2 : 1];
       {
-        float m0 = FBIAS ? fminf(fmaxf(m_run, -kStartLim), kStartLim) : m_run;
+        float m0 = m_run;
         if constexpr (FUSED) asm volatile("" : "+v"(m0));
         if constexpr (FBIAS) {
           s_start(bx, m0, c0);
