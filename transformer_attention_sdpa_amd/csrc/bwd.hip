@@ -49,7 +49,7 @@ __device__ __forceinline__ void load8(const void* base, int64_t idx, int dtype, 
 
 constexpr int kPrepRows = 4;                     // rows per 16-lane group
 
-__global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs g, int vec) {
+__global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs g, int vec, int stat_mfma) {
   const AttnArgs& a = g.a;
   const int l16 = threadIdx.x & 15;
   // grid: x = head * n_ib + block of kPrepRows * 16 queries, y = batch (a scalar division per
@@ -112,8 +112,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs g, int ve
     const bool in = i0 + r < a.Lq;
     const bool part = in && i0 + r < nq && lse[r] > -INFINITY && lse[r] < INFINITY;
     if (in && l16 == 0) {
-      g.w_dsum[row0 + r] = part ? acc[r] : 0.f;
-      g.w_lse[row0 + r] = part ? lse[r] : INFINITY;
+      if (stat_mfma) {                     // the matrix-core route's form (BwdArgs)
+        g.w_dsum[row0 + r] = part ? -acc[r] : 0.f;
+        g.w_lse[row0 + r] = part ? -lse[r] / a.scale : -INFINITY;
+      } else {
+        g.w_dsum[row0 + r] = part ? acc[r] : 0.f;
+        g.w_lse[row0 + r] = part ? lse[r] : INFINITY;
+      }
     }
   }
 }
@@ -300,6 +305,7 @@ hipError_t launch_bwd(const BwdArgs& g, hipStream_t s) {
   const AttnArgs& a = g.a;
   const int64_t n_rows = (int64_t)a.B * a.Hq * a.Lq;
   const int rpw = kBwdThreads / 64;
+  const bool mf = bwd_mfma_supports(g);
   if (n_rows > 0) {
     const int pe = a.out_dtype == SDPA_F32 ? 4 : 8, de = g.do_dtype == SDPA_F32 ? 4 : 8;   // elements per 16 B
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
@@ -307,11 +313,10 @@ hipError_t launch_bwd(const BwdArgs& g, hipStream_t s) {
                     ((g.do_sb | g.do_ss | g.do_sh) % de == 0);
     const int rpb = kBwdThreads / 16 * kPrepRows;
     hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((int64_t)((a.Lq + rpb - 1) / rpb) * a.Hq), (unsigned)a.B),
-                       dim3(kBwdThreads), 0, s, g, vec);
+                       dim3(kBwdThreads), 0, s, g, vec, mf ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const bool mf = bwd_mfma_supports(g);
   if (a.Lkv > 0 && a.B > 0) {
     if (mf) {
       hipError_t e = launch_bwd_mfma_dkdv(g, s);

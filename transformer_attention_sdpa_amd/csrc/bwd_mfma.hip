@@ -240,7 +240,9 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
   constexpr int KVSPT = RB * CPR / NT8;              // direct loads per thread for K (and V)
   __shared__ __align__(16) uint16_t kbuf[RB * D], vbuf[RB * D];
   __shared__ __align__(16) uint16_t qbuf0[TILE], qbuf1[TILE], obuf0[TILE], obuf1[TILE];
-  __shared__ __align__(16) float stat[2][2][QT8];    // [buffer][lse / scale, D][query]
+  // row statistics [-lse / scale, -D][query], one array per buffer: as one array, a read of one
+  // buffer waited for the direct load in flight into the other at the start of every step
+  __shared__ __align__(16) float stat0[2][QT8], stat1[2][QT8];
   // mask tile [buffer][query][key]: U8 128 bytes a query, U1 4 words a query
   __shared__ __align__(16) uint8_t mraw[MK ? 2 : 1][MK == MK_U8 ? QT8 * RB : QT8 * 16];
   __shared__ uint64_t live_bits[MK == MK_BI ? kLiveWords : 1];   // block info: bit s, step s is not empty
@@ -301,19 +303,19 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
     to.load(static_cast<const uint16_t*>(g.dout) + b * g.do_sb + h * g.do_sh, g.do_ss, i0, a.Lq, (int)(g.do_ss * 2),
             od, wave);
   };
-  // statistics of the step's queries into stat[buf] by direct loads, like the tiles: wave 0 the
-  // lse of queries it_q0 .. + 63, wave 1 their D. The prep pass wrote +inf and 0 for rows that
-  // take no part; rows past Lq read 0 (buffer range), harmless there since their Q and dO tiles
-  // are zeros too. (Loaded into registers instead, the values made the compiler wait for every
+  // statistics of the step's queries into buffer buf by direct loads, like the tiles: wave 0
+  // -lse / scale of queries it_q0 .. + 63, wave 1 their -D, the start values of S and dP as the
+  // prep pass wrote them for this route (-inf and 0 for rows that take no part); rows past Lq
+  // read 0 (buffer range), harmless there since their Q and dO tiles are zeros too. (Loaded into registers instead, the values made the compiler wait for every
   // load in flight where the branches on the thread index met, or spill.)
   auto dma_stat = [&](int it, int buf) {
     if (wave < 2) {
       const int i0 = it_q0(it);
       const float* src = (wave == 0 ? g.w_lse : g.w_dsum) + ((int64_t)b * a.Hq + it_head(it)) * a.Lq + i0;
-      dma4(make_rsrc(src, (int64_t)(a.Lq - i0) * 4), reinterpret_cast<uint32_t*>(&stat[buf][wave][0]), lane * 4);
+      float* dst = buf ? &stat1[wave][0] : &stat0[wave][0];
+      dma4(make_rsrc(src, (int64_t)(a.Lq - i0) * 4), reinterpret_cast<uint32_t*>(dst), lane * 4);
     }
   };
-  const float neg_inv_scale = -1.0f / a.scale;          // scale > 0 on this path
   // mask rows of step it (queries it_q0 .. + 63, keys k0 .. k0 + 127) into mraw[buf]
   auto load_mask = [&](int it, int buf) {
     if constexpr (MK == MK_U8 || MK == MK_U1) {
@@ -419,30 +421,43 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
     const int i0 = it_q0(it);
     // this wave's block: queries i0 + 32 * qp .. + 31 against keys wk0 .. wk0 + 31
     if (wave_live && (int64_t)i0 + 32 * qp + 31 >= wi_lo) {
-      const float* st = &stat[P][0][0];
+      // entries below e_min: before this key's causal limit (or the key lies past kv_lengths)
+      auto entry_min = [&]() {
+        int em = 0;
+        if (causal) {
+          const int64_t m = (int64_t)key_me - off - (i0 + 32 * qp + 16 * hh);
+          em = m < 0 ? 0 : (m > 16 ? 16 : (int)m);
+        }
+        return key_me >= nkv ? 16 : em;
+      };
+      const float* st = P ? &stat1[0][0] : &stat0[0][0];
       f32x16 s, dp;
       const float4* ls = reinterpret_cast<const float4*>(st + 32 * qp + 16 * hh);
       const float4* ds = reinterpret_cast<const float4*>(st + QT8 + 32 * qp + 16 * hh);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 l4 = ls[i], d4 = ds[i];
-        s[4 * i] = l4.x * neg_inv_scale; s[4 * i + 1] = l4.y * neg_inv_scale;
-        s[4 * i + 2] = l4.z * neg_inv_scale; s[4 * i + 3] = l4.w * neg_inv_scale;
-        dp[4 * i] = -d4.x; dp[4 * i + 1] = -d4.y; dp[4 * i + 2] = -d4.z; dp[4 * i + 3] = -d4.w;
+        s[4 * i] = l4.x; s[4 * i + 1] = l4.y; s[4 * i + 2] = l4.z; s[4 * i + 3] = l4.w;
+        dp[4 * i] = d4.x; dp[4 * i + 1] = d4.y; dp[4 * i + 2] = d4.z; dp[4 * i + 3] = d4.w;
+      }
+      if constexpr (MK == MK_NONE) {
+        // without a mask the limits enter as -inf start values (the products keep -inf, so the
+        // weight is 0), and only in blocks that some lane does not keep whole (wave-uniform;
+        // most blocks of a causal call are kept whole)
+        const int e_min = entry_min();
+        if (__builtin_amdgcn_ballot_w64(e_min != 0)) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[e] = e >= e_min ? s[e] : -INFINITY;
+        }
       }
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
         s = E::mfma(tq.arow(qs, qp, c, hh), bkv(kbuf, c), s);
         dp = E::mfma(to.arow(os, qp, c, hh), bkv(vbuf, c), dp);
       }
-      int e_min = 0;                                  // entries below: before this key's causal limit
-      if (causal) {
-        const int64_t m = (int64_t)key_me - off - (i0 + 32 * qp + 16 * hh);
-        e_min = m < 0 ? 0 : (m > 16 ? 16 : (int)m);
-      }
-      if (key_me >= nkv) e_min = 16;
       uint32_t valid = 0;                             // masked: bit e set where query e keeps this key
       if constexpr (MK != MK_NONE) {
+        const int e_min = entry_min();
         const int r0 = 32 * qp + 16 * hh;
         if constexpr (MK == MK_U8) {
           const uint8_t* mp = mraw[P] + r0 * RB + 32 * kw + ql;
@@ -461,7 +476,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
         const float x = s[e] * c2;
         float p;
         if constexpr (MK != MK_NONE) p = __builtin_amdgcn_exp2f(keep_or_ninf(valid, e, x));
-        else p = __builtin_amdgcn_exp2f(e >= e_min ? x : -INFINITY);
+        else p = __builtin_amdgcn_exp2f(x);           // the limit is in the start values
         pv[e] = p;
         sv[e] = p * dp[e];
       }
@@ -567,8 +582,9 @@ __global__ __launch_bounds__(NTB, MK == MK_NONE ? 1 : 2) void bwd_dq_mfma_kernel
   const float c2 = a.scale * LOG2E;
   const int i_me = q0 + 32 * wave + ql;
   const int64_t wrow = ((int64_t)b * a.Hq + h) * a.Lq + i_me;
-  const float lse2 = i_me < nq ? g.w_lse[wrow] * LOG2E : INFINITY;
-  const float dsum = i_me < nq ? g.w_dsum[wrow] : 0.f;
+  // the prep pass wrote -lse / scale and -D for this route (BwdArgs)
+  const float lse2 = i_me < nq ? -g.w_lse[wrow] * c2 : INFINITY;
+  const float dsum = i_me < nq ? -g.w_dsum[wrow] : 0.f;
 
   // keys the workgroup and this wave visit
   const int row_end = min(q0 + RB, nq);

@@ -104,9 +104,11 @@ struct BwdArgs {
   int64_t dq_sb, dq_ss, dq_sh, dk_sb, dk_ss, dk_sh, dv_sb, dv_ss, dv_sh;
   int dq_dtype, dk_dtype, dv_dtype;
   float* dscale;               // one float, or nullptr
-  // workspace rows, [B][Hq][Lq] each: rowsum(dO * O) (0 for rows that take no part), the lse of
-  // rows that take part (+inf for the others, so that every weight of such a row is 0), and
-  // each row's share of dscale
+  // workspace rows, [B][Hq][Lq] each: D = rowsum(dO * O) (0 for rows that take no part), the lse
+  // of rows that take part (+inf for the others, so that every weight of such a row is 0), and
+  // each row's share of dscale. On the matrix-core route (stat_mfma) the first two hold -D and
+  // -lse / scale (-inf for rows that take no part; scale > 0 there): the start values of that
+  // route's S and dP products, taken as they are.
   float* w_dsum;
   float* w_lse;
   float* w_dsc;
