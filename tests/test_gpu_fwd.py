@@ -326,3 +326,25 @@ def test_logit_jumps_move_the_running_max(lib, dtype, D, causal):
     ref = run_oracle(w)
     assert np.isfinite(ref).all()
     assert_close(run_gpu(w).cpu().numpy(), ref, dtype, "logit jumps")
+
+
+@pytest.mark.parametrize("slope", [0.3, 2.0])
+@pytest.mark.parametrize("D,bias_dtype,info", [(64, "bf16", False), (64, "bf16", True), (128, "bf16", False),
+                                               (64, "f32", False), (128, "f32", True)])
+def test_rising_bias_moves_the_running_max(lib, slope, D, bias_dtype, info):
+    # a bias rising along the keys, slope * (j - i) (the ALiBi form of the fourth workload, with
+    # a steep slope): a row's max grows by slope * 64 per 64-key tile, so the kernels move it on
+    # many tiles, each time past the new maximum. slope 2 moves it on every tile, slope 0.3 on
+    # about every third; causal with a random mask, also through block info
+    say(f"rising bias slope {slope} D={D} bias {bias_dtype} info={info}")
+    B, Lq, Lkv, H = 2, 200, 400, 4
+    w = workloads.random_attention(4300 + D + int(10 * slope), B, Lq, Lkv, H, 2, D, dtype="bf16",
+                                   bias_shape=(1, H, Lq, Lkv), bias_dtype=bias_dtype,
+                                   mask_shape=(1, 1, Lq, Lkv), mask_p=0.6, is_causal=True, q_offset=150)
+    i = np.arange(Lq)[:, None]
+    j = np.arange(Lkv)[None, :]
+    ramp = slope * (j - i).astype(np.float64) * (1.0 + 0.25 * np.arange(H))[:, None, None]
+    w.bias = (workloads.f64_to_bf16(ramp) if bias_dtype == "bf16" else ramp.astype(np.float32))[None]
+    ref = run_oracle(w)
+    assert_close(run_gpu(w, use_mask_info=info, bq=128, bkv=64).cpu().numpy(), ref, "bf16",
+                 f"rising bias slope {slope}")

@@ -89,6 +89,15 @@ constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
 constexpr int kWaitVm4Lgkm0 = 0x4 | (0x7 << 4) | (0x0 << 8);
 constexpr float kLazyBound = 18446744073709551616.0f;   // 2^64
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units: the running max moves only when a row's max grows by more
+// With a bias (logits in natural units) a row's max can grow on every tile -- an ALiBi bias rises
+// along the keys by its slope times the tile width -- and each move rescales O. There the max
+// moves only when it grows by more than kNatSlack, and a move sets it kNatOver beyond the new
+// maximum, so that the next move waits until the row has grown by kNatSlack + kNatOver. The
+// largest probability stays below e^16 and the largest of a moved tile at e^-24, both far inside
+// fp32 and bf16 range (the probabilities' relative precision does not depend on their scale);
+// f16 probabilities have no such range, so f16 inputs keep the plain slack.
+constexpr float kNatSlack = 16.0f;
+constexpr float kNatOver = 24.0f;
 // The fused bias path takes its probabilities against m_s = m_run clamped to [-kStartLim,
 // kStartLim] (natural units), so that m_s * log2e is finite and one fma per score turns a logit
 // into the exponent; a row max beyond the clamp (a bias at the dtype's most negative value) is
@@ -116,7 +125,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   constexpr bool FBIAS = BIAS == BIAS_BF16 && D == 64 && !NORM;
   constexpr bool FUSED = (BIAS == BIAS_NONE || FBIAS) && !NORM;
   constexpr bool NAT = BIAS != BIAS_NONE;
-  constexpr float SLACK = NAT ? RESCALE_SLACK * LN2 : RESCALE_SLACK;   // in the logits' units
+  // in the logits' units; f16 probabilities (largest 65504, smallest normal 2^-14) keep the
+  // narrow slack and no overshoot
+  constexpr float SLACK = NAT ? (F16 ? RESCALE_SLACK * LN2 : kNatSlack) : RESCALE_SLACK;
+  constexpr float OVER = (NAT && !F16) ? kNatOver : 0.f;        // see kNatOver
   // Four statically distinct tile buffers, so that the compiler's wait-count tracking can tell a
   // read of one from a direct load in flight into another.
   __shared__ __align__(16) uint16_t kbuf0[TILE], kbuf1[TILE], vbuf0[TILE], vbuf1[TILE];
@@ -701,8 +713,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
         if (__builtin_amdgcn_ballot_w64(mt - off > thr || off != 0.f)) {
           mt = fmaxf(mt, __shfl_xor(mt, 32, 64));        // row max over both halves
           const bool grow = mt - off > thr;              // thr and off are the same for both halves
-          const float dlt = grow ? mt : off;             // the scores become relative to m_new
-          const float m_new = grow ? m_s + mt : m_run;
+          const float dlt = grow ? mt + OVER : off;      // the scores become relative to m_new
+          const float m_new = grow ? m_s + mt + OVER : m_run;
           // a row's first keys: nothing accumulated yet (and the exp2 may overflow)
           const float alpha = thr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * LOG2E);
           l_run *= alpha;
@@ -740,7 +752,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       } else if (__builtin_amdgcn_ballot_w64(mt > m_run + SLACK)) {
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));          // row max over both halves
         const bool grow = mt > m_run + SLACK;
-        const float m_new = grow ? mt : m_run;
+        const float m_new = grow ? mt + OVER : m_run;
         // 0 on a row's first finite logit (m_run = -inf)
         const float alpha = __builtin_amdgcn_exp2f(NAT ? (m_run - m_new) * LOG2E : m_run - m_new);
         l_run *= alpha;
