@@ -394,7 +394,8 @@ def main():
         dout = sa.from_numpy(workloads.output_cotangent(w, 7), "bf16")
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
                  torch.empty(1, dtype=torch.float32, device="cuda"))
-        bws = torch.empty(sa.bwd_workspace_bytes(q, k, v), dtype=torch.uint8, device="cuda")
+        # the workspace with room for the stored dS: the dK/dV pass writes dS, the dQ pass reads it
+        bws = torch.empty(sa.bwd_workspace_bytes(q, k, v, store_ds=True), dtype=torch.uint8, device="cuda")
         bstep = lambda: sa.sdpa_bwd(q, k, v, outb, dout, lse, is_causal=True, scale=w.scale, grads=grads,
                                     workspace=bws)
         bsteps = max(1, args.steps // 2)
@@ -409,7 +410,7 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(tf_b, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "traffic": counters_traffic(BACKWARD_COUNTERS),
                          "flops_per_call": flops_b, "frac_of_measured": frac_measured(tf_b, "mfma_bf16_tflops"),
-                         "kernel": "bwd_prep + bwd_dkdv8_kernel<128> + bwd_dq_mfma_kernel<128> + bwd_dscale"},
+                         "kernel": "bwd_prep + bwd_dkdv8_kernel<128> (stores dS) + bwd_dq_ds_kernel<128> + bwd_dscale"},
             "parity": backward_parity(w, q, k, v, outb, dout, lse, grads),
             "timing": TIMINGS["backward"],
         }

@@ -165,7 +165,12 @@ SDPA_API sdpa_status sdpa_fwd_lse(const sdpa_tensor* q, const sdpa_tensor* k, co
  *      head_dim stride 1; every element is written (0 for keys that no query attends).
  * dscale  device fp32 scalar, or NULL: sum over all pairs of dS_ij * <q_i, k_j>.
  * workspace  device scratch of at least sdpa_bwd_workspace_bytes(); results are deterministic
- *      (no atomics, fixed reduction order).
+ *      (no atomics, fixed reduction order). With at least sdpa_bwd_workspace_bytes_ds() bytes
+ *      (when that is not 0) and neither block info nor a call the matrix-core kernels decline,
+ *      the dK/dV pass also stores every dS tile it forms, and the dQ pass reads them instead of
+ *      forming the weights a second time; the results agree to rounding (the dQ products take
+ *      a 16-bit dS either way), and dscale is then summed over the keys j as
+ *      <sum_i dS_ij q_i, k_j>.
  * ------------------------------------------------------------------------------------- */
 SDPA_API sdpa_status sdpa_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
                               const sdpa_tensor* out, const sdpa_tensor* dout, const float* lse,
@@ -179,6 +184,12 @@ SDPA_API sdpa_status sdpa_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const 
 
 /* Bytes of workspace sdpa_bwd needs for these shapes. Host only. */
 SDPA_API size_t sdpa_bwd_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v);
+
+/* Bytes of workspace with which sdpa_bwd stores dS for its dQ pass: the bytes above plus
+ * B*Hq*ceil(Lq/64)*ceil(Lkv/128)*16 KiB of dS tiles and the dK/dV workgroups' dscale shares.
+ * 0 where that route does not apply (inputs other than bf16/f16, D != Dv, D not 64 or 128) or
+ * the dS tiles would exceed 8 GiB. Host only. */
+SDPA_API size_t sdpa_bwd_workspace_bytes_ds(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v);
 
 /* ---------------------------------------------------------------------------------------
  * sdpa_fwd_packed -- attention over packed sequences (page "Neural Network primitives from

@@ -246,6 +246,24 @@ def test_bwd_workspace_bytes(lib):
     assert n == 3 * ((rows * 4 + 255) // 256 * 256) + 256      # + one chunk of first-stage dscale sums
 
 
+def test_bwd_workspace_bytes_ds(lib):
+    # the stored-dS route: the minimum, the dK/dV workgroups' dscale shares (8 each, one 128-key
+    # block of 2 K/V heads in 3 batches), one chunk of their first-stage sums, and one 16 KiB dS
+    # tile per (batch, query head, 64-query tile, 128-key block)
+    f = lambda ts: lib.sdpa_bwd_workspace_bytes_ds(*(ctypes.byref(t) for t in ts[:3]))
+    base = lib.sdpa_bwd_workspace_bytes(*(ctypes.byref(t) for t in good_bwd()[:3]))
+    assert f(good_bwd()) == base + 256 + 256 + 3 * 8 * 1 * 1 * 16384
+    assert f(good_bwd(Lq=65, Lkv=129)) == (lib.sdpa_bwd_workspace_bytes(*(ctypes.byref(t) for t in good_bwd(Lq=65, Lkv=129)[:3]))
+                                          + 512 + 256 + 3 * 8 * 2 * 2 * 16384)   # 96 shares: 384 bytes
+    assert f(good_bwd(D=128, dt=N.SDPA_F16)) > 0
+    assert f(good_bwd(dt=N.SDPA_F32)) == 0                 # 16-bit inputs only
+    assert f(good_bwd(D=32)) == 0                          # head dims 64 and 128 only
+    assert f(good_bwd(Lq=0)) == 0
+    # dS tiles above 8 GiB: the dQ pass forms the weights again
+    assert f(good_bwd(D=128, Hq=16, Hkv=16, Lq=8192, Lkv=8192, B=5)) == 0
+    assert f(good_bwd(D=128, Hq=16, Hkv=16, Lq=8192, Lkv=8192, B=4)) > 0
+
+
 def test_decode_per_batch_lengths_are_checked_on_the_host(lib):
     # the kernels read kv_lengths[b] (and write_index[b]) for every batch element: a shorter
     # array is refused before anything reaches the device; an int or one entry broadcasts

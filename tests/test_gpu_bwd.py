@@ -13,13 +13,16 @@ import torch
 import oracle
 import workloads
 import transformer_attention_sdpa_amd as sa
-from gpu_util import say, dev, per_batch, gpu_inputs, assert_close, assert_grad_close
+from gpu_util import say, dev, per_batch, gpu_inputs, assert_close, assert_grad_close, nan_like
 
 pytestmark = pytest.mark.gpu
 
 
 def run_bwd(w, dout, q_lengths=None, grad_dtype=torch.float32, use_mask_info=False, bq=128, bkv=128,
-            out_dtype=torch.float32, mask=None):
+            out_dtype=torch.float32, mask=None, store_ds=True):
+    # store_ds: a workspace with room for the stored dS (the dK/dV pass writes dS and the dQ pass
+    # reads it) or the minimum one (the dQ pass forms the weights again); NaN-filled either way,
+    # so a dS block the dQ pass reads without its having been written shows
     t = gpu_inputs(w)
     if mask is not None:
         t["mask"] = mask
@@ -28,8 +31,10 @@ def run_bwd(w, dout, q_lengths=None, grad_dtype=torch.float32, use_mask_info=Fal
               kv_lengths=per_batch(w.kv_lengths), q_lengths=per_batch(q_lengths))
     out, lse = sa.sdpa(t["q"], t["k"], t["v"], None, None if info else t["mask"], mask_info=info,
                        return_lse=True, out_dtype=out_dtype, **kw)
+    ws = nan_like((max(1, sa.bwd_workspace_bytes(t["q"], t["k"], t["v"], store_ds)),), torch.uint8)
     dq, dk, dv, dsc = sa.sdpa_bwd(t["q"], t["k"], t["v"], out, dev(dout, w.dtype), lse,
-                                  None if info else t["mask"], mask_info=info, grad_dtype=grad_dtype, **kw)
+                                  None if info else t["mask"], mask_info=info, grad_dtype=grad_dtype,
+                                  workspace=ws, **kw)
     torch.cuda.synchronize()
     f = lambda x: x.float().cpu().numpy()
     return dict(dq=f(dq), dk=f(dk), dv=f(dv), dscale=float(dsc.item()), lse=lse.cpu().numpy())
@@ -71,11 +76,12 @@ FEATURES = [
 ]
 
 
+@pytest.mark.parametrize("store_ds", [True, False])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("D", [16, 64, 128])
 @pytest.mark.parametrize("hkv", [4, 1])
 @pytest.mark.parametrize("case", range(len(FEATURES)))
-def test_grad_features(lib, case, hkv, D, dtype):
+def test_grad_features(lib, case, hkv, D, dtype, store_ds):
     f = dict(FEATURES[case])
     kvl = f.pop("kv_lengths", None)
     qo = f.pop("q_offset", 0)
@@ -83,8 +89,8 @@ def test_grad_features(lib, case, hkv, D, dtype):
                                    q_offset=np.array(qo, dtype=np.int32) if isinstance(qo, list) else qo,
                                    kv_lengths=None if kvl is None else np.array(kvl, dtype=np.int32), **f)
     dout = workloads.output_cotangent(w, 3000 + case)
-    say(f"grad case={case} {FEATURES[case]} hkv={hkv} D={D} {dtype}")
-    check(run_bwd(w, dout), run_ref(w, dout), dtype, f"case {case}")
+    say(f"grad case={case} {FEATURES[case]} hkv={hkv} D={D} {dtype} store_ds={store_ds}")
+    check(run_bwd(w, dout, store_ds=store_ds), run_ref(w, dout), dtype, f"case {case}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -126,7 +132,8 @@ def test_grad_mask_info_equals_dense(lib, Lkv, bq, bkv, D):
     out, lse = sa.sdpa(t["q"], t["k"], t["v"], None, t["mask"], return_lse=True, out_dtype=torch.float32, **kw)
     d_o = dev(dout, w.dtype)
     info = sa.build_block_mask_info(t["mask"], bq, bkv)
-    g_dense = sa.sdpa_bwd(t["q"], t["k"], t["v"], out, d_o, lse, t["mask"], **kw)
+    # (the dense call on the same route as block info: the dQ pass forms the weights again)
+    g_dense = sa.sdpa_bwd(t["q"], t["k"], t["v"], out, d_o, lse, t["mask"], store_ds=False, **kw)
     g_info = sa.sdpa_bwd(t["q"], t["k"], t["v"], out, d_o, lse, None, mask_info=info, **kw)
     torch.cuda.synchronize()
     for n, x, y in zip(("dq", "dk", "dv", "dscale"), g_info, g_dense):
@@ -146,10 +153,11 @@ def test_grad_mask_info_unaligned_dense(lib):
     check(run_bwd(w, dout, use_mask_info=True, bq=128, bkv=64), ref, "bf16", "block info")
 
 
+@pytest.mark.parametrize("store_ds", [True, False])
 @pytest.mark.parametrize("kind", ["u8", "u1"])
 @pytest.mark.parametrize("dtype,D,mshape,causal", [("bf16", 128, (2, 8), False), ("f16", 64, (1, 1), "bottom_right"),
                                                    ("bf16", 64, (2, 1), True), ("f16", 128, (1, 8), True)])
-def test_grad_mask_matrix_tiles(lib, kind, dtype, D, mshape, causal):
+def test_grad_mask_matrix_tiles(lib, kind, dtype, D, mshape, causal, store_ds):
     # masks whose rows suit the 16-bit matrix-core kernels (496 keys: 31 16-byte runs of bytes,
     # 16 words of bits) over several query and key tiles, ragged tails, GQA, per-batch kv_lengths,
     # and rows left with no allowed key; U1 padding bits are set, so a read of one would show
@@ -162,11 +170,11 @@ def test_grad_mask_matrix_tiles(lib, kind, dtype, D, mshape, causal):
     m = None
     if kind == "u1":
         m = sa.PackedMask(torch.as_tensor(workloads.pack_mask_bits(w.mask, 1), device="cuda"), w.mask.shape[-1])
-    say(f"grad mask {kind} {dtype} D={D} mask {mshape} causal={causal}")
-    got = run_bwd(w, dout, mask=m)
+    say(f"grad mask {kind} {dtype} D={D} mask {mshape} causal={causal} store_ds={store_ds}")
+    got = run_bwd(w, dout, mask=m, store_ds=store_ds)
     check(got, run_ref(w, dout), dtype, f"mask {kind}")
     if kind == "u1":
-        dense = run_bwd(w, dout)
+        dense = run_bwd(w, dout, store_ds=store_ds)
         for n in ("dq", "dk", "dv"):
             np.testing.assert_array_equal(got[n], dense[n])
 
@@ -216,13 +224,14 @@ def test_grad_degenerate_lengths(lib, Lq, Lkv):
     assert abs(got["dscale"] - ref["dscale"]) <= 2e-2
 
 
+@pytest.mark.parametrize("store_ds", [True, False])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
-def test_grad_gqa_ragged_several_tiles(lib, dtype, D):
+def test_grad_gqa_ragged_several_tiles(lib, dtype, D, store_ds):
     # several 128-key and 128-query tiles with ragged tails, 4 query heads per K/V head,
     # bottom-right causal with per-batch kv_lengths
     w = workloads.random_attention(2700 + D, 2, 300, 777, 8, 2, D, dtype=dtype, is_causal="bottom_right",
                                    kv_lengths=np.array([700, 777], dtype=np.int32))
     dout = workloads.output_cotangent(w, 3700)
-    say(f"grad GQA ragged {dtype} D={D}")
-    check(run_bwd(w, dout), run_ref(w, dout), dtype, "gqa ragged")
+    say(f"grad GQA ragged {dtype} D={D} store_ds={store_ds}")
+    check(run_bwd(w, dout, store_ds=store_ds), run_ref(w, dout), dtype, "gqa ragged")

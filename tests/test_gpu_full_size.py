@@ -145,12 +145,13 @@ def _poisoned_grads(q, k, v):
             nan_like((1,), torch.float32))
 
 
-def test_causal_prefill_gradient_b4_h16_d128_l4096(lib):
+@pytest.mark.parametrize("store_ds", [True, False])
+def test_causal_prefill_gradient_b4_h16_d128_l4096(lib, store_ds):
     # the gradient in the benchmark's configuration (bf16 inputs, saved output and gradients in
     # bf16): every row of two whole (batch, head) slices against the fp64 oracle gradient of the
     # slice (one K/V head per query head, so a slice is an independent attention); every entry
     # of all slices finite, with outputs and workspace NaN-filled first
-    say("full size: gradient of the causal prefill B4 H16 D128 L4096")
+    say(f"full size: gradient of the causal prefill B4 H16 D128 L4096, store_ds={store_ds}")
     from gpu_util import assert_grad_close
     w = workloads.causal_prefill()
     t = gpu_inputs(w)
@@ -158,7 +159,7 @@ def test_causal_prefill_gradient_b4_h16_d128_l4096(lib):
                        return_lse=True)
     dout_np = workloads.output_cotangent(w, 7)
     grads = _poisoned_grads(t["q"], t["k"], t["v"])
-    ws = nan_like((sa.bwd_workspace_bytes(t["q"], t["k"], t["v"]),), torch.uint8)
+    ws = nan_like((sa.bwd_workspace_bytes(t["q"], t["k"], t["v"], store_ds),), torch.uint8)
     dq, dk, dv, dsc = sa.sdpa_bwd(t["q"], t["k"], t["v"], out.to(torch.bfloat16), dev(dout_np, "bf16"), lse,
                                   is_causal=True, scale=w.scale, grads=grads, workspace=ws)
     torch.cuda.synchronize()

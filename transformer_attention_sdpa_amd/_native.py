@@ -59,6 +59,7 @@ PROTOTYPES = {
     "sdpa_bwd": (I32, [T, T, T, T, T, VP, T, ctypes.POINTER(BlockMaskInfoC), ctypes.c_float, I32,
                        I32P, I32, I32P, I32, I32P, I32, T, T, T, VP, VP, SZ, VP]),
     "sdpa_bwd_workspace_bytes": (SZ, [T, T, T]),
+    "sdpa_bwd_workspace_bytes_ds": (SZ, [T, T, T]),
     "sdpa_fwd_packed": (I32, [T, T, T, I32P, I32P, I32, I32, ctypes.c_float, I32,
                               I32P, I32, I32P, I32, I32P, I32, I32, T, VP, SZ, VP]),
     "sdpa_fwd_workspace_bytes": (SZ, [T, T, T, I32]),

@@ -242,13 +242,16 @@ def sdpa(q, k, v, bias=None, mask=None, *, mask_info: BlockMaskInfo = None, scal
 @_on_stream
 def sdpa_bwd(q, k, v, out, dout, lse, mask=None, *, mask_info: BlockMaskInfo = None, scale=None,
              is_causal=False, q_offset=0, kv_lengths=None, q_lengths=None, grad_dtype=None, grads=None,
-             workspace=None):
+             workspace=None, store_ds=True):
     """Gradient of ``sdpa`` with respect to q, k, v and scale (sdpa_bwd).
 
     out and lse come from ``sdpa(..., return_lse=True)`` of the same call; dout is the cotangent
     of out. Returns (dq, dk, dv, dscale): dq/dk/dv of q/k/v's shapes in grad_dtype (default
     q.dtype), dscale a one-element fp32 tensor. ``grads`` may pass those four tensors to be
-    written instead, and ``workspace`` a uint8 device tensor of bwd_workspace_bytes().
+    written instead, and ``workspace`` a uint8 device tensor of bwd_workspace_bytes() (its size
+    picks the route: with bwd_workspace_bytes(store_ds=True) bytes the dK/dV pass stores dS for
+    the dQ pass; with fewer the dQ pass forms the weights again). ``store_ds`` sizes the
+    workspace allocated here when none is passed.
     """
     lib = N.load()
     B, Lq, Hq, _ = q.shape
@@ -268,7 +271,9 @@ def sdpa_bwd(q, k, v, out, dout, lse, mask=None, *, mask_info: BlockMaskInfo = N
     kv_ptr, kv_all, kv_keep = _per_batch_arg(kv_lengths, B, q.device, -1)
     ql_ptr, ql_all, ql_keep = _per_batch_arg(q_lengths, B, q.device, -1)
     ws_bytes = lib.sdpa_bwd_workspace_bytes(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv))
-    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_bytes(q, k, v, store_ds), 1), dtype=torch.uint8, device=q.device)
+    ws = workspace
     if ws.numel() < ws_bytes:
         raise ValueError(f"workspace needs {ws_bytes} bytes")
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Lq):
@@ -280,7 +285,7 @@ def sdpa_bwd(q, k, v, out, dout, lse, mask=None, *, mask_info: BlockMaskInfo = N
                       float("nan") if scale is None else float(scale), _CAUSAL[is_causal],
                       qo_ptr, qo_all, kv_ptr, kv_all, ql_ptr, ql_all,
                       ctypes.byref(gq), ctypes.byref(gk), ctypes.byref(gv), ctypes.c_void_p(dscale.data_ptr()),
-                      ctypes.c_void_p(ws.data_ptr()), ws_bytes, sp)
+                      ctypes.c_void_p(ws.data_ptr()), ws.numel(), sp)
     N.check(st)
     return dq_t, dk_t, dv_t, dscale
 
@@ -324,11 +329,15 @@ def sdpa_packed(q, k, v, q_segments, kv_segments=None, *, maxlen=None, scale=Non
     return out
 
 
-def bwd_workspace_bytes(q, k, v) -> int:
-    """Bytes of workspace sdpa_bwd needs for these tensors."""
+def bwd_workspace_bytes(q, k, v, store_ds=False) -> int:
+    """Bytes of workspace sdpa_bwd needs for these tensors; with store_ds, the bytes with which
+    it stores dS for its dQ pass where that route applies (else the same minimum)."""
     lib = N.load()
     tq, tk, tv = desc(q), desc(k), desc(v)
-    return int(lib.sdpa_bwd_workspace_bytes(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv)))
+    n = int(lib.sdpa_bwd_workspace_bytes(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv)))
+    if store_ds:
+        n = max(n, int(lib.sdpa_bwd_workspace_bytes_ds(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv))))
+    return n
 
 
 def decode_workspace_bytes(q, k_cache, num_splits=0) -> int:

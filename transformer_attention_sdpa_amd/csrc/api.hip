@@ -336,6 +336,19 @@ size_t sdpa_bwd_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k, cons
   return 3 * ((rows * sizeof(float) + 255) & ~(size_t)255) + ((chunks * sizeof(double) + 255) & ~(size_t)255);
 }
 
+// the stored-dS extension, after the bytes above: dK/dV workgroup shares of dscale, their
+// first-stage sums, the dS tiles
+size_t sdpa_bwd_workspace_bytes_ds(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v) {
+  if (!q || !k || !v) return 0;
+  const int64_t tiles = bwd_ds_tile_bytes(q->dims[3], q->dims[1], q->dims[2], k->dims[2], q->dims[0], v->dims[0],
+                                          q->dtype);
+  if (tiles <= 0 || k->dims[3] <= 0 || k->dims[1] <= 0) return 0;
+  const size_t n_dsp = (size_t)bwd_dkdv_workgroups(k->dims[3], k->dims[1], k->dims[2]) * 8;
+  const size_t chunks = (n_dsp + 4095) / 4096;
+  return sdpa_bwd_workspace_bytes(q, k, v) + ((n_dsp * sizeof(float) + 255) & ~(size_t)255) +
+         ((chunks * sizeof(double) + 255) & ~(size_t)255) + (size_t)tiles;
+}
+
 sdpa_status sdpa_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v, const sdpa_tensor* out,
                      const sdpa_tensor* dout, const float* lse, const sdpa_tensor* mask,
                      const sdpa_block_mask_info* mask_info, float scale, int32_t is_causal,
@@ -385,6 +398,16 @@ sdpa_status sdpa_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tens
   g.w_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + seg);
   g.w_dsc = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * seg);
   g.w_dsc2 = reinterpret_cast<double*>(static_cast<char*>(workspace) + 3 * seg);
+  const size_t need_ds = sdpa_bwd_workspace_bytes_ds(q, k, v);
+  if (need_ds && workspace_bytes >= need_ds) {
+    const size_t n_dsp = (size_t)bwd_dkdv_workgroups(k->dims[3], k->dims[1], k->dims[2]) * 8;
+    char* x = static_cast<char*>(workspace) + need;
+    g.w_dsp = reinterpret_cast<float*>(x);
+    x += (n_dsp * sizeof(float) + 255) & ~(size_t)255;
+    g.w_dsc2_ds = reinterpret_cast<double*>(x);
+    x += (((n_dsp + 4095) / 4096) * sizeof(double) + 255) & ~(size_t)255;
+    g.w_ds = reinterpret_cast<uint16_t*>(x);
+  }
   return hip_status(launch_bwd(g, static_cast<hipStream_t>(stream)), "sdpa_bwd");
 }
 

@@ -298,6 +298,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dscale_stage2(const double* p
 }  // namespace
 
 bool bwd_mfma_supports(const BwdArgs& g);
+bool bwd_stores_ds(const BwdArgs& g);
 hipError_t launch_bwd_mfma_dkdv(const BwdArgs& g, hipStream_t s);
 hipError_t launch_bwd_mfma_dq(const BwdArgs& g, hipStream_t s);
 
@@ -339,13 +340,18 @@ hipError_t launch_bwd(const BwdArgs& g, hipStream_t s) {
     }
   }
   if (g.dscale) {
-    const int64_t n2 = (n_rows + kDscChunk - 1) / kDscChunk;
+    // the stored-dS route sums the dK/dV workgroups' shares, the other the dQ rows' shares
+    const bool ds = mf && bwd_stores_ds(g);
+    const int64_t n = ds ? (a.Lkv > 0 ? bwd_dkdv_workgroups(a.B, a.Hkv, a.Lkv) * 8 : 0) : n_rows;
+    const float* part = ds ? g.w_dsp : g.w_dsc;
+    double* part2 = ds ? g.w_dsc2_ds : g.w_dsc2;
+    const int64_t n2 = (n + kDscChunk - 1) / kDscChunk;
     if (n2 > 0) {
-      hipLaunchKernelGGL(bwd_dscale_stage1, dim3((unsigned)n2), dim3(kBwdThreads), 0, s, g.w_dsc, n_rows, g.w_dsc2);
+      hipLaunchKernelGGL(bwd_dscale_stage1, dim3((unsigned)n2), dim3(kBwdThreads), 0, s, part, n, part2);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(bwd_dscale_stage2, dim3(1), dim3(kBwdThreads), 0, s, g.w_dsc2, n2, g.dscale);
+    hipLaunchKernelGGL(bwd_dscale_stage2, dim3(1), dim3(kBwdThreads), 0, s, part2, n2, g.dscale);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -148,6 +148,13 @@ __device__ __forceinline__ void store4(void* base, int64_t off, int dtype, float
 // (direct loads, no registers held across the step). U8: one byte per key; U1: 32 keys a word.
 constexpr int MK_NONE = 0, MK_U8 = 1, MK_U1 = 2, MK_BI = 3;
 
+// cache-policy operand of a buffer access: the NT (streaming) bit
+constexpr int kStreamPolicy = 2;
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
+// vmcnt(n) lgkmcnt(0), n < 64
+constexpr int vm_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
+
 // Buffer resource over the mask rows of (b, h): loads past its last row read 0
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t mask_rsrc(const AttnArgs& a, int b, int h) {
   const int64_t eb = a.mask_u1 ? 4 : 1;
@@ -219,6 +226,13 @@ __device__ __forceinline__ float keep_or_ninf(uint32_t valid, int e, float x) {
   return __uint_as_float((__float_as_uint(x) & keep) | (0xff800000u & ~keep));
 }
 
+// Byte offset, within a stored dS tile, of the 8 queries 8 * c .. + 7 (c = 0 .. 7) of key row
+// r (0 .. 127): written by lane 32 * ((c >> 1) & 1) + r % 32 of the dK/dV wave owning keys
+// 32 * (r / 32) .. and queries 32 * (c >> 2) .., as its operand sB[c & 1]
+__device__ __forceinline__ int ds_offset(int r, int c) {
+  return ((4 * (r >> 5) + 2 * (c >> 2) + (c & 1)) << 10) + ((((c >> 1) & 1) << 5) + (r & 31)) * 16;
+}
+
 // ================================ dK / dV ====================================================
 // Eight waves: waves w and w + 4 own the same 32 keys and take the two 32-query blocks of each
 // 64-query tile, so each holds only its accumulators and the S/dP pair, and two waves share
@@ -232,7 +246,7 @@ constexpr int QT8 = 64;
 template <int D>
 __device__ __forceinline__ int kvswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
 
-template <int D, bool F16, int MK>
+template <int D, bool F16, int MK, bool DS>
 __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap) {
   using E = In<F16>;
   using x8 = typename E::x8;
@@ -386,6 +400,23 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
 #pragma unroll
     for (int e = 0; e < 16; ++e) dk[d][e] = dv[d][e] = 0.f;
 
+  // stored-dS route: the step's dS tile (128 keys x 64 queries of one head, 16 KiB) goes to HBM
+  // for the dQ pass, each store instruction of a wave writing 1 KiB in lane order: KiB
+  // 4 * kw + 2 * qp + e holds, at 16 * lane, the entries of the lane's packed operand sB[e],
+  // dS of key 32 * kw + ql and queries 32 * qp + 16 * hh + 8 * e .. + 7 (ds_offset). A wave that
+  // skips its block (all weights 0) stores nothing: the dQ pass skips that block by the same test.
+  const int ds_voff = (4 * kw + 2 * qp) * 1024 + 16 * lane;
+  auto ds_store = [&](int it, x8 lo, x8 hi) {
+    if constexpr (DS) {
+      const int64_t tile = (((int64_t)b * a.Hq + it_head(it)) * ((a.Lq + QT8 - 1) / QT8) + it_q0(it) / QT8) *
+                               ((a.Lkv + RB - 1) / RB) + kt;
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(g.w_ds + tile * (RB * QT8), RB * QT8 * 2);
+      // streaming stores (cache policy NT): the dQ pass reads them back only after this pass
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), r, ds_voff, 0, kStreamPolicy);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), r, ds_voff + 1024, 0, kStreamPolicy);
+    }
+  };
+
   const int first = next_step(-1), second = next_step(first);
   if (first < n_it) {
     dma_stat(first, 0);
@@ -483,6 +514,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
       // the four B operands packed first (the fp32 probabilities end here), then each pair of
       // transposed A operands read one MFMA pair ahead of its use
       const x8 pB[2] = {pack8<F16>(pv), pack8<F16>(pv + 8)}, sB[2] = {pack8<F16>(sv), pack8<F16>(sv + 8)};
+      ds_store(it, sB[0], sB[1]);
       x8 ao = to.atr(os, qp, 0, 0), aq = tq.atr(qs, qp, 0, 0);
 #pragma unroll
       for (int n = 0; n < 2 * DB; ++n) {
@@ -539,6 +571,25 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
     }
     __syncthreads();
   };
+  if constexpr (DS) {
+    // this wave's share of dscale = sum_ij dS_ij <q_i, k_j> = sum_j <dk_j, k_j>, dk_j being the
+    // wave's sum_i dS_ij q_i (so the waves' shares add up), read before the merge overwrites K.
+    // Lane (ql, hh) holds dk[d][4 i + t] of key kvrow at head-dim 32 d + 8 i + 4 hh + t.
+    float part = 0.f;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint2 kk = *reinterpret_cast<const uint2*>(kbuf + kvrow * D + (((4 * d + i) ^ kvsw) << 3) + 4 * hh);
+        part = fmaf(dk[d][4 * i], E::lo(kk.x), part);
+        part = fmaf(dk[d][4 * i + 1], E::hi(kk.x), part);
+        part = fmaf(dk[d][4 * i + 2], E::lo(kk.y), part);
+        part = fmaf(dk[d][4 * i + 3], E::hi(kk.y), part);
+      }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+    if (lane == 0 && g.w_dsp) g.w_dsp[(int64_t)blockIdx.x * (NT8 / 64) + wave] = part;
+  }
   merge(dv);
   merge(dk);
   if (qp == 1 || key_me >= a.Lkv) return;
@@ -820,7 +871,199 @@ __global__ __launch_bounds__(NTB, MK == MK_NONE ? 1 : 2) void bwd_dq_mfma_kernel
     }
 }
 
+// ================================ dQ from the stored dS ======================================
+// A workgroup of 8 waves owns 256 queries of one head and streams tiles of 64 keys. Wave w forms
+// dQ^T += K^T dS^T for queries q0 + 32 w .. + 31, both operands by transposed LDS reads: K^T from
+// the K tile, dS^T from the tile's four pieces of stored dS (queries q0 + 64 p .. + 63, 64 x 64
+// each, written to LDS row-major by key). The dS stream comes from HBM, whose latency is far
+// longer than a tile's products, so it is loaded DQA tiles ahead into registers (each thread 16
+// bytes of each piece, in the order the dK/dV pass stored them) and written to LDS only when its
+// tile comes up; K, read again by every query tile of the head and mostly found in L2, goes
+// straight to LDS (a stage per tile in flight), requested once the stage's previous tile has
+// been read. Loads past the last tile read an empty range, so every
+// step issues the same loads and the waits are fixed counts. A piece the dK/dV pass did not
+// write (no query of it sees a key of its block) is read from an empty range too: zeros. Within
+// a written piece, a 32-key x 32-query block whose weights are all 0 holds stale bytes (the
+// dK/dV wave skips it), and the same test skips it here.
+constexpr int DQW = 256;          // queries of a dQ workgroup on this route
+constexpr int DQA = 3;            // tiles of dS in flight (in registers)
+
+template <int D, bool F16>
+__global__ __launch_bounds__(NT8, 1) void bwd_dq_ds_kernel(BwdArgs g, int n_qt, int remap) {
+  using E = In<F16>;
+  using x8 = typename E::x8;
+  constexpr int DB = D / 32, TILE = ST * D, PIECE = 64 * 64, NP = DQW / 64, QT = 64;
+  using TK = Tiles<D, F16, ST, NT8>;
+  constexpr int LT = TK::SPT + NP;                    // loads per thread and tile
+  // Each step issues the dS loads of the tile DQA ahead, then (after its barriers) the K loads
+  // of the same tile. Waits, vmcnt(n) lgkmcnt(0): (a) the dS registers of the step's tile have
+  // arrived (then issued: its K, and dS + K of the next DQA - 1 tiles); (c) its K has landed
+  // (then issued: dS + K of the next DQA - 1 tiles, and the dS just requested)
+  constexpr int kWaitA = vm_wait(TK::SPT + (DQA - 1) * LT);
+  constexpr int kWaitC = vm_wait(NP + (DQA - 1) * LT);
+  // one K array per stage: the compiler's wait analysis tells the direct loads into one array
+  // from the reads of another only by the array (stages of one array look aliased)
+  __shared__ __align__(16) uint16_t kbuf0[TILE], kbuf1[TILE], kbuf2[TILE], sbuf[NP * PIECE];
+  auto kst = [&](auto S_) -> uint16_t* {
+    constexpr int S = decltype(S_)::value % DQA;
+    return S == 0 ? kbuf0 : (S == 1 ? kbuf1 : kbuf2);
+  };
+  const AttnArgs& a = g.a;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ql = lane & 31, hh = lane >> 5;
+
+  int rank, bh;
+  wg_map(blockIdx.x, a.Hq * a.B, remap, rank, bh);
+  const int qt = n_qt - 1 - rank;                 // causal: the last query tiles are the heaviest
+  const int h = bh % a.Hq, b = bh / a.Hq;
+  const int gk = h / (a.Hq / a.Hkv);
+  const int q0 = qt * DQW;
+  const int nkv = batch_kv_len(a, b), nq = batch_q_len(a, b);
+  const int64_t off = batch_causal_offset(a, b);
+  const bool causal = a.causal != SDPA_CAUSAL_NONE;
+  const int i_me = q0 + 32 * wave + ql;
+
+  // keys the workgroup and this wave visit (the wave's later tiles hold only zeros of dS)
+  const int row_end = min(q0 + DQW, nq);
+  int64_t k_end = nkv;
+  if (causal) { const int64_t l = off + row_end; if (l < k_end) k_end = l; }
+  if (row_end <= q0 || k_end < 0) k_end = 0;
+  const int w_last = min(q0 + 32 * wave + 31, row_end - 1);
+  int64_t k_end_w = nkv;
+  if (causal) { const int64_t l = off + w_last + 1; if (l < k_end_w) k_end_w = l; }
+  if (w_last < q0 + 32 * wave || k_end_w < 0) k_end_w = 0;
+  const int n_tiles = (int)((k_end + ST - 1) / ST);
+
+  // the dK/dV pass wrote dS tile (query tile qt64, key block kb) iff the block starts before
+  // kv_lengths and qt64 lies between the first query tile that sees the block and the last one
+  // before q_lengths
+  const int n_qt64 = (nq + QT - 1) / QT, ds_nqt = (a.Lq + QT - 1) / QT, ds_nkb = (a.Lkv + RB - 1) / RB;
+  auto written = [&](int qt64, int kb) -> bool {
+    const int k0 = kb * RB;
+    if (k0 >= nkv || qt64 >= n_qt64) return false;
+    int64_t i_lo = causal ? (int64_t)k0 - off : 0;
+    i_lo = i_lo < 0 ? 0 : i_lo;
+    return i_lo < nq && qt64 >= (int)(i_lo / QT);
+  };
+
+  TK tk;
+  tk.init((int)(a.k_ss * 2), lane, tid);
+  // transposed reads of this wave's query columns 32 * (wave & 1) .. + 31 of a dS piece (the
+  // pattern of Tiles::atr at D = 64, with the column block fixed per wave)
+  const int s_vr = 16 * (lane >> 5) + ((lane & 15) >> 2);
+  const int s_vc = 32 * (wave & 1) + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int s_lo = s_vr * 64 + ((((s_vc >> 3) ^ bswz<64>(s_vr)) << 3) | (s_vc & 7));
+  const int s_hi = (s_vr + 4) * 64 + ((((s_vc >> 3) ^ bswz<64>(s_vr + 4)) << 3) | (s_vc & 7));
+  auto atr_s = [&](const uint16_t* t, int rb, int sh) -> x8 {
+    const int rows = (32 * rb + 8 * sh) * 64;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(t + rows + s_lo));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(t + rows + s_hi));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(x8, v);
+  };
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + gk * a.k_sh;
+  const uint16_t* dsp = g.w_ds + (((int64_t)b * a.Hq + h) * ds_nqt + NP * qt) * ds_nkb * (RB * QT);
+  // thread tid reads bytes 16 * tid of a piece: KiB `wave`, lane `lane` of the dK/dV layout
+  // (ds_offset), i.e. key row 32 * (wave >> 2) + ql, queries 8 * c .. + 7 with
+  // c = 4 * ((wave >> 1) & 1) + 2 * hh + (wave & 1); it writes them to that row's swizzled chunk
+  const int s_row = 32 * (wave >> 2) + ql;
+  const int s_lds = s_row * 64 + (((4 * ((wave >> 1) & 1) + 2 * hh + (wave & 1)) ^ bswz<64>(s_row)) << 3);
+  auto load_ds = [&](int t, uint4 (&r)[NP]) {
+    const int kb = t >> 1;
+    const bool in = t < n_tiles;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint16_t* src = dsp + ((int64_t)p * ds_nkb + kb) * (RB * QT) + (t & 1) * PIECE;
+      const bool w = in && written(NP * qt + p, kb);
+      r[p] = buf_load16(make_rsrc(w ? src : g.w_ds, w ? PIECE * 2 : 0), 16 * tid);
+    }
+  };
+  auto load_k = [&](int t, uint16_t* kd) { tk.load(kp, a.k_ss, t * ST, t < n_tiles ? nkv : t * ST, (int)(a.k_ss * 2), kd, wave); };
+  auto put_ds = [&](const uint4 (&r)[NP]) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) *reinterpret_cast<uint4*>(sbuf + p * PIECE + s_lds) = r[p];
+  };
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[d][e] = 0.f;
+
+  // prologue: dS of tiles 0 .. DQA - 1 and K of tiles 0 .. DQA - 2, in the order the steps issue
+  // them (dS of a tile, then K of the tile before it), so that the fixed wait counts hold
+  std::integral_constant<int, 0> I0;
+  std::integral_constant<int, 1> I1;
+  std::integral_constant<int, 2> I2;
+  uint4 rb[DQA][NP];
+  load_ds(0, rb[0]);
+  load_k(0, kst(I0));
+  load_ds(1, rb[1]);
+  load_k(1, kst(I1));
+  load_ds(2, rb[2]);
+  load_k(2, kst(I2));
+
+  // tile t: its dS in registers rb[t % DQA], its K in kbuf[t % DQA]
+  auto iter = [&](auto S_, int t) {
+    constexpr int S = decltype(S_)::value;
+    __builtin_amdgcn_s_waitcnt(kWaitA);               // (a) dS of tile t has arrived
+    put_ds(rb[S]);
+    load_ds(t + DQA, rb[S]);
+    __builtin_amdgcn_s_waitcnt(kWaitC);               // (c) K of tile t has landed, dS is in LDS
+    __builtin_amdgcn_s_barrier();
+    const uint16_t* ks = kst(S_);
+    const uint16_t* ss = sbuf + (wave >> 1) * PIECE;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // the dK/dV wave of these 32 keys and 32 queries formed (and stored) its dS block iff its
+      // keys start before kv_lengths and the causal limit of its last query
+      const int wk0 = t * ST + 32 * kb;
+      if (wk0 < k_end_w && (!causal || (int64_t)q0 + 32 * wave + 31 >= (int64_t)wk0 - off)) {
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          const x8 sB = atr_s(ss, kb, sh);
+#pragma unroll
+          for (int d = 0; d < DB; ++d) dq[d] = E::mfma(tk.atr(ks, kb, sh, d), sB, dq[d]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);           // this wave's reads of sbuf and kbuf[S] are done
+    __builtin_amdgcn_s_barrier();
+    load_k(t + DQA, kst(S_));
+  };
+  // whole periods of DQA steps, the last one's steps past n_tiles doing nothing but their
+  // (empty) loads: every path into the loop head then carries the same loads in flight, which
+  // the compiler's wait analysis needs to keep its counts exact across the back edge
+  static_assert(DQA == 3, "the loop below is unrolled by DQA");
+  for (int t = 0; t < n_tiles; t += DQA) {
+    iter(I0, t);
+    iter(I1, t + 1);
+    iter(I2, t + 2);
+  }
+  __builtin_amdgcn_s_waitcnt(0);                      // the loads past the last tile
+
+  if (i_me >= a.Lq) return;
+  const int64_t qr = b * g.dq_sb + (int64_t)i_me * g.dq_ss + h * g.dq_sh;
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = 32 * d + 8 * i + 4 * hh;
+      store4(g.dq, qr + col, g.dq_dtype, dq[d][4 * i] * a.scale, dq[d][4 * i + 1] * a.scale,
+             dq[d][4 * i + 2] * a.scale, dq[d][4 * i + 3] * a.scale);
+    }
+}
+
 bool al(const void* p, int n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+}  // namespace
+
+// The stored-dS route runs: the matrix-core kernels take the call (checked by the caller), the
+// workspace holds the dS tiles, and no block info (whose skipped steps would leave tiles unwritten).
+bool bwd_stores_ds(const BwdArgs& g) { return g.w_ds != nullptr && g.w_dsp != nullptr && !g.a.bm_class; }
+
+namespace {
 
 template <int D, bool F16>
 hipError_t launch_dq_t(const BwdArgs& g, hipStream_t s) {
@@ -829,7 +1072,11 @@ hipError_t launch_dq_t(const BwdArgs& g, hipStream_t s) {
   const int HB = a.Hq * a.B;
   const dim3 grid((unsigned)((int64_t)n_qt * HB));
   const int remap = HB % 8 == 0 ? 1 : 0;
-  if (a.bm_class)
+  if (bwd_stores_ds(g)) {
+    const int n_qw = (a.Lq + DQW - 1) / DQW;
+    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, F16>), dim3((unsigned)((int64_t)n_qw * HB)), dim3(NT8), 0, s, g, n_qw,
+                       remap);
+  } else if (a.bm_class)
     hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, F16, MK_BI>), grid, dim3(NTB), 0, s, g, n_qt, remap);
   else if (!a.mask)
     hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, F16, MK_NONE>), grid, dim3(NTB), 0, s, g, n_qt, remap);
@@ -879,14 +1126,21 @@ hipError_t launch_dkdv8_t(const BwdArgs& g, hipStream_t s) {
   const int HB = a.Hkv * a.B;
   const dim3 grid((unsigned)((int64_t)n_kt * HB));
   const int remap = HB % 8 == 0 ? 1 : 0;
+  const bool ds = bwd_stores_ds(g);
   if (a.bm_class)
-    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_BI>), grid, dim3(NT8), 0, s, g, remap);
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_BI, false>), grid, dim3(NT8), 0, s, g, remap);
+  else if (!a.mask && ds)
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_NONE, true>), grid, dim3(NT8), 0, s, g, remap);
   else if (!a.mask)
-    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_NONE>), grid, dim3(NT8), 0, s, g, remap);
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_NONE, false>), grid, dim3(NT8), 0, s, g, remap);
+  else if (a.mask_u1 && ds)
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_U1, true>), grid, dim3(NT8), 0, s, g, remap);
   else if (a.mask_u1)
-    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_U1>), grid, dim3(NT8), 0, s, g, remap);
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_U1, false>), grid, dim3(NT8), 0, s, g, remap);
+  else if (ds)
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_U8, true>), grid, dim3(NT8), 0, s, g, remap);
   else
-    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_U8>), grid, dim3(NT8), 0, s, g, remap);
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, F16, MK_U8, false>), grid, dim3(NT8), 0, s, g, remap);
   return hipGetLastError();
 }
 

@@ -112,8 +112,29 @@ struct BwdArgs {
   float* w_dsum;
   float* w_lse;
   float* w_dsc;
-  double* w_dsc2;              // [ceil(B*Hq*Lq / 4096)]: first-stage sums of w_dsc
+  double* w_dsc2;              // first-stage sums of w_dsc (or of w_dsp)
+  // Stored-dS route (matrix-core kernels, no block info), else nullptr: the dK/dV pass writes
+  // every dS tile it forms, 16-bit, as tiles of 128 keys x 64 queries (queries contiguous, key
+  // rows of 128 bytes) indexed [B][Hq][ceil(Lq/64)][ceil(Lkv/128)], and its workgroups' shares
+  // of dscale (8 floats each, w_dsp); the dQ pass then reads dS instead of forming S and dP again.
+  uint16_t* w_ds;
+  float* w_dsp;
+  double* w_dsc2_ds;           // first-stage sums of w_dsp
 };
+
+// Workgroups of the dK/dV pass (128 keys of one K/V head each) and their dscale shares (8 each)
+inline int64_t bwd_dkdv_workgroups(int64_t B, int64_t Hkv, int64_t Lkv) { return B * Hkv * ((Lkv + 127) / 128); }
+
+// Stored-dS route: bytes of the dS tiles (0 where the route does not apply: 16-bit inputs,
+// D == Dv in {64, 128}) and the cap above which the gradient forms S and dP again in its dQ pass
+constexpr int64_t kDsCapBytes = (int64_t)8 << 30;
+inline int64_t bwd_ds_tile_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t Lkv, int64_t D, int64_t Dv, int dtype) {
+  if ((dtype != SDPA_BF16 && dtype != SDPA_F16) || D != Dv || (D != 64 && D != 128) || B <= 0 || Hq <= 0 ||
+      Lq <= 0 || Lkv <= 0)
+    return 0;
+  const int64_t n = B * Hq * ((Lq + 63) / 64) * ((Lkv + 127) / 128) * (64 * 128 * 2);
+  return n <= kDsCapBytes ? n : 0;
+}
 
 constexpr float kRmsEps = 1e-6f;
 

@@ -50,6 +50,7 @@ template <> struct In<true> {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 // One wave instruction of a direct global -> LDS load: lane l copies 16 bytes from byte offset
