@@ -48,14 +48,37 @@ __device__ __forceinline__ void load8(const void* base, int64_t idx, int dtype, 
 }
 
 constexpr int kPrepRows = 4;                     // rows per 16-lane group
+constexpr int kPastRange = 0x7ffffff0;           // a buffer offset past every range used here
+
+// The 16-lane sums of a group's rows, then the row statistics (BwdArgs) by lane 0 of the group
+__device__ __forceinline__ void prep_store(const BwdArgs& g, float (&acc)[kPrepRows], const float (&lse)[kPrepRows],
+                                           int i0, int64_t row0, int nq, int l16, int stat_mfma) {
+  const AttnArgs& a = g.a;
+#pragma unroll
+  for (int r = 0; r < kPrepRows; ++r) {
+#pragma unroll
+    for (int m = 8; m > 0; m >>= 1) acc[r] += __shfl_xor(acc[r], m, 64);
+    const bool in = i0 + r < a.Lq;
+    const bool part = in && i0 + r < nq && lse[r] > -INFINITY && lse[r] < INFINITY;
+    if (in && l16 == 0) {
+      if (stat_mfma) {                     // the matrix-core route's form (BwdArgs)
+        g.w_dsum[row0 + r] = part ? -acc[r] : 0.f;
+        g.w_lse[row0 + r] = part ? -lse[r] / a.scale : -INFINITY;
+      } else {
+        g.w_dsum[row0 + r] = part ? acc[r] : 0.f;
+        g.w_lse[row0 + r] = part ? lse[r] : INFINITY;
+      }
+    }
+  }
+}
 
 __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs g, int vec, int stat_mfma) {
   const AttnArgs& a = g.a;
   const int l16 = threadIdx.x & 15;
-  // grid: x = head * n_ib + block of kPrepRows * 16 queries, y = batch (a scalar division per
-  // workgroup, none per row); rows of the stats are [b][h][i]
-  const int n_ib = (a.Lq + kPrepRows * (kBwdThreads / 16) - 1) / (kPrepRows * (kBwdThreads / 16));
-  const int h = (int)blockIdx.x / n_ib, ib = (int)blockIdx.x - h * n_ib, b = blockIdx.y;
+  // grid: x = block of kPrepRows * 16 queries * Hq + head, y = batch (a scalar division per
+  // workgroup, none per row); rows of the stats are [b][h][i]. Head innermost: workgroups that
+  // run together read the heads of the same rows, i.e. whole contiguous rows of O and dO.
+  const int ib = (int)blockIdx.x / a.Hq, h = (int)blockIdx.x - ib * a.Hq, b = blockIdx.y;
   const int i0 = (ib * (kBwdThreads / 16) + (threadIdx.x >> 4)) * kPrepRows;
   const int64_t row0 = ((int64_t)b * a.Hq + h) * a.Lq + i0;
   const int nq = batch_q_len(a, b);
@@ -105,22 +128,56 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs g, int ve
       }
     }
   }
+  prep_store(g, acc, lse, i0, row0, nq, l16, stat_mfma);
+}
+
+// 16-bit O and dO, Dv <= 128, rows of whole 16-byte runs: the rows of bwd_prep_kernel by buffer
+// loads whose range checks stand in for the row and head-dim limits (a load past them reads 0),
+// so the lse and all 8 row loads of a lane go out together, with no branch between them
+template <int OD, int DD>
+__global__ __launch_bounds__(kBwdThreads) void bwd_prep16_kernel(BwdArgs g, int stat_mfma) {
+  const AttnArgs& a = g.a;
+  const int l16 = threadIdx.x & 15;
+  const int ib = (int)blockIdx.x / a.Hq, h = (int)blockIdx.x - ib * a.Hq, b = blockIdx.y;
+  const int i0 = (ib * (kBwdThreads / 16) + (threadIdx.x >> 4)) * kPrepRows;
+  const int64_t row0 = ((int64_t)b * a.Hq + h) * a.Lq + i0;
+  const int nq = batch_q_len(a, b);
+  auto rsrc = [](const void* p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t ro = rsrc(static_cast<const uint16_t*>(a.out) + b * a.o_sb + h * a.o_sh,
+                                         (int64_t)a.Lq * a.o_ss * 2);
+  const __amdgpu_buffer_rsrc_t rd = rsrc(static_cast<const uint16_t*>(g.dout) + b * g.do_sb + h * g.do_sh,
+                                         (int64_t)a.Lq * g.do_ss * 2);
+  const __amdgpu_buffer_rsrc_t rl = rsrc(g.lse + ((int64_t)b * a.Hq + h) * a.Lq, (int64_t)a.Lq * 4);
+  const bool lane_in = 8 * l16 < a.Dv;
+  uint4 xo[kPrepRows], xd[kPrepRows];
+  float lse[kPrepRows], acc[kPrepRows];
 #pragma unroll
   for (int r = 0; r < kPrepRows; ++r) {
-#pragma unroll
-    for (int m = 8; m > 0; m >>= 1) acc[r] += __shfl_xor(acc[r], m, 64);
-    const bool in = i0 + r < a.Lq;
-    const bool part = in && i0 + r < nq && lse[r] > -INFINITY && lse[r] < INFINITY;
-    if (in && l16 == 0) {
-      if (stat_mfma) {                     // the matrix-core route's form (BwdArgs)
-        g.w_dsum[row0 + r] = part ? -acc[r] : 0.f;
-        g.w_lse[row0 + r] = part ? -lse[r] / a.scale : -INFINITY;
-      } else {
-        g.w_dsum[row0 + r] = part ? acc[r] : 0.f;
-        g.w_lse[row0 + r] = part ? lse[r] : INFINITY;
-      }
-    }
+    const int i = i0 + r;
+    lse[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * i, 0, 0));
+    const int oo = lane_in ? i * (int)(a.o_ss * 2) + 16 * l16 : kPastRange;
+    const int od = lane_in ? i * (int)(g.do_ss * 2) + 16 * l16 : kPastRange;
+    xo[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ro, oo, 0, 0));
+    xd[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, od, 0, 0));
   }
+  auto f = [](uint32_t w, bool hi, int dt) {
+    const uint16_t x = hi ? (uint16_t)(w >> 16) : (uint16_t)w;
+    return dt == SDPA_BF16 ? bf16_bits_to_float(x) : f16_bits_to_float(x);
+  };
+#pragma unroll
+  for (int r = 0; r < kPrepRows; ++r) {
+    const uint32_t wo[4] = {xo[r].x, xo[r].y, xo[r].z, xo[r].w}, wd[4] = {xd[r].x, xd[r].y, xd[r].z, xd[r].w};
+    float s_ = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      s_ = fmaf(f(wo[t], false, OD), f(wd[t], false, DD), s_);
+      s_ = fmaf(f(wo[t], true, OD), f(wd[t], true, DD), s_);
+    }
+    acc[r] = s_;
+  }
+  prep_store(g, acc, lse, i0, row0, nq, l16, stat_mfma);
 }
 
 // ---- 2. dK/dV: one wave per key (b, kv head, j); lanes hold head-dim columns ------------------
@@ -288,6 +345,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dscale_stage1(const float* pa
   if (threadIdx.x == 0) part2[blockIdx.x] = t;
 }
 
+// One workgroup over at most kDscSmall float shares (fixed order, fp64 sums)
+constexpr int64_t kDscSmall = 65536;
+__global__ __launch_bounds__(kBwdThreads) void bwd_dscale_small(const float* part, int64_t n, float* out) {
+  double acc = 0.0;
+  // buffer loads: past n they read 0, so the 16 loads go out together with no branch between
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(part), (short)0,
+                                                                      (int)(n * 4), 0x00020000);
+  for (int base = threadIdx.x; base < n; base += 16 * kBwdThreads) {
+    float v[16];                                   // 16 loads in flight at once
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      v[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 4 * (base + u * kBwdThreads), 0, 0));
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc += (double)v[u];
+  }
+  const double t = block_sum(acc);
+  if (threadIdx.x == 0) *out = (float)t;
+}
+
 __global__ __launch_bounds__(kBwdThreads) void bwd_dscale_stage2(const double* part2, int64_t n, float* out) {
   double acc = 0.0;
   for (int64_t e = threadIdx.x; e < n; e += kBwdThreads) acc += part2[e];
@@ -313,8 +389,24 @@ hipError_t launch_bwd(const BwdArgs& g, hipStream_t s) {
     const int vec = (a.Dv % 8 == 0) && al16(a.out) && al16(g.dout) && ((a.o_sb | a.o_ss | a.o_sh) % pe == 0) &&
                     ((g.do_sb | g.do_ss | g.do_sh) % de == 0);
     const int rpb = kBwdThreads / 16 * kPrepRows;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((int64_t)((a.Lq + rpb - 1) / rpb) * a.Hq), (unsigned)a.B),
-                       dim3(kBwdThreads), 0, s, g, vec, mf ? 1 : 0);
+    const dim3 grid((unsigned)((int64_t)((a.Lq + rpb - 1) / rpb) * a.Hq), (unsigned)a.B);
+    auto is16 = [](int dt) { return dt == SDPA_BF16 || dt == SDPA_F16; };
+    // 32-bit buffer offsets: every row start and the past-range offset stay apart
+    const int64_t lim = kPastRange - 256;
+    if (vec && a.Dv <= 128 && is16(a.out_dtype) && is16(g.do_dtype) && (int64_t)(a.Lq + rpb) * a.o_ss * 2 < lim &&
+        (int64_t)(a.Lq + rpb) * g.do_ss * 2 < lim && (int64_t)(a.Lq + rpb) * 4 < lim) {
+      const bool ob = a.out_dtype == SDPA_BF16, db = g.do_dtype == SDPA_BF16;
+      if (ob && db)
+        hipLaunchKernelGGL((bwd_prep16_kernel<SDPA_BF16, SDPA_BF16>), grid, dim3(kBwdThreads), 0, s, g, mf ? 1 : 0);
+      else if (ob)
+        hipLaunchKernelGGL((bwd_prep16_kernel<SDPA_BF16, SDPA_F16>), grid, dim3(kBwdThreads), 0, s, g, mf ? 1 : 0);
+      else if (db)
+        hipLaunchKernelGGL((bwd_prep16_kernel<SDPA_F16, SDPA_BF16>), grid, dim3(kBwdThreads), 0, s, g, mf ? 1 : 0);
+      else
+        hipLaunchKernelGGL((bwd_prep16_kernel<SDPA_F16, SDPA_F16>), grid, dim3(kBwdThreads), 0, s, g, mf ? 1 : 0);
+    } else {
+      hipLaunchKernelGGL(bwd_prep_kernel, grid, dim3(kBwdThreads), 0, s, g, vec, mf ? 1 : 0);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -345,6 +437,10 @@ hipError_t launch_bwd(const BwdArgs& g, hipStream_t s) {
     const int64_t n = ds ? (a.Lkv > 0 ? bwd_dkdv_workgroups(a.B, a.Hkv, a.Lkv) * 8 : 0) : n_rows;
     const float* part = ds ? g.w_dsp : g.w_dsc;
     double* part2 = ds ? g.w_dsc2_ds : g.w_dsc2;
+    if (n <= kDscSmall) {
+      hipLaunchKernelGGL(bwd_dscale_small, dim3(1), dim3(kBwdThreads), 0, s, part, n, g.dscale);
+      return hipGetLastError();
+    }
     const int64_t n2 = (n + kDscChunk - 1) / kDscChunk;
     if (n2 > 0) {
       hipLaunchKernelGGL(bwd_dscale_stage1, dim3((unsigned)n2), dim3(kBwdThreads), 0, s, part, n, part2);

@@ -873,18 +873,19 @@ __global__ __launch_bounds__(NTB, MK == MK_NONE ? 1 : 2) void bwd_dq_mfma_kernel
 
 // ================================ dQ from the stored dS ======================================
 // A workgroup of 8 waves owns 256 queries of one head and streams tiles of 64 keys. Wave w forms
-// dQ^T += K^T dS^T for queries q0 + 32 w .. + 31, both operands by transposed LDS reads: K^T from
-// the K tile, dS^T from the tile's four pieces of stored dS (queries q0 + 64 p .. + 63, 64 x 64
-// each, written to LDS row-major by key). The dS stream comes from HBM, whose latency is far
-// longer than a tile's products, so it is loaded DQA tiles ahead into registers (each thread 16
-// bytes of each piece, in the order the dK/dV pass stored them) and written to LDS only when its
-// tile comes up; K, read again by every query tile of the head and mostly found in L2, goes
-// straight to LDS (a stage per tile in flight), requested once the stage's previous tile has
-// been read. Loads past the last tile read an empty range, so every
-// step issues the same loads and the waits are fixed counts. A piece the dK/dV pass did not
-// write (no query of it sees a key of its block) is read from an empty range too: zeros. Within
-// a written piece, a 32-key x 32-query block whose weights are all 0 holds stale bytes (the
-// dK/dV wave skips it), and the same test skips it here.
+// dQ^T += K^T dS^T for the 64 queries q0 + 64 (w / 2) .. + 63 and half of the head dim (32-wide
+// blocks (w % 2) * DB / 2 ..), both operands by transposed LDS reads: K^T from the K tile, dS^T
+// from the tile's four pieces of stored dS (queries q0 + 64 p .. + 63, 64 x 64 each, written to
+// LDS row-major by key). The pass is bound by those LDS reads; 64 x D/2 per wave reads 20% less
+// than 32 x D. The dS stream comes from HBM, whose latency is far longer than a tile's products,
+// so it is loaded DQA tiles ahead into registers (each thread 16 bytes of each piece, in the order
+// the dK/dV pass stored them) and written to LDS only when its tile comes up; K, read again by
+// every query tile of the head and mostly found in L2, goes straight to LDS (a stage per tile in
+// flight), requested once the stage's previous tile has been read. Loads past the last tile read
+// an empty range, so every step issues the same loads and the waits are fixed counts. A piece the
+// dK/dV pass did not write (no query of it sees a key of its block) is read from an empty range
+// too: zeros. Within a written piece, a 32-key x 32-query block whose weights are all 0 holds
+// stale bytes (the dK/dV wave skips it), and the same test skips it here.
 constexpr int DQW = 256;          // queries of a dQ workgroup on this route
 constexpr int DQA = 3;            // tiles of dS in flight (in registers)
 
@@ -892,7 +893,7 @@ template <int D, bool F16>
 __global__ __launch_bounds__(NT8, 1) void bwd_dq_ds_kernel(BwdArgs g, int n_qt, int remap) {
   using E = In<F16>;
   using x8 = typename E::x8;
-  constexpr int DB = D / 32, TILE = ST * D, PIECE = 64 * 64, NP = DQW / 64, QT = 64;
+  constexpr int DB = D / 32, DW = DB / 2, TILE = ST * D, PIECE = 64 * 64, NP = DQW / 64, QT = 64;
   using TK = Tiles<D, F16, ST, NT8>;
   constexpr int LT = TK::SPT + NP;                    // loads per thread and tile
   // Each step issues the dS loads of the tile DQA ahead, then (after its barriers) the K loads
@@ -912,6 +913,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dq_ds_kernel(BwdArgs g, int n_qt, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, hh = lane >> 5;
+  const int wq = wave >> 1, wd = wave & 1;            // the wave's 64 queries (a piece), head-dim half
 
   int rank, bh;
   wg_map(blockIdx.x, a.Hq * a.B, remap, rank, bh);
@@ -922,18 +924,22 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dq_ds_kernel(BwdArgs g, int n_qt, 
   const int nkv = batch_kv_len(a, b), nq = batch_q_len(a, b);
   const int64_t off = batch_causal_offset(a, b);
   const bool causal = a.causal != SDPA_CAUSAL_NONE;
-  const int i_me = q0 + 32 * wave + ql;
 
-  // keys the workgroup and this wave visit (the wave's later tiles hold only zeros of dS)
+  // keys the workgroup visits, and the end of the keys each 32-query block of the wave sees
+  // (past it the block's dS is all zeros)
   const int row_end = min(q0 + DQW, nq);
   int64_t k_end = nkv;
   if (causal) { const int64_t l = off + row_end; if (l < k_end) k_end = l; }
   if (row_end <= q0 || k_end < 0) k_end = 0;
-  const int w_last = min(q0 + 32 * wave + 31, row_end - 1);
-  int64_t k_end_w = nkv;
-  if (causal) { const int64_t l = off + w_last + 1; if (l < k_end_w) k_end_w = l; }
-  if (w_last < q0 + 32 * wave || k_end_w < 0) k_end_w = 0;
   const int n_tiles = (int)((k_end + ST - 1) / ST);
+  int64_t k_end_b[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r0 = q0 + 64 * wq + 32 * j, last = min(r0 + 31, row_end - 1);
+    int64_t e = nkv;
+    if (causal) { const int64_t l = off + last + 1; if (l < e) e = l; }
+    k_end_b[j] = (last < r0 || e < 0) ? 0 : e;
+  }
 
   // the dK/dV pass wrote dS tile (query tile qt64, key block kb) iff the block starts before
   // kv_lengths and qt64 lies between the first query tile that sees the block and the last one
@@ -949,19 +955,31 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dq_ds_kernel(BwdArgs g, int n_qt, 
 
   TK tk;
   tk.init((int)(a.k_ss * 2), lane, tid);
-  // transposed reads of this wave's query columns 32 * (wave & 1) .. + 31 of a dS piece (the
-  // pattern of Tiles::atr at D = 64, with the column block fixed per wave)
-  const int s_vr = 16 * (lane >> 5) + ((lane & 15) >> 2);
-  const int s_vc = 32 * (wave & 1) + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int s_lo = s_vr * 64 + ((((s_vc >> 3) ^ bswz<64>(s_vr)) << 3) | (s_vc & 7));
-  const int s_hi = (s_vr + 4) * 64 + ((((s_vc >> 3) ^ bswz<64>(s_vr + 4)) << 3) | (s_vc & 7));
-  auto atr_s = [&](const uint16_t* t, int rb, int sh) -> x8 {
-    const int rows = (32 * rb + 8 * sh) * 64;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(t + rows + s_lo));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(t + rows + s_hi));
-    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  // transposed-read offsets (the pattern of Tiles::atr, with the wave's column blocks fixed):
+  // rows 16 * hh + (lane % 16) / 4 (+ 4), columns 16 * ((lane / 16) % 2) + 4 * (lane % 4) of
+  // each 32-wide block; dS^T: query blocks 0 and 1 of the wave's piece, K^T: its head-dim blocks
+  const int t_vr = 16 * hh + ((lane & 15) >> 2);
+  const int t_vc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int s_lo[2], s_hi[2], k_lo[DW], k_hi[DW];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = 32 * j + t_vc;
+    s_lo[j] = t_vr * 64 + ((((c >> 3) ^ bswz<64>(t_vr)) << 3) | (c & 7));
+    s_hi[j] = (t_vr + 4) * 64 + ((((c >> 3) ^ bswz<64>(t_vr + 4)) << 3) | (c & 7));
+  }
+#pragma unroll
+  for (int j = 0; j < DW; ++j) {
+    const int c = 32 * (DW * wd + j) + t_vc;
+    k_lo[j] = t_vr * D + ((((c >> 3) ^ bswz<D>(t_vr)) << 3) | (c & 7));
+    k_hi[j] = (t_vr + 4) * D + ((((c >> 3) ^ bswz<D>(t_vr + 4)) << 3) | (c & 7));
+  }
+  auto tr = [&](const uint16_t* t, int lo, int hi) -> x8 {
+    const s16x4 l = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(t + lo));
+    const s16x4 u = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(t + hi));
+    const s16x8 v = {l[0], l[1], l[2], l[3], u[0], u[1], u[2], u[3]};
     return __builtin_bit_cast(x8, v);
   };
+
   const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + gk * a.k_sh;
   const uint16_t* dsp = g.w_ds + (((int64_t)b * a.Hq + h) * ds_nqt + NP * qt) * ds_nkb * (RB * QT);
   // thread tid reads bytes 16 * tid of a piece: KiB `wave`, lane `lane` of the dK/dV layout
@@ -985,14 +1003,15 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dq_ds_kernel(BwdArgs g, int n_qt, 
     for (int p = 0; p < NP; ++p) *reinterpret_cast<uint4*>(sbuf + p * PIECE + s_lds) = r[p];
   };
 
-  f32x16 dq[DB];
+  f32x16 dq[2][DW];
 #pragma unroll
-  for (int d = 0; d < DB; ++d)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dq[d][e] = 0.f;
+    for (int d = 0; d < DW; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dq[j][d][e] = 0.f;
 
-  // prologue: dS of tiles 0 .. DQA - 1 and K of tiles 0 .. DQA - 2, in the order the steps issue
-  // them (dS of a tile, then K of the tile before it), so that the fixed wait counts hold
+  // prologue: dS and K of tiles 0 .. DQA - 1, in the order the steps issue them
   std::integral_constant<int, 0> I0;
   std::integral_constant<int, 1> I1;
   std::integral_constant<int, 2> I2;
@@ -1004,7 +1023,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dq_ds_kernel(BwdArgs g, int n_qt, 
   load_ds(2, rb[2]);
   load_k(2, kst(I2));
 
-  // tile t: its dS in registers rb[t % DQA], its K in kbuf[t % DQA]
+  // tile t: its dS in registers rb[t % DQA], its K in stage t % DQA
   auto iter = [&](auto S_, int t) {
     constexpr int S = decltype(S_)::value;
     __builtin_amdgcn_s_waitcnt(kWaitA);               // (a) dS of tile t has arrived
@@ -1013,22 +1032,34 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dq_ds_kernel(BwdArgs g, int n_qt, 
     __builtin_amdgcn_s_waitcnt(kWaitC);               // (c) K of tile t has landed, dS is in LDS
     __builtin_amdgcn_s_barrier();
     const uint16_t* ks = kst(S_);
-    const uint16_t* ss = sbuf + (wave >> 1) * PIECE;
+    const uint16_t* ss = sbuf + wq * PIECE;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      // the dK/dV wave of these 32 keys and 32 queries formed (and stored) its dS block iff its
-      // keys start before kv_lengths and the causal limit of its last query
+      // the dK/dV wave of these 32 keys and a 32-query block formed (and stored) its dS block
+      // iff its keys start before the end of the keys the block sees
       const int wk0 = t * ST + 32 * kb;
-      if (wk0 < k_end_w && (!causal || (int64_t)q0 + 32 * wave + 31 >= (int64_t)wk0 - off)) {
+      const bool live0 = wk0 < k_end_b[0], live1 = wk0 < k_end_b[1];
+      if (live0 || live1) {
 #pragma unroll
         for (int sh = 0; sh < 2; ++sh) {
-          const x8 sB = atr_s(ss, kb, sh);
+          const int rows = (32 * kb + 8 * sh);
+          x8 kA[DW];
 #pragma unroll
-          for (int d = 0; d < DB; ++d) dq[d] = E::mfma(tk.atr(ks, kb, sh, d), sB, dq[d]);
+          for (int d = 0; d < DW; ++d) kA[d] = tr(ks + rows * D, k_lo[d], k_hi[d]);
+          if (live0) {
+            const x8 sB = tr(ss + rows * 64, s_lo[0], s_hi[0]);
+#pragma unroll
+            for (int d = 0; d < DW; ++d) dq[0][d] = E::mfma(kA[d], sB, dq[0][d]);
+          }
+          if (live1) {
+            const x8 sB = tr(ss + rows * 64, s_lo[1], s_hi[1]);
+#pragma unroll
+            for (int d = 0; d < DW; ++d) dq[1][d] = E::mfma(kA[d], sB, dq[1][d]);
+          }
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);           // this wave's reads of sbuf and kbuf[S] are done
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);           // this wave's reads of sbuf and stage S are done
     __builtin_amdgcn_s_barrier();
     load_k(t + DQA, kst(S_));
   };
@@ -1043,16 +1074,20 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dq_ds_kernel(BwdArgs g, int n_qt, 
   }
   __builtin_amdgcn_s_waitcnt(0);                      // the loads past the last tile
 
-  if (i_me >= a.Lq) return;
-  const int64_t qr = b * g.dq_sb + (int64_t)i_me * g.dq_ss + h * g.dq_sh;
 #pragma unroll
-  for (int d = 0; d < DB; ++d)
+  for (int j = 0; j < 2; ++j) {
+    const int i_me = q0 + 64 * wq + 32 * j + ql;
+    if (i_me >= a.Lq) continue;
+    const int64_t qr = b * g.dq_sb + (int64_t)i_me * g.dq_ss + h * g.dq_sh;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int col = 32 * d + 8 * i + 4 * hh;
-      store4(g.dq, qr + col, g.dq_dtype, dq[d][4 * i] * a.scale, dq[d][4 * i + 1] * a.scale,
-             dq[d][4 * i + 2] * a.scale, dq[d][4 * i + 3] * a.scale);
-    }
+    for (int d = 0; d < DW; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = 32 * (DW * wd + d) + 8 * i + 4 * hh;
+        store4(g.dq, qr + col, g.dq_dtype, dq[j][d][4 * i] * a.scale, dq[j][d][4 * i + 1] * a.scale,
+               dq[j][d][4 * i + 2] * a.scale, dq[j][d][4 * i + 3] * a.scale);
+      }
+  }
 }
 
 bool al(const void* p, int n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
