@@ -942,16 +942,10 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dq_ds_kernel(BwdArgs g, int n_qt, 
   }
 
   // the dK/dV pass wrote dS tile (query tile qt64, key block kb) iff the block starts before
-  // kv_lengths and qt64 lies between the first query tile that sees the block and the last one
-  // before q_lengths
+  // kv_lengths (kb * RB < nkv), qt64 lies before q_lengths (qt64 < n_qt64), and qt64 is not
+  // below the first query tile that sees the block: with i_lo = max(0, kb * RB - off) (causal,
+  // else 0), i_lo < nq and qt64 >= i_lo / QT
   const int n_qt64 = (nq + QT - 1) / QT, ds_nqt = (a.Lq + QT - 1) / QT, ds_nkb = (a.Lkv + RB - 1) / RB;
-  auto written = [&](int qt64, int kb) -> bool {
-    const int k0 = kb * RB;
-    if (k0 >= nkv || qt64 >= n_qt64) return false;
-    int64_t i_lo = causal ? (int64_t)k0 - off : 0;
-    i_lo = i_lo < 0 ? 0 : i_lo;
-    return i_lo < nq && qt64 >= (int)(i_lo / QT);
-  };
 
   TK tk;
   tk.init((int)(a.k_ss * 2), lane, tid);
@@ -987,15 +981,31 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dq_ds_kernel(BwdArgs g, int n_qt, 
   // c = 4 * ((wave >> 1) & 1) + 2 * hh + (wave & 1); it writes them to that row's swizzled chunk
   const int s_row = 32 * (wave >> 2) + ql;
   const int s_lds = s_row * 64 + (((4 * ((wave >> 1) & 1) + 2 * hh + (wave & 1)) ^ bswz<64>(s_row)) << 3);
-  auto load_ds = [&](int t, uint4 (&r)[NP]) {
-    const int kb = t >> 1;
-    const bool in = t < n_tiles;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const uint16_t* src = dsp + ((int64_t)p * ds_nkb + kb) * (RB * QT) + (t & 1) * PIECE;
-      const bool w = in && written(NP * qt + p, kb);
-      r[p] = buf_load16(make_rsrc(w ? src : g.w_ds, w ? PIECE * 2 : 0), 16 * tid);
+  // Tile t of piece p is the PIECE at dsp + (p * ds_nkb + t / 2) * RB * QT + (t % 2) * PIECE,
+  // i.e. at t * PIECE from the piece's first tile. The test above holds exactly for kb below
+  // kb_lim(qt64) (the same test solved for kb), so each piece is read through one buffer range
+  // that ends after its last written tile and before n_tiles: every other load returns zeros,
+  // with no per-tile address or range arithmetic.
+  auto kb_lim = [&](int qt64) -> int64_t {
+    if (qt64 >= n_qt64 || nkv <= 0) return 0;
+    int64_t lim = ((int64_t)nkv + RB - 1) / RB;
+    if (causal) {
+      const int64_t e = off + min((int64_t)nq, (int64_t)(qt64 + 1) * QT);
+      const int64_t c = e > 0 ? (e + RB - 1) / RB : 0;
+      lim = c < lim ? c : lim;
     }
+    return lim;
+  };
+  __amdgpu_buffer_rsrc_t rds[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int64_t nt = min(2 * kb_lim(NP * qt + p), (int64_t)n_tiles);
+    rds[p] = make_rsrc(dsp + (int64_t)p * ds_nkb * (RB * QT), nt * (PIECE * 2));
+  }
+  auto load_ds = [&](int t, uint4 (&r)[NP]) {
+    const int vo = 16 * tid + t * (PIECE * 2);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) r[p] = buf_load16(rds[p], vo);
   };
   auto load_k = [&](int t, uint16_t* kd) { tk.load(kp, a.k_ss, t * ST, t < n_tiles ? nkv : t * ST, (int)(a.k_ss * 2), kd, wave); };
   auto put_ds = [&](const uint4 (&r)[NP]) {
@@ -1033,29 +1043,31 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dq_ds_kernel(BwdArgs g, int n_qt, 
     __builtin_amdgcn_s_barrier();
     const uint16_t* ks = kst(S_);
     const uint16_t* ss = sbuf + wq * PIECE;
+    // The tile's four (key block kb, 8-row step) sections in one branch-free chain, each
+    // section's fragments read while the previous section's products run. The dK/dV wave of 32
+    // keys and a 32-query block formed (and stored) its dS block iff the keys start before the
+    // end of the keys the block sees; a block it skipped holds stale bytes in LDS, so its
+    // operand is replaced by zeros (products of exact zeros, on edge tiles only).
+    const int tk0 = t * ST;
+    if (tk0 < k_end_b[0] || tk0 < k_end_b[1]) {
+      x8 kA[2][DW], sB[2][2];
+      auto rd = [&](int sc, int buf) {
+        const int rows = 32 * (sc >> 1) + 8 * (sc & 1);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // the dK/dV wave of these 32 keys and a 32-query block formed (and stored) its dS block
-      // iff its keys start before the end of the keys the block sees
-      const int wk0 = t * ST + 32 * kb;
-      const bool live0 = wk0 < k_end_b[0], live1 = wk0 < k_end_b[1];
-      if (live0 || live1) {
+        for (int d = 0; d < DW; ++d) kA[buf][d] = tr(ks + rows * D, k_lo[d], k_hi[d]);
 #pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          const int rows = (32 * kb + 8 * sh);
-          x8 kA[DW];
+        for (int j = 0; j < 2; ++j) sB[buf][j] = tr(ss + rows * 64, s_lo[j], s_hi[j]);
+      };
+      rd(0, 0);
 #pragma unroll
-          for (int d = 0; d < DW; ++d) kA[d] = tr(ks + rows * D, k_lo[d], k_hi[d]);
-          if (live0) {
-            const x8 sB = tr(ss + rows * 64, s_lo[0], s_hi[0]);
+      for (int sc = 0; sc < 4; ++sc) {
+        if (sc + 1 < 4) rd(sc + 1, (sc + 1) & 1);
 #pragma unroll
-            for (int d = 0; d < DW; ++d) dq[0][d] = E::mfma(kA[d], sB, dq[0][d]);
-          }
-          if (live1) {
-            const x8 sB = tr(ss + rows * 64, s_lo[1], s_hi[1]);
+        for (int j = 0; j < 2; ++j) {
+          const bool live = tk0 + 32 * (sc >> 1) < k_end_b[j];
+          const x8 bj = live ? sB[sc & 1][j] : x8{};
 #pragma unroll
-            for (int d = 0; d < DW; ++d) dq[1][d] = E::mfma(kA[d], sB, dq[1][d]);
-          }
+          for (int d = 0; d < DW; ++d) dq[j][d] = E::mfma(kA[sc & 1][d], bj, dq[j][d]);
         }
       }
     }

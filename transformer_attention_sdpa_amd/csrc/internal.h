@@ -132,6 +132,8 @@ inline int64_t bwd_ds_tile_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t Lkv,
   if ((dtype != SDPA_BF16 && dtype != SDPA_F16) || D != Dv || (D != 64 && D != 128) || B <= 0 || Hq <= 0 ||
       Lq <= 0 || Lkv <= 0)
     return 0;
+  // the dQ pass reads a query tile's row of dS tiles with 32-bit offsets (at most 65536 tiles)
+  if ((Lkv + 127) / 128 > 65536) return 0;
   const int64_t n = B * Hq * ((Lq + 63) / 64) * ((Lkv + 127) / 128) * (64 * 128 * 2);
   return n <= kDsCapBytes ? n : 0;
 }
