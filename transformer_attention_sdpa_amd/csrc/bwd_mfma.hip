@@ -246,6 +246,25 @@ constexpr int QT8 = 64;
 template <int D>
 __device__ __forceinline__ int kvswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
 
+// Quotient by a workgroup-invariant divisor 1 <= d < 2^31 for dividends below 2^31, by one
+// multiply-high: the round-up method of Granlund and Montgomery ("Division by invariant integers
+// using multiplication", 1994), with l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1 and
+// q = (t + ((n - t) >> 1)) >> (l - 1), t = mulhi(m, n); d = 1 is n itself.
+struct DivU {
+  uint32_t m;
+  int l;
+  __device__ void init(uint32_t d) {
+    l = 0;
+    while ((1u << l) < d) ++l;
+    m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+  }
+  __device__ uint32_t div(uint32_t n) const {
+    if (l == 0) return n;
+    const uint32_t t = __umulhi(m, n);
+    return (t + ((n - t) >> 1)) >> (l - 1);
+  }
+};
+
 template <int D, bool F16, int MK, bool DS>
 __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap) {
   using E = In<F16>;
@@ -309,8 +328,12 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
   Tiles<D, F16, QT8, NT8> tq, to;
   tq.init((int)(a.q_ss * 2), lane, tid);
   to.init((int)(g.do_ss * 2), lane, tid);
-  auto it_head = [&](int it) { return gk * grp + it / per_head; };
-  auto it_q0 = [&](int it) { return (qt0 + it % per_head) * QT8; };
+  // step it = (head - gk * grp) * per_head + (query tile - qt0); the quotient by one multiply
+  // (a runtime division costs some thirty scalar instructions, several times a step)
+  DivU dph;
+  dph.init(per_head > 0 ? per_head : 1);
+  auto it_head = [&](int it) { return gk * grp + (int)dph.div((uint32_t)it); };
+  auto it_q0 = [&](int it) { return (qt0 + it - (int)dph.div((uint32_t)it) * per_head) * QT8; };
   auto load_tiles = [&](int it, uint16_t* qd, uint16_t* od) {
     const int h = it_head(it), i0 = it_q0(it);
     tq.load(static_cast<const uint16_t*>(a.q) + b * a.q_sb + h * a.q_sh, a.q_ss, i0, a.Lq, (int)(a.q_ss * 2), qd, wave);
