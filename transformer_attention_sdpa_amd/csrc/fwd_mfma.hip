@@ -329,8 +329,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
   // ---- K/V tiles: direct global -> LDS loads --------------------------------------------
   // Instruction u of wave w fills slots 256*u + 64*w + lane of a tile (slot = 16 bytes). K slot
   // (row R, position p) holds chunk p ^ k_swz(R) of key 32*(R/32) + k_row_key(R%32); V slot
-  // (row r, position p) holds chunk p ^ v_swz(r) of key r. Each tile gets fresh buffer resources
-  // whose range ends at kv_len, so keys past kv_lengths arrive as zeros (never a poisoned tail).
+  // (row r, position p) holds chunk p ^ v_swz(r) of key r. One buffer resource per operand spans
+  // the keys below kv_len, so keys past kv_lengths arrive as zeros (never a poisoned tail); a
+  // tile's first key enters the per-lane offset (the host keeps (Lkv + BN) rows of either
+  // operand within 32-bit offsets), so a tile costs no address or range arithmetic.
   int kdoff[SPT], vdoff[SPT];
 #pragma unroll
   for (int u = 0; u < SPT; ++u) {
@@ -338,15 +340,17 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     kdoff[u] = ((row & ~31) + k_row_key(row & 31)) * k_row_bytes + (pos ^ k_swz<D>(row)) * 16;
     vdoff[u] = row * v_row_bytes + (pos ^ v_swz<D>(row)) * 16;
   }
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, (int64_t)nkv * k_row_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, (int64_t)nkv * v_row_bytes);
   auto dma_k = [&](int k0, uint16_t* dst) {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (int64_t)k0 * a.k_ss, (int64_t)(nkv - k0) * k_row_bytes);
+    const int ko = k0 * k_row_bytes;
 #pragma unroll
-    for (int u = 0; u < SPT; ++u) dma16(rk, dst + 8 * (NT * u + 64 * wave), kdoff[u]);
+    for (int u = 0; u < SPT; ++u) dma16(rk, dst + 8 * (NT * u + 64 * wave), kdoff[u] + ko);
   };
   auto dma_v = [&](int k0, uint16_t* dst) {
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (int64_t)k0 * a.v_ss, (int64_t)(nkv - k0) * v_row_bytes);
+    const int vo = k0 * v_row_bytes;
 #pragma unroll
-    for (int u = 0; u < SPT; ++u) dma16(rv, dst + 8 * (NT * u + 64 * wave), vdoff[u]);
+    for (int u = 0; u < SPT; ++u) dma16(rv, dst + 8 * (NT * u + 64 * wave), vdoff[u] + vo);
   };
   // key factors 1/rms of the keys of a tile (QK-norm only): one per thread below BN
   float krv = 0.f;
@@ -438,15 +442,20 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       bdoff[u] = row * bias_row_bytes + ((pos ^ (row & 7)) << 4);
     }
   }
+  // one buffer resource over the workgroup's bias rows (the host keeps them within 32-bit
+  // offsets); a tile's first key enters the per-lane offset
   const int rows_valid = min(BM, a.Lq - q0);
+  const __amdgpu_buffer_rsrc_t rbias = [&]() {
+    if constexpr (FBIAS)
+      return make_rsrc(static_cast<const uint16_t*>(a.bias) + b * a.bias_sb + h * a.bias_sh + (int64_t)q0 * a.bias_sq,
+                       (int64_t)(rows_valid - 1) * bias_row_bytes + (int64_t)a.Lkv * 2);
+    else
+      return make_rsrc(nullptr, 0);
+  }();
   auto dma_bias = [&](int k0t, uint16_t* dst) {
     if constexpr (FBIAS) {
-      const uint16_t* base = static_cast<const uint16_t*>(a.bias) + b * a.bias_sb + h * a.bias_sh +
-                             (int64_t)q0 * a.bias_sq + k0t;
-      const __amdgpu_buffer_rsrc_t rb =
-          make_rsrc(base, (int64_t)(rows_valid - 1) * bias_row_bytes + (int64_t)(a.Lkv - k0t) * 2);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) dma16(rb, dst + 8 * (256 * wave + 64 * u), bdoff[u]);
+      for (int u = 0; u < 4; ++u) dma16(rbias, dst + 8 * (256 * wave + 64 * u), bdoff[u] + 2 * k0t);
     }
   };
   // the lane's bias of a tile from LDS: query i_me, keys 32*kb + 16*hh + 0..15 (two chunks)
@@ -1038,8 +1047,9 @@ bool fwd_mfma_supports(const AttnArgs& a) {
   if (!(a.scale > 0.f)) return false;
   // buffer loads: rows at least head_dim long, 32-bit byte ranges per (batch, head) slice
   if (a.q_ss < a.D || a.k_ss < a.D || a.v_ss < a.D) return false;
-  if ((int64_t)a.Lq * a.q_ss * 2 > INT32_MAX || (int64_t)a.Lkv * a.k_ss * 2 > INT32_MAX ||
-      (int64_t)a.Lkv * a.v_ss * 2 > INT32_MAX)
+  // (K and V: a tile's row offset is added to offsets within the tile, up to Lkv + BN rows)
+  if ((int64_t)a.Lq * a.q_ss * 2 > INT32_MAX || ((int64_t)a.Lkv + BN) * a.k_ss * 2 > INT32_MAX ||
+      ((int64_t)a.Lkv + BN) * a.v_ss * 2 > INT32_MAX)
     return false;
   if (a.q_seg && (a.bias || a.mask || a.bm_class)) return false;
   const int64_t nwg = (a.q_seg ? packed_tiles_bound(a, BM) : (int64_t)((a.Lq + BM - 1) / BM) * a.B) * a.Hq;
