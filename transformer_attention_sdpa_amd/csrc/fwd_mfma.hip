@@ -670,22 +670,18 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
             }
           }
           if (edge) {
-            const int64_t lim = causal ? off + i_me : (int64_t)INT32_MAX;
+            // the keys this row may see are those below min(kv_len, its causal limit + 1): a
+            // prefix of the 16 keys from jb
+            const int64_t lim = causal ? off + i_me + 1 : (int64_t)nkv;
+            const int64_t nk = (lim < nkv ? lim : (int64_t)nkv) - jb;
+            bits &= nk >= 16 ? 0xffffu : (nk <= 0 ? 0u : (1u << nk) - 1u);
+          }
+          // bit e sign-extended is all ones (keep the score) or zero (take -inf): one bit select
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int j = jb + e;
-              const bool ok = (j < nkv) && ((int64_t)j <= lim) && ((bits >> e) & 1u);
-              s_cur[kb][e] = ok ? s_cur[kb][e] : -INFINITY;
-            }
-          } else {
-            // inside kv_lengths and the causal limit: only the mask bit decides. Bit e
-            // sign-extended is all ones (keep the score) or zero (take -inf), one bit select
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const uint32_t keep = (uint32_t)((int32_t)(bits << (31 - e)) >> 31);
-              const uint32_t x = __float_as_uint(s_cur[kb][e]);
-              s_cur[kb][e] = __uint_as_float((x & keep) | (0xff800000u & ~keep));
-            }
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t keep = (uint32_t)((int32_t)(bits << (31 - e)) >> 31);
+            const uint32_t x = __float_as_uint(s_cur[kb][e]);
+            s_cur[kb][e] = __uint_as_float((x & keep) | (0xff800000u & ~keep));
           }
         }
       }
