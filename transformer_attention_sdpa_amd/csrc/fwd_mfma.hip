@@ -300,8 +300,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
         uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float lo = E::lo(w[t]) * c_lane, hi = E::hi(w[t]) * c_lane;
-          w[t] = (uint32_t)E::bits(lo) | ((uint32_t)E::bits(hi) << 16);
+          w[t] = E::pack(E::lo(w[t]) * c_lane, E::hi(w[t]) * c_lane);
         }
         x = make_uint4(w[0], w[1], w[2], w[3]);
       }
@@ -951,18 +950,17 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
     for (int i = 0; i < 4; ++i) {
       const int dcol = 32 * d + 8 * i + 4 * hh;
       float r[4];
+      // inv is NaN for a row without keys, so the product is too
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r[j] = zero_row ? 0.f : (l_tot > 0.f ? o[d][4 * i + j] * inv : NAN);
+      for (int j = 0; j < 4; ++j) r[j] = zero_row ? 0.f : o[d][4 * i + j] * inv;
       if (a.out_dtype == SDPA_F32) {
         *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow + dcol) = make_float4(r[0], r[1], r[2], r[3]);
       } else if (a.out_dtype == SDPA_F16) {
-        const uint32_t w0 = (uint32_t)float_to_f16_bits(r[0]) | ((uint32_t)float_to_f16_bits(r[1]) << 16);
-        const uint32_t w1 = (uint32_t)float_to_f16_bits(r[2]) | ((uint32_t)float_to_f16_bits(r[3]) << 16);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow + dcol) = make_uint2(w0, w1);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow + dcol) =
+            make_uint2(In<true>::pack(r[0], r[1]), In<true>::pack(r[2], r[3]));
       } else {
-        const uint32_t w0 = (uint32_t)float_to_bf16_bits(r[0]) | ((uint32_t)float_to_bf16_bits(r[1]) << 16);
-        const uint32_t w1 = (uint32_t)float_to_bf16_bits(r[2]) | ((uint32_t)float_to_bf16_bits(r[3]) << 16);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow + dcol) = make_uint2(w0, w1);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow + dcol) =
+            make_uint2(In<false>::pack(r[0], r[1]), In<false>::pack(r[2], r[3]));
       }
     }
 }
