@@ -813,24 +813,34 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(AttnArgs args, int n_qt
       // LDS fragments are read PF chunks ahead of the MFMA that consumes them
       constexpr int PF = 2;
       bf16x8 kf[PF + 1][2];
+#pragma unroll
+      for (int c = 0; c < PF; ++c) {
+        kf[c][0] = kfrag(c, 0);
+        kf[c][1] = kfrag(c, 1);
+      }
       // the C operand that starts S(t+1): zero, -m_run broadcast (FUSED), or the bias (FBIAS:
-      // one start vector per 32-key block, the bias of tile t + 1). Built here from an opaque
-      // copy of m_run, so that its 16 registers live only until the first two MFMAs.
+      // one start vector per 32-key block, the bias of tile t + 1). Built here, after the first
+      // fragment reads are under way, from an opaque copy of m_run, so that its 16 registers
+      // live only until the first two MFMAs.
       f32x16 c0[FBIAS ? 2 : 1];
       {
         float m0 = m_run;
         if constexpr (FUSED) asm volatile("" : "+v"(m0));
         if constexpr (FBIAS) {
           s_start(bx, m0, c0);
+        } else if constexpr (FUSED) {
+          // -m broadcast as eight 64-bit pairs (64-bit moves: half the instructions)
+          const uint32_t nm = __float_as_uint(-m0);
+          const uint64_t pr = ((uint64_t)nm << 32) | nm;
+          uint64_t cu[8];
+          cu[0] = pr;
+#pragma unroll
+          for (int e = 1; e < 8; ++e) asm volatile("v_mov_b64 %0, %1" : "=v"(cu[e]) : "v"(pr));
+          c0[0] = __builtin_bit_cast(f32x16, cu);
         } else {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) c0[0][e] = FUSED ? -m0 : 0.f;
+          for (int e = 0; e < 16; ++e) c0[0][e] = 0.f;
         }
-      }
-#pragma unroll
-      for (int c = 0; c < PF; ++c) {
-        kf[c][0] = kfrag(c, 0);
-        kf[c][1] = kfrag(c, 1);
       }
       bf16x8 vf[PF + 1];
 #pragma unroll
