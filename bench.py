@@ -376,6 +376,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": counters_traffic(PREFILL_COUNTERS),
                      "kernel": "fwd_mfma_kernel<128,0,0>", "flops_per_launch": flops,
+                     "path": sa.sdpa_fwd_path(q, k, v, is_causal=True, scale=w.scale),
                      "measured_peak": peaks["mfma_bf16_tflops"] if peaks else None,
                      "frac_of_measured": frac_measured(tflops, "mfma_bf16_tflops")},
         "timing": TIMINGS["prefill"],
@@ -409,6 +410,8 @@ def main():
                        "is_causal": True, "grad_dtype": "bf16", "saved_out_dtype": "bf16"},
             "roofline": {"bound": "mfma", "achieved": round(tf_b, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "traffic": counters_traffic(BACKWARD_COUNTERS),
+                         "path": sa.sdpa_bwd_path(q, k, v, outb, dout, is_causal=True, scale=w.scale,
+                                                  workspace_bytes=bws.numel()),
                          "flops_per_call": flops_b, "frac_of_measured": frac_measured(tf_b, "mfma_bf16_tflops"),
                          "kernel": "bwd_prep + bwd_dkdv8_kernel<128> (stores dS) + bwd_dq_ds_kernel<128> + bwd_dscale"},
             "parity": backward_parity(w, q, k, v, outb, dout, lse, grads),

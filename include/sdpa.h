@@ -187,9 +187,36 @@ SDPA_API size_t sdpa_bwd_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor
 
 /* Bytes of workspace with which sdpa_bwd stores dS for its dQ pass: the bytes above plus
  * B*Hq*ceil(Lq/64)*ceil(Lkv/128)*16 KiB of dS tiles and the dK/dV workgroups' dscale shares.
- * 0 where that route does not apply (inputs other than bf16/f16, D != Dv, D not 64 or 128) or
- * the dS tiles would exceed 8 GiB. Host only. */
+ * 0 where that route does not apply (inputs other than bf16/f16, D != Dv, D not 64 or 128),
+ * Lkv is above 8M keys, or the dS tiles would exceed 8 GiB. Host only. */
 SDPA_API size_t sdpa_bwd_workspace_bytes_ds(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v);
+
+/* ---------------------------------------------------------------------------------------
+ * sdpa_fwd_path / sdpa_bwd_path -- which kernels sdpa_fwd (sdpa_fwd_lse) or sdpa_bwd would run
+ * for these arguments. Nothing is launched and no device memory is read; the descriptors'
+ * data pointers count only for their alignment. The arguments mean what they mean for
+ * sdpa_fwd and sdpa_bwd (q_offset, kv_lengths and q_lengths do not change the choice);
+ * workspace_bytes is the size the gradient call would be given. On success *path is:
+ *   SDPA_PATH_MATRIX_CORE           the bf16/f16 matrix-core kernels;
+ *   SDPA_PATH_MATRIX_CORE_STORED_DS the gradient's matrix-core kernels with dS kept in the
+ *                                   workspace for the dQ pass (sdpa_bwd_workspace_bytes_ds());
+ *   SDPA_PATH_FP32                  the fp32 vector kernels, which take every other accepted
+ *                                   call (fp32 inputs, head dims other than 64/128, D != Dv, an
+ *                                   f16 bias, scale <= 0, unaligned or oddly strided views,
+ *                                   per-(batch, head) slices beyond 32-bit offsets) and are many
+ *                                   times slower.
+ * Errors are those the call itself would return for invalid arguments; *path is then unset.
+ * Host only. */
+typedef enum { SDPA_PATH_MATRIX_CORE = 1, SDPA_PATH_FP32 = 2, SDPA_PATH_MATRIX_CORE_STORED_DS = 3 } sdpa_path;
+SDPA_API sdpa_status sdpa_fwd_path(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
+                                   const sdpa_tensor* bias, const sdpa_tensor* mask,
+                                   const sdpa_block_mask_info* mask_info, float scale, int32_t is_causal,
+                                   int32_t qk_norm, const sdpa_tensor* out, int32_t* path);
+SDPA_API sdpa_status sdpa_bwd_path(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
+                                   const sdpa_tensor* out, const sdpa_tensor* dout, const sdpa_tensor* mask,
+                                   const sdpa_block_mask_info* mask_info, float scale, int32_t is_causal,
+                                   const sdpa_tensor* dq, const sdpa_tensor* dk, const sdpa_tensor* dv,
+                                   size_t workspace_bytes, int32_t* path);
 
 /* ---------------------------------------------------------------------------------------
  * sdpa_fwd_packed -- attention over packed sequences (page "Neural Network primitives from

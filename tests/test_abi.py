@@ -298,3 +298,55 @@ def test_decode_noalloc_refuses_more_than_its_scratch(lib):
     assert st == N.SDPA_ERR_WORKSPACE
     assert "device scratch holds" in lib.sdpa_last_error().decode()
     assert sa.decode_workspace_bytes(q, kc, 0) > sa.decode_noalloc_max_scratch_bytes()
+
+
+def fwd_path(lib, q, k, v, out, bias=None, scale=math.nan, causal=0, qk_norm=0):
+    p = ctypes.c_int32(0)
+    r = lib.sdpa_fwd_path(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(bias) if bias else None,
+                          None, None, scale, causal, qk_norm, ctypes.byref(out), ctypes.byref(p))
+    return r, p.value
+
+
+def test_fwd_path_names_the_kernel_family(lib):
+    # bf16 at D = 128 with aligned contiguous views: matrix cores; each thing the matrix-core
+    # kernels decline moves the call to the fp32 kernels (nothing is launched)
+    B, L, H, D = 2, 256, 4, 128
+    q, k, v, o = (T([D, H, L, B]) for _ in range(4))
+    assert fwd_path(lib, q, k, v, o) == (N.SDPA_OK, N.PATH_MATRIX_CORE)
+    assert fwd_path(lib, q, k, v, o, causal=N.CAUSAL_TRUE) == (N.SDPA_OK, N.PATH_MATRIX_CORE)
+    f32 = [T([D, H, L, B], N.SDPA_F32) for _ in range(4)]
+    assert fwd_path(lib, *f32) == (N.SDPA_OK, N.PATH_FP32)
+    q96, k96, v96, o96 = (T([96, H, L, B]) for _ in range(4))
+    assert fwd_path(lib, q96, k96, v96, o96) == (N.SDPA_OK, N.PATH_FP32)
+    assert fwd_path(lib, q, k, v, o, scale=-0.1) == (N.SDPA_OK, N.PATH_FP32)
+    qmis = T([D, H, L, B], data=FAKE + 8)          # not 16-byte aligned
+    assert fwd_path(lib, qmis, k, v, o) == (N.SDPA_OK, N.PATH_FP32)
+    b16 = T([L, L, H, 1], N.SDPA_F16, strides=[1, L, L * L, 0])
+    assert fwd_path(lib, q, k, v, o, bias=b16) == (N.SDPA_OK, N.PATH_FP32)
+    bbf = T([L, L, H, 1], N.SDPA_BF16, strides=[1, L, L * L, 0])
+    assert fwd_path(lib, q, k, v, o, bias=bbf) == (N.SDPA_OK, N.PATH_MATRIX_CORE)
+    # invalid arguments: the call's own status
+    kbad = T([D, H, L + 1, B + 1])
+    assert fwd_path(lib, q, kbad, v, o)[0] == N.SDPA_ERR_SHAPE
+
+
+def test_bwd_path_names_the_route(lib):
+    B, L, H, D = 2, 256, 4, 128
+    q, k, v, o, do, dq, dk, dv = (T([D, H, L, B]) for _ in range(8))
+    need = lib.sdpa_bwd_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v))
+    need_ds = lib.sdpa_bwd_workspace_bytes_ds(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v))
+    assert need_ds > need > 0
+
+    def path(ws, *t, scale=math.nan):
+        p = ctypes.c_int32(0)
+        r = lib.sdpa_bwd_path(*(ctypes.byref(x) for x in t[:5]), None, None, scale, N.CAUSAL_TRUE,
+                              *(ctypes.byref(x) for x in t[5:]), ws, ctypes.byref(p))
+        return r, p.value
+
+    assert path(need_ds, q, k, v, o, do, dq, dk, dv) == (N.SDPA_OK, N.PATH_MATRIX_CORE_STORED_DS)
+    assert path(need, q, k, v, o, do, dq, dk, dv) == (N.SDPA_OK, N.PATH_MATRIX_CORE)
+    f32 = [T([D, H, L, B], N.SDPA_F32) for _ in range(8)]
+    assert path(need_ds, *f32) == (N.SDPA_OK, N.PATH_FP32)
+    assert path(need_ds, q, k, v, o, do, dq, dk, dv, scale=-1.0) == (N.SDPA_OK, N.PATH_FP32)
+    dq_bad = T([D, H, L + 1, B])
+    assert path(need_ds, q, k, v, o, do, dq_bad, dk, dv)[0] == N.SDPA_ERR_SHAPE

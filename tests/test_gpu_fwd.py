@@ -348,3 +348,22 @@ def test_rising_bias_moves_the_running_max(lib, slope, D, bias_dtype, info):
     ref = run_oracle(w)
     assert_close(run_gpu(w, use_mask_info=info, bq=128, bkv=64).cpu().numpy(), ref, "bf16",
                  f"rising bias slope {slope}")
+
+
+def test_path_queries_name_the_kernels_that_run(lib):
+    # the benchmark's shapes on the matrix cores (the stored-dS gradient with the default
+    # workspace, the recompute route with the minimum one), fp32 inputs and an odd head dim on
+    # the fp32 kernels; the fp32 call's result still matches the oracle
+    say("path queries")
+    q, k, v = (torch.zeros((2, 256, 4, 128), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    assert sa.sdpa_fwd_path(q, k, v, is_causal=True) == "matrix_core"
+    o = torch.zeros_like(q)
+    assert sa.sdpa_bwd_path(q, k, v, o, o, is_causal=True) == "matrix_core_stored_ds"
+    assert sa.sdpa_bwd_path(q, k, v, o, o, is_causal=True, store_ds=False) == "matrix_core"
+    q96 = torch.zeros((2, 64, 4, 96), dtype=torch.bfloat16, device="cuda")
+    assert sa.sdpa_fwd_path(q96, q96, q96) == "fp32"
+    w = workloads.random_attention(4401, 1, 40, 50, 4, 2, 64, dtype="f32", is_causal=True)
+    t = gpu_inputs(w)
+    qf, kf, vf = t["q"], t["k"], t["v"]
+    assert sa.sdpa_fwd_path(qf, kf, vf, is_causal=True) == "fp32"
+    assert_close(run_gpu(w).cpu().numpy(), run_oracle(w), "f32", "fp32 path")

@@ -18,6 +18,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "sdpa.h")
 SDPA_OK, SDPA_ERR_NULL, SDPA_ERR_SHAPE, SDPA_ERR_DTYPE, SDPA_ERR_UNSUPPORTED, SDPA_ERR_WORKSPACE, SDPA_ERR_HIP = range(7)
 SDPA_F32, SDPA_BF16, SDPA_U8, SDPA_F16, SDPA_U1 = 0, 1, 2, 3, 4
 CAUSAL_NONE, CAUSAL_TRUE, CAUSAL_BOTTOM_RIGHT = 0, 1, 2
+PATH_MATRIX_CORE, PATH_FP32, PATH_MATRIX_CORE_STORED_DS = 1, 2, 3
+PATH_NAMES = {PATH_MATRIX_CORE: "matrix_core", PATH_FP32: "fp32", PATH_MATRIX_CORE_STORED_DS: "matrix_core_stored_ds"}
 
 
 class SdpaTensor(ctypes.Structure):
@@ -60,6 +62,10 @@ PROTOTYPES = {
                        I32P, I32, I32P, I32, I32P, I32, T, T, T, VP, VP, SZ, VP]),
     "sdpa_bwd_workspace_bytes": (SZ, [T, T, T]),
     "sdpa_bwd_workspace_bytes_ds": (SZ, [T, T, T]),
+    "sdpa_fwd_path": (I32, [T, T, T, T, T, ctypes.POINTER(BlockMaskInfoC), ctypes.c_float, I32, I32, T,
+                            ctypes.POINTER(I32)]),
+    "sdpa_bwd_path": (I32, [T, T, T, T, T, T, ctypes.POINTER(BlockMaskInfoC), ctypes.c_float, I32, T, T, T, SZ,
+                            ctypes.POINTER(I32)]),
     "sdpa_fwd_packed": (I32, [T, T, T, I32P, I32P, I32, I32, ctypes.c_float, I32,
                               I32P, I32, I32P, I32, I32P, I32, I32, T, VP, SZ, VP]),
     "sdpa_fwd_workspace_bytes": (SZ, [T, T, T, I32]),

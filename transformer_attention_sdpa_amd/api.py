@@ -329,6 +329,50 @@ def sdpa_packed(q, k, v, q_segments, kv_segments=None, *, maxlen=None, scale=Non
     return out
 
 
+def sdpa_fwd_path(q, k, v, bias=None, mask=None, *, mask_info: BlockMaskInfo = None, scale=None, is_causal=False,
+                  qk_norm=False, out=None, out_dtype=None) -> str:
+    """Which kernels ``sdpa`` would run for these arguments (sdpa_fwd_path; nothing is launched):
+    "matrix_core" (the bf16/f16 matrix-core kernels) or "fp32" (the fp32 vector kernels)."""
+    lib = N.load()
+    B, Lq, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty((B, Lq, Hq, v.shape[-1]), dtype=out_dtype or q.dtype, device=q.device)
+    dq, dk, dv, do = desc(q), desc(k), desc(v), desc(out)
+    db = desc(bias) if bias is not None else None
+    m = _mask_u8(mask) if mask_info is None else None
+    dm = _mask_desc(m) if m is not None else None
+    path = ctypes.c_int32(0)
+    N.check(lib.sdpa_fwd_path(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                              ctypes.byref(db) if db is not None else None, ctypes.byref(dm) if dm is not None else None,
+                              ctypes.byref(mask_info.c) if mask_info is not None else None,
+                              float("nan") if scale is None else float(scale), _CAUSAL[is_causal],
+                              int(bool(qk_norm)), ctypes.byref(do), ctypes.byref(path)))
+    return N.PATH_NAMES[path.value]
+
+
+def sdpa_bwd_path(q, k, v, out, dout, mask=None, *, mask_info: BlockMaskInfo = None, scale=None, is_causal=False,
+                  grad_dtype=None, workspace_bytes=None, store_ds=True) -> str:
+    """Which kernels ``sdpa_bwd`` would run (sdpa_bwd_path; nothing is launched): "matrix_core",
+    "matrix_core_stored_ds" or "fp32". workspace_bytes defaults to what sdpa_bwd allocates
+    itself (bwd_workspace_bytes(q, k, v, store_ds))."""
+    lib = N.load()
+    gd = grad_dtype or q.dtype
+    gq = desc(torch.empty(q.shape, dtype=gd, device=q.device))
+    gk = desc(torch.empty(k.shape, dtype=gd, device=q.device))
+    gv = desc(torch.empty(v.shape, dtype=gd, device=q.device))
+    tq, tk, tv, to, tdo = desc(q), desc(k), desc(v), desc(out), desc(dout)
+    m = _mask_u8(mask) if mask_info is None else None
+    dm = _mask_desc(m) if m is not None else None
+    wb = bwd_workspace_bytes(q, k, v, store_ds) if workspace_bytes is None else int(workspace_bytes)
+    path = ctypes.c_int32(0)
+    N.check(lib.sdpa_bwd_path(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(to), ctypes.byref(tdo),
+                              ctypes.byref(dm) if dm is not None else None,
+                              ctypes.byref(mask_info.c) if mask_info is not None else None,
+                              float("nan") if scale is None else float(scale), _CAUSAL[is_causal],
+                              ctypes.byref(gq), ctypes.byref(gk), ctypes.byref(gv), wb, ctypes.byref(path)))
+    return N.PATH_NAMES[path.value]
+
+
 def bwd_workspace_bytes(q, k, v, store_ds=False) -> int:
     """Bytes of workspace sdpa_bwd needs for these tensors; with store_ds, the bytes with which
     it stores dS for its dQ pass where that route applies (else the same minimum)."""

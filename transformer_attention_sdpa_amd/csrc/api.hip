@@ -349,22 +349,19 @@ size_t sdpa_bwd_workspace_bytes_ds(const sdpa_tensor* q, const sdpa_tensor* k, c
          ((chunks * sizeof(double) + 255) & ~(size_t)255) + (size_t)tiles;
 }
 
-sdpa_status sdpa_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v, const sdpa_tensor* out,
-                     const sdpa_tensor* dout, const float* lse, const sdpa_tensor* mask,
-                     const sdpa_block_mask_info* mask_info, float scale, int32_t is_causal,
-                     const int32_t* q_offset, int32_t q_offset_all, const int32_t* kv_lengths,
-                     int32_t kv_length_all, const int32_t* q_lengths, int32_t q_length_all, sdpa_tensor* dq,
-                     sdpa_tensor* dk, sdpa_tensor* dv, float* dscale, void* workspace, size_t workspace_bytes,
-                     void* stream) {
-  g_err.clear();
+// The gradient's arguments (everything but lse, dscale and the workspace) into g, validated.
+static sdpa_status resolve_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
+                               const sdpa_tensor* out, const sdpa_tensor* dout, const sdpa_tensor* mask,
+                               const sdpa_block_mask_info* mask_info, float scale, int32_t is_causal,
+                               const int32_t* q_offset, int32_t q_offset_all, const int32_t* kv_lengths,
+                               int32_t kv_length_all, const int32_t* q_lengths, int32_t q_length_all,
+                               const sdpa_tensor* dq, const sdpa_tensor* dk, const sdpa_tensor* dv, BwdArgs& g) {
   if (!v || !out || !dout || !dq || !dk || !dv)
     return fail(SDPA_ERR_NULL, "v, out, dout, dq, dk and dv descriptors are required");
-  BwdArgs g;
   std::memset(&g, 0, sizeof g);
   sdpa_status st = resolve_attention(q, k, v, nullptr, mask, mask_info, scale, is_causal, q_offset, q_offset_all,
                                      kv_lengths, kv_length_all, q_lengths, q_length_all, 0, out, g.a);
   if (st != SDPA_OK) return st;
-  const AttnArgs& a = g.a;
   auto same = [](const sdpa_tensor* x, const sdpa_tensor* y) {
     for (int i = 0; i < 4; ++i)
       if (x->dims[i] != y->dims[i]) return false;
@@ -377,6 +374,28 @@ sdpa_status sdpa_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tens
     return fail(SDPA_ERR_DTYPE, "dout, dq, dk and dv must be F32, BF16 or F16");
   if (dout->strides[0] != 1 || dq->strides[0] != 1 || dk->strides[0] != 1 || dv->strides[0] != 1)
     return fail(SDPA_ERR_SHAPE, "dout, dq, dk and dv need head_dim stride 1");
+  g.dout = dout->data; g.do_sb = dout->strides[3]; g.do_ss = dout->strides[2]; g.do_sh = dout->strides[1];
+  g.do_dtype = dout->dtype;
+  g.dq = dq->data; g.dq_sb = dq->strides[3]; g.dq_ss = dq->strides[2]; g.dq_sh = dq->strides[1];
+  g.dk = dk->data; g.dk_sb = dk->strides[3]; g.dk_ss = dk->strides[2]; g.dk_sh = dk->strides[1];
+  g.dv = dv->data; g.dv_sb = dv->strides[3]; g.dv_ss = dv->strides[2]; g.dv_sh = dv->strides[1];
+  g.dq_dtype = dq->dtype; g.dk_dtype = dk->dtype; g.dv_dtype = dv->dtype;
+  return SDPA_OK;
+}
+
+sdpa_status sdpa_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v, const sdpa_tensor* out,
+                     const sdpa_tensor* dout, const float* lse, const sdpa_tensor* mask,
+                     const sdpa_block_mask_info* mask_info, float scale, int32_t is_causal,
+                     const int32_t* q_offset, int32_t q_offset_all, const int32_t* kv_lengths,
+                     int32_t kv_length_all, const int32_t* q_lengths, int32_t q_length_all, sdpa_tensor* dq,
+                     sdpa_tensor* dk, sdpa_tensor* dv, float* dscale, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  g_err.clear();
+  BwdArgs g;
+  sdpa_status st = resolve_bwd(q, k, v, out, dout, mask, mask_info, scale, is_causal, q_offset, q_offset_all,
+                               kv_lengths, kv_length_all, q_lengths, q_length_all, dq, dk, dv, g);
+  if (st != SDPA_OK) return st;
+  const AttnArgs& a = g.a;
   const size_t need = sdpa_bwd_workspace_bytes(q, k, v);
   if (workspace_bytes < need || (need && !workspace))
     return fail(SDPA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
@@ -385,13 +404,7 @@ sdpa_status sdpa_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tens
   if ((rows > 0 && (!a.q || !a.out || !dout->data || !dq->data)) ||
       ((int64_t)a.B * a.Lkv > 0 && (!a.k || !a.v || !dk->data || !dv->data)))
     return fail(SDPA_ERR_NULL, "a tensor's data is NULL");
-  g.dout = dout->data; g.do_sb = dout->strides[3]; g.do_ss = dout->strides[2]; g.do_sh = dout->strides[1];
-  g.do_dtype = dout->dtype;
   g.lse = lse;
-  g.dq = dq->data; g.dq_sb = dq->strides[3]; g.dq_ss = dq->strides[2]; g.dq_sh = dq->strides[1];
-  g.dk = dk->data; g.dk_sb = dk->strides[3]; g.dk_ss = dk->strides[2]; g.dk_sh = dk->strides[1];
-  g.dv = dv->data; g.dv_sb = dv->strides[3]; g.dv_ss = dv->strides[2]; g.dv_sh = dv->strides[1];
-  g.dq_dtype = dq->dtype; g.dk_dtype = dk->dtype; g.dv_dtype = dv->dtype;
   g.dscale = dscale;
   const size_t seg = ((size_t)rows * sizeof(float) + 255) & ~(size_t)255;
   g.w_dsum = static_cast<float*>(workspace);
@@ -409,6 +422,42 @@ sdpa_status sdpa_bwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tens
     g.w_ds = reinterpret_cast<uint16_t*>(x);
   }
   return hip_status(launch_bwd(g, static_cast<hipStream_t>(stream)), "sdpa_bwd");
+}
+
+sdpa_status sdpa_fwd_path(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v, const sdpa_tensor* bias,
+                          const sdpa_tensor* mask, const sdpa_block_mask_info* mask_info, float scale,
+                          int32_t is_causal, int32_t qk_norm, const sdpa_tensor* out, int32_t* path) {
+  g_err.clear();
+  if (!path) return fail(SDPA_ERR_NULL, "path is required");
+  if (!v || !out) return fail(SDPA_ERR_NULL, "v and out descriptors are required");
+  AttnArgs a;
+  const sdpa_status st = resolve_attention(q, k, v, bias, mask, mask_info, scale, is_causal, nullptr, 0, nullptr, -1,
+                                           nullptr, -1, qk_norm, out, a);
+  if (st != SDPA_OK) return st;
+  *path = fwd_mfma_supports(a) ? SDPA_PATH_MATRIX_CORE : SDPA_PATH_FP32;
+  return SDPA_OK;
+}
+
+sdpa_status sdpa_bwd_path(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v, const sdpa_tensor* out,
+                          const sdpa_tensor* dout, const sdpa_tensor* mask, const sdpa_block_mask_info* mask_info,
+                          float scale, int32_t is_causal, const sdpa_tensor* dq, const sdpa_tensor* dk,
+                          const sdpa_tensor* dv, size_t workspace_bytes, int32_t* path) {
+  g_err.clear();
+  if (!path) return fail(SDPA_ERR_NULL, "path is required");
+  BwdArgs g;
+  const sdpa_status st = resolve_bwd(q, k, v, out, dout, mask, mask_info, scale, is_causal, nullptr, 0, nullptr, -1,
+                                     nullptr, -1, dq, dk, dv, g);
+  if (st != SDPA_OK) return st;
+  if (!bwd_mfma_supports(g)) {
+    *path = SDPA_PATH_FP32;
+    return SDPA_OK;
+  }
+  // sdpa_bwd hands the dS tiles a workspace of sdpa_bwd_workspace_bytes_ds() bytes; block info
+  // keeps the route that forms the weights again
+  const size_t need_ds = sdpa_bwd_workspace_bytes_ds(q, k, v);
+  *path = (need_ds && workspace_bytes >= need_ds && !g.a.bm_class) ? SDPA_PATH_MATRIX_CORE_STORED_DS
+                                                                    : SDPA_PATH_MATRIX_CORE;
+  return SDPA_OK;
 }
 
 size_t sdpa_decode_workspace_bytes(const sdpa_tensor* q, const sdpa_tensor* k_cache, int32_t num_splits) {

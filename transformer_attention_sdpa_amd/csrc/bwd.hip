@@ -373,7 +373,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dscale_stage2(const double* p
 
 }  // namespace
 
-bool bwd_mfma_supports(const BwdArgs& g);
 bool bwd_stores_ds(const BwdArgs& g);
 hipError_t launch_bwd_mfma_dkdv(const BwdArgs& g, hipStream_t s);
 hipError_t launch_bwd_mfma_dq(const BwdArgs& g, hipStream_t s);

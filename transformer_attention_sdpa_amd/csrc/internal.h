@@ -171,6 +171,8 @@ hipError_t launch_kv_cache_update(void* kc, void* vc, const void* kn, const void
                                   const int32_t* write_index, hipStream_t s);
 hipError_t launch_mask_info(const MaskInfoArgs& m, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& g, hipStream_t s);
+// whether the gradient runs on the matrix-core kernels (else the fp32 ones)
+bool bwd_mfma_supports(const BwdArgs& g);
 hipError_t launch_measure_mfma(int workgroups, int iters, float* sink, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t s);
 hipError_t launch_debug_allowed(const AttnArgs& a, uint8_t* out, int64_t sb, int64_t sh, int64_t sq,
