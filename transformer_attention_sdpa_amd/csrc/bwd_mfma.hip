@@ -92,6 +92,12 @@ struct Tiles {
 #pragma unroll
     for (int u = 0; u < SPT; ++u) dma16(r, dst + 8 * (NTH * u + 64 * wave), doff[u]);
   }
+  // the same through a resource `r` over the whole slice (rows past its end read zeros), row r0
+  // at byte r0_bytes of it (the caller keeps every offset within 32 bits)
+  __device__ void load_at(__amdgpu_buffer_rsrc_t r, int r0_bytes, uint16_t* dst, int wave) const {
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) dma16(r, dst + 8 * (NTH * u + 64 * wave), doff[u] + r0_bytes);
+  }
   // A operand: 32-row block rb, head-dim chunk c (16 elements), rows in perm32 order
   __device__ x8 arow(const uint16_t* t, int rb, int c, int hh) const {
     const int row = 32 * rb + nrow;
@@ -334,11 +340,26 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
   dph.init(per_head > 0 ? per_head : 1);
   auto it_head = [&](int it) { return gk * grp + (int)dph.div((uint32_t)it); };
   auto it_q0 = [&](int it) { return (qt0 + it - (int)dph.div((uint32_t)it) * per_head) * QT8; };
+  // buffer resources over one query head's Q and dO rows and its row statistics; with one
+  // query head per K/V head (grp == 1) the workgroup's resources never change, else a step
+  // builds those of its head. A step's first row enters the per-lane offsets (the host keeps
+  // Lq + 64 rows within 32-bit offsets).
+  auto q_rs = [&](int h) {
+    return make_rsrc(static_cast<const uint16_t*>(a.q) + b * a.q_sb + (int64_t)h * a.q_sh, (int64_t)a.Lq * a.q_ss * 2);
+  };
+  auto o_rs = [&](int h) {
+    return make_rsrc(static_cast<const uint16_t*>(g.dout) + b * g.do_sb + (int64_t)h * g.do_sh,
+                     (int64_t)a.Lq * g.do_ss * 2);
+  };
+  auto st_rs = [&](int h) {
+    return make_rsrc((wave == 0 ? g.w_lse : g.w_dsum) + ((int64_t)b * a.Hq + h) * a.Lq, (int64_t)a.Lq * 4);
+  };
+  const __amdgpu_buffer_rsrc_t rq0 = q_rs(gk * grp), ro0 = o_rs(gk * grp), rs0 = st_rs(gk * grp);
+  const int q_row_bytes = (int)(a.q_ss * 2), o_row_bytes = (int)(g.do_ss * 2);
   auto load_tiles = [&](int it, uint16_t* qd, uint16_t* od) {
     const int h = it_head(it), i0 = it_q0(it);
-    tq.load(static_cast<const uint16_t*>(a.q) + b * a.q_sb + h * a.q_sh, a.q_ss, i0, a.Lq, (int)(a.q_ss * 2), qd, wave);
-    to.load(static_cast<const uint16_t*>(g.dout) + b * g.do_sb + h * g.do_sh, g.do_ss, i0, a.Lq, (int)(g.do_ss * 2),
-            od, wave);
+    tq.load_at(grp == 1 ? rq0 : q_rs(h), i0 * q_row_bytes, qd, wave);
+    to.load_at(grp == 1 ? ro0 : o_rs(h), i0 * o_row_bytes, od, wave);
   };
   // statistics of the step's queries into buffer buf by direct loads, like the tiles: wave 0
   // -lse / scale of queries it_q0 .. + 63, wave 1 their -D, the start values of S and dP as the
@@ -347,10 +368,8 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
   // load in flight where the branches on the thread index met, or spill.)
   auto dma_stat = [&](int it, int buf) {
     if (wave < 2) {
-      const int i0 = it_q0(it);
-      const float* src = (wave == 0 ? g.w_lse : g.w_dsum) + ((int64_t)b * a.Hq + it_head(it)) * a.Lq + i0;
       float* dst = buf ? &stat1[wave][0] : &stat0[wave][0];
-      dma4(make_rsrc(src, (int64_t)(a.Lq - i0) * 4), reinterpret_cast<uint32_t*>(dst), lane * 4);
+      dma4(grp == 1 ? rs0 : st_rs(it_head(it)), reinterpret_cast<uint32_t*>(dst), (lane + it_q0(it)) * 4);
     }
   };
   // mask rows of step it (queries it_q0 .. + 63, keys k0 .. k0 + 127) into mraw[buf]
@@ -1182,8 +1201,10 @@ bool bwd_mfma_supports(const BwdArgs& g) {
   if (!al(g.dq, (int)(4 * eq)) || !al(g.dk, (int)(4 * ek)) || !al(g.dv, (int)(4 * ev))) return false;
   if ((g.dq_sb | g.dq_ss | g.dq_sh | g.dk_sb | g.dk_ss | g.dk_sh | g.dv_sb | g.dv_ss | g.dv_sh) & 3) return false;
   if (a.q_ss < a.D || a.k_ss < a.D || a.v_ss < a.D || g.do_ss < a.D) return false;
-  if ((int64_t)a.Lq * a.q_ss * 2 > INT32_MAX || (int64_t)a.Lkv * a.k_ss * 2 > INT32_MAX ||
-      (int64_t)a.Lkv * a.v_ss * 2 > INT32_MAX || (int64_t)a.Lq * g.do_ss * 2 > INT32_MAX)
+  // (the dK/dV pass adds a step's first row to offsets within its 64-row tiles)
+  if (((int64_t)a.Lq + QT8) * a.q_ss * 2 > INT32_MAX || (int64_t)a.Lkv * a.k_ss * 2 > INT32_MAX ||
+      (int64_t)a.Lkv * a.v_ss * 2 > INT32_MAX || ((int64_t)a.Lq + QT8) * g.do_ss * 2 > INT32_MAX ||
+      ((int64_t)a.Lq + QT8) * 4 > INT32_MAX)
     return false;
   const int64_t n1 = (int64_t)((a.Lkv + RB - 1) / RB) * a.Hkv * a.B, n2 = (int64_t)((a.Lq + RB - 1) / RB) * a.Hq * a.B;
   return n1 < (int64_t)INT32_MAX && n2 < (int64_t)INT32_MAX;
