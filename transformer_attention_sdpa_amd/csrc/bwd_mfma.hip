@@ -523,10 +523,30 @@ __global__ __launch_bounds__(NT8, 1) void bwd_dkdv8_kernel(BwdArgs g, int remap)
           for (int e = 0; e < 16; ++e) s[e] = e >= e_min ? s[e] : -INFINITY;
         }
       }
+      if constexpr (MK == MK_NONE) {
+        // the four operands of head-dim chunk c + 1 are read while chunk c's two products run
+        // (the masked variants' extra registers would spill)
+        x8 fa[2][4];
+        auto rd = [&](int c, int buf) {
+          fa[buf][0] = tq.arow(qs, qp, c, hh);
+          fa[buf][1] = bkv(kbuf, c);
+          fa[buf][2] = to.arow(os, qp, c, hh);
+          fa[buf][3] = bkv(vbuf, c);
+        };
+        rd(0, 0);
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        s = E::mfma(tq.arow(qs, qp, c, hh), bkv(kbuf, c), s);
-        dp = E::mfma(to.arow(os, qp, c, hh), bkv(vbuf, c), dp);
+        for (int c = 0; c < DC; ++c) {
+          if (c + 1 < DC) rd(c + 1, (c + 1) & 1);
+          s = E::mfma(fa[c & 1][0], fa[c & 1][1], s);
+          dp = E::mfma(fa[c & 1][2], fa[c & 1][3], dp);
+          __builtin_amdgcn_sched_barrier(0);           // keeps the next chunk's reads ahead
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          s = E::mfma(tq.arow(qs, qp, c, hh), bkv(kbuf, c), s);
+          dp = E::mfma(to.arow(os, qp, c, hh), bkv(vbuf, c), dp);
+        }
       }
       uint32_t valid = 0;                             // masked: bit e set where query e keeps this key
       if constexpr (MK != MK_NONE) {
